@@ -1,0 +1,155 @@
+"""Benchmark: DM0-base suffix denoise (28 layers, 10 Euler steps, chunk 50, 816-token prefix KV,
+bf16 weights/activations, fp32 accumulation) on one MI355X, through the C ABI.
+
+A "step" is one action chunk: one replay of the captured hipGraph that runs all 10 Euler steps
+(time embedding + action_in_proj, 28 merged-attention layers over the cached prefix,
+action_out_proj + Euler update) for the batch.  Inputs are resident in HBM before timing.
+
+Prints one JSON line: chunks/s (whole job), p50/p90/p99 chunk latency, the roofline of the
+dominant kernel, and the float64 oracle timed on the host cores as a CPU baseline.
+
+  python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config 3|4] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(wl, lens):
+    """Bytes and FLOPs of one chunk: every weight byte and every visible prefix K/V byte once per
+    Euler step, plus x in and out; GEMM FLOPs 2*params*tokens, attention 4*D*Hq per unmasked
+    (query, key) pair."""
+    s = wl.shape
+    es = 2 if s.dtype == "bf16" else 4
+    H, F, D, Hq, Hkv, S, A, L = (s.act_hidden, s.act_ffn, s.head_dim, s.n_q_heads, s.n_kv_heads, s.chunk,
+                                 s.action_dim, s.n_layers)
+    mat = (s.qkv_rows * H + H * Hq * D + 2 * F * H + H * F) * L
+    vec = (2 * H * L + H * A + H + H + A * H + A) * 4          # norms, in/out projections and biases (fp32)
+    kv = int(np.sum(lens)) * L * Hkv * D * 2 * es
+    x_io = wl.batch * S * A * 4 * 2
+    per_step_bytes = mat * es + vec + kv + x_io
+    tokens = wl.batch * S
+    gemm = 2 * mat * tokens + 2 * (2 * A * H) * tokens
+    attn = sum(4 * D * Hq * S * (int(p) + S) for p in lens) * L
+    return {"bytes": per_step_bytes * wl.steps, "flops": (gemm + attn) * wl.steps,
+            "weight_bytes_per_step": mat * es + vec, "kv_bytes_per_step": kv}
+
+
+def cpu_baseline(wl, aw, kc, vc, x1, lens):
+    """The oracle as it stands (float64 numpy), one full chunk of sample 0."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    P = int(lens[0])
+    t0 = time.perf_counter()
+    O.suffix_denoise(x1[0], aw, kc[:, 0, :, :P], vc[:, 0, :, :P], wl.shape, wl.steps)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "chunks/s", "cores": blas_threads or cores, "kind": "oracle",
+            "sample": f"one full chunk of sample 0 ({wl.steps} Euler steps x {wl.shape.n_layers} layers, "
+                      f"P={P}) in float64 numpy; {dt:.2f} s on {cores} host cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, choices=[3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the suffix denoise path is built for a single MI355X "
+              f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dual_expert_merged_amd import binding as bd
+    from dual_expert_merged_amd import inputs
+    from dual_expert_merged_amd.configs import workload
+
+    wl = workload(args.config)
+    s = wl.shape
+    log(f"[bench] generating inputs for: {wl.name}")
+    aw = inputs.make_action_weights(wl)
+    kc, vc = inputs.make_kv_cache(wl)
+    x1 = inputs.make_noise(wl)
+    lens = inputs.make_prefix_lens(wl)
+
+    torch.cuda.set_device(0)
+    ctx = bd.Context(s, 0)
+    td = bd.torch_dtype(s.dtype)
+    da = bd.DeviceAction(aw, s.dtype)
+    k = bd.to_device(kc, td)
+    v = bd.to_device(vc, td)
+    ld = torch.from_numpy(lens).cuda()
+    x0 = torch.from_numpy(x1).cuda()
+    x = x0.clone()
+    ws = ctx.workspace(bd.OP_DENOISE, wl.batch, wl.prefix_len)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        plan = ctx.denoise_plan(da, k, v, ld, x, wl.steps, ws, stream=stream)
+        log(f"[bench] plan captured; warmup {args.warmup}")
+        for _ in range(args.warmup):
+            plan.launch(stream=stream)
+        stream.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            starts[i].record(stream)
+            plan.launch(stream=stream)
+            ends[i].record(stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    lat = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])  # ms per chunk, GPU clock
+    alg = algorithmic(wl, lens)
+    ms = wall * 1e3 / args.steps
+    value = wl.batch * args.steps / wall
+    chunk_s = float(np.mean(lat)) * 1e-3
+    achieved = alg["bytes"] / chunk_s / 1e9
+    roof = {"bound": "hbm", "kernel": "denoise graph replay (all kernels of one chunk)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": alg["bytes"],
+            "mfma_frac": round(alg["flops"] / chunk_s / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    out = {
+        "metric": "action chunks/s + p50 chunk latency (DM0-base suffix, 10 steps); % HBM/MFMA peak",
+        "value": round(value, 2), "unit": "chunks/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": s.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "prefix_len": int(lens.max()),
+                   "prefix_len_mean": float(lens.mean()), "chunk": s.chunk, "action_dim": s.action_dim,
+                   "euler_steps": wl.steps, "layers": s.n_layers, "parallelism": "single GPU"},
+        "latency_ms": {"p50": round(float(np.percentile(lat, 50)), 4), "p90": round(float(np.percentile(lat, 90)), 4),
+                       "p99": round(float(np.percentile(lat, 99)), 4), "mean": round(float(np.mean(lat)), 4)},
+        "roofline": roof,
+    }
+    plan.close()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host cores")
+        out["cpu_baseline"] = cpu_baseline(wl, aw, kc, vc, x1, lens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,271 @@
+// Merged grouped-query attention on gfx950 MFMA.
+// Page "DM0 paper definition vs. Dexbotic code", section 1: the two experts' Q/K/V are joined
+// along the sequence for one attention (16 query heads over 8 KV heads).  With the block mask,
+// a prefix query sees the sample's P_b prefix keys and an action query sees those plus all S
+// action keys; page "DM0.5: High-Performance Embodied VLA ...", section 5.1: the prefix keys
+// are the cached VLM K/V, so the kernel streams them straight from the cache layout
+// [B][Hkv][P_cap][D] followed by the action keys [B][Hkv][S][D], never concatenating them.
+//
+// One 256-thread workgroup takes one (sample, KV head, query block, key chunk): 128 query
+// slots = the G query heads of the KV head x 128/G query rows, 32 slots per wave.  Key tiles
+// of 32 rows stage through LDS (K row-major, V transposed).  Scores are formed transposed,
+// S^T = K Q^T, so that every lane owns one query column: the online-softmax statistics stay
+// in-lane (plus two cross-lane-group exchanges) and the probabilities are already laid out as
+// the B operand of O^T = V^T P^T.  The key rows of each 16-key score tile are permuted so a
+// lane's probabilities are consecutive keys of the next MFMA's contraction chunk.
+// Softmax runs in float32 with base-2 exponentials (scores pre-scaled by log2(e)/sqrt(D)).
+// With several key chunks, each writes unnormalised (O, m, l) and attn_combine merges them.
+#include "common.h"
+#include "kernels.h"
+
+namespace dm {
+
+constexpr int ATT_SLOTS = 128;
+constexpr int ATT_KT = 32;
+
+int attn_qblocks(int q_rows, int Hq, int Hkv) {
+  const int rph = ATT_SLOTS / (Hq / Hkv);
+  return (q_rows + rph - 1) / rph;
+}
+size_t attn_partial_bytes(int B, int Hkv, int n_qblocks, int n_chunks, int D) {
+  return (size_t)B * Hkv * n_qblocks * n_chunks * ATT_SLOTS * (D + 2) * sizeof(float);
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  typedef Mfma<T> MF;
+  typedef typename MF::frag frag;
+  constexpr int EPL = MF::EPL, KC = 4 * EPL;
+  constexpr int DC = D / KC;       // contraction chunks of Q K^T
+  constexpr int DT = D / 16;       // 16-row tiles of O^T
+  constexpr int NPV = ATT_KT / KC; // contraction chunks of V^T P^T per key tile
+  constexpr int SUB = EPL / 4;     // 16-key score tiles per P^T chunk
+  constexpr int RPH = ATT_SLOTS / G;
+  constexpr int KLD = D + EPL, VLD = ATT_KT + EPL;
+  __shared__ __attribute__((aligned(16))) T Ks[ATT_KT * KLD];
+  __shared__ __attribute__((aligned(16))) T Vt[D * VLD];
+
+  const T *__restrict__ q = (const T *)a.q;
+  const T *__restrict__ kp = (const T *)a.kp;
+  const T *__restrict__ vp = (const T *)a.vp;
+  const T *__restrict__ ks = (const T *)a.ks;
+  const T *__restrict__ vs = (const T *)a.vs;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int chunk = blockIdx.x, qb = blockIdx.y, bk = blockIdx.z;
+  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+  const int P = max(0, min(a.lens[b], a.kp_rows));
+  const int nq = a.suffix ? a.S : P;
+  const int nkeys = P + (a.suffix ? a.S : 0);
+  const int k_begin = chunk * a.chunk_keys;
+  const int k_end = min(nkeys, k_begin + a.chunk_keys);
+  if (qb * RPH >= nq || k_begin >= k_end) return;  // uniform over the workgroup
+
+  const int slot0 = wave * 32;
+  const int h = kvh * G + slot0 / RPH;
+  const int r0 = qb * RPH + (slot0 % RPH);
+  const int HD = a.Hq * D;
+
+  frag qf[2][DC];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int row = r0 + qt * 16 + c16;
+    const T *qrow = q + (size_t)(b * a.q_rows_per_b + (row < nq ? row : 0)) * HD + h * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      qf[qt][dc] = row < nq ? load_frag<T>(qrow + dc * KC + g * EPL) : zero_frag<T>();
+  }
+
+  f32x4 o[2][DT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  const float sc = 1.4426950408889634f / sqrtf((float)D);
+
+  const size_t pre_base = (size_t)(b * a.Hkv + kvh) * a.kp_rows * D;
+  const size_t suf_base = (size_t)(b * a.Hkv + kvh) * a.S * D;
+  constexpr int VPRW = D / EPL;  // 16-byte vectors per key row
+
+  for (int kt0 = k_begin; kt0 < k_end; kt0 += ATT_KT) {
+    __syncthreads();
+    for (int idx = tid; idx < ATT_KT * VPRW; idx += 256) {
+      const int r = idx / VPRW, cv = idx - r * VPRW;
+      const int key = kt0 + r;
+      frag kv = zero_frag<T>(), vv = zero_frag<T>();
+      if (key < k_end) {
+        const T *ksrc, *vsrc;
+        if (key < P) {
+          ksrc = kp + pre_base + (size_t)key * D;
+          vsrc = vp + pre_base + (size_t)key * D;
+        } else {
+          ksrc = ks + suf_base + (size_t)(key - P) * D;
+          vsrc = vs + suf_base + (size_t)(key - P) * D;
+        }
+        kv = load_frag<T>(ksrc + cv * EPL);
+        vv = load_frag<T>(vsrc + cv * EPL);
+      }
+      *reinterpret_cast<frag *>(&Ks[r * KLD + cv * EPL]) = kv;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) Vt[(cv * EPL + e) * VLD + r] = vv[e];
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      f32x4 st[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int pv = s / SUB, kk = s % SUB;
+        const int krow = pv * KC + (c16 >> 2) * EPL + 4 * kk + (c16 & 3);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+          acc = MF::mma(*reinterpret_cast<const frag *>(&Ks[krow * KLD + dc * KC + g * EPL]), qf[qt][dc], acc);
+        st[s] = acc;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int pv = s / SUB, kk = s % SUB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kt0 + pv * KC + g * EPL + 4 * kk + i;
+          const float v = key < k_end ? st[s][i] * sc : -INFINITY;
+          st[s][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+      const float m_new = fmaxf(m[qt], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m[qt] - m_use);
+      float sum = 0.f;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2f(st[s][i] - m_use);
+          st[s][i] = p;
+          sum += p;
+        }
+      sum += __shfl_xor(sum, 16, WAVE);
+      sum += __shfl_xor(sum, 32, WAVE);
+      l[qt] = l[qt] * alpha + sum;
+      m[qt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
+#pragma unroll
+      for (int pv = 0; pv < NPV; ++pv) {
+        frag pf;
+#pragma unroll
+        for (int kk = 0; kk < SUB; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pf[kk * 4 + i] = from_f32<T>(st[pv * SUB + kk][i]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          o[qt][dt] = MF::mma(*reinterpret_cast<const frag *>(&Vt[(dt * 16 + c16) * VLD + pv * KC + g * EPL]),
+                              pf, o[qt][dt]);
+      }
+    }
+  }
+
+  if (a.n_chunks == 1) {
+    T *out = (T *)a.out;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int row = r0 + qt * 16 + c16;
+      if (row >= nq) continue;
+      const float inv = 1.0f / l[qt];
+      T *orow = out + (size_t)(b * a.q_rows_per_b + row) * HD + h * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) orow[dt * 16 + 4 * g + i] = from_f32<T>(o[qt][dt][i] * inv);
+    }
+  } else {
+    const int nqb = gridDim.y;
+    float *pp = a.part + (((size_t)bk * nqb + qb) * a.n_chunks + chunk) * ATT_SLOTS * (D + 2);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int row = r0 + qt * 16 + c16;
+      if (row >= nq) continue;
+      const int slot = slot0 + qt * 16 + c16;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4 *>(&pp[slot * D + dt * 16 + 4 * g]) = o[qt][dt];
+      if (g == 0) {
+        pp[ATT_SLOTS * D + slot * 2] = m[qt];
+        pp[ATT_SLOTS * D + slot * 2 + 1] = l[qt];
+      }
+    }
+  }
+}
+
+// Merge the key chunks of every query slot: O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int rph) {
+  const int qb = blockIdx.x, bk = blockIdx.y;
+  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+  const int P = max(0, min(a.lens[b], a.kp_rows));
+  const int nq = a.suffix ? a.S : P;
+  const int nkeys = P + (a.suffix ? a.S : 0);
+  const int nch = (nkeys + a.chunk_keys - 1) / a.chunk_keys;
+  const int slot = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int row = qb * rph + slot % rph;
+  if (row >= nq) return;
+  const int h = kvh * (ATT_SLOTS / rph) + slot / rph;
+  const float *pp = a.part + ((size_t)bk * gridDim.x + qb) * a.n_chunks * ATT_SLOTS * (D + 2);
+  const size_t cstride = (size_t)ATT_SLOTS * (D + 2);
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, pp[c * cstride + ATT_SLOTS * D + slot * 2]);
+  float L = 0.f;
+  for (int c = 0; c < nch; ++c)
+    L += exp2f(pp[c * cstride + ATT_SLOTS * D + slot * 2] - M) * pp[c * cstride + ATT_SLOTS * D + slot * 2 + 1];
+  const float inv = 1.0f / L;
+  T *orow = (T *)a.out + (size_t)(b * a.q_rows_per_b + row) * a.Hq * D + h * D;
+  constexpr int HALF = D / 2;
+  float acc[HALF];
+#pragma unroll
+  for (int d = 0; d < HALF; ++d) acc[d] = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const float w = exp2f(pp[c * cstride + ATT_SLOTS * D + slot * 2] - M);
+    const float *op = pp + c * cstride + slot * D + half * HALF;
+#pragma unroll
+    for (int d = 0; d < HALF; ++d) acc[d] += w * op[d];
+  }
+#pragma unroll
+  for (int d = 0; d < HALF; ++d) orow[half * HALF + d] = from_f32<T>(acc[d] * inv);
+}
+
+template <typename T, int D, int G> static void attn_t(const AttnArgs &a, hipStream_t s) {
+  const int q_rows = a.suffix ? a.S : a.kp_rows;
+  const int nqb = attn_qblocks(q_rows, a.Hq, a.Hkv);
+  dim3 grid(a.n_chunks, nqb, a.B * a.Hkv);
+  hipLaunchKernelGGL((attn_kernel<T, D, G>), grid, dim3(256), 0, s, a);
+  if (a.n_chunks > 1)
+    hipLaunchKernelGGL((attn_combine<T, D>), dim3(nqb, a.B * a.Hkv), dim3(256), 0, s, a, ATT_SLOTS / G);
+}
+
+template <typename T, int D> static void attn_g(const AttnArgs &a, hipStream_t s) {
+  switch (a.Hq / a.Hkv) {
+    case 1: attn_t<T, D, 1>(a, s); break;
+    case 2: attn_t<T, D, 2>(a, s); break;
+    default: attn_t<T, D, 4>(a, s); break;
+  }
+}
+template <typename T> static void attn_d(const AttnArgs &a, hipStream_t s) {
+  switch (a.D) {
+    case 32: attn_g<T, 32>(a, s); break;
+    case 64: attn_g<T, 64>(a, s); break;
+    default: attn_g<T, 128>(a, s); break;
+  }
+}
+void launch_attention(Dt dt, const AttnArgs &a, hipStream_t s) {
+  if (dt == DT_BF16) attn_d<bf16>(a, s); else attn_d<float>(a, s);
+}
+
+}  // namespace dm

@@ -1,0 +1,90 @@
+"""The C-ABI library: it loads, exports every entry point include/dm.h declares, and rejects bad
+arguments on the host before any HIP call (CPU only: no compute call is made)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from dual_expert_merged_amd import binding as bd
+from dual_expert_merged_amd.configs import DM0_BASE, TINY
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "dm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("dm_prefill_kv", "dm_merged_layer", "dm_suffix_denoise", "dm_denoise_plan_create",
+                     "dm_denoise_plan_launch", "dm_denoise_plan_destroy"):
+        assert required in names
+    assert sorted(bd.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bd.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert b"gfx950" in lib.dm_version()
+
+
+def _cfg(**kw):
+    c = bd.make_config(TINY)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 48, bd.DM_ERR_UNSUPPORTED),
+    ("n_kv_heads", 3, bd.DM_ERR_SHAPE),
+    ("act_hidden", 100, bd.DM_ERR_SHAPE),
+    ("vlm_ffn", 0, bd.DM_ERR_SHAPE),
+    ("action_dim", 65, bd.DM_ERR_UNSUPPORTED),
+    ("chunk", 0, bd.DM_ERR_UNSUPPORTED),
+    ("dtype", 7, bd.DM_ERR_UNSUPPORTED),
+    ("vlm_mlp_dtype", bd.DM_FP8_E4M3, bd.DM_ERR_UNSUPPORTED),  # FP8 MLP needs a bf16 model
+    ("rms_eps", 0.0, bd.DM_ERR_INVALID_ARG),
+    ("n_layers", 0, bd.DM_ERR_SHAPE),
+])
+def test_bad_config_rejected_before_any_hip_call(field, value, status):
+    lib = bd.lib()
+    h = C.c_void_p()
+    cfg = _cfg(**{field: value})
+    assert lib.dm_ctx_create(C.byref(cfg), 0, C.byref(h)) == status
+    assert not h.value
+    assert len(lib.dm_last_error()) > 0
+
+
+def test_null_arguments_rejected():
+    lib = bd.lib()
+    assert lib.dm_ctx_create(None, 0, None) == bd.DM_ERR_INVALID_ARG
+    assert lib.dm_workspace_bytes(None, bd.OP_DENOISE, 1, 816) == 0
+    assert lib.dm_suffix_denoise(None, None, None, None, None, 1, 816, None, 10, None, 0, None) == bd.DM_ERR_INVALID_ARG
+    assert lib.dm_prefill_kv(None, None, None, None, 1, 816, None, None, None, 0, None) == bd.DM_ERR_INVALID_ARG
+    assert lib.dm_merged_layer(None, None, None, 0, None, None, None, 1, 816, None, None, None, 0,
+                               None) == bd.DM_ERR_INVALID_ARG
+    assert lib.dm_denoise_plan_launch(None, 10, None) == bd.DM_ERR_INVALID_ARG
+    assert lib.dm_quantize_fp8_rows(None, None, None, 4, 4, None) == bd.DM_ERR_INVALID_ARG
+    assert b"NULL" in lib.dm_last_error()
+    lib.dm_ctx_destroy(None)
+    lib.dm_denoise_plan_destroy(None)
+
+
+def test_dm0_base_config_is_accepted_by_validation():
+    # a good config fails only at the device query on a machine without a GPU
+    lib = bd.lib()
+    h = C.c_void_p()
+    cfg = bd.make_config(DM0_BASE)
+    st = lib.dm_ctx_create(C.byref(cfg), 0, C.byref(h))
+    if st == bd.DM_OK:
+        lib.dm_ctx_destroy(h)
+    else:
+        assert st == bd.DM_ERR_HIP or st == bd.DM_ERR_INVALID_ARG, st
+        assert b"hipGetDeviceCount" in lib.dm_last_error() or b"device" in lib.dm_last_error()
