@@ -7,28 +7,37 @@
 // [B][Hkv][P_cap][D] followed by the action keys [B][Hkv][S][D], never concatenating them.
 //
 // One 256-thread workgroup takes one (sample, KV head, query block, key chunk): 128 query
-// slots = the G query heads of the KV head x 128/G query rows, 32 slots per wave.  Key tiles
-// of 32 rows stage through LDS (K row-major, V transposed).  Scores are formed transposed,
-// S^T = K Q^T, so that every lane owns one query column: the online-softmax statistics stay
-// in-lane (plus two cross-lane-group exchanges) and the probabilities are already laid out as
-// the B operand of O^T = V^T P^T.  The key rows of each 16-key score tile are permuted so a
-// lane's probabilities are consecutive keys of the next MFMA's contraction chunk.
-// Softmax runs in float32 with base-2 exponentials (scores pre-scaled by log2(e)/sqrt(D)).
-// With several key chunks, each writes unnormalised (O, m, l) and attn_combine merges them.
+// slots = the G query heads of the KV head x 128/G query rows, 32 slots per wave.  Keys stage
+// through LDS 128 at a time (K row-major, V transposed), every load of a stage issued before the
+// first is consumed.  Scores are formed transposed, S^T = K Q^T, so every lane owns one query
+// column: the online-softmax statistics stay in-lane (plus two cross-lane-group exchanges) and
+// the probabilities already sit in the B-operand layout of O^T = V^T P^T.  The key rows of each
+// 16-key score tile are permuted so a lane's probabilities are consecutive keys of the next
+// MFMA's contraction chunk.  Softmax is float32 with base-2 exponentials (scores pre-scaled by
+// log2(e)/sqrt(D)).
+// With several key chunks, each workgroup stores its normalised partial output (weight dtype)
+// with its running max and sum; the last workgroup of a (sample, KV head, query block) to arrive
+// merges them in chunk order, so the result does not depend on scheduling.
 #include "common.h"
 #include "kernels.h"
 
 namespace dm {
 
 constexpr int ATT_SLOTS = 128;
-constexpr int ATT_KT = 32;
+constexpr int ATT_KT = 32;   // keys per MFMA score tile pair
+constexpr int ATT_CH = 128;  // keys staged in LDS per pass
 
 int attn_qblocks(int q_rows, int Hq, int Hkv) {
   const int rph = ATT_SLOTS / (Hq / Hkv);
   return (q_rows + rph - 1) / rph;
 }
-size_t attn_partial_bytes(int B, int Hkv, int n_qblocks, int n_chunks, int D) {
-  return (size_t)B * Hkv * n_qblocks * n_chunks * ATT_SLOTS * (D + 2) * sizeof(float);
+__host__ __device__ static size_t part_o_elems(int B, int Hkv, int nqb, int n_chunks, int D) {
+  return (size_t)B * Hkv * nqb * n_chunks * ATT_SLOTS * D;
+}
+size_t attn_partial_bytes(Dt dt, int B, int Hkv, int nqb, int n_chunks, int D) {
+  const size_t o = part_o_elems(B, Hkv, nqb, n_chunks, D) * (dt == DT_BF16 ? 2 : 4);
+  const size_t ml = (size_t)B * Hkv * nqb * n_chunks * ATT_SLOTS * 2 * sizeof(float);
+  return ((o + 255) & ~(size_t)255) + ml;
 }
 
 template <typename T, int D, int G>
@@ -38,12 +47,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int EPL = MF::EPL, KC = 4 * EPL;
   constexpr int DC = D / KC;       // contraction chunks of Q K^T
   constexpr int DT = D / 16;       // 16-row tiles of O^T
-  constexpr int NPV = ATT_KT / KC; // contraction chunks of V^T P^T per key tile
+  constexpr int NPV = ATT_KT / KC; // contraction chunks of V^T P^T per 32-key tile
   constexpr int SUB = EPL / 4;     // 16-key score tiles per P^T chunk
   constexpr int RPH = ATT_SLOTS / G;
-  constexpr int KLD = D + EPL, VLD = ATT_KT + EPL;
-  __shared__ __attribute__((aligned(16))) T Ks[ATT_KT * KLD];
+  constexpr int KLD = D + EPL, VLD = ATT_CH + EPL;
+  constexpr int VPRW = D / EPL;                     // 16-byte vectors per key row
+  constexpr int LPT = ATT_CH * VPRW / 256;          // vectors per thread per stage
+  __shared__ __attribute__((aligned(16))) T Ks[ATT_CH * KLD];
   __shared__ __attribute__((aligned(16))) T Vt[D * VLD];
+  __shared__ int s_last;
 
   const T *__restrict__ q = (const T *)a.q;
   const T *__restrict__ kp = (const T *)a.kp;
@@ -53,122 +65,134 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int chunk = blockIdx.x, qb = blockIdx.y, bk = blockIdx.z;
+  const int chunk = blockIdx.x, qb = blockIdx.y, bk = blockIdx.z, nqb = gridDim.y;
   const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
   const int P = max(0, min(a.lens[b], a.kp_rows));
   const int nq = a.suffix ? a.S : P;
   const int nkeys = P + (a.suffix ? a.S : 0);
+  const int nch = (nkeys + a.chunk_keys - 1) / a.chunk_keys;  // chunks holding keys
   const int k_begin = chunk * a.chunk_keys;
   const int k_end = min(nkeys, k_begin + a.chunk_keys);
-  if (qb * RPH >= nq || k_begin >= k_end) return;  // uniform over the workgroup
+  if (qb * RPH >= nq) return;  // no query rows here: uniform, and no merge is needed
 
   const int slot0 = wave * 32;
   const int h = kvh * G + slot0 / RPH;
   const int r0 = qb * RPH + (slot0 % RPH);
   const int HD = a.Hq * D;
+  const size_t grp = (size_t)bk * nqb + qb;
+  T *part_o = (T *)a.part;
+  float *part_ml = (float *)((char *)a.part + ((part_o_elems(a.B, a.Hkv, nqb, a.n_chunks, D) * sizeof(T) + 255) &
+                                               ~(size_t)255));
 
-  frag qf[2][DC];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int row = r0 + qt * 16 + c16;
-    const T *qrow = q + (size_t)(b * a.q_rows_per_b + (row < nq ? row : 0)) * HD + h * D;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-      qf[qt][dc] = row < nq ? load_frag<T>(qrow + dc * KC + g * EPL) : zero_frag<T>();
-  }
-
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   f32x4 o[2][DT];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  const float sc = 1.4426950408889634f / sqrtf((float)D);
 
-  const size_t pre_base = (size_t)(b * a.Hkv + kvh) * a.kp_rows * D;
-  const size_t suf_base = (size_t)(b * a.Hkv + kvh) * a.S * D;
-  constexpr int VPRW = D / EPL;  // 16-byte vectors per key row
-
-  for (int kt0 = k_begin; kt0 < k_end; kt0 += ATT_KT) {
-    __syncthreads();
-    for (int idx = tid; idx < ATT_KT * VPRW; idx += 256) {
-      const int r = idx / VPRW, cv = idx - r * VPRW;
-      const int key = kt0 + r;
-      frag kv = zero_frag<T>(), vv = zero_frag<T>();
-      if (key < k_end) {
-        const T *ksrc, *vsrc;
-        if (key < P) {
-          ksrc = kp + pre_base + (size_t)key * D;
-          vsrc = vp + pre_base + (size_t)key * D;
-        } else {
-          ksrc = ks + suf_base + (size_t)(key - P) * D;
-          vsrc = vs + suf_base + (size_t)(key - P) * D;
-        }
-        kv = load_frag<T>(ksrc + cv * EPL);
-        vv = load_frag<T>(vsrc + cv * EPL);
-      }
-      *reinterpret_cast<frag *>(&Ks[r * KLD + cv * EPL]) = kv;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) Vt[(cv * EPL + e) * VLD + r] = vv[e];
-    }
-    __syncthreads();
-
+  if (k_begin < k_end) {
+    frag qf[2][DC];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      f32x4 st[2];
+      const int row = r0 + qt * 16 + c16;
+      const T *qrow = q + (size_t)(b * a.q_rows_per_b + (row < nq ? row : 0)) * HD + h * D;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int pv = s / SUB, kk = s % SUB;
-        const int krow = pv * KC + (c16 >> 2) * EPL + 4 * kk + (c16 & 3);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int dc = 0; dc < DC; ++dc)
+        qf[qt][dc] = row < nq ? load_frag<T>(qrow + dc * KC + g * EPL) : zero_frag<T>();
+    }
+    const float sc = 1.4426950408889634f / sqrtf((float)D);
+    const size_t pre_base = (size_t)(b * a.Hkv + kvh) * a.kp_rows * D;
+    const size_t suf_base = (size_t)(b * a.Hkv + kvh) * a.S * D;
+
+    for (int ks0 = k_begin; ks0 < k_end; ks0 += ATT_CH) {
+      frag kv[LPT], vv[LPT];
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-          acc = MF::mma(*reinterpret_cast<const frag *>(&Ks[krow * KLD + dc * KC + g * EPL]), qf[qt][dc], acc);
-        st[s] = acc;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int pv = s / SUB, kk = s % SUB;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kt0 + pv * KC + g * EPL + 4 * kk + i;
-          const float v = key < k_end ? st[s][i] * sc : -INFINITY;
-          st[s][i] = v;
-          mx = fmaxf(mx, v);
+      for (int v = 0; v < LPT; ++v) {
+        const int idx = tid + v * 256;
+        const int r = idx / VPRW, cv = idx - r * VPRW;
+        const int key = ks0 + r;
+        kv[v] = zero_frag<T>();
+        vv[v] = zero_frag<T>();
+        if (key < k_end) {
+          const size_t off = key < P ? pre_base + (size_t)key * D : suf_base + (size_t)(key - P) * D;
+          const T *kb = key < P ? kp : ks;
+          const T *vb = key < P ? vp : vs;
+          kv[v] = load_frag<T>(kb + off + cv * EPL);
+          vv[v] = load_frag<T>(vb + off + cv * EPL);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      const float m_new = fmaxf(m[qt], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m[qt] - m_use);
-      float sum = 0.f;
+      __syncthreads();  // the previous stage is consumed
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int v = 0; v < LPT; ++v) {
+        const int idx = tid + v * 256;
+        const int r = idx / VPRW, cv = idx - r * VPRW;
+        *reinterpret_cast<frag *>(&Ks[r * KLD + cv * EPL]) = kv[v];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(st[s][i] - m_use);
-          st[s][i] = p;
-          sum += p;
+        for (int e = 0; e < EPL; ++e) Vt[(cv * EPL + e) * VLD + r] = vv[v][e];
+      }
+      __syncthreads();
+
+      const int stage_keys = min(ATT_CH, k_end - ks0);
+      for (int t0 = 0; t0 < stage_keys; t0 += ATT_KT) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x4 st[2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int pv = s / SUB, kk = s % SUB;
+            const int krow = t0 + pv * KC + (c16 >> 2) * EPL + 4 * kk + (c16 & 3);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc)
+              acc = MF::mma(*reinterpret_cast<const frag *>(&Ks[krow * KLD + dc * KC + g * EPL]), qf[qt][dc], acc);
+            st[s] = acc;
+          }
+          float mx = -INFINITY;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int pv = s / SUB, kk = s % SUB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = ks0 + t0 + pv * KC + g * EPL + 4 * kk + i;
+              const float v = key < k_end ? st[s][i] * sc : -INFINITY;
+              st[s][i] = v;
+              mx = fmaxf(mx, v);
+            }
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+          const float m_new = fmaxf(m[qt], mx);
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;
+          const float alpha = exp2f(m[qt] - m_use);
+          float sum = 0.f;
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float p = exp2f(st[s][i] - m_use);
+              st[s][i] = p;
+              sum += p;
+            }
+          sum += __shfl_xor(sum, 16, WAVE);
+          sum += __shfl_xor(sum, 32, WAVE);
+          l[qt] = l[qt] * alpha + sum;
+          m[qt] = m_new;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
+#pragma unroll
+          for (int pv = 0; pv < NPV; ++pv) {
+            frag pf;
+#pragma unroll
+            for (int kk = 0; kk < SUB; ++kk)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) pf[kk * 4 + i] = from_f32<T>(st[pv * SUB + kk][i]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+              o[qt][dt] = MF::mma(*reinterpret_cast<const frag *>(&Vt[(dt * 16 + c16) * VLD + t0 + pv * KC + g * EPL]),
+                                  pf, o[qt][dt]);
+          }
         }
-      sum += __shfl_xor(sum, 16, WAVE);
-      sum += __shfl_xor(sum, 32, WAVE);
-      l[qt] = l[qt] * alpha + sum;
-      m[qt] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
-#pragma unroll
-      for (int pv = 0; pv < NPV; ++pv) {
-        frag pf;
-#pragma unroll
-        for (int kk = 0; kk < SUB; ++kk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pf[kk * 4 + i] = from_f32<T>(st[pv * SUB + kk][i]);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          o[qt][dt] = MF::mma(*reinterpret_cast<const frag *>(&Vt[(dt * 16 + c16) * VLD + pv * KC + g * EPL]),
-                              pf, o[qt][dt]);
       }
     }
   }
@@ -186,59 +210,64 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) orow[dt * 16 + 4 * g + i] = from_f32<T>(o[qt][dt][i] * inv);
     }
-  } else {
-    const int nqb = gridDim.y;
-    float *pp = a.part + (((size_t)bk * nqb + qb) * a.n_chunks + chunk) * ATT_SLOTS * (D + 2);
+    return;
+  }
+
+  // several chunks: publish this chunk's normalised output and statistics
+  if (chunk < nch) {
+    T *po = part_o + (grp * a.n_chunks + chunk) * ATT_SLOTS * D;
+    float *pml = part_ml + (grp * a.n_chunks + chunk) * ATT_SLOTS * 2;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int row = r0 + qt * 16 + c16;
       if (row >= nq) continue;
       const int slot = slot0 + qt * 16 + c16;
+      const float inv = 1.0f / l[qt];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<f32x4 *>(&pp[slot * D + dt * 16 + 4 * g]) = o[qt][dt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) po[slot * D + dt * 16 + 4 * g + i] = from_f32<T>(o[qt][dt][i] * inv);
       if (g == 0) {
-        pp[ATT_SLOTS * D + slot * 2] = m[qt];
-        pp[ATT_SLOTS * D + slot * 2 + 1] = l[qt];
+        pml[slot * 2] = m[qt];
+        pml[slot * 2 + 1] = l[qt];
       }
     }
   }
-}
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.counters[grp], 1u) == (unsigned)(a.n_chunks - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
 
-// Merge the key chunks of every query slot: O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int rph) {
-  const int qb = blockIdx.x, bk = blockIdx.y;
-  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
-  const int P = max(0, min(a.lens[b], a.kp_rows));
-  const int nq = a.suffix ? a.S : P;
-  const int nkeys = P + (a.suffix ? a.S : 0);
-  const int nch = (nkeys + a.chunk_keys - 1) / a.chunk_keys;
-  const int slot = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const int row = qb * rph + slot % rph;
-  if (row >= nq) return;
-  const int h = kvh * (ATT_SLOTS / rph) + slot / rph;
-  const float *pp = a.part + ((size_t)bk * gridDim.x + qb) * a.n_chunks * ATT_SLOTS * (D + 2);
-  const size_t cstride = (size_t)ATT_SLOTS * (D + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, pp[c * cstride + ATT_SLOTS * D + slot * 2]);
-  float L = 0.f;
-  for (int c = 0; c < nch; ++c)
-    L += exp2f(pp[c * cstride + ATT_SLOTS * D + slot * 2] - M) * pp[c * cstride + ATT_SLOTS * D + slot * 2 + 1];
-  const float inv = 1.0f / L;
-  T *orow = (T *)a.out + (size_t)(b * a.q_rows_per_b + row) * a.Hq * D + h * D;
-  constexpr int HALF = D / 2;
-  float acc[HALF];
+  // merge: two threads per query slot, each half of D
+  {
+    const int slot = tid >> 1, half = tid & 1;
+    const int row = qb * RPH + slot % RPH;
+    const int hh = kvh * G + slot / RPH;
+    if (row < nq) {
+      const float *pml = part_ml + grp * a.n_chunks * ATT_SLOTS * 2;
+      float M = -INFINITY;
+      for (int c = 0; c < nch; ++c) M = fmaxf(M, pml[(c * ATT_SLOTS + slot) * 2]);
+      float L = 0.f;
+      for (int c = 0; c < nch; ++c) L += exp2f(pml[(c * ATT_SLOTS + slot) * 2] - M) * pml[(c * ATT_SLOTS + slot) * 2 + 1];
+      const float invL = 1.0f / L;
+      constexpr int HALF = D / 2;
+      float acc[HALF];
 #pragma unroll
-  for (int d = 0; d < HALF; ++d) acc[d] = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float w = exp2f(pp[c * cstride + ATT_SLOTS * D + slot * 2] - M);
-    const float *op = pp + c * cstride + slot * D + half * HALF;
+      for (int d = 0; d < HALF; ++d) acc[d] = 0.f;
+      for (int c = 0; c < nch; ++c) {
+        const float w = exp2f(pml[(c * ATT_SLOTS + slot) * 2] - M) * pml[(c * ATT_SLOTS + slot) * 2 + 1];
+        const T *op = part_o + ((grp * a.n_chunks + c) * ATT_SLOTS + slot) * D + half * HALF;
 #pragma unroll
-    for (int d = 0; d < HALF; ++d) acc[d] += w * op[d];
+        for (int d = 0; d < HALF; ++d) acc[d] += w * to_f32(op[d]);
+      }
+      T *orow = (T *)a.out + (size_t)(b * a.q_rows_per_b + row) * HD + hh * D + half * HALF;
+#pragma unroll
+      for (int d = 0; d < HALF; ++d) orow[d] = from_f32<T>(acc[d] * invL);
+    }
   }
-#pragma unroll
-  for (int d = 0; d < HALF; ++d) orow[half * HALF + d] = from_f32<T>(acc[d] * inv);
+  if (tid == 0) a.counters[grp] = 0u;
 }
 
 template <typename T, int D, int G> static void attn_t(const AttnArgs &a, hipStream_t s) {
@@ -246,8 +275,6 @@ template <typename T, int D, int G> static void attn_t(const AttnArgs &a, hipStr
   const int nqb = attn_qblocks(q_rows, a.Hq, a.Hkv);
   dim3 grid(a.n_chunks, nqb, a.B * a.Hkv);
   hipLaunchKernelGGL((attn_kernel<T, D, G>), grid, dim3(256), 0, s, a);
-  if (a.n_chunks > 1)
-    hipLaunchKernelGGL((attn_combine<T, D>), dim3(nqb, a.B * a.Hkv), dim3(256), 0, s, a, ATT_SLOTS / G);
 }
 
 template <typename T, int D> static void attn_g(const AttnArgs &a, hipStream_t s) {

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <new>
 #include <string>
 
@@ -67,10 +68,18 @@ struct Region {
   size_t off = 0, bytes = 0;
 };
 
+// Tile plans of the GEMMs of one expert at one row count.
+struct ExpertPlans {
+  GemmPlan qkv, o, gu, down;
+};
+
 struct Layout {
-  Region rope, h, xn, q, ks, vs, o, act, part;             // action side / shared
-  Region xn_p, q_p, kp, vp, o_p, act_p, part_p;           // prefix side
+  Region rope, counters;
+  Region h, hg, ssq, q, ks, vs, o, act, apart, split;          // action side (h: denoise only)
+  Region hp, hg_p, ssq_p, q_p, kp, vp, o_p, act_p, apart_p;    // prefix side (hp: prefill only)
   int n_chunks = 1, chunk_keys = 32, n_chunks_p = 1, chunk_keys_p = 32;
+  size_t attn_counters = 0, attn_counters_p = 0, gemm_counters = 0;
+  ExpertPlans pa, pv;  // action expert, VLM expert
   size_t total = 0;
   void put(Region &r, size_t bytes) {
     r.off = total;
@@ -91,15 +100,55 @@ void attn_split(int B, int Hkv, int nqb, int max_keys, int *n_chunks, int *chunk
   *n_chunks = (max_keys + ck - 1) / ck;
 }
 
+// M <= 64 rows: the skinny kernel.  Wide GEMMs give every workgroup 16 columns over the full K;
+// narrow ones (the residual projections) take 32 columns and split K until ~256 workgroups.
+GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
+  GemmPlan p{};
+  p.sk.k_split = 1;
+  if (M > 64) {
+    p.skinny = 0;
+    p.nt = 64;
+    return p;
+  }
+  p.skinny = 1;
+  const int kq = gemm_k_quantum(dt);
+  p.nt = (split_ok && N % 32 == 0) ? 32 : 16;
+  const int tiles = N / p.nt;
+  if (split_ok)
+    while (tiles * p.sk.k_split < 256 && K % (2 * p.sk.k_split * kq) == 0) p.sk.k_split *= 2;
+  return p;
+}
+
+ExpertPlans plan_expert(const dm_config &c, Dt dt, int M, int H, int F) {
+  ExpertPlans e;
+  const int QKV = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, QD = c.n_q_heads * c.head_dim;
+  e.qkv = plan_gemm(dt, M, QKV, H, false);
+  e.o = plan_gemm(dt, M, H, QD, true);
+  e.gu = plan_gemm(dt, M, 2 * F, H, false);
+  e.down = plan_gemm(dt, M, H, F, true);
+  return e;
+}
+
+size_t split_bytes(const GemmPlan &p, int N) {
+  return p.sk.k_split > 1 ? (size_t)N * p.sk.k_split * 256 : 0;
+}
+size_t split_counters(const GemmPlan &p, int N) { return p.sk.k_split > 1 ? (size_t)(N / p.nt) : 0; }
+
 Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
   Layout L;
+  const Dt dt = es == 2 ? DT_BF16 : DT_F32;
   const int S = c.chunk, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int Ha = c.act_hidden, Hv = c.vlm_hidden;
   const size_t Ms = (size_t)B * S, Mp = (size_t)B * P_cap;
-  const int npos = P_cap + S;
-  L.put(L.rope, (size_t)npos * (D / 2) * sizeof(float2));
+  L.put(L.rope, (size_t)(P_cap + S) * (D / 2) * sizeof(float2));
+  size_t split = 0, gcount = 0;
   if (op == DM_OP_DENOISE || op == DM_OP_MERGED_LAYER) {
-    if (op == DM_OP_DENOISE) L.put(L.h, Ms * c.act_hidden * sizeof(float));
-    L.put(L.xn, Ms * c.act_hidden * es);
+    L.pa = plan_expert(c, dt, (int)Ms, Ha, c.act_ffn);
+    split = std::max(split_bytes(L.pa.o, Ha), split_bytes(L.pa.down, Ha));
+    gcount = std::max(split_counters(L.pa.o, Ha), split_counters(L.pa.down, Ha));
+    if (op == DM_OP_DENOISE) L.put(L.h, Ms * Ha * sizeof(float));
+    L.put(L.hg, Ms * Ha * es);
+    L.put(L.ssq, Ms * (Ha / 16) * sizeof(float));
     L.put(L.q, Ms * Hq * D * es);
     L.put(L.ks, (size_t)B * Hkv * S * D * es);
     L.put(L.vs, (size_t)B * Hkv * S * D * es);
@@ -107,11 +156,16 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
     L.put(L.act, Ms * c.act_ffn * es);
     const int nqb = attn_qblocks(S, Hq, Hkv);
     attn_split(B, Hkv, nqb, P_cap + S, &L.n_chunks, &L.chunk_keys);
-    if (L.n_chunks > 1) L.put(L.part, attn_partial_bytes(B, Hkv, nqb, L.n_chunks, D));
+    if (L.n_chunks > 1) L.put(L.apart, attn_partial_bytes(dt, B, Hkv, nqb, L.n_chunks, D));
+    L.attn_counters = (size_t)B * Hkv * nqb;
   }
   if (op == DM_OP_PREFILL || op == DM_OP_MERGED_LAYER) {
-    if (op == DM_OP_PREFILL) L.put(L.h, Mp * c.vlm_hidden * sizeof(float));
-    L.put(L.xn_p, Mp * c.vlm_hidden * es);
+    L.pv = plan_expert(c, dt, (int)Mp, Hv, c.vlm_ffn);
+    split = std::max(split, std::max(split_bytes(L.pv.o, Hv), split_bytes(L.pv.down, Hv)));
+    gcount = std::max(gcount, std::max(split_counters(L.pv.o, Hv), split_counters(L.pv.down, Hv)));
+    if (op == DM_OP_PREFILL) L.put(L.hp, Mp * Hv * sizeof(float));
+    L.put(L.hg_p, Mp * Hv * es);
+    L.put(L.ssq_p, Mp * (Hv / 16) * sizeof(float));
     L.put(L.q_p, Mp * Hq * D * es);
     if (op == DM_OP_MERGED_LAYER) {
       L.put(L.kp, (size_t)B * Hkv * P_cap * D * es);
@@ -121,8 +175,12 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
     L.put(L.act_p, Mp * c.vlm_ffn * es);
     const int nqb = attn_qblocks(P_cap, Hq, Hkv);
     attn_split(B, Hkv, nqb, P_cap, &L.n_chunks_p, &L.chunk_keys_p);
-    if (L.n_chunks_p > 1) L.put(L.part_p, attn_partial_bytes(B, Hkv, nqb, L.n_chunks_p, D));
+    if (L.n_chunks_p > 1) L.put(L.apart_p, attn_partial_bytes(dt, B, Hkv, nqb, L.n_chunks_p, D));
+    L.attn_counters_p = (size_t)B * Hkv * nqb;
   }
+  if (split) L.put(L.split, split);
+  L.gemm_counters = gcount;
+  L.put(L.counters, (gcount + L.attn_counters + L.attn_counters_p) * sizeof(unsigned));
   return L;
 }
 
@@ -147,6 +205,10 @@ dm_status check_config(const dm_config *c) {
   REQUIRE((c->n_q_heads * c->head_dim) % 64 == 0, DM_ERR_SHAPE, "n_q_heads*head_dim must be a multiple of 64");
   REQUIRE(((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim) % 64 == 0, DM_ERR_SHAPE,
           "(n_q_heads+2*n_kv_heads)*head_dim must be a multiple of 64");
+  const int kq = c->dtype == DM_BF16 ? 128 : 64;  // one K step of the skinny kernel (4 waves x one MFMA chunk)
+  REQUIRE(c->vlm_hidden % kq == 0 && c->act_hidden % kq == 0 && (c->n_q_heads * c->head_dim) % kq == 0 &&
+              c->vlm_ffn % kq == 0 && c->act_ffn % kq == 0,
+          DM_ERR_SHAPE, "hidden, FFN and n_q_heads*head_dim must be multiples of %d for this dtype", kq);
   REQUIRE(c->action_dim >= 1 && c->action_dim <= 64, DM_ERR_UNSUPPORTED, "action_dim must be 1..64");
   REQUIRE(c->chunk >= 1 && c->chunk <= 64, DM_ERR_UNSUPPORTED, "chunk must be 1..64");
   REQUIRE(c->rms_eps > 0.f && std::isfinite(c->rms_eps), DM_ERR_INVALID_ARG, "rms_eps must be positive");
@@ -211,26 +273,28 @@ Expert expert_layer(const dm_config &c, const dm_expert_weights &w, int l, int H
   return e;
 }
 
-// One expert's Q/K/V over its rows (norm -> fused QKV GEMM with RoPE).
-void enqueue_qkv(const dm_ctx *ctx, const Expert &e, const float *h, void *xn, int M, int H, RowMap rows,
-                 void *q, void *k, void *v, int kv_rows, const float2 *rope, hipStream_t s) {
-  const dm_config &c = ctx->cfg;
-  launch_rmsnorm(ctx->dt, h, e.attn_norm, xn, M, H, c.rms_eps, s);
-  QkvArgs a{xn, M, H, e.w_qkv, q, k, v, kv_rows, rows, rope, c.n_q_heads, c.n_kv_heads, c.head_dim};
-  launch_qkv(ctx->dt, a, s);
+SplitK splitk(const Layout &L, void *ws, const GemmPlan &p) {
+  SplitK s = p.sk;
+  s.part = L.split.bytes ? at<float>(ws, L.split) : nullptr;
+  s.counters = at<unsigned>(ws, L.counters);
+  return s;
 }
 
-// One expert's O-projection + residual and MLP + residual.
-void enqueue_finish(const dm_ctx *ctx, const Expert &e, float *h, const void *o, void *xn, void *act, int M, int H,
-                    int F, RowMap rows, hipStream_t s) {
+// One expert's O-projection + residual and MLP + residual.  `next_attn_norm` is the gain of
+// the norm that follows the layer (NULL after the last layer of a stack).
+void enqueue_finish(const dm_ctx *ctx, const Layout &L, void *ws, const ExpertPlans &pl, const Expert &e,
+                    const Hidden &hid, const void *o, void *act, int M, int F, RowMap rows,
+                    const float *next_attn_norm, hipStream_t s) {
   const dm_config &c = ctx->cfg;
-  ResidArgs ro{o, M, c.n_q_heads * c.head_dim, H, e.w_o, h, rows};
-  launch_resid(ctx->dt, ro, s);
-  launch_rmsnorm(ctx->dt, h, e.mlp_norm, xn, M, H, c.rms_eps, s);
-  SwigluArgs sg{xn, M, H, F, e.w_gate, e.w_up, act, rows};
-  launch_swiglu(ctx->dt, sg, s);
-  ResidArgs rd{act, M, F, H, e.w_down, h, rows};
-  launch_resid(ctx->dt, rd, s);
+  GemmPlan po = pl.o, pg = pl.gu, pd = pl.down;
+  po.sk = splitk(L, ws, pl.o);
+  pd.sk = splitk(L, ws, pl.down);
+  ResidArgs ro{o, M, c.n_q_heads * c.head_dim, e.w_o, hid, e.mlp_norm, rows};
+  launch_resid(ctx->dt, ro, po, s);
+  SwigluArgs sg{hid, M, F, c.rms_eps, e.w_gate, e.w_up, act, rows};
+  launch_swiglu(ctx->dt, sg, pg, s);
+  ResidArgs rd{act, M, F, e.w_down, hid, next_attn_norm, rows};
+  launch_resid(ctx->dt, rd, pd, s);
 }
 
 dm_status enqueue_denoise(const dm_ctx *ctx, const dm_action_weights *aw, const void *k_cache, const void *v_cache,
@@ -240,27 +304,33 @@ dm_status enqueue_denoise(const dm_ctx *ctx, const dm_action_weights *aw, const 
   const int S = c.chunk, Ha = c.act_hidden, Fa = c.act_ffn, D = c.head_dim, Hkv = c.n_kv_heads;
   const int M = B * S;
   float2 *rope = at<float2>(ws, L.rope);
-  float *h = at<float>(ws, L.h);
-  void *xn = at<void>(ws, L.xn), *q = at<void>(ws, L.q), *ks = at<void>(ws, L.ks), *vs = at<void>(ws, L.vs);
+  const Hidden hid{at<float>(ws, L.h), at<void>(ws, L.hg), at<float>(ws, L.ssq), Ha};
+  void *q = at<void>(ws, L.q), *ks = at<void>(ws, L.ks), *vs = at<void>(ws, L.vs);
   void *o = at<void>(ws, L.o), *act = at<void>(ws, L.act);
-  float *part = L.n_chunks > 1 ? at<float>(ws, L.part) : nullptr;
+  unsigned *cnt = at<unsigned>(ws, L.counters);
   const RowMap rows{S, lens, 0, P_cap};
   const size_t layer_cache = (size_t)B * Hkv * P_cap * D;
+  const GemmPlan pq = L.pa.qkv;
 
+  launch_zero_u32(cnt, L.gemm_counters + L.attn_counters, s);
   launch_rope_table(rope, P_cap + S, D, c.rope_base, s);
   for (int k = 0; k < num_steps; ++k) {
     const float t = 1.0f - (float)k / (float)num_steps;
-    launch_embed(x, aw->w_in, aw->b_in, h, M, c.action_dim, Ha, t, s);
+    launch_embed(ctx->dt, x, aw->w_in, aw->b_in, hid, aw->body.attn_norm, M, c.action_dim, t, s);
     for (int l = 0; l < c.n_layers; ++l) {
       const Expert e = expert_layer(c, aw->body, l, Ha, Fa, ctx->es);
-      enqueue_qkv(ctx, e, h, xn, M, Ha, rows, q, ks, vs, S, rope, s);
-      AttnArgs at{q, S, 1,
+      QkvArgs qa{hid, M, c.rms_eps, e.w_qkv, q, ks, vs, S, rows, rope, c.n_q_heads, Hkv, D};
+      launch_qkv(ctx->dt, qa, pq, s);
+      AttnArgs aa{q, S, 1,
                   layer_ptr(k_cache, layer_cache, l, ctx->es), layer_ptr(v_cache, layer_cache, l, ctx->es), P_cap,
-                  ks, vs, S, lens, B, c.n_q_heads, Hkv, D, L.n_chunks, L.chunk_keys, o, part};
-      launch_attention(ctx->dt, at, s);
-      enqueue_finish(ctx, e, h, o, xn, act, M, Ha, Fa, rows, s);
+                  ks, vs, S, lens, B, c.n_q_heads, Hkv, D, L.n_chunks, L.chunk_keys, o,
+                  L.n_chunks > 1 ? at<void>(ws, L.apart) : nullptr, cnt + L.gemm_counters};
+      launch_attention(ctx->dt, aa, s);
+      const float *next = l + 1 < c.n_layers ? aw->body.attn_norm + (size_t)(l + 1) * Ha : nullptr;
+      enqueue_finish(ctx, L, ws, L.pa, e, hid, o, act, M, Fa, rows, next, s);
     }
-    launch_velocity_euler(h, aw->final_norm, aw->w_out, aw->b_out, x, M, Ha, c.action_dim, c.rms_eps, num_steps, s);
+    launch_velocity_euler(hid.h, aw->final_norm, aw->w_out, aw->b_out, x, M, Ha, c.action_dim, c.rms_eps, num_steps,
+                          s);
   }
   return DM_OK;
 }
@@ -418,26 +488,34 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   const int S = c.chunk, D = c.head_dim, Hkv = c.n_kv_heads, Hq = c.n_q_heads;
   const int Ms = B * S, Mp = B * P_cap;
   float2 *rope = at<float2>(ws, L.rope);
+  unsigned *cnt = at<unsigned>(ws, L.counters);
   void *kp = k_out ? k_out : at<void>(ws, L.kp), *vp = v_out ? v_out : at<void>(ws, L.vp);
   const RowMap prow{P_cap, prefix_lens, 1, P_cap}, srow{S, prefix_lens, 0, P_cap};
   const Expert ev = expert_layer(c, *vlm, layer, c.vlm_hidden, c.vlm_ffn, ctx->es);
   const Expert ea = expert_layer(c, *act, layer, c.act_hidden, c.act_ffn, ctx->es);
+  const Hidden hp{h_prefix, at<void>(ws, L.hg_p), at<float>(ws, L.ssq_p), c.vlm_hidden};
+  const Hidden hs{h_suffix, at<void>(ws, L.hg), at<float>(ws, L.ssq), c.act_hidden};
 
+  launch_zero_u32(cnt, L.gemm_counters + L.attn_counters + L.attn_counters_p, s);
   launch_rope_table(rope, P_cap + S, D, c.rope_base, s);
-  enqueue_qkv(ctx, ev, h_prefix, at<void>(ws, L.xn_p), Mp, c.vlm_hidden, prow, at<void>(ws, L.q_p), kp, vp, P_cap,
-              rope, s);
-  enqueue_qkv(ctx, ea, h_suffix, at<void>(ws, L.xn), Ms, c.act_hidden, srow, at<void>(ws, L.q), at<void>(ws, L.ks),
-              at<void>(ws, L.vs), S, rope, s);
+  launch_norm_prep(ctx->dt, h_prefix, hp, ev.attn_norm, Mp, s);
+  launch_norm_prep(ctx->dt, h_suffix, hs, ea.attn_norm, Ms, s);
+  QkvArgs qv{hp, Mp, c.rms_eps, ev.w_qkv, at<void>(ws, L.q_p), kp, vp, P_cap, prow, rope, Hq, Hkv, D};
+  launch_qkv(ctx->dt, qv, L.pv.qkv, s);
+  QkvArgs qa{hs, Ms, c.rms_eps, ea.w_qkv, at<void>(ws, L.q), at<void>(ws, L.ks), at<void>(ws, L.vs), S, srow, rope,
+             Hq, Hkv, D};
+  launch_qkv(ctx->dt, qa, L.pa.qkv, s);
   AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kp, vp, P_cap, nullptr, nullptr, S, prefix_lens, B, Hq, Hkv, D,
-              L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p), L.n_chunks_p > 1 ? at<float>(ws, L.part_p) : nullptr};
+              L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),
+              L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr, cnt + L.gemm_counters + L.attn_counters};
   launch_attention(ctx->dt, ap, s);
   AttnArgs as{at<void>(ws, L.q), S, 1, kp, vp, P_cap, at<void>(ws, L.ks), at<void>(ws, L.vs), S, prefix_lens, B, Hq,
-              Hkv, D, L.n_chunks, L.chunk_keys, at<void>(ws, L.o), L.n_chunks > 1 ? at<float>(ws, L.part) : nullptr};
+              Hkv, D, L.n_chunks, L.chunk_keys, at<void>(ws, L.o), L.n_chunks > 1 ? at<void>(ws, L.apart) : nullptr,
+              cnt + L.gemm_counters};
   launch_attention(ctx->dt, as, s);
-  enqueue_finish(ctx, ev, h_prefix, at<void>(ws, L.o_p), at<void>(ws, L.xn_p), at<void>(ws, L.act_p), Mp,
-                 c.vlm_hidden, c.vlm_ffn, prow, s);
-  enqueue_finish(ctx, ea, h_suffix, at<void>(ws, L.o), at<void>(ws, L.xn), at<void>(ws, L.act), Ms, c.act_hidden,
-                 c.act_ffn, srow, s);
+  enqueue_finish(ctx, L, ws, L.pv, ev, hp, at<void>(ws, L.o_p), at<void>(ws, L.act_p), Mp, c.vlm_ffn, prow, nullptr,
+                 s);
+  enqueue_finish(ctx, L, ws, L.pa, ea, hs, at<void>(ws, L.o), at<void>(ws, L.act), Ms, c.act_ffn, srow, nullptr, s);
   HIP_TRY(hipGetLastError());
   return DM_OK;
 }
@@ -458,24 +536,27 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *
   const int D = c.head_dim, Hkv = c.n_kv_heads, Hq = c.n_q_heads, Hv = c.vlm_hidden;
   const int Mp = B * P_cap;
   float2 *rope = at<float2>(ws, L.rope);
-  float *h = at<float>(ws, L.h);
+  unsigned *cnt = at<unsigned>(ws, L.counters);
+  const Hidden hp{at<float>(ws, L.hp), at<void>(ws, L.hg_p), at<float>(ws, L.ssq_p), Hv};
   const RowMap prow{P_cap, prefix_lens, 1, P_cap};
   const size_t layer_cache = (size_t)B * Hkv * P_cap * D;
 
+  launch_zero_u32(cnt, L.gemm_counters + L.attn_counters_p, s);
   launch_rope_table(rope, P_cap, D, c.rope_base, s);
-  launch_copy_f32(prefix_embeds, h, (size_t)Mp * Hv, s);
+  launch_norm_prep(ctx->dt, prefix_embeds, hp, vlm->attn_norm, Mp, s);
   for (int l = 0; l < c.n_layers; ++l) {
     const Expert e = expert_layer(c, *vlm, l, Hv, c.vlm_ffn, ctx->es);
     void *kc = (void *)layer_ptr(k_cache, layer_cache, l, ctx->es);
     void *vc = (void *)layer_ptr(v_cache, layer_cache, l, ctx->es);
-    enqueue_qkv(ctx, e, h, at<void>(ws, L.xn_p), Mp, Hv, prow, at<void>(ws, L.q_p), kc, vc, P_cap, rope, s);
+    QkvArgs qv{hp, Mp, c.rms_eps, e.w_qkv, at<void>(ws, L.q_p), kc, vc, P_cap, prow, rope, Hq, Hkv, D};
+    launch_qkv(ctx->dt, qv, L.pv.qkv, s);
     if (l == c.n_layers - 1) break;  // the last layer's outputs past its K/V are never read
     AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kc, vc, P_cap, nullptr, nullptr, c.chunk, prefix_lens, B, Hq, Hkv, D,
                 L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),
-                L.n_chunks_p > 1 ? at<float>(ws, L.part_p) : nullptr};
+                L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr, cnt + L.gemm_counters};
     launch_attention(ctx->dt, ap, s);
-    enqueue_finish(ctx, e, h, at<void>(ws, L.o_p), at<void>(ws, L.xn_p), at<void>(ws, L.act_p), Mp, Hv, c.vlm_ffn,
-                   prow, s);
+    enqueue_finish(ctx, L, ws, L.pv, e, hp, at<void>(ws, L.o_p), at<void>(ws, L.act_p), Mp, c.vlm_ffn, prow,
+                   vlm->attn_norm + (size_t)(l + 1) * Hv, s);
   }
   HIP_TRY(hipGetLastError());
   return DM_OK;

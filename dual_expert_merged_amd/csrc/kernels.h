@@ -14,38 +14,68 @@ struct RowMap {
   int rows_per_b;
   const int32_t *lens;  // [B] prefix lengths (device)
   int is_prefix;        // 1: prefix tokens (position = token), 0: action tokens (position = P_b + token)
-  int cap;              // P_cap: prefix lengths are clamped to it
+  int cap;              // P_cap: prefix lengths are clamped to [0, cap]
 };
 
-// C[M x N] = A[M x K] * W^T for the fused Q/K/V projection: RoPE on the query and key columns,
-// queries stored token-major [M][Hq*D], keys and values head-major [B][Hkv][kv_rows][D].
+// The hidden stream between sublayers.  h is the fp32 residual stream [M][H].  hg holds
+// h * gain of the next RMSNorm rounded to the weight dtype (the next GEMM's operand), and ssq
+// the sums of squares of h over every 16-column group, [M][H/16]: the next GEMM scales its
+// output rows by 1/sqrt(sum(ssq)/H + eps), which completes RMSNorm(h) W^T.
+struct Hidden {
+  float *h;
+  void *hg;
+  float *ssq;
+  int H;
+};
+
+// Split-K scratch: fp32 partial tiles and one arrival counter per output tile.
+struct SplitK {
+  int k_split;       // number of K slices (1: no split)
+  float *part;
+  unsigned *counters;
+};
+
+// C[M x N] = RMSNorm-scaled A W^T for the fused Q/K/V projection: A = in.hg, rows scaled by
+// 1/rms from in.ssq, RoPE on query/key columns, queries token-major [M][Hq*D], keys and values
+// head-major [B][Hkv][kv_rows][D].
 struct QkvArgs {
-  const void *a; int M, K;
-  const void *w;                 // [(Hq+2Hkv)*D][K]
+  Hidden in; int M; float eps;
+  const void *w;                 // [(Hq+2Hkv)*D][H]
   void *q; void *k; void *v;
-  int kv_rows;                   // rows per (sample, kv head) in k/v
+  int kv_rows;
   RowMap rows;
   const float2 *rope;            // [positions][D/2] (cos, sin)
   int Hq, Hkv, D;
 };
-// h[M x N] += A[M x K] * W^T (float32 residual stream), rows outside RowMap untouched.
+// out.h += A W^T, then out.hg = (h * next_gain) and out.ssq for the next sublayer
+// (next_gain NULL: skip them).  Rows outside RowMap untouched.
 struct ResidArgs {
-  const void *a; int M, K, N;
-  const void *w;                 // [N][K]
-  float *h;                      // [M][N]
+  const void *a; int M, K;       // A [M][K]
+  const void *w;                 // [H][K]
+  Hidden out;
+  const float *next_gain;
   RowMap rows;
 };
-// act[M x F] = silu(A Wg^T) * (A Wu^T)
+// act[M x F] = silu(n Wg^T) * (n Wu^T), n = RMSNorm(h) from in.hg / in.ssq.
 struct SwigluArgs {
-  const void *a; int M, K, F;
-  const void *wg, *wu;           // [F][K] each
+  Hidden in; int M, F; float eps;
+  const void *wg, *wu;           // [F][H] each
   void *act;                     // [M][F]
   RowMap rows;
 };
 
-void launch_qkv(Dt dt, const QkvArgs &a, hipStream_t s);
-void launch_resid(Dt dt, const ResidArgs &a, hipStream_t s);
-void launch_swiglu(Dt dt, const SwigluArgs &a, hipStream_t s);
+// Tile plan of one GEMM launch, chosen by the host.
+struct GemmPlan {
+  int skinny;   // 1: M <= 64 kernel (K split across waves and workgroups), 0: tiled kernel
+  int nt;       // skinny: output columns per workgroup (16, 32 or 64)
+  SplitK sk;
+};
+
+void launch_qkv(Dt dt, const QkvArgs &a, const GemmPlan &p, hipStream_t s);
+void launch_resid(Dt dt, const ResidArgs &a, const GemmPlan &p, hipStream_t s);
+void launch_swiglu(Dt dt, const SwigluArgs &a, const GemmPlan &p, hipStream_t s);
+// Splits that the skinny kernel supports for K (multiple of 4 waves x one MFMA k-chunk).
+int gemm_k_quantum(Dt dt);
 
 // Attention of one query set against [prefix keys ; optional action keys].
 struct AttnArgs {
@@ -57,21 +87,23 @@ struct AttnArgs {
   int B, Hq, Hkv, D;
   int n_chunks, chunk_keys;          // split of the key range (chunk_keys multiple of 32)
   void *out;                         // token-major [B*q_rows_per_b][Hq*D]
-  float *part;                       // partial results when n_chunks > 1
+  void *part;                        // partial results when n_chunks > 1 (see attn_partial_bytes)
+  unsigned *counters;                // [B*Hkv*n_qblocks] arrival counters (zero between uses)
 };
-size_t attn_partial_bytes(int B, int Hkv, int n_qblocks, int n_chunks, int D);
+size_t attn_partial_bytes(Dt dt, int B, int Hkv, int n_qblocks, int n_chunks, int D);
 int attn_qblocks(int q_rows, int Hq, int Hkv);
 void launch_attention(Dt dt, const AttnArgs &a, hipStream_t s);
 
 void launch_rope_table(float2 *table, int n_pos, int D, float base, hipStream_t s);
-void launch_rmsnorm(Dt dt, const float *h, const float *gain, void *out, int M, int H, float eps,
-                    hipStream_t s);
-void launch_embed(const float *x, const float *w_in, const float *b_in, float *h, int M, int A,
-                  int H, float t, hipStream_t s);
+void launch_zero_u32(unsigned *p, size_t n, hipStream_t s);
+// h = src (if src != h), hg = h * gain, ssq per 16 columns: the entry into the first sublayer.
+void launch_norm_prep(Dt dt, const float *src, const Hidden &hid, const float *gain, int M, hipStream_t s);
+// h = x w_in^T + b_in + tau(t), then hg / ssq for the first layer's attention norm.
+void launch_embed(Dt dt, const float *x, const float *w_in, const float *b_in, const Hidden &hid,
+                  const float *gain, int M, int A, float t, hipStream_t s);
 void launch_velocity_euler(const float *h, const float *gain, const float *w_out,
                            const float *b_out, float *x, int M, int H, int A, float eps,
                            int num_steps, hipStream_t s);
-void launch_copy_f32(const float *src, float *dst, size_t n, hipStream_t s);
 void launch_fp8_quantize_rows(const void *src, uint8_t *dst, float *scales, int rows, int cols,
                               hipStream_t s);
 

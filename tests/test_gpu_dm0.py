@@ -87,12 +87,17 @@ def test_suffix_denoise_b32_ragged_bf16():
     for b in samples:
         ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :lens[b]], vc[:, b, :, :lens[b]], wl.shape, wl.steps)
         _chunk_ok(got[b], ref, f"config-4 sample {b} (P={lens[b]})")
+    # Batch invariance: the sample run alone takes the batch-1 kernels (skinny split-K GEMMs,
+    # split-key attention with bf16 partials), the batch the tiled ones, so the two agree to the
+    # bf16 bound rather than bit for bit; each is held to the oracle bound on its own.
     b = samples[0]
     kb, vb = gpu.cache_to_device(kc[:, b:b + 1], vc[:, b:b + 1])
     alone = gpu.denoise(kb, vb, lens[b:b + 1], x1[b:b + 1], wl.steps)
+    ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :lens[b]], vc[:, b, :, :lens[b]], wl.shape, wl.steps)
+    _chunk_ok(alone[0], ref, f"config-4 sample {b} alone at B=1")
     mx, mean = err_stats(alone[0], got[b])
     print(f"batch invariance sample {b}: max {mx:.3e} mean {mean:.3e}", flush=True)
-    assert mx <= 5e-3
+    assert mx <= CHUNK_MAX and mean <= CHUNK_MEAN
 
 
 def test_prefill_then_denoise_bf16():
