@@ -16,8 +16,7 @@
 // MFMA's contraction chunk.  Softmax is float32 with base-2 exponentials (scores pre-scaled by
 // log2(e)/sqrt(D)).
 // With several key chunks, each workgroup stores its normalised partial output (weight dtype)
-// with its running max and sum; the last workgroup of a (sample, KV head, query block) to arrive
-// merges them in chunk order, so the result does not depend on scheduling.
+// with its running max and sum, and attn_combine_kernel merges them in chunk order.
 #include "common.h"
 #include "kernels.h"
 
@@ -55,7 +54,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int LPT = ATT_CH * VPRW / 256;          // vectors per thread per stage
   __shared__ __attribute__((aligned(16))) T Ks[ATT_CH * KLD];
   __shared__ __attribute__((aligned(16))) T Vt[D * VLD];
-  __shared__ int s_last;
 
   const T *__restrict__ q = (const T *)a.q;
   const T *__restrict__ kp = (const T *)a.kp;
@@ -65,7 +63,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int chunk = blockIdx.x, qb = blockIdx.y, bk = blockIdx.z, nqb = gridDim.y;
+  const int bk = blockIdx.x, qb = blockIdx.y, chunk = blockIdx.z, nqb = gridDim.y;
   const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
   const int P = max(0, min(a.lens[b], a.kp_rows));
   const int nq = a.suffix ? a.S : P;
@@ -96,31 +94,35 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int row = r0 + qt * 16 + c16;
-      const T *qrow = q + (size_t)(b * a.q_rows_per_b + (row < nq ? row : 0)) * HD + h * D;
+      const T *qrow = q + (size_t)(b * a.q_rows_per_b + (row < nq ? row : nq - 1)) * HD + h * D;
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        qf[qt][dc] = row < nq ? load_frag<T>(qrow + dc * KC + g * EPL) : zero_frag<T>();
+      for (int dc = 0; dc < DC; ++dc) qf[qt][dc] = load_frag_masked<T>(qrow + dc * KC + g * EPL, row < nq);
     }
     const float sc = 1.4426950408889634f / sqrtf((float)D);
     const size_t pre_base = (size_t)(b * a.Hkv + kvh) * a.kp_rows * D;
     const size_t suf_base = (size_t)(b * a.Hkv + kvh) * a.S * D;
 
     for (int ks0 = k_begin; ks0 < k_end; ks0 += ATT_CH) {
+      // K: 16-byte vectors, lanes along a row (coalesced).  V: lanes along keys, so the
+      // transposed LDS stores of a wave hit consecutive addresses.
       frag kv[LPT], vv[LPT];
 #pragma unroll
       for (int v = 0; v < LPT; ++v) {
         const int idx = tid + v * 256;
         const int r = idx / VPRW, cv = idx - r * VPRW;
         const int key = ks0 + r;
-        kv[v] = zero_frag<T>();
-        vv[v] = zero_frag<T>();
-        if (key < k_end) {
-          const size_t off = key < P ? pre_base + (size_t)key * D : suf_base + (size_t)(key - P) * D;
-          const T *kb = key < P ? kp : ks;
-          const T *vb = key < P ? vp : vs;
-          kv[v] = load_frag<T>(kb + off + cv * EPL);
-          vv[v] = load_frag<T>(vb + off + cv * EPL);
-        }
+        const int kc = min(key, k_end - 1);
+        const size_t off = kc < P ? pre_base + (size_t)kc * D : suf_base + (size_t)(kc - P) * D;
+        kv[v] = load_frag_masked<T>((kc < P ? kp : ks) + off + cv * EPL, key < k_end);
+      }
+#pragma unroll
+      for (int v = 0; v < LPT; ++v) {
+        const int idx = tid + v * 256;
+        const int cv = idx / ATT_CH, r = idx - cv * ATT_CH;
+        const int key = ks0 + r;
+        const int kc = min(key, k_end - 1);
+        const size_t off = kc < P ? pre_base + (size_t)kc * D : suf_base + (size_t)(kc - P) * D;
+        vv[v] = load_frag_masked<T>((kc < P ? vp : vs) + off + cv * EPL, key < k_end);
       }
       __syncthreads();  // the previous stage is consumed
 #pragma unroll
@@ -128,6 +130,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const int idx = tid + v * 256;
         const int r = idx / VPRW, cv = idx - r * VPRW;
         *reinterpret_cast<frag *>(&Ks[r * KLD + cv * EPL]) = kv[v];
+      }
+#pragma unroll
+      for (int v = 0; v < LPT; ++v) {
+        const int idx = tid + v * 256;
+        const int cv = idx / ATT_CH, r = idx - cv * ATT_CH;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) Vt[(cv * EPL + e) * VLD + r] = vv[v][e];
       }
@@ -160,8 +167,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
               mx = fmaxf(mx, v);
             }
           }
-          mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+          mx = max_xor32(max_xor16(mx));
           const float m_new = fmaxf(m[qt], mx);
           const float m_use = m_new == -INFINITY ? 0.f : m_new;
           const float alpha = exp2f(m[qt] - m_use);
@@ -174,8 +180,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
               st[s][i] = p;
               sum += p;
             }
-          sum += __shfl_xor(sum, 16, WAVE);
-          sum += __shfl_xor(sum, 32, WAVE);
+          sum = sum_xor32(sum_xor16(sum));
           l[qt] = l[qt] * alpha + sum;
           m[qt] = m_new;
 #pragma unroll
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     return;
   }
 
-  // several chunks: publish this chunk's normalised output and statistics
+  // several chunks: publish this chunk's normalised output and statistics; attn_combine merges
   if (chunk < nch) {
     T *po = part_o + (grp * a.n_chunks + chunk) * ATT_SLOTS * D;
     float *pml = part_ml + (grp * a.n_chunks + chunk) * ATT_SLOTS * 2;
@@ -233,48 +238,111 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[grp], 1u) == (unsigned)(a.n_chunks - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
-  // merge: two threads per query slot, each half of D
-  {
-    const int slot = tid >> 1, half = tid & 1;
-    const int row = qb * RPH + slot % RPH;
-    const int hh = kvh * G + slot / RPH;
-    if (row < nq) {
-      const float *pml = part_ml + grp * a.n_chunks * ATT_SLOTS * 2;
-      float M = -INFINITY;
-      for (int c = 0; c < nch; ++c) M = fmaxf(M, pml[(c * ATT_SLOTS + slot) * 2]);
-      float L = 0.f;
-      for (int c = 0; c < nch; ++c) L += exp2f(pml[(c * ATT_SLOTS + slot) * 2] - M) * pml[(c * ATT_SLOTS + slot) * 2 + 1];
-      const float invL = 1.0f / L;
-      constexpr int HALF = D / 2;
-      float acc[HALF];
+// Merge the key chunks of every query slot (a separate launch: the kernel boundary makes the
+// partial results visible, with no device-scope fence inside a kernel):
+//   O = sum_c 2^(m_c - M) l_c O_c / sum_c 2^(m_c - M) l_c, summed in chunk order.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  typedef Mfma<T> MF;
+  constexpr int EPL = MF::EPL, RPH = ATT_SLOTS / G, MAXC = 16;
+  __shared__ float wts[ATT_SLOTS * MAXC];
+  const int tid = threadIdx.x;
+  const int bk = blockIdx.x, qb = blockIdx.y, nqb = gridDim.y;
+  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+  const int P = max(0, min(a.lens[b], a.kp_rows));
+  const int nq = a.suffix ? a.S : P;
+  const int nkeys = P + (a.suffix ? a.S : 0);
+  const int nch = (nkeys + a.chunk_keys - 1) / a.chunk_keys;
+  if (qb * RPH >= nq) return;
+  const int HD = a.Hq * D;
+  const size_t grp = (size_t)bk * nqb + qb;
+  const T *part_o = (const T *)a.part;
+  const float *part_ml = (const float *)((const char *)a.part +
+                                         ((part_o_elems(a.B, a.Hkv, nqb, a.n_chunks, D) * sizeof(T) + 255) & ~(size_t)255));
+  // 1: per query slot the weight 2^(m_c - M) l_c / L of every chunk
+  if (tid < ATT_SLOTS) {
+    const int slot = tid;
+    const float *pml = part_ml + grp * a.n_chunks * ATT_SLOTS * 2;
+    float mc[MAXC], lc[MAXC];
 #pragma unroll
-      for (int d = 0; d < HALF; ++d) acc[d] = 0.f;
-      for (int c = 0; c < nch; ++c) {
-        const float w = exp2f(pml[(c * ATT_SLOTS + slot) * 2] - M) * pml[(c * ATT_SLOTS + slot) * 2 + 1];
-        const T *op = part_o + ((grp * a.n_chunks + c) * ATT_SLOTS + slot) * D + half * HALF;
+    for (int c = 0; c < MAXC; ++c) {  // unconditional loads (clamped chunk) stay in flight together
+      const float2 v = *reinterpret_cast<const float2 *>(&pml[(min(c, nch - 1) * ATT_SLOTS + slot) * 2]);
+      mc[c] = v.x;
+      lc[c] = v.y;
+    }
+    float M = -INFINITY;
 #pragma unroll
-        for (int d = 0; d < HALF; ++d) acc[d] += w * to_f32(op[d]);
+    for (int c = 0; c < MAXC; ++c)
+      if (c < nch) M = fmaxf(M, mc[c]);
+    float L = 0.f;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      mc[c] = c < nch ? exp2f(mc[c] - M) * lc[c] : 0.f;
+      L += mc[c];
+    }
+    const float invL = 1.0f / L;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) wts[slot * MAXC + c] = mc[c] * invL;
+  }
+  __syncthreads();
+  // 2: out = sum_c w_c O_c over 16-byte vectors, four chunks of loads in flight at a time
+  constexpr int VPRW = D / EPL;
+  constexpr int ITEMS = ATT_SLOTS * VPRW / 256;
+  float acc[ITEMS][EPL];
+  int srow[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int slot = (tid + it * 256) / VPRW;
+    srow[it] = qb * RPH + slot % RPH;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[it][e] = 0.f;
+  }
+  for (int c0 = 0; c0 < nch; c0 += 4) {
+    typename MF::frag pv[ITEMS][4];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = tid + it * 256, slot = idx / VPRW, cv = idx - slot * VPRW;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int c = min(c0 + cc, nch - 1);
+        pv[it][cc] = load_frag_masked<T>(part_o + ((grp * a.n_chunks + c) * ATT_SLOTS + slot) * D + cv * EPL,
+                                         c0 + cc < nch && srow[it] < nq);
       }
-      T *orow = (T *)a.out + (size_t)(b * a.q_rows_per_b + row) * HD + hh * D + half * HALF;
+    }
 #pragma unroll
-      for (int d = 0; d < HALF; ++d) orow[d] = from_f32<T>(acc[d] * invL);
+    for (int it = 0; it < ITEMS; ++it) {
+      const int slot = (tid + it * 256) / VPRW;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const float w = wts[slot * MAXC + min(c0 + cc, MAXC - 1)];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[it][e] += w * to_f32(pv[it][cc][e]);
+      }
     }
   }
-  if (tid == 0) a.counters[grp] = 0u;
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    if (srow[it] >= nq) continue;
+    const int idx = tid + it * 256, slot = idx / VPRW, cv = idx - slot * VPRW;
+    const int hh = kvh * G + slot / RPH;
+    typename MF::frag o8;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o8[e] = from_f32<T>(acc[it][e]);
+    *reinterpret_cast<typename MF::frag *>((T *)a.out + (size_t)(b * a.q_rows_per_b + srow[it]) * HD + hh * D +
+                                           cv * EPL) = o8;
+  }
 }
 
 template <typename T, int D, int G> static void attn_t(const AttnArgs &a, hipStream_t s) {
   const int q_rows = a.suffix ? a.S : a.kp_rows;
   const int nqb = attn_qblocks(q_rows, a.Hq, a.Hkv);
-  dim3 grid(a.n_chunks, nqb, a.B * a.Hkv);
+  // (sample, KV head) varies fastest: consecutive workgroups go to consecutive XCDs, so all key
+  // chunks of one KV head share an XCD and its L2 holds their partial results for the merge.
+  dim3 grid(a.B * a.Hkv, nqb, a.n_chunks);
   hipLaunchKernelGGL((attn_kernel<T, D, G>), grid, dim3(256), 0, s, a);
+  if (a.n_chunks > 1) hipLaunchKernelGGL((attn_combine_kernel<T, D, G>), dim3(a.B * a.Hkv, nqb), dim3(256), 0, s, a);
 }
 
 template <typename T, int D> static void attn_g(const AttnArgs &a, hipStream_t s) {

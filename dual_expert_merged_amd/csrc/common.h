@@ -49,6 +49,14 @@ template <typename T> __device__ __forceinline__ typename Mfma<T>::frag load_fra
   return *reinterpret_cast<const typename Mfma<T>::frag *>(p);
 }
 
+// Loads a fragment from a valid address and zeroes it when `ok` is false, without a branch
+// around the load (so all loads of an unrolled sequence stay in flight together).
+template <typename T> __device__ __forceinline__ typename Mfma<T>::frag load_frag_masked(const T *p, bool ok) {
+  const i32x4 v = __builtin_bit_cast(i32x4, *reinterpret_cast<const typename Mfma<T>::frag *>(p));
+  const int m = ok ? -1 : 0;
+  return __builtin_bit_cast(typename Mfma<T>::frag, v & i32x4{m, m, m, m});
+}
+
 template <typename T> __device__ __forceinline__ typename Mfma<T>::frag zero_frag() {
   typename Mfma<T>::frag z;
 #pragma unroll
@@ -70,16 +78,46 @@ __device__ __forceinline__ float to_f32(bf16 x) {
   return __uint_as_float(((uint32_t)__builtin_bit_cast(uint16_t, x)) << 16);
 }
 
-// --------------------------------------------------------------------------- reductions
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
+// --------------------------------------------------------------------------- cross-lane
+// Lane exchanges: DPP within 16-lane rows (no LDS crossbar), ds_swizzle / ds_bpermute across
+// rows.  A row is lanes 16r..16r+15.
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within each 8 lanes
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within each row
+constexpr int DPP_ROR8 = 0x128;        // lane i <- lane (i+8) mod 16: the same as i^8
+
+__device__ __forceinline__ float lane_xor8(float v) { return dpp<DPP_ROR8>(v); }
+// Across rows: lane l^16 through ds_swizzle (swap of the 16-lane halves of each 32 lanes), lane
+// l^32 through ds_bpermute.
+__device__ __forceinline__ float lane_xor16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+__device__ __forceinline__ float lane_xor32(float v) { return __shfl_xor(v, 32, WAVE); }
+__device__ __forceinline__ float sum_xor16(float v) { return v + lane_xor16(v); }
+__device__ __forceinline__ float sum_xor32(float v) { return v + lane_xor32(v); }
+__device__ __forceinline__ float max_xor16(float v) { return fmaxf(v, lane_xor16(v)); }
+__device__ __forceinline__ float max_xor32(float v) { return fmaxf(v, lane_xor32(v)); }
+// Sum over the 4 lanes of a quad, the 16 lanes of a row, and the whole wave.
+__device__ __forceinline__ float sum4(float v) {
+  v += dpp<DPP_XOR1>(v);
+  return v + dpp<DPP_XOR2>(v);
+}
+__device__ __forceinline__ float sum16(float v) {
+  v = sum4(v);
+  v += dpp<DPP_HALF_MIRROR>(v);
+  return v + dpp<DPP_MIRROR>(v);
+}
+__device__ __forceinline__ float wave_sum(float v) { return sum_xor32(sum_xor16(sum16(v))); }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-  return v;
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR>(v));
+  return max_xor32(max_xor16(v));
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }

@@ -74,11 +74,10 @@ struct ExpertPlans {
 };
 
 struct Layout {
-  Region rope, counters;
+  Region rope;
   Region h, hg, ssq, q, ks, vs, o, act, apart, split;          // action side (h: denoise only)
   Region hp, hg_p, ssq_p, q_p, kp, vp, o_p, act_p, apart_p;    // prefix side (hp: prefill only)
   int n_chunks = 1, chunk_keys = 32, n_chunks_p = 1, chunk_keys_p = 32;
-  size_t attn_counters = 0, attn_counters_p = 0, gemm_counters = 0;
   ExpertPlans pa, pv;  // action expert, VLM expert
   size_t total = 0;
   void put(Region &r, size_t bytes) {
@@ -91,6 +90,7 @@ struct Layout {
 void attn_split(int B, int Hkv, int nqb, int max_keys, int *n_chunks, int *chunk_keys) {
   const int blocks = B * Hkv * nqb;
   int want = (256 + blocks - 1) / blocks;
+  if (want > 16) want = 16;  // the merge keeps every chunk's statistics in registers
   const int maxc = (max_keys + 127) / 128;
   if (want > maxc) want = maxc;
   if (want < 1) want = 1;
@@ -102,20 +102,25 @@ void attn_split(int B, int Hkv, int nqb, int max_keys, int *n_chunks, int *chunk
 
 // M <= 64 rows: the skinny kernel.  Wide GEMMs give every workgroup 16 columns over the full K;
 // narrow ones (the residual projections) take 32 columns and split K until ~256 workgroups.
+// Each wave of the skinny kernel holds its whole K slice in registers: at most 8 MFMA k-chunks,
+// otherwise K is split further (residual projections) or the tiled kernel is used.
 GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
   GemmPlan p{};
   p.sk.k_split = 1;
-  if (M > 64) {
-    p.skinny = 0;
-    p.nt = 64;
-    return p;
+  p.skinny = 0;
+  p.nt = 64;
+  if (M > 64) return p;
+  const int kq = gemm_k_quantum(dt);  // K per k-chunk across the 4 waves
+  const int nt = (split_ok && N % 32 == 0) ? 32 : 16;
+  int ks = 1;
+  if (split_ok) {
+    while ((N / nt) * ks < 256 && ks < 16 && K % (2 * ks * kq) == 0) ks *= 2;
+    while (K / (ks * kq) > 8 && ks < 16 && K % (2 * ks * kq) == 0) ks *= 2;
   }
+  if (K % (ks * kq) != 0 || K / (ks * kq) > 8) return p;
   p.skinny = 1;
-  const int kq = gemm_k_quantum(dt);
-  p.nt = (split_ok && N % 32 == 0) ? 32 : 16;
-  const int tiles = N / p.nt;
-  if (split_ok)
-    while (tiles * p.sk.k_split < 256 && K % (2 * p.sk.k_split * kq) == 0) p.sk.k_split *= 2;
+  p.nt = nt;
+  p.sk.k_split = ks;
   return p;
 }
 
@@ -129,10 +134,9 @@ ExpertPlans plan_expert(const dm_config &c, Dt dt, int M, int H, int F) {
   return e;
 }
 
-size_t split_bytes(const GemmPlan &p, int N) {
-  return p.sk.k_split > 1 ? (size_t)N * p.sk.k_split * 256 : 0;
+size_t split_bytes(const GemmPlan &p, int M, int N) {
+  return p.sk.k_split > 1 ? (size_t)p.sk.k_split * M * N * sizeof(float) : 0;
 }
-size_t split_counters(const GemmPlan &p, int N) { return p.sk.k_split > 1 ? (size_t)(N / p.nt) : 0; }
 
 Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
   Layout L;
@@ -141,11 +145,10 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
   const int Ha = c.act_hidden, Hv = c.vlm_hidden;
   const size_t Ms = (size_t)B * S, Mp = (size_t)B * P_cap;
   L.put(L.rope, (size_t)(P_cap + S) * (D / 2) * sizeof(float2));
-  size_t split = 0, gcount = 0;
+  size_t split = 0;
   if (op == DM_OP_DENOISE || op == DM_OP_MERGED_LAYER) {
     L.pa = plan_expert(c, dt, (int)Ms, Ha, c.act_ffn);
-    split = std::max(split_bytes(L.pa.o, Ha), split_bytes(L.pa.down, Ha));
-    gcount = std::max(split_counters(L.pa.o, Ha), split_counters(L.pa.down, Ha));
+    split = std::max(split_bytes(L.pa.o, (int)Ms, Ha), split_bytes(L.pa.down, (int)Ms, Ha));
     if (op == DM_OP_DENOISE) L.put(L.h, Ms * Ha * sizeof(float));
     L.put(L.hg, Ms * Ha * es);
     L.put(L.ssq, Ms * (Ha / 16) * sizeof(float));
@@ -157,12 +160,10 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
     const int nqb = attn_qblocks(S, Hq, Hkv);
     attn_split(B, Hkv, nqb, P_cap + S, &L.n_chunks, &L.chunk_keys);
     if (L.n_chunks > 1) L.put(L.apart, attn_partial_bytes(dt, B, Hkv, nqb, L.n_chunks, D));
-    L.attn_counters = (size_t)B * Hkv * nqb;
   }
   if (op == DM_OP_PREFILL || op == DM_OP_MERGED_LAYER) {
     L.pv = plan_expert(c, dt, (int)Mp, Hv, c.vlm_ffn);
-    split = std::max(split, std::max(split_bytes(L.pv.o, Hv), split_bytes(L.pv.down, Hv)));
-    gcount = std::max(gcount, std::max(split_counters(L.pv.o, Hv), split_counters(L.pv.down, Hv)));
+    split = std::max(split, std::max(split_bytes(L.pv.o, (int)Mp, Hv), split_bytes(L.pv.down, (int)Mp, Hv)));
     if (op == DM_OP_PREFILL) L.put(L.hp, Mp * Hv * sizeof(float));
     L.put(L.hg_p, Mp * Hv * es);
     L.put(L.ssq_p, Mp * (Hv / 16) * sizeof(float));
@@ -176,11 +177,8 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
     const int nqb = attn_qblocks(P_cap, Hq, Hkv);
     attn_split(B, Hkv, nqb, P_cap, &L.n_chunks_p, &L.chunk_keys_p);
     if (L.n_chunks_p > 1) L.put(L.apart_p, attn_partial_bytes(dt, B, Hkv, nqb, L.n_chunks_p, D));
-    L.attn_counters_p = (size_t)B * Hkv * nqb;
   }
   if (split) L.put(L.split, split);
-  L.gemm_counters = gcount;
-  L.put(L.counters, (gcount + L.attn_counters + L.attn_counters_p) * sizeof(unsigned));
   return L;
 }
 
@@ -209,7 +207,9 @@ dm_status check_config(const dm_config *c) {
   REQUIRE(c->vlm_hidden % kq == 0 && c->act_hidden % kq == 0 && (c->n_q_heads * c->head_dim) % kq == 0 &&
               c->vlm_ffn % kq == 0 && c->act_ffn % kq == 0,
           DM_ERR_SHAPE, "hidden, FFN and n_q_heads*head_dim must be multiples of %d for this dtype", kq);
-  REQUIRE(c->action_dim >= 1 && c->action_dim <= 64, DM_ERR_UNSUPPORTED, "action_dim must be 1..64");
+  REQUIRE(c->vlm_hidden <= 4096 && c->act_hidden <= 4096, DM_ERR_UNSUPPORTED, "hidden sizes above 4096");
+  REQUIRE(c->action_dim >= 4 && c->action_dim <= 64 && c->action_dim % 4 == 0, DM_ERR_UNSUPPORTED,
+          "action_dim must be a multiple of 4 in 4..64");
   REQUIRE(c->chunk >= 1 && c->chunk <= 64, DM_ERR_UNSUPPORTED, "chunk must be 1..64");
   REQUIRE(c->rms_eps > 0.f && std::isfinite(c->rms_eps), DM_ERR_INVALID_ARG, "rms_eps must be positive");
   REQUIRE(c->rope_base > 1.f && std::isfinite(c->rope_base), DM_ERR_INVALID_ARG, "rope_base must be > 1");
@@ -276,7 +276,6 @@ Expert expert_layer(const dm_config &c, const dm_expert_weights &w, int l, int H
 SplitK splitk(const Layout &L, void *ws, const GemmPlan &p) {
   SplitK s = p.sk;
   s.part = L.split.bytes ? at<float>(ws, L.split) : nullptr;
-  s.counters = at<unsigned>(ws, L.counters);
   return s;
 }
 
@@ -307,12 +306,10 @@ dm_status enqueue_denoise(const dm_ctx *ctx, const dm_action_weights *aw, const 
   const Hidden hid{at<float>(ws, L.h), at<void>(ws, L.hg), at<float>(ws, L.ssq), Ha};
   void *q = at<void>(ws, L.q), *ks = at<void>(ws, L.ks), *vs = at<void>(ws, L.vs);
   void *o = at<void>(ws, L.o), *act = at<void>(ws, L.act);
-  unsigned *cnt = at<unsigned>(ws, L.counters);
   const RowMap rows{S, lens, 0, P_cap};
   const size_t layer_cache = (size_t)B * Hkv * P_cap * D;
   const GemmPlan pq = L.pa.qkv;
 
-  launch_zero_u32(cnt, L.gemm_counters + L.attn_counters, s);
   launch_rope_table(rope, P_cap + S, D, c.rope_base, s);
   for (int k = 0; k < num_steps; ++k) {
     const float t = 1.0f - (float)k / (float)num_steps;
@@ -324,7 +321,7 @@ dm_status enqueue_denoise(const dm_ctx *ctx, const dm_action_weights *aw, const 
       AttnArgs aa{q, S, 1,
                   layer_ptr(k_cache, layer_cache, l, ctx->es), layer_ptr(v_cache, layer_cache, l, ctx->es), P_cap,
                   ks, vs, S, lens, B, c.n_q_heads, Hkv, D, L.n_chunks, L.chunk_keys, o,
-                  L.n_chunks > 1 ? at<void>(ws, L.apart) : nullptr, cnt + L.gemm_counters};
+                  L.n_chunks > 1 ? at<void>(ws, L.apart) : nullptr};
       launch_attention(ctx->dt, aa, s);
       const float *next = l + 1 < c.n_layers ? aw->body.attn_norm + (size_t)(l + 1) * Ha : nullptr;
       enqueue_finish(ctx, L, ws, L.pa, e, hid, o, act, M, Fa, rows, next, s);
@@ -488,7 +485,6 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   const int S = c.chunk, D = c.head_dim, Hkv = c.n_kv_heads, Hq = c.n_q_heads;
   const int Ms = B * S, Mp = B * P_cap;
   float2 *rope = at<float2>(ws, L.rope);
-  unsigned *cnt = at<unsigned>(ws, L.counters);
   void *kp = k_out ? k_out : at<void>(ws, L.kp), *vp = v_out ? v_out : at<void>(ws, L.vp);
   const RowMap prow{P_cap, prefix_lens, 1, P_cap}, srow{S, prefix_lens, 0, P_cap};
   const Expert ev = expert_layer(c, *vlm, layer, c.vlm_hidden, c.vlm_ffn, ctx->es);
@@ -496,7 +492,6 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   const Hidden hp{h_prefix, at<void>(ws, L.hg_p), at<float>(ws, L.ssq_p), c.vlm_hidden};
   const Hidden hs{h_suffix, at<void>(ws, L.hg), at<float>(ws, L.ssq), c.act_hidden};
 
-  launch_zero_u32(cnt, L.gemm_counters + L.attn_counters + L.attn_counters_p, s);
   launch_rope_table(rope, P_cap + S, D, c.rope_base, s);
   launch_norm_prep(ctx->dt, h_prefix, hp, ev.attn_norm, Mp, s);
   launch_norm_prep(ctx->dt, h_suffix, hs, ea.attn_norm, Ms, s);
@@ -507,11 +502,10 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   launch_qkv(ctx->dt, qa, L.pa.qkv, s);
   AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kp, vp, P_cap, nullptr, nullptr, S, prefix_lens, B, Hq, Hkv, D,
               L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),
-              L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr, cnt + L.gemm_counters + L.attn_counters};
+              L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr};
   launch_attention(ctx->dt, ap, s);
   AttnArgs as{at<void>(ws, L.q), S, 1, kp, vp, P_cap, at<void>(ws, L.ks), at<void>(ws, L.vs), S, prefix_lens, B, Hq,
-              Hkv, D, L.n_chunks, L.chunk_keys, at<void>(ws, L.o), L.n_chunks > 1 ? at<void>(ws, L.apart) : nullptr,
-              cnt + L.gemm_counters};
+              Hkv, D, L.n_chunks, L.chunk_keys, at<void>(ws, L.o), L.n_chunks > 1 ? at<void>(ws, L.apart) : nullptr};
   launch_attention(ctx->dt, as, s);
   enqueue_finish(ctx, L, ws, L.pv, ev, hp, at<void>(ws, L.o_p), at<void>(ws, L.act_p), Mp, c.vlm_ffn, prow, nullptr,
                  s);
@@ -536,12 +530,10 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *
   const int D = c.head_dim, Hkv = c.n_kv_heads, Hq = c.n_q_heads, Hv = c.vlm_hidden;
   const int Mp = B * P_cap;
   float2 *rope = at<float2>(ws, L.rope);
-  unsigned *cnt = at<unsigned>(ws, L.counters);
   const Hidden hp{at<float>(ws, L.hp), at<void>(ws, L.hg_p), at<float>(ws, L.ssq_p), Hv};
   const RowMap prow{P_cap, prefix_lens, 1, P_cap};
   const size_t layer_cache = (size_t)B * Hkv * P_cap * D;
 
-  launch_zero_u32(cnt, L.gemm_counters + L.attn_counters_p, s);
   launch_rope_table(rope, P_cap, D, c.rope_base, s);
   launch_norm_prep(ctx->dt, prefix_embeds, hp, vlm->attn_norm, Mp, s);
   for (int l = 0; l < c.n_layers; ++l) {
@@ -553,7 +545,7 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *
     if (l == c.n_layers - 1) break;  // the last layer's outputs past its K/V are never read
     AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kc, vc, P_cap, nullptr, nullptr, c.chunk, prefix_lens, B, Hq, Hkv, D,
                 L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),
-                L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr, cnt + L.gemm_counters};
+                L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr};
     launch_attention(ctx->dt, ap, s);
     enqueue_finish(ctx, L, ws, L.pv, e, hp, at<void>(ws, L.o_p), at<void>(ws, L.act_p), Mp, c.vlm_ffn, prow,
                    vlm->attn_norm + (size_t)(l + 1) * Hv, s);

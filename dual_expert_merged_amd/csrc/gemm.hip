@@ -14,10 +14,10 @@
 // Two kernels share the epilogues:
 //  * skinny (M <= 64, the batch-1 action chunk): one workgroup owns NT output columns for all
 //    rows and one K slice; its 4 waves each take a quarter of the slice and load MFMA fragments
-//    straight from global memory (16 bytes per lane, four k-chunks in flight), then reduce
-//    through LDS.  Narrow-N GEMMs also split K across workgroups: each writes an fp32 partial
-//    tile, and the last to arrive (arrival counter) sums the partials in split order, so results
-//    do not depend on scheduling, and runs the epilogue.
+//    straight from global memory (16 bytes per lane, the whole slice in flight at once), then
+//    reduce through LDS.  Narrow-N GEMMs also split K across workgroups: each writes an fp32 partial
+//    tile and a second launch (resid_reduce_kernel) sums them in split order and runs the
+//    residual epilogue; the kernel boundary orders the two, so no device-scope fence is needed.
 //  * tiled (larger M): a 64x64 output tile per workgroup, A and W staged through LDS.
 // Column permutations put the two halves of every RoPE pair, and the gate/up pair of every
 // SwiGLU column, in lanes l and l^8 of one MFMA tile, so one cross-lane exchange joins them.
@@ -26,30 +26,64 @@
 
 namespace dm {
 
-__device__ __forceinline__ bool row_valid(const RowMap &rm, int row, int M, int *b_out, int *s_out) {
-  if (row >= M) return false;
-  const int b = row / rm.rows_per_b, s = row - b * rm.rows_per_b;
-  *b_out = b;
-  *s_out = s;
-  return rm.is_prefix ? (s < max(0, min(rm.lens[b], rm.cap))) : true;
-}
 
-// 1/rms of rows m0..m0+63 into inv[64], from per-16-column sums of squares; 4 threads per row,
-// fixed summation order.
+// 1/rms of rows m0..m0+63 into inv[64], from per-16-column sums of squares: 4 threads per row,
+// each summing a contiguous quarter of the row's partials with all its loads in flight, then a
+// fixed-order exchange.  Rows past M use row M-1 (the value is never read).
 __device__ __forceinline__ void rms_prepare(const Hidden &in, int M, float eps, int m0, float *inv) {
   const int t = threadIdx.x, row = t >> 2, part = t & 3;
   const int nt = in.H >> 4;
+  const float *p = in.ssq + (size_t)min(m0 + row, M - 1) * nt;
   float s = 0.f;
-  const int m = m0 + row;
-  if (m < M)
-    for (int i = part; i < nt; i += 4) s += in.ssq[(size_t)m * nt + i];
-  s += __shfl_xor(s, 1, WAVE);
-  s += __shfl_xor(s, 2, WAVE);
+  if ((nt & 15) == 0) {
+    const int per = nt >> 4;  // float4 per thread, at most 16 (H <= 4096)
+    const float4 *q4 = reinterpret_cast<const float4 *>(p) + part * per;
+    float4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = q4[min(j, per - 1)];  // unconditional: loads stay in flight
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < per) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+  } else {
+    for (int i = part; i < nt; i += 4) s += p[i];
+  }
+  s = sum4(s);
   if (part == 0) inv[row] = rsqrtf(s / (float)in.H + eps);
+}
+
+// Epilogues run in two phases per 16x16 tile so that all their global loads (prefix lengths,
+// RoPE table, residual rows) are issued before any is consumed: load() gathers, store() computes
+// and writes.  Rows past M read row M-1 (masked at the store).
+struct RowInfo {
+  int b[4], s[4];
+  bool ok[4];
+  int plen[4];
+};
+__device__ __forceinline__ RowInfo row_info(const RowMap &rm, int row0, int M) {
+  RowInfo ri;
+  int len[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rc = min(row0 + r, M - 1);
+    ri.b[r] = rc / rm.rows_per_b;
+    ri.s[r] = rc - ri.b[r] * rm.rows_per_b;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) len[r] = rm.lens[ri.b[r]];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    ri.plen[r] = max(0, min(len[r], rm.cap));
+    ri.ok[r] = (row0 + r < M) && (rm.is_prefix ? ri.s[r] < ri.plen[r] : true);
+  }
+  return ri;
 }
 
 template <typename T> struct EpiQkv {
   QkvArgs a;
+  struct St {
+    RowInfo ri;
+    float2 cs[4];
+  };
   __device__ __forceinline__ int col(int c) const {
     const int qd = a.Hq * a.D, kd = a.Hkv * a.D;
     const int base = c < qd ? 0 : (c < qd + kd ? qd : qd + kd);
@@ -62,32 +96,39 @@ template <typename T> struct EpiQkv {
   __device__ __forceinline__ const T *wrow(int c) const { return (const T *)a.w + (size_t)col(c) * a.in.H; }
   __device__ __forceinline__ void prepare(int m0, float *inv) const { rms_prepare(a.in, a.M, a.eps, m0, inv); }
 
-  __device__ __forceinline__ void tile(int row0, int c, f32x4 acc, const float *inv, int m0) const {
+  __device__ __forceinline__ St load(int row0, int c) const {
+    St st;
+    st.ri = row_info(a.rows, row0, a.M);
+    const int gc = col(c);
+    const int D = a.D, half = D >> 1;
+    const int d = gc % D;
+    const int i = d < half ? d : d - half;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pos = a.rows.is_prefix ? st.ri.s[r] : st.ri.plen[r] + st.ri.s[r];
+      st.cs[r] = a.rope[(size_t)pos * half + i];  // also read for value columns (unused there)
+    }
+    return st;
+  }
+  __device__ __forceinline__ void store(const St &st, int row0, int c, f32x4 acc, const float *inv, int m0) const {
     const int gc = col(c);
     const int D = a.D, qd = a.Hq * D, kd = a.Hkv * D;
     const int sec = gc < qd ? 0 : (gc < qd + kd ? 1 : 2);
     const int local = gc - (sec == 0 ? 0 : (sec == 1 ? qd : qd + kd));
     const int head = local / D, d = local - head * D;
-    const int half = D >> 1;
-    const int upper = d >= half;
-    const int i = d - upper * half;
+    const int upper = d >= (D >> 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float u = acc[r] * inv[row0 + r - m0];
-      const float pu = __shfl_xor(u, 8, WAVE);
-      int b, s;
-      if (!row_valid(a.rows, row0 + r, a.M, &b, &s)) continue;
-      if (sec < 2) {
-        const int pos = a.rows.is_prefix ? s : max(0, min(a.rows.lens[b], a.rows.cap)) + s;
-        const float2 cs = a.rope[(size_t)pos * half + i];
-        u = upper ? (u * cs.x + pu * cs.y) : (u * cs.x - pu * cs.y);
-      }
+      const float pu = lane_xor8(u);
+      if (sec < 2) u = upper ? (u * st.cs[r].x + pu * st.cs[r].y) : (u * st.cs[r].x - pu * st.cs[r].y);
+      if (!st.ri.ok[r]) continue;
       const T val = from_f32<T>(u);
       if (sec == 0) {
         ((T *)a.q)[(size_t)(row0 + r) * qd + gc] = val;
       } else {
         T *dst = (T *)(sec == 1 ? a.k : a.v);
-        dst[((size_t)(b * a.Hkv + head) * a.kv_rows + s) * D + d] = val;
+        dst[((size_t)(st.ri.b[r] * a.Hkv + head) * a.kv_rows + st.ri.s[r]) * D + d] = val;
       }
     }
   }
@@ -95,27 +136,34 @@ template <typename T> struct EpiQkv {
 
 template <typename T> struct EpiResid {
   ResidArgs a;
+  struct St {
+    RowInfo ri;
+    float hv[4];
+    float gain;
+  };
   __device__ __forceinline__ const T *wrow(int c) const { return (const T *)a.w + (size_t)c * a.K; }
   __device__ __forceinline__ void prepare(int, float *) const {}
-  __device__ __forceinline__ void tile(int row0, int c, f32x4 acc, const float *, int) const {
+  __device__ __forceinline__ St load(int row0, int c) const {
+    St st;
+    st.ri = row_info(a.rows, row0, a.M);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st.hv[r] = a.out.h[(size_t)min(row0 + r, a.M - 1) * a.out.H + c];
+    st.gain = a.next_gain ? a.next_gain[c] : 0.f;
+    return st;
+  }
+  __device__ __forceinline__ void store(const St &st, int row0, int c, f32x4 acc, const float *, int) const {
     const int H = a.out.H;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + r;
-      int b, s;
-      const bool ok = row_valid(a.rows, row, a.M, &b, &s);
-      float hn = 0.f;
+      const bool ok = st.ri.ok[r];
+      const float hn = ok ? st.hv[r] + acc[r] : 0.f;
       if (ok) {
-        hn = a.out.h[(size_t)row * H + c] + acc[r];
         a.out.h[(size_t)row * H + c] = hn;
-        if (a.next_gain) ((T *)a.out.hg)[(size_t)row * H + c] = from_f32<T>(hn * a.next_gain[c]);
+        if (a.next_gain) ((T *)a.out.hg)[(size_t)row * H + c] = from_f32<T>(hn * st.gain);
       }
       if (a.next_gain) {
-        float sq = hn * hn;
-        sq += __shfl_xor(sq, 1, WAVE);
-        sq += __shfl_xor(sq, 2, WAVE);
-        sq += __shfl_xor(sq, 4, WAVE);
-        sq += __shfl_xor(sq, 8, WAVE);
+        const float sq = sum16(hn * hn);
         if (ok && (c & 15) == 0) a.out.ssq[(size_t)row * (H >> 4) + (c >> 4)] = sq;
       }
     }
@@ -124,45 +172,46 @@ template <typename T> struct EpiResid {
 
 template <typename T> struct EpiSwiglu {
   SwigluArgs a;
+  struct St {
+    RowInfo ri;
+  };
   __device__ __forceinline__ const T *wrow(int c) const {
     const int f = (c >> 4) * 8 + (c & 7);
     return (const T *)((c >> 3) & 1 ? a.wu : a.wg) + (size_t)f * a.in.H;
   }
   __device__ __forceinline__ void prepare(int m0, float *inv) const { rms_prepare(a.in, a.M, a.eps, m0, inv); }
-  __device__ __forceinline__ void tile(int row0, int c, f32x4 acc, const float *inv, int m0) const {
+  __device__ __forceinline__ St load(int row0, int) const { return St{row_info(a.rows, row0, a.M)}; }
+  __device__ __forceinline__ void store(const St &st, int row0, int c, f32x4 acc, const float *inv, int m0) const {
     const int f = (c >> 4) * 8 + (c & 7);
     const int up = (c >> 3) & 1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float g = acc[r] * inv[row0 + r - m0];
-      const float u = __shfl_xor(g, 8, WAVE);
-      int b, s;
-      if (up || !row_valid(a.rows, row0 + r, a.M, &b, &s)) continue;
+      const float u = lane_xor8(g);
+      if (up || !st.ri.ok[r]) continue;
       ((T *)a.act)[(size_t)(row0 + r) * a.F + f] = from_f32<T>(silu(g) * u);
     }
   }
 };
 
 // ------------------------------------------------------------------------ skinny kernel (M <= 64)
-template <typename T, int NT, class Epi>
+// NK: MFMA k-chunks per wave; every fragment of the workgroup's slice is loaded before the first
+// MFMA, so each wave keeps NK*(CT+4) 16-byte loads per lane in flight.
+template <typename T, int NT, int NK, class Epi>
 __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, int M, int K, Epi epi, SplitK sk) {
   typedef Mfma<T> MF;
   typedef typename MF::frag frag;
-  constexpr int EPL = MF::EPL, KC = 4 * EPL, CT = NT / 16, U = 4;
+  constexpr int EPL = MF::EPL, KC = 4 * EPL, CT = NT / 16;
   __shared__ __attribute__((aligned(16))) f32x4 red[4 * 4 * CT * 64];
   __shared__ float rinv[64];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int tile = blockIdx.x, split = blockIdx.y, mt = blockIdx.z, m0 = mt * 64;
   const int n0 = tile * NT;
-  const int Ks = K / sk.k_split, Kw = Ks >> 2;
-  const int k0 = split * Ks + wave * Kw;
-  const int nk = Kw / KC;
+  const int Ks = K / sk.k_split;
+  const int k0 = split * Ks + wave * (Ks >> 2);
   const int nrt = min(4, (M - m0 + 15) >> 4);  // row tiles holding valid rows (uniform)
-
-  epi.prepare(m0, rinv);
 
   const T *wp[CT];
 #pragma unroll
@@ -173,38 +222,35 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + i * 16 + c16;
     aok[i] = row < M;
-    ap[i] = A + (size_t)(aok[i] ? row : 0) * K + k0 + g * EPL;
+    ap[i] = A + (size_t)(aok[i] ? row : M - 1) * K + k0 + g * EPL;
   }
+
+  frag wf[NK][CT], af[NK][4];
+#pragma unroll
+  for (int u = 0; u < NK; ++u)
+#pragma unroll
+    for (int j = 0; j < CT; ++j) wf[u][j] = load_frag<T>(wp[j] + u * KC);
+  // No branch may sit between these loads: a load under a condition is followed by a wait for
+  // it, which would serialise the whole sequence.  Rows past M read row M-1 and are masked.
+#pragma unroll
+  for (int u = 0; u < NK; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[u][i] = load_frag_masked<T>(ap[i] + u * KC, aok[i]);
+
+  epi.prepare(m0, rinv);
 
   f32x4 acc[4][CT];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < CT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kc = 0; kc < nk; kc += U) {
-    frag wf[U][CT], af[U][4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (kc + u < nk) {
+  for (int u = 0; u < NK; ++u)
 #pragma unroll
-        for (int j = 0; j < CT; ++j) wf[u][j] = load_frag<T>(wp[j] + (kc + u) * KC);
+    for (int i = 0; i < 4; ++i)
+      if (i < nrt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[u][i] = (i < nrt && aok[i]) ? load_frag<T>(ap[i] + (kc + u) * KC) : zero_frag<T>();
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (kc + u < nk) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (i < nrt)
-#pragma unroll
-            for (int j = 0; j < CT; ++j) acc[i][j] = MF::mma(af[u][i], wf[u][j], acc[i][j]);
-      }
-    }
-  }
+        for (int j = 0; j < CT; ++j) acc[i][j] = MF::mma(af[u][i], wf[u][j], acc[i][j]);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -221,27 +267,67 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
   }
 
   if (sk.k_split > 1) {
-    const size_t tile_id = (size_t)mt * gridDim.x + tile;
-    f32x4 *part = reinterpret_cast<f32x4 *>(sk.part) + tile_id * sk.k_split * (4 * CT * 64);
+    // K split across workgroups: store this slice's partial sums [split][M][N] (row-major) and
+    // leave the sum and the epilogue to resid_reduce_kernel, launched next.
+    if (wave < nrt) {
+      const int N = gridDim.x * NT;
 #pragma unroll
-    for (int j = 0; j < CT; ++j) part[(size_t)split * (4 * CT * 64) + (wave * CT + j) * 64 + lane] = sum[j];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&sk.counters[tile_id], 1u) == (unsigned)(sk.k_split - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+      for (int j = 0; j < CT; ++j)
 #pragma unroll
-    for (int j = 0; j < CT; ++j) {
-      f32x4 t = part[(wave * CT + j) * 64 + lane];
-      for (int sp = 1; sp < sk.k_split; ++sp) t += part[(size_t)sp * (4 * CT * 64) + (wave * CT + j) * 64 + lane];
-      sum[j] = t;
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wave * 16 + 4 * g + r;
+          if (row < M) sk.part[((size_t)split * M + row) * N + n0 + j * 16 + c16] = sum[j][r];
+        }
     }
-    if (tid == 0) sk.counters[tile_id] = 0u;
+    return;
   }
   if (wave < nrt) {
+    typename Epi::St st[CT];
 #pragma unroll
-    for (int j = 0; j < CT; ++j) epi.tile(m0 + wave * 16 + 4 * g, n0 + j * 16 + c16, sum[j], rinv, m0);
+    for (int j = 0; j < CT; ++j) st[j] = epi.load(m0 + wave * 16 + 4 * g, n0 + j * 16 + c16);
+#pragma unroll
+    for (int j = 0; j < CT; ++j) epi.store(st[j], m0 + wave * 16 + 4 * g, n0 + j * 16 + c16, sum[j], rinv, m0);
+  }
+}
+
+// Sum of the K-split partials of a residual projection plus the residual epilogue:
+// h += sum_s part[s], hg = h * next_gain, per-16-column sums of squares.  Thread = 4 columns of
+// one row; the split sum runs in split order.
+template <typename T>
+__global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const float *__restrict__ part, int ks) {
+  const int H = a.out.H, q4 = H >> 2;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int row = min(idx / q4, a.M - 1), c = (idx - (idx / q4) * q4) * 4;
+  const bool in_range = idx < a.M * q4;
+  float4 pv[16];
+#pragma unroll
+  for (int sp = 0; sp < 16; ++sp)  // unconditional (clamped) loads stay in flight together
+    pv[sp] = *reinterpret_cast<const float4 *>(part + ((size_t)min(sp, ks - 1) * a.M + row) * H + c);
+  float4 hv = *reinterpret_cast<const float4 *>(a.out.h + (size_t)row * H + c);
+  float4 gv = a.next_gain ? *reinterpret_cast<const float4 *>(a.next_gain + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const int b = row / a.rows.rows_per_b, s = row - b * a.rows.rows_per_b;
+  const int plen = max(0, min(a.rows.lens[b], a.rows.cap));
+  const bool ok = in_range && (a.rows.is_prefix ? s < plen : true);
+  float4 t = pv[0];
+#pragma unroll
+  for (int sp = 1; sp < 16; ++sp)
+    if (sp < ks) {
+      t.x += pv[sp].x; t.y += pv[sp].y; t.z += pv[sp].z; t.w += pv[sp].w;
+    }
+  const float4 hn = make_float4(hv.x + t.x, hv.y + t.y, hv.z + t.z, hv.w + t.w);
+  if (ok) {
+    *reinterpret_cast<float4 *>(a.out.h + (size_t)row * H + c) = hn;
+    if (a.next_gain) {
+      T *hg = (T *)a.out.hg + (size_t)row * H + c;
+      hg[0] = from_f32<T>(hn.x * gv.x);
+      hg[1] = from_f32<T>(hn.y * gv.y);
+      hg[2] = from_f32<T>(hn.z * gv.z);
+      hg[3] = from_f32<T>(hn.w * gv.w);
+    }
+  }
+  if (a.next_gain) {
+    const float sq = sum4(ok ? hn.x * hn.x + hn.y * hn.y + hn.z * hn.z + hn.w * hn.w : 0.f);
+    if (ok && (c & 15) == 0) a.out.ssq[(size_t)row * (H >> 4) + (c >> 4)] = sq;
   }
 }
 
@@ -265,7 +351,6 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  epi.prepare(m0, rinv);
 
   const T *asrc[AV];
   bool aok[AV];
@@ -274,7 +359,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
   for (int v = 0; v < AV; ++v) {
     const int idx = tid + v * 256, r = idx / VPR, cv = idx % VPR;
     aok[v] = (m0 + r) < M;
-    asrc[v] = A + (size_t)(aok[v] ? m0 + r : 0) * K + cv * EPL;
+    asrc[v] = A + (size_t)(aok[v] ? m0 + r : M - 1) * K + cv * EPL;
     adst[v] = r * LDR + cv * EPL;
   }
   const T *wsrc[WV];
@@ -289,7 +374,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
   frag ra[AV], rw[WV];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int v = 0; v < AV; ++v) ra[v] = aok[v] ? load_frag<T>(asrc[v] + k0) : zero_frag<T>();
+    for (int v = 0; v < AV; ++v) ra[v] = load_frag_masked<T>(asrc[v] + k0, aok[v]);
 #pragma unroll
     for (int v = 0; v < WV; ++v) rw[v] = load_frag<T>(wsrc[v] + k0);
   };
@@ -301,6 +386,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   gload(0);
+  epi.prepare(m0, rinv);
   for (int k0 = 0; k0 < K; k0 += BK) {
     __syncthreads();
 #pragma unroll
@@ -326,22 +412,39 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
     }
   }
 
+  typename Epi::St st[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      epi.tile(m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4), n0 + wn * (BN / 2) + j * 16 + (lane & 15),
-               acc[i][j], rinv, m0);
+      st[i][j] = epi.load(m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4), n0 + wn * (BN / 2) + j * 16 + (lane & 15));
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      epi.store(st[i][j], m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4), n0 + wn * (BN / 2) + j * 16 + (lane & 15),
+                acc[i][j], rinv, m0);
+}
+
+template <typename T, int NT, class Epi>
+static void run_skinny(const T *A, int M, int N, int K, const Epi &epi, const GemmPlan &p, hipStream_t s) {
+  dim3 grid(N / NT, p.sk.k_split, (M + 63) / 64);
+  const int nk = K / p.sk.k_split / 4 / (4 * Mfma<T>::EPL);
+  switch (nk) {
+#define DM_NK(n) case n: hipLaunchKernelGGL((skinny_kernel<T, NT, n, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk); break;
+    DM_NK(1) DM_NK(2) DM_NK(3) DM_NK(4) DM_NK(5) DM_NK(6) DM_NK(7) DM_NK(8)
+#undef DM_NK
+    default: break;  // the host plan never asks for more than 8 k-chunks per wave
+  }
 }
 
 template <typename T, class Epi>
 static void run_gemm(const T *A, int M, int N, int K, const Epi &epi, const GemmPlan &p, hipStream_t s) {
   if (p.skinny) {
-    dim3 grid(N / p.nt, p.sk.k_split, (M + 63) / 64);
     switch (p.nt) {
-      case 16: hipLaunchKernelGGL((skinny_kernel<T, 16, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk); break;
-      case 32: hipLaunchKernelGGL((skinny_kernel<T, 32, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk); break;
-      default: hipLaunchKernelGGL((skinny_kernel<T, 64, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk); break;
+      case 16: run_skinny<T, 16>(A, M, N, K, epi, p, s); break;
+      case 32: run_skinny<T, 32>(A, M, N, K, epi, p, s); break;
+      default: run_skinny<T, 64>(A, M, N, K, epi, p, s); break;
     }
   } else {
     dim3 grid(N / 64, (M + 63) / 64);
@@ -354,6 +457,10 @@ template <typename T> static void qkv_t(const QkvArgs &a, const GemmPlan &p, hip
 }
 template <typename T> static void resid_t(const ResidArgs &a, const GemmPlan &p, hipStream_t s) {
   run_gemm<T>((const T *)a.a, a.M, a.out.H, a.K, EpiResid<T>{a}, p, s);
+  if (p.skinny && p.sk.k_split > 1) {
+    const int n = a.M * (a.out.H / 4);
+    hipLaunchKernelGGL(resid_reduce_kernel<T>, dim3((n + 255) / 256), dim3(256), 0, s, a, p.sk.part, p.sk.k_split);
+  }
 }
 template <typename T> static void swiglu_t(const SwigluArgs &a, const GemmPlan &p, hipStream_t s) {
   run_gemm<T>((const T *)a.in.hg, a.M, 2 * a.F, a.in.H, EpiSwiglu<T>{a}, p, s);

@@ -28,11 +28,10 @@ struct Hidden {
   int H;
 };
 
-// Split-K scratch: fp32 partial tiles and one arrival counter per output tile.
+// Split-K scratch: fp32 partial sums [k_split][M][N].
 struct SplitK {
   int k_split;       // number of K slices (1: no split)
   float *part;
-  unsigned *counters;
 };
 
 // C[M x N] = RMSNorm-scaled A W^T for the fused Q/K/V projection: A = in.hg, rows scaled by
@@ -88,7 +87,6 @@ struct AttnArgs {
   int n_chunks, chunk_keys;          // split of the key range (chunk_keys multiple of 32)
   void *out;                         // token-major [B*q_rows_per_b][Hq*D]
   void *part;                        // partial results when n_chunks > 1 (see attn_partial_bytes)
-  unsigned *counters;                // [B*Hkv*n_qblocks] arrival counters (zero between uses)
 };
 size_t attn_partial_bytes(Dt dt, int B, int Hkv, int n_qblocks, int n_chunks, int D);
 int attn_qblocks(int q_rows, int Hq, int Hkv);

@@ -50,7 +50,7 @@ __device__ __forceinline__ void write_hidden8(const Hidden &hid, const float *ga
     gr[e] = from_f32<T>(v[e] * gain[c0 + e]);
     sq += v[e] * v[e];
   }
-  sq += __shfl_xor(sq, 1, WAVE);
+  sq += dpp<DPP_XOR1>(sq);
   if ((c0 & 15) == 0) hid.ssq[(size_t)m * (hid.H >> 4) + (c0 >> 4)] = sq;
 }
 
@@ -78,92 +78,125 @@ void launch_norm_prep(Dt dt, const float *src, const Hidden &hid, const float *g
 // Page "DM0.5: High-Performance Embodied VLA ...", section 5.2: action_in_proj lifts each
 // action vector to the expert width; the flow time enters as sin/cos(t * 10000^(-2i/H)) added
 // to every action token: h[m][i] = sum_a x[m][a] w_in[i][a] + b_in[i] + tau_i(t).
-// Also writes hg / sums of squares for the first layer's attention norm.
+// Also writes hg / sums of squares for the first layer's attention norm.  Thread = column i
+// (its w_in row loaded once, all loads in flight), workgroup = 256 columns x 8 action tokens.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const float *__restrict__ x, const float *__restrict__ w_in,
                                                     const float *__restrict__ b_in, Hidden hid,
                                                     const float *__restrict__ gain, int M, int A, float t) {
-  constexpr int R = 8;  // action tokens per workgroup
-  extern __shared__ float smem[];
-  float *tau = smem;       // [H]
-  float *xs = smem + hid.H;  // [R][A]
+  constexpr int R = 8;
+  __shared__ float xs[R * 64];
   const int H = hid.H, half = H / 2;
   const int m0 = blockIdx.x * R;
-  for (int i = threadIdx.x; i < half; i += 256) {
-    const double w = pow(10000.0, -2.0 * i / H);
-    tau[i] = (float)sin((double)t * w);
-    tau[i + half] = (float)cos((double)t * w);
-  }
+  const int i_raw = blockIdx.y * 256 + threadIdx.x;
+  const bool col_ok = i_raw < H;  // H is a multiple of 16: whole 16-lane groups agree
+  const int i = col_ok ? i_raw : H - 1;
   for (int j = threadIdx.x; j < R * A; j += 256) xs[j] = (m0 + j / A) < M ? x[(size_t)m0 * A + j] : 0.f;
-  __syncthreads();
-  const int per_row = H / 8;
-  for (int idx = threadIdx.x; idx < R * per_row; idx += 256) {
-    const int r = idx / per_row, c0 = (idx - r * per_row) * 8;
-    const int m = m0 + r;
-    float v[8];
+  float4 w4[16];
+  const float4 *wr = reinterpret_cast<const float4 *>(w_in + (size_t)i * A);
+  const int nw4 = A / 4;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float acc = 0.f;
-      const float *wr = w_in + (size_t)(c0 + e) * A;
-      for (int a = 0; a < A; ++a) acc += wr[a] * xs[r * A + a];
-      v[e] = acc + b_in[c0 + e] + tau[c0 + e];
-    }
-    if (m < M) write_hidden8<T>(hid, gain, m, c0, v, true);
-    else {  // keep the pair exchange of write_hidden8 in step
-      float sq = 0.f;
-      sq += __shfl_xor(sq, 1, WAVE);
+  for (int j = 0; j < 16; ++j) w4[j] = wr[min(j, nw4 - 1)];  // unconditional: loads stay in flight
+  const float bias = b_in[i], gn = gain[i];
+  const int j = i < half ? i : i - half;
+  const double w = pow(10000.0, -2.0 * j / H);
+  const float tau = (float)(i < half ? sin((double)t * w) : cos((double)t * w));
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int m = m0 + r;
+    float acc = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+      if (4 * jj < A) {
+        const float *xr = xs + r * A + 4 * jj;
+        acc += w4[jj].x * xr[0] + w4[jj].y * xr[1] + w4[jj].z * xr[2] + w4[jj].w * xr[3];
+      }
+    const float v = acc + bias + tau;
+    const float sq = sum16(v * v);
+    if (m < M && col_ok) {
+      hid.h[(size_t)m * H + i] = v;
+      ((T *)hid.hg)[(size_t)m * H + i] = from_f32<T>(v * gn);
+      if ((i & 15) == 0) hid.ssq[(size_t)m * (H >> 4) + (i >> 4)] = sq;
     }
   }
 }
 void launch_embed(Dt dt, const float *x, const float *w_in, const float *b_in, const Hidden &hid, const float *gain,
                   int M, int A, float t, hipStream_t s) {
-  const size_t lds = (size_t)(hid.H + 8 * A) * sizeof(float);
+  dim3 grid((M + 7) / 8, (hid.H + 255) / 256);
   if (dt == DT_BF16)
-    hipLaunchKernelGGL(embed_kernel<bf16>, dim3((M + 7) / 8), dim3(256), lds, s, x, w_in, b_in, hid, gain, M, A, t);
+    hipLaunchKernelGGL(embed_kernel<bf16>, grid, dim3(256), 0, s, x, w_in, b_in, hid, gain, M, A, t);
   else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3((M + 7) / 8), dim3(256), lds, s, x, w_in, b_in, hid, gain, M, A, t);
+    hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(256), 0, s, x, w_in, b_in, hid, gain, M, A, t);
 }
 
-__device__ __forceinline__ float block_sum(float v, float *red) {
-  v = wave_sum(v);
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  float t = 0.f;
-  for (int w = 0; w < nw; ++w) t += red[w];
-  return t;
-}
 
 // Page "DM0.5: High-Performance Embodied VLA ...", sections 5.2-5.3: action_out_proj gives the
 // velocity and one explicit Euler step moves x toward t = 0:
 //   v = RMSNorm(h; gain) w_out^T + b_out ;  x <- x - v / N.
-// One workgroup per action token; each wave computes A/4 outputs with lanes across H.
+// One workgroup per action token; thread t owns columns 4t.. of every 1024-column block and
+// issues its w_out loads 16 outputs at a time, then partial sums reduce across the workgroup.
 __global__ __launch_bounds__(256) void velocity_euler_kernel(const float *__restrict__ h, const float *__restrict__ gain,
                                                              const float *__restrict__ w_out,
                                                              const float *__restrict__ b_out, float *__restrict__ x,
                                                              int H, int A, float eps, float inv_steps) {
-  __shared__ float red[4];
-  extern __shared__ float nrm[];
-  const int m = blockIdx.x;
-  const float *row = h + (size_t)m * H;
+  __shared__ float red[4][64];
+  __shared__ float red1[4];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float4 hv[4], gv[4];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += 256) ss += row[i] * row[i];
-  const float inv = rsqrtf(block_sum(ss, red) / H + eps);
-  for (int i = threadIdx.x; i < H; i += 256) nrm[i] = row[i] * inv * gain[i];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // unconditional loads (clamped column) stay in flight together
+    const int c = min(4 * tid + 1024 * j, H - 4);
+    hv[j] = *reinterpret_cast<const float4 *>(h + (size_t)m * H + c);
+    gv[j] = *reinterpret_cast<const float4 *>(gain + c);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (4 * tid + 1024 * j >= H) hv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += hv[j].x * hv[j].x + hv[j].y * hv[j].y + hv[j].z * hv[j].z + hv[j].w * hv[j].w;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red1[wave] = ss;
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int a = wave; a < A; a += 4) {
-    float acc = 0.f;
-    for (int i = lane; i < H; i += 64) acc += w_out[(size_t)a * H + i] * nrm[i];
-    acc = wave_sum(acc);
-    if (lane == 0) x[(size_t)m * A + a] -= (acc + b_out[a]) * inv_steps;
+  const float inv = rsqrtf((red1[0] + red1[1] + red1[2] + red1[3]) / H + eps);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hv[j].x *= inv * gv[j].x; hv[j].y *= inv * gv[j].y; hv[j].z *= inv * gv[j].z; hv[j].w *= inv * gv[j].w;
+  }
+  for (int a0 = 0; a0 < A; a0 += 16) {
+    float part[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) part[k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (1024 * j >= H) break;  // uniform
+      const int c = min(4 * tid + 1024 * j, H - 4);
+      float4 wv[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)  // unconditional loads (clamped row) stay in flight together
+        wv[k] = *reinterpret_cast<const float4 *>(w_out + (size_t)min(a0 + k, A - 1) * H + c);
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        part[k] += wv[k].x * hv[j].x + wv[k].y * hv[j].y + wv[k].z * hv[j].z + wv[k].w * hv[j].w;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float v = wave_sum(part[k]);
+      if (lane == 0) red[wave][k] = v;
+    }
+    __syncthreads();
+    if (tid < 16 && a0 + tid < A) {
+      const float v = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid] + b_out[a0 + tid];
+      x[(size_t)m * A + a0 + tid] -= v * inv_steps;
+    }
+    __syncthreads();
   }
 }
 void launch_velocity_euler(const float *h, const float *gain, const float *w_out, const float *b_out, float *x, int M,
                            int H, int A, float eps, int num_steps, hipStream_t s) {
-  hipLaunchKernelGGL(velocity_euler_kernel, dim3(M), dim3(256), H * sizeof(float), s, h, gain, w_out, b_out, x, H, A,
-                     eps, 1.0f / (float)num_steps);
+  hipLaunchKernelGGL(velocity_euler_kernel, dim3(M), dim3(256), 0, s, h, gain, w_out, b_out, x, H, A, eps,
+                     1.0f / (float)num_steps);
 }
 
 // Nearest E4M3 (OCP e4m3fn) code of a float32 value, ties to even, saturating at +-448:

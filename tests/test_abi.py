@@ -47,6 +47,7 @@ def _cfg(**kw):
     ("act_hidden", 100, bd.DM_ERR_SHAPE),
     ("vlm_ffn", 0, bd.DM_ERR_SHAPE),
     ("action_dim", 65, bd.DM_ERR_UNSUPPORTED),
+    ("action_dim", 30, bd.DM_ERR_UNSUPPORTED),
     ("chunk", 0, bd.DM_ERR_UNSUPPORTED),
     ("dtype", 7, bd.DM_ERR_UNSUPPORTED),
     ("vlm_mlp_dtype", bd.DM_FP8_E4M3, bd.DM_ERR_UNSUPPORTED),  # FP8 MLP needs a bf16 model
