@@ -94,9 +94,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int row = r0 + qt * 16 + c16;
-      const T *qrow = q + (size_t)(b * a.q_rows_per_b + (row < nq ? row : nq - 1)) * HD + h * D;
+      // rows past nq read row nq-1: their columns of the score tile are never stored
+      const T *qrow = q + (size_t)(b * a.q_rows_per_b + min(row, nq - 1)) * HD + h * D;
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) qf[qt][dc] = load_frag_masked<T>(qrow + dc * KC + g * EPL, row < nq);
+      for (int dc = 0; dc < DC; ++dc) qf[qt][dc] = load_frag<T>(qrow + dc * KC + g * EPL);
     }
     const float sc = 1.4426950408889634f / sqrtf((float)D);
     const size_t pre_base = (size_t)(b * a.Hkv + kvh) * a.kp_rows * D;
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const int key = ks0 + r;
         const int kc = min(key, k_end - 1);
         const size_t off = kc < P ? pre_base + (size_t)kc * D : suf_base + (size_t)(kc - P) * D;
-        kv[v] = load_frag_masked<T>((kc < P ? kp : ks) + off + cv * EPL, key < k_end);
+        kv[v] = load_frag<T>((kc < P ? kp : ks) + off + cv * EPL);  // keys past k_end: score -inf
       }
 #pragma unroll
       for (int v = 0; v < LPT; ++v) {
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const int key = ks0 + r;
         const int kc = min(key, k_end - 1);
         const size_t off = kc < P ? pre_base + (size_t)kc * D : suf_base + (size_t)(kc - P) * D;
-        vv[v] = load_frag_masked<T>((kc < P ? vp : vs) + off + cv * EPL, key < k_end);
+        vv[v] = load_frag<T>((kc < P ? vp : vs) + off + cv * EPL);  // finite rows, weight 0
       }
       __syncthreads();  // the previous stage is consumed
 #pragma unroll
@@ -307,8 +308,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         const int c = min(c0 + cc, nch - 1);
-        pv[it][cc] = load_frag_masked<T>(part_o + ((grp * a.n_chunks + c) * ATT_SLOTS + slot) * D + cv * EPL,
-                                         c0 + cc < nch && srow[it] < nq);
+        // chunks past nch re-read chunk nch-1 (weight 0); slots past nq are never stored
+        pv[it][cc] = load_frag<T>(part_o + ((grp * a.n_chunks + c) * ATT_SLOTS + slot) * D + cv * EPL);
       }
     }
 #pragma unroll

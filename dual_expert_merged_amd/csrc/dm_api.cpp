@@ -100,8 +100,9 @@ void attn_split(int B, int Hkv, int nqb, int max_keys, int *n_chunks, int *chunk
   *n_chunks = (max_keys + ck - 1) / ck;
 }
 
-// M <= 64 rows: the skinny kernel.  Wide GEMMs give every workgroup 16 columns over the full K;
-// narrow ones (the residual projections) take 32 columns and split K until ~256 workgroups.
+// M <= 64 rows: the skinny kernel.  Every workgroup takes 32 output columns (each re-reads the
+// whole activation slice from L2, so wider tiles cut that traffic); narrow GEMMs (the residual
+// projections) also split K until ~256 workgroups.
 // Each wave of the skinny kernel holds its whole K slice in registers: at most 8 MFMA k-chunks,
 // otherwise K is split further (residual projections) or the tiled kernel is used.
 GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
@@ -111,7 +112,7 @@ GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
   p.nt = 64;
   if (M > 64) return p;
   const int kq = gemm_k_quantum(dt);  // K per k-chunk across the 4 waves
-  const int nt = (split_ok && N % 32 == 0) ? 32 : 16;
+  const int nt = N % 32 == 0 ? 32 : 16;
   int ks = 1;
   if (split_ok) {
     while ((N / nt) * ks < 256 && ks < 16 && K % (2 * ks * kq) == 0) ks *= 2;

@@ -217,27 +217,29 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
 #pragma unroll
   for (int j = 0; j < CT; ++j) wp[j] = epi.wrow(n0 + j * 16 + c16) + k0 + g * EPL;
   const T *ap[4];
-  bool aok[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + i * 16 + c16;
-    aok[i] = row < M;
-    ap[i] = A + (size_t)(aok[i] ? row : M - 1) * K + k0 + g * EPL;
-  }
+  for (int i = 0; i < 4; ++i) ap[i] = A + (size_t)min(m0 + i * 16 + c16, M - 1) * K + k0 + g * EPL;
 
   frag wf[NK][CT], af[NK][4];
 #pragma unroll
   for (int u = 0; u < NK; ++u)
 #pragma unroll
     for (int j = 0; j < CT; ++j) wf[u][j] = load_frag<T>(wp[j] + u * KC);
-  // No branch may sit between these loads: a load under a condition is followed by a wait for
-  // it, which would serialise the whole sequence.  Rows past M read row M-1 and are masked.
+  // No branch or mask may sit between these loads and their use: a load under a condition, or
+  // one whose value is masked right away, is waited for at once and serialises the sequence.
+  // Rows past M read row M-1; their outputs are never stored, so they need no mask.
 #pragma unroll
   for (int u = 0; u < NK; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[u][i] = load_frag_masked<T>(ap[i] + u * KC, aok[i]);
+    for (int i = 0; i < 4; ++i) af[u][i] = load_frag<T>(ap[i] + u * KC);
 
   epi.prepare(m0, rinv);
+  // the epilogue's own loads (row lengths, RoPE table, residual rows) go out with the operands
+  typename Epi::St st[CT];
+  if (wave < nrt) {
+#pragma unroll
+    for (int j = 0; j < CT; ++j) st[j] = epi.load(m0 + wave * 16 + 4 * g, n0 + j * 16 + c16);
+  }
 
   f32x4 acc[4][CT];
 #pragma unroll
@@ -282,9 +284,6 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
     return;
   }
   if (wave < nrt) {
-    typename Epi::St st[CT];
-#pragma unroll
-    for (int j = 0; j < CT; ++j) st[j] = epi.load(m0 + wave * 16 + 4 * g, n0 + j * 16 + c16);
 #pragma unroll
     for (int j = 0; j < CT; ++j) epi.store(st[j], m0 + wave * 16 + 4 * g, n0 + j * 16 + c16, sum[j], rinv, m0);
   }
@@ -352,14 +351,12 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
 
-  const T *asrc[AV];
-  bool aok[AV];
+  const T *asrc[AV];  // rows past M read row M-1: their outputs are never stored
   int adst[AV];
 #pragma unroll
   for (int v = 0; v < AV; ++v) {
     const int idx = tid + v * 256, r = idx / VPR, cv = idx % VPR;
-    aok[v] = (m0 + r) < M;
-    asrc[v] = A + (size_t)(aok[v] ? m0 + r : M - 1) * K + cv * EPL;
+    asrc[v] = A + (size_t)min(m0 + r, M - 1) * K + cv * EPL;
     adst[v] = r * LDR + cv * EPL;
   }
   const T *wsrc[WV];
@@ -374,7 +371,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
   frag ra[AV], rw[WV];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int v = 0; v < AV; ++v) ra[v] = load_frag_masked<T>(asrc[v] + k0, aok[v]);
+    for (int v = 0; v < AV; ++v) ra[v] = load_frag<T>(asrc[v] + k0);
 #pragma unroll
     for (int v = 0; v < WV; ++v) rw[v] = load_frag<T>(wsrc[v] + k0);
   };
@@ -387,6 +384,12 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
 
   gload(0);
   epi.prepare(m0, rinv);
+  typename Epi::St st[TM][TN];  // the epilogue's loads go out with the first operand tiles
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      st[i][j] = epi.load(m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4), n0 + wn * (BN / 2) + j * 16 + (lane & 15));
   for (int k0 = 0; k0 < K; k0 += BK) {
     __syncthreads();
 #pragma unroll
@@ -412,12 +415,6 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
     }
   }
 
-  typename Epi::St st[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      st[i][j] = epi.load(m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4), n0 + wn * (BN / 2) + j * 16 + (lane & 15));
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
