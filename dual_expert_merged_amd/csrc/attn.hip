@@ -103,16 +103,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const size_t pre_base = (size_t)(b * a.Hkv + kvh) * a.kp_rows * D;
     const size_t suf_base = (size_t)(b * a.Hkv + kvh) * a.S * D;
 
-    for (int ks0 = k_begin; ks0 < k_end; ks0 += ATT_CH) {
-      // K: 16-byte vectors, lanes along a row (coalesced).  V: lanes along keys, so the
-      // transposed LDS stores of a wave hit consecutive addresses.
-      frag kv[LPT], vv[LPT];
+    // K: 16-byte vectors, lanes along a row (coalesced).  V: lanes along keys, so the transposed
+    // LDS stores of a wave hit consecutive addresses.  The next stage is loaded into registers
+    // while the current one is multiplied.
+    frag kv[LPT], vv[LPT];
+    auto stage_load = [&](int ks0) {
 #pragma unroll
       for (int v = 0; v < LPT; ++v) {
         const int idx = tid + v * 256;
         const int r = idx / VPRW, cv = idx - r * VPRW;
-        const int key = ks0 + r;
-        const int kc = min(key, k_end - 1);
+        const int kc = min(ks0 + r, k_end - 1);
         const size_t off = kc < P ? pre_base + (size_t)kc * D : suf_base + (size_t)(kc - P) * D;
         kv[v] = load_frag<T>((kc < P ? kp : ks) + off + cv * EPL);  // keys past k_end: score -inf
       }
@@ -120,11 +120,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       for (int v = 0; v < LPT; ++v) {
         const int idx = tid + v * 256;
         const int cv = idx / ATT_CH, r = idx - cv * ATT_CH;
-        const int key = ks0 + r;
-        const int kc = min(key, k_end - 1);
+        const int kc = min(ks0 + r, k_end - 1);
         const size_t off = kc < P ? pre_base + (size_t)kc * D : suf_base + (size_t)(kc - P) * D;
         vv[v] = load_frag<T>((kc < P ? vp : vs) + off + cv * EPL);  // finite rows, weight 0
       }
+    };
+    stage_load(k_begin);
+    for (int ks0 = k_begin; ks0 < k_end; ks0 += ATT_CH) {
       __syncthreads();  // the previous stage is consumed
 #pragma unroll
       for (int v = 0; v < LPT; ++v) {
@@ -140,6 +142,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int e = 0; e < EPL; ++e) Vt[(cv * EPL + e) * VLD + r] = vv[v][e];
       }
       __syncthreads();
+      if (ks0 + ATT_CH < k_end) stage_load(ks0 + ATT_CH);
 
       const int stage_keys = min(ATT_CH, k_end - ks0);
       for (int t0 = 0; t0 < stage_keys; t0 += ATT_KT) {
@@ -157,13 +160,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             st[s] = acc;
           }
           float mx = -INFINITY;
+          const bool partial = ks0 + t0 + ATT_KT > k_end;  // uniform: only the last tile masks keys
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             const int pv = s / SUB, kk = s % SUB;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int key = ks0 + t0 + pv * KC + g * EPL + 4 * kk + i;
-              const float v = key < k_end ? st[s][i] * sc : -INFINITY;
+              float v = st[s][i] * sc;
+              if (partial && ks0 + t0 + pv * KC + g * EPL + 4 * kk + i >= k_end) v = -INFINITY;
               st[s][i] = v;
               mx = fmaxf(mx, v);
             }

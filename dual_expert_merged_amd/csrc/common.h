@@ -67,12 +67,8 @@ template <typename T> __device__ __forceinline__ typename Mfma<T>::frag zero_fra
 // --------------------------------------------------------------------------- conversions
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
-// Round to nearest even, written out on the bit pattern (finite inputs).
-template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return __builtin_bit_cast(bf16, (uint16_t)(u >> 16));
-}
+// Round to nearest even: one v_cvt_pk_bf16_f32 on gfx950.
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) {
   return __uint_as_float(((uint32_t)__builtin_bit_cast(uint16_t, x)) << 16);
@@ -120,6 +116,7 @@ __device__ __forceinline__ float wave_max(float v) {
   return max_xor32(max_xor16(v));
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware exponential and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 }  // namespace dm

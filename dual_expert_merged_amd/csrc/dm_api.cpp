@@ -110,7 +110,18 @@ GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
   p.sk.k_split = 1;
   p.skinny = 0;
   p.nt = 64;
-  if (M > 64) return p;
+  if (M > 64) {
+    // bf16: 128-row tiles, 256 columns when that still gives >= 128 workgroups, else 128; narrow
+    // GEMMs split K (multiples of 64) until ~200 workgroups.
+    if (dt != DT_BF16 || N % 128 != 0 || K % 64 != 0) return p;
+    const int mt = (M + 127) / 128;
+    p.nt = (N % 256 == 0 && (N / 256) * mt >= 128) ? 256 : 128;
+    if (split_ok)
+      while ((N / p.nt) * mt * p.sk.k_split < 200 && p.sk.k_split < 8 && K % (2 * p.sk.k_split * 64) == 0 &&
+             K / (2 * p.sk.k_split) >= 256)
+        p.sk.k_split *= 2;
+    return p;
+  }
   const int kq = gemm_k_quantum(dt);  // K per k-chunk across the 4 waves
   const int nt = N % 32 == 0 ? 32 : 16;
   int ks = 1;

@@ -18,43 +18,50 @@
 //    reduce through LDS.  Narrow-N GEMMs also split K across workgroups: each writes an fp32 partial
 //    tile and a second launch (resid_reduce_kernel) sums them in split order and runs the
 //    residual epilogue; the kernel boundary orders the two, so no device-scope fence is needed.
-//  * tiled (larger M): a 64x64 output tile per workgroup, A and W staged through LDS.
+//  * big (bf16, larger M): 128 x 256 (or 128 x 128) per workgroup, double-buffered LDS.
+//  * tiled (fp32, larger M): a 64x64 output tile per workgroup, A and W staged through LDS.
 // Column permutations put the two halves of every RoPE pair, and the gate/up pair of every
 // SwiGLU column, in lanes l and l^8 of one MFMA tile, so one cross-lane exchange joins them.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace dm {
 
 
-// 1/rms of rows m0..m0+63 into inv[64], from per-16-column sums of squares: 4 threads per row,
-// each summing a contiguous quarter of the row's partials with all its loads in flight, then a
-// fixed-order exchange.  Rows past M use row M-1 (the value is never read).
-__device__ __forceinline__ void rms_prepare(const Hidden &in, int M, float eps, int m0, float *inv) {
-  const int t = threadIdx.x, row = t >> 2, part = t & 3;
+// 1/rms of rows m0..m0+rows-1 into inv[], from per-16-column sums of squares: 4 threads per row
+// (64 rows per pass of 256 threads), each summing a contiguous quarter of the row's partials with
+// all its loads in flight, then a fixed-order exchange.  Rows past M use row M-1 (never read).
+__device__ __forceinline__ void rms_prepare(const Hidden &in, int M, float eps, int m0, int rows, float *inv) {
   const int nt = in.H >> 4;
-  const float *p = in.ssq + (size_t)min(m0 + row, M - 1) * nt;
-  float s = 0.f;
-  if ((nt & 15) == 0) {
-    const int per = nt >> 4;  // float4 per thread, at most 16 (H <= 4096)
-    const float4 *q4 = reinterpret_cast<const float4 *>(p) + part * per;
-    float4 v[16];
+  for (int base = 0; base < rows; base += 64) {
+    const int t = threadIdx.x, row = base + (t >> 2), part = t & 3;
+    const float *p = in.ssq + (size_t)min(m0 + row, M - 1) * nt;
+    float s = 0.f;
+    if ((nt & 15) == 0) {
+      const int per = nt >> 4;  // float4 per thread, at most 16 (H <= 4096)
+      const float4 *q4 = reinterpret_cast<const float4 *>(p) + part * per;
+      float4 v[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = q4[min(j, per - 1)];  // unconditional: loads stay in flight
+      for (int j = 0; j < 16; ++j) v[j] = q4[min(j, per - 1)];  // unconditional: loads stay in flight
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < per) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
-  } else {
-    for (int i = part; i < nt; i += 4) s += p[i];
+      for (int j = 0; j < 16; ++j)
+        if (j < per) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+    } else {
+      for (int i = part; i < nt; i += 4) s += p[i];
+    }
+    s = sum4(s);
+    if (part == 0) inv[row] = rsqrtf(s / (float)in.H + eps);
   }
-  s = sum4(s);
-  if (part == 0) inv[row] = rsqrtf(s / (float)in.H + eps);
 }
 
-// Epilogues run in two phases per 16x16 tile so that all their global loads (prefix lengths,
-// RoPE table, residual rows) are issued before any is consumed: load() gathers, store() computes
-// and writes.  Rows past M read row M-1 (masked at the store).
+// Epilogues run per 16x16 tile in two phases so that their global loads (RoPE table, residual
+// rows) are all issued before any is consumed: load() gathers, store() computes and writes.  The
+// row facts (sample, token, validity) of a 16-row tile are shared by all its column tiles.
+// Rows past M read row M-1 (masked at the store).
 struct RowInfo {
+  int rc[4];  // row index clamped to M-1
   int b[4], s[4];
   bool ok[4];
   int plen[4];
@@ -62,11 +69,17 @@ struct RowInfo {
 __device__ __forceinline__ RowInfo row_info(const RowMap &rm, int row0, int M) {
   RowInfo ri;
   int len[4];
+  // one division for the tile; the 4 consecutive rows step across at most one sample boundary
+  const int r0c = min(row0, M - 1);
+  const int b0 = r0c / rm.rows_per_b, s0 = r0c - b0 * rm.rows_per_b;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int rc = min(row0 + r, M - 1);
-    ri.b[r] = rc / rm.rows_per_b;
-    ri.s[r] = rc - ri.b[r] * rm.rows_per_b;
+    const int s = s0 + (rc - r0c);
+    const int wrap = s >= rm.rows_per_b;
+    ri.rc[r] = rc;
+    ri.b[r] = b0 + wrap;
+    ri.s[r] = s - wrap * rm.rows_per_b;
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) len[r] = rm.lens[ri.b[r]];
@@ -81,54 +94,56 @@ __device__ __forceinline__ RowInfo row_info(const RowMap &rm, int row0, int M) {
 template <typename T> struct EpiQkv {
   QkvArgs a;
   struct St {
-    RowInfo ri;
     float2 cs[4];
   };
+  __device__ __forceinline__ const RowMap &rows() const { return a.rows; }
+  // head_dim is a power of two: divisions by D and D/2 are shifts and masks
+  __device__ __forceinline__ int dlog() const { return 31 - __builtin_clz(a.D); }
   __device__ __forceinline__ int col(int c) const {
     const int qd = a.Hq * a.D, kd = a.Hkv * a.D;
     const int base = c < qd ? 0 : (c < qd + kd ? qd : qd + kd);
     const int local = c - base;
-    const int half = a.D >> 1;
+    const int hl = dlog() - 1, half = a.D >> 1;
     const int p = (local >> 4) * 8 + (local & 7);
     const int upper = (local >> 3) & 1;
-    return base + (p / half) * a.D + (p % half) + upper * half;
+    return base + ((p >> hl) << (hl + 1)) + (p & (half - 1)) + upper * half;
   }
   __device__ __forceinline__ const T *wrow(int c) const { return (const T *)a.w + (size_t)col(c) * a.in.H; }
-  __device__ __forceinline__ void prepare(int m0, float *inv) const { rms_prepare(a.in, a.M, a.eps, m0, inv); }
-
-  __device__ __forceinline__ St load(int row0, int c) const {
+  __device__ __forceinline__ void prepare(int m0, int rows, float *inv) const {
+    rms_prepare(a.in, a.M, a.eps, m0, rows, inv);
+  }
+  __device__ __forceinline__ St load(const RowInfo &ri, int c) const {
     St st;
-    st.ri = row_info(a.rows, row0, a.M);
-    const int gc = col(c);
     const int D = a.D, half = D >> 1;
-    const int d = gc % D;
-    const int i = d < half ? d : d - half;
+    const int d = col(c) & (D - 1);
+    const int i = d & (half - 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int pos = a.rows.is_prefix ? st.ri.s[r] : st.ri.plen[r] + st.ri.s[r];
+      const int pos = a.rows.is_prefix ? ri.s[r] : ri.plen[r] + ri.s[r];
       st.cs[r] = a.rope[(size_t)pos * half + i];  // also read for value columns (unused there)
     }
     return st;
   }
-  __device__ __forceinline__ void store(const St &st, int row0, int c, f32x4 acc, const float *inv, int m0) const {
+  __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
+                                        int m0) const {
     const int gc = col(c);
     const int D = a.D, qd = a.Hq * D, kd = a.Hkv * D;
     const int sec = gc < qd ? 0 : (gc < qd + kd ? 1 : 2);
     const int local = gc - (sec == 0 ? 0 : (sec == 1 ? qd : qd + kd));
-    const int head = local / D, d = local - head * D;
+    const int head = local >> dlog(), d = local & (D - 1);
     const int upper = d >= (D >> 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float u = acc[r] * inv[row0 + r - m0];
       const float pu = lane_xor8(u);
       if (sec < 2) u = upper ? (u * st.cs[r].x + pu * st.cs[r].y) : (u * st.cs[r].x - pu * st.cs[r].y);
-      if (!st.ri.ok[r]) continue;
+      if (!ri.ok[r]) continue;
       const T val = from_f32<T>(u);
       if (sec == 0) {
         ((T *)a.q)[(size_t)(row0 + r) * qd + gc] = val;
       } else {
         T *dst = (T *)(sec == 1 ? a.k : a.v);
-        dst[((size_t)(st.ri.b[r] * a.Hkv + head) * a.kv_rows + st.ri.s[r]) * D + d] = val;
+        dst[((size_t)(ri.b[r] * a.Hkv + head) * a.kv_rows + ri.s[r]) * D + d] = val;
       }
     }
   }
@@ -137,26 +152,26 @@ template <typename T> struct EpiQkv {
 template <typename T> struct EpiResid {
   ResidArgs a;
   struct St {
-    RowInfo ri;
     float hv[4];
     float gain;
   };
+  __device__ __forceinline__ const RowMap &rows() const { return a.rows; }
   __device__ __forceinline__ const T *wrow(int c) const { return (const T *)a.w + (size_t)c * a.K; }
-  __device__ __forceinline__ void prepare(int, float *) const {}
-  __device__ __forceinline__ St load(int row0, int c) const {
+  __device__ __forceinline__ void prepare(int, int, float *) const {}
+  __device__ __forceinline__ St load(const RowInfo &ri, int c) const {
     St st;
-    st.ri = row_info(a.rows, row0, a.M);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st.hv[r] = a.out.h[(size_t)min(row0 + r, a.M - 1) * a.out.H + c];
+    for (int r = 0; r < 4; ++r) st.hv[r] = a.out.h[(size_t)ri.rc[r] * a.out.H + c];
     st.gain = a.next_gain ? a.next_gain[c] : 0.f;
     return st;
   }
-  __device__ __forceinline__ void store(const St &st, int row0, int c, f32x4 acc, const float *, int) const {
+  __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *,
+                                        int) const {
     const int H = a.out.H;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + r;
-      const bool ok = st.ri.ok[r];
+      const bool ok = ri.ok[r];
       const float hn = ok ? st.hv[r] + acc[r] : 0.f;
       if (ok) {
         a.out.h[(size_t)row * H + c] = hn;
@@ -172,23 +187,25 @@ template <typename T> struct EpiResid {
 
 template <typename T> struct EpiSwiglu {
   SwigluArgs a;
-  struct St {
-    RowInfo ri;
-  };
+  struct St {};
+  __device__ __forceinline__ const RowMap &rows() const { return a.rows; }
   __device__ __forceinline__ const T *wrow(int c) const {
     const int f = (c >> 4) * 8 + (c & 7);
     return (const T *)((c >> 3) & 1 ? a.wu : a.wg) + (size_t)f * a.in.H;
   }
-  __device__ __forceinline__ void prepare(int m0, float *inv) const { rms_prepare(a.in, a.M, a.eps, m0, inv); }
-  __device__ __forceinline__ St load(int row0, int) const { return St{row_info(a.rows, row0, a.M)}; }
-  __device__ __forceinline__ void store(const St &st, int row0, int c, f32x4 acc, const float *inv, int m0) const {
+  __device__ __forceinline__ void prepare(int m0, int rows, float *inv) const {
+    rms_prepare(a.in, a.M, a.eps, m0, rows, inv);
+  }
+  __device__ __forceinline__ St load(const RowInfo &, int) const { return St{}; }
+  __device__ __forceinline__ void store(const St &, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
+                                        int m0) const {
     const int f = (c >> 4) * 8 + (c & 7);
     const int up = (c >> 3) & 1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float g = acc[r] * inv[row0 + r - m0];
       const float u = lane_xor8(g);
-      if (up || !st.ri.ok[r]) continue;
+      if (up || !ri.ok[r]) continue;
       ((T *)a.act)[(size_t)(row0 + r) * a.F + f] = from_f32<T>(silu(g) * u);
     }
   }
@@ -233,13 +250,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) af[u][i] = load_frag<T>(ap[i] + u * KC);
 
-  epi.prepare(m0, rinv);
+  epi.prepare(m0, 64, rinv);
   // the epilogue's own loads (row lengths, RoPE table, residual rows) go out with the operands
+  const RowInfo ri = row_info(epi.rows(), m0 + wave * 16 + 4 * g, M);
   typename Epi::St st[CT];
-  if (wave < nrt) {
 #pragma unroll
-    for (int j = 0; j < CT; ++j) st[j] = epi.load(m0 + wave * 16 + 4 * g, n0 + j * 16 + c16);
-  }
+  for (int j = 0; j < CT; ++j) st[j] = epi.load(ri, n0 + j * 16 + c16);
 
   f32x4 acc[4][CT];
 #pragma unroll
@@ -285,7 +301,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
   }
   if (wave < nrt) {
 #pragma unroll
-    for (int j = 0; j < CT; ++j) epi.store(st[j], m0 + wave * 16 + 4 * g, n0 + j * 16 + c16, sum[j], rinv, m0);
+    for (int j = 0; j < CT; ++j) epi.store(st[j], ri, m0 + wave * 16 + 4 * g, n0 + j * 16 + c16, sum[j], rinv, m0);
   }
 }
 
@@ -327,6 +343,117 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
   if (a.next_gain) {
     const float sq = sum4(ok ? hn.x * hn.x + hn.y * hn.y + hn.z * hn.z + hn.w * hn.w : 0.f);
     if (ok && (c & 15) == 0) a.out.ssq[(size_t)row * (H >> 4) + (c >> 4)] = sq;
+  }
+}
+
+// ------------------------------------------------------------------------ big kernel (bf16, M > 64)
+// Workgroup tile 128 x BN (BN = 256 or 128); four waves as 2 x 2, each 64 x BN/2, i.e. 4 x BN/32
+// MFMA 16x16 tiles, so every 16-byte LDS fragment read feeds several MFMAs.  K advances 64 at a
+// time through two LDS buffers: the next k-step is loaded into registers while the current one
+// is multiplied, then stored to the other buffer, one barrier per k-step.  Rows are padded to 144
+// bytes, which spreads the 16 rows of a fragment read over all LDS banks.  grid.z splits K (the
+// narrow residual projections), each split writing fp32 partial sums for resid_reduce_kernel.
+template <int BN, class Epi>
+__global__ __launch_bounds__(256) void big_kernel(const bf16 *__restrict__ A, int M, int K, Epi epi, SplitK sk) {
+  typedef Mfma<bf16> MF;
+  typedef MF::frag frag;
+  constexpr int BM = 128, BK = 64, LD = BK + 8;
+  constexpr int TN = BN / 32;
+  constexpr int AV = BM * BK / 8 / 256, WV = BN * BK / 8 / 256;
+  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LD];
+  __shared__ __attribute__((aligned(16))) bf16 Ws[2][BN * LD];
+  __shared__ float rinv[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM, split = blockIdx.z;
+  const int Ks = K / sk.k_split, kb = split * Ks, nkt = Ks / BK;
+
+  const bf16 *asrc[AV];
+  int adst[AV];
+#pragma unroll
+  for (int v = 0; v < AV; ++v) {
+    const int idx = tid + v * 256, r = idx >> 3, cv = idx & 7;
+    asrc[v] = A + (size_t)min(m0 + r, M - 1) * K + kb + cv * 8;  // rows past M: never stored
+    adst[v] = r * LD + cv * 8;
+  }
+  const bf16 *wsrc[WV];
+  int wdst[WV];
+#pragma unroll
+  for (int v = 0; v < WV; ++v) {
+    const int idx = tid + v * 256, r = idx >> 3, cv = idx & 7;
+    wsrc[v] = epi.wrow(n0 + r) + kb + cv * 8;
+    wdst[v] = r * LD + cv * 8;
+  }
+  frag ra[AV], rw[WV];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int v = 0; v < AV; ++v) ra[v] = load_frag<bf16>(asrc[v] + kt * BK);
+#pragma unroll
+    for (int v = 0; v < WV; ++v) rw[v] = load_frag<bf16>(wsrc[v] + kt * BK);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int v = 0; v < AV; ++v) *reinterpret_cast<frag *>(&As[buf][adst[v]]) = ra[v];
+#pragma unroll
+    for (int v = 0; v < WV; ++v) *reinterpret_cast<frag *>(&Ws[buf][wdst[v]]) = rw[v];
+  };
+
+  f32x4 acc[4][TN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  epi.prepare(m0, BM, rinv);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nkt) gload(kt + 1);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      frag fa[4], fb[TN];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const frag *>(&As[cur][(wm * 64 + i * 16 + c16) * LD + kc * 32 + g * 8]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[j] = *reinterpret_cast<const frag *>(&Ws[cur][(wn * (BN / 2) + j * 16 + c16) * LD + kc * 32 + g * 8]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[i], fb[j], acc[i][j]);
+    }
+    if (kt + 1 < nkt) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (sk.k_split > 1) {  // partial sums [split][M][N], row-major; resid_reduce_kernel finishes
+    const int N = gridDim.x * BN;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * 64 + i * 16 + 4 * g + r;
+          if (row < M) sk.part[((size_t)split * M + row) * N + n0 + wn * (BN / 2) + j * 16 + c16] = acc[i][j][r];
+        }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row0 = m0 + wm * 64 + i * 16 + 4 * g;
+    if (row0 - 4 * g >= M) break;  // uniform over the wave: the whole 16-row tile is past M
+    const RowInfo ri = row_info(epi.rows(), row0, M);
+    typename Epi::St st[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) st[j] = epi.load(ri, n0 + wn * (BN / 2) + j * 16 + c16);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) epi.store(st[j], ri, row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], rinv, m0);
   }
 }
 
@@ -383,13 +510,15 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   gload(0);
-  epi.prepare(m0, rinv);
+  epi.prepare(m0, 64, rinv);
+  RowInfo ri[TM];
   typename Epi::St st[TM][TN];  // the epilogue's loads go out with the first operand tiles
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    ri[i] = row_info(epi.rows(), m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4), M);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      st[i][j] = epi.load(m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4), n0 + wn * (BN / 2) + j * 16 + (lane & 15));
+    for (int j = 0; j < TN; ++j) st[i][j] = epi.load(ri[i], n0 + wn * (BN / 2) + j * 16 + (lane & 15));
+  }
   for (int k0 = 0; k0 < K; k0 += BK) {
     __syncthreads();
 #pragma unroll
@@ -419,8 +548,8 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      epi.store(st[i][j], m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4), n0 + wn * (BN / 2) + j * 16 + (lane & 15),
-                acc[i][j], rinv, m0);
+      epi.store(st[i][j], ri[i], m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4),
+                n0 + wn * (BN / 2) + j * 16 + (lane & 15), acc[i][j], rinv, m0);
 }
 
 template <typename T, int NT, class Epi>
@@ -443,6 +572,14 @@ static void run_gemm(const T *A, int M, int N, int K, const Epi &epi, const Gemm
       case 32: run_skinny<T, 32>(A, M, N, K, epi, p, s); break;
       default: run_skinny<T, 64>(A, M, N, K, epi, p, s); break;
     }
+  } else if (p.nt >= 128) {
+    if constexpr (std::is_same<T, bf16>::value) {
+      dim3 grid(N / p.nt, (M + 127) / 128, p.sk.k_split);
+      if (p.nt == 256)
+        hipLaunchKernelGGL((big_kernel<256, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk);
+      else
+        hipLaunchKernelGGL((big_kernel<128, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk);
+    }
   } else {
     dim3 grid(N / 64, (M + 63) / 64);
     hipLaunchKernelGGL((tiled_kernel<T, Epi>), grid, dim3(256), 0, s, A, M, K, epi);
@@ -454,7 +591,7 @@ template <typename T> static void qkv_t(const QkvArgs &a, const GemmPlan &p, hip
 }
 template <typename T> static void resid_t(const ResidArgs &a, const GemmPlan &p, hipStream_t s) {
   run_gemm<T>((const T *)a.a, a.M, a.out.H, a.K, EpiResid<T>{a}, p, s);
-  if (p.skinny && p.sk.k_split > 1) {
+  if (p.sk.k_split > 1) {
     const int n = a.M * (a.out.H / 4);
     hipLaunchKernelGGL(resid_reduce_kernel<T>, dim3((n + 255) / 256), dim3(256), 0, s, a, p.sk.part, p.sk.k_split);
   }
