@@ -67,6 +67,48 @@ def cpu_baseline(wl, aw, kc, vc, x1, lens):
                       f"P={P}) in float64 numpy; {dt:.2f} s on {cores} host cores"}
 
 
+def prefill_times(reps=3):
+    """Prefix encoding of the prefill workload (B=8, 816 tokens, 28 VLM layers) with the bf16
+    MLP and with the FP8 E4M3 MLP: mean ms per call over `reps` calls after one warm-up."""
+    import torch
+    from dataclasses import replace
+    from dual_expert_merged_amd import binding as bd
+    from dual_expert_merged_amd import inputs
+    from dual_expert_merged_amd.configs import FP8, workload
+
+    wl = workload(5)
+    vlm = inputs.make_vlm_weights(wl)
+    emb = torch.from_numpy(inputs.make_prefix_embeds(wl)).cuda()
+    lens = torch.from_numpy(inputs.make_prefix_lens(wl)).cuda()
+    s = wl.shape
+    out = {}
+    for name, shape in (("bf16", s), ("fp8_mlp", replace(s, vlm_mlp_dtype=FP8))):
+        ctx = bd.Context(shape, 0)
+        dv = bd.DeviceExpert(vlm, s.dtype, fp8_mlp=name == "fp8_mlp")
+        cshape = (s.n_layers, wl.batch, s.n_kv_heads, wl.prefix_len, s.head_dim)
+        k = torch.empty(cshape, dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        ws = ctx.workspace(bd.OP_PREFILL, wl.batch, wl.prefix_len)
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            ctx.prefill_kv(dv, emb, lens, k, v, ws, stream=stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                ctx.prefill_kv(dv, emb, lens, k, v, ws, stream=stream)
+            e1.record(stream)
+            stream.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / reps, 3)
+        del dv, k, v, ws
+        ctx.close()
+        torch.cuda.empty_cache()
+    flops = 2 * wl.batch * wl.prefix_len * s.n_layers * (s.qkv_rows * s.vlm_hidden + s.vlm_hidden * s.n_q_heads *
+                                                         s.head_dim + 3 * s.vlm_ffn * s.vlm_hidden)
+    out["workload"] = wl.name
+    out["bf16_mfma_frac_of_gemm_flops"] = round(flops / (out["bf16"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -74,6 +116,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, choices=[3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", action="store_true",
+                    help="also time the prefix encoding (B=8, 816 tokens) with the bf16 and the FP8 MLP")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the suffix denoise path is built for a single MI355X "
@@ -145,6 +189,9 @@ def main():
         "roofline": roof,
     }
     plan.close()
+    if args.prefill:
+        log("[bench] timing the prefix encoding (bf16 and FP8 MLP)")
+        out["prefill_ms"] = prefill_times()
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
         out["cpu_baseline"] = cpu_baseline(wl, aw, kc, vc, x1, lens)

@@ -118,9 +118,12 @@ def to_device(a: np.ndarray, dtype=torch.float32, device="cuda"):
 
 
 class DeviceExpert:
-    """One expert's stacked weights resident on the device, plus the C struct pointing at them."""
+    """One expert's stacked weights resident on the device, plus the C struct pointing at them.
 
-    def __init__(self, w, dtype, device="cuda"):
+    fp8_mlp: keep gate/up/down as E4M3 codes with per-output-channel scales, quantised on the
+    device by dm_quantize_fp8_rows from the weight-dtype matrices (bf16 only)."""
+
+    def __init__(self, w, dtype, device="cuda", fp8_mlp=False):
         td = torch_dtype(dtype)
         self.t = {
             "attn_norm": to_device(w.attn_norm, torch.float32, device),
@@ -131,8 +134,17 @@ class DeviceExpert:
             "w_up": to_device(w.w_up, td, device),
             "w_down": to_device(w.w_down, td, device),
         }
+        scales = [None, None, None]
+        if fp8_mlp:
+            if td != torch.bfloat16:
+                raise DMError(DM_ERR_INVALID_ARG, "the FP8 MLP needs bf16 weights")
+            for i, k in enumerate(("w_gate", "w_up", "w_down")):
+                codes, s = quantize_fp8_rows(self.t[k])
+                self.t[k], self.t["s" + k[1:]] = codes, s
+                scales[i] = ptr(s)
+            torch.cuda.current_stream().synchronize()
         self.c = ExpertWeightsC(*(ptr(self.t[k]) for k in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate",
-                                                            "w_up", "w_down")), None, None, None)
+                                                            "w_up", "w_down")), *scales)
 
 
 class DeviceAction:

@@ -45,6 +45,21 @@ template <> struct Mfma<float> {
   }
 };
 
+// FP8 E4M3 (OCP e4m3fn) codes, one byte per element.  One 16x16x128 MFMA per k-chunk: lane l
+// supplies row (l % 16) of A and column (l % 16) of B for 32 contraction indices, 32 bytes per
+// lane; A and B fragments are loaded with the same byte-to-index map, so the product is exact
+// whatever order the hardware walks those 32 indices in.  Scale operands 0x7F are E8M0 2^0
+// (unscaled); the per-token and per-channel scales are applied in the epilogue.
+typedef uint8_t fp8;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+struct Mfma8 {
+  typedef i32x8 frag;
+  static constexpr int EPL = 32;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+  }
+};
+
 template <typename T> __device__ __forceinline__ typename Mfma<T>::frag load_frag(const T *p) {
   return *reinterpret_cast<const typename Mfma<T>::frag *>(p);
 }

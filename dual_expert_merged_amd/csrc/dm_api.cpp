@@ -77,6 +77,7 @@ struct Layout {
   Region rope;
   Region h, hg, ssq, q, ks, vs, o, act, apart, split;          // action side (h: denoise only)
   Region hp, hg_p, ssq_p, q_p, kp, vp, o_p, act_p, apart_p;    // prefix side (hp: prefill only)
+  Region q8_p, qs_p;                                           // FP8 MLP operand codes and row scales
   int n_chunks = 1, chunk_keys = 32, n_chunks_p = 1, chunk_keys_p = 32;
   ExpertPlans pa, pv;  // action expert, VLM expert
   size_t total = 0;
@@ -186,6 +187,10 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
     }
     L.put(L.o_p, Mp * Hq * D * es);
     L.put(L.act_p, Mp * c.vlm_ffn * es);
+    if (op == DM_OP_PREFILL && c.vlm_mlp_dtype == DM_FP8_E4M3) {
+      L.put(L.q8_p, Mp * (size_t)std::max(Hv, c.vlm_ffn));
+      L.put(L.qs_p, Mp * sizeof(float));
+    }
     const int nqb = attn_qblocks(P_cap, Hq, Hkv);
     attn_split(B, Hkv, nqb, P_cap, &L.n_chunks_p, &L.chunk_keys_p);
     if (L.n_chunks_p > 1) L.put(L.apart_p, attn_partial_bytes(dt, B, Hkv, nqb, L.n_chunks_p, D));
@@ -220,6 +225,8 @@ dm_status check_config(const dm_config *c) {
               c->vlm_ffn % kq == 0 && c->act_ffn % kq == 0,
           DM_ERR_SHAPE, "hidden, FFN and n_q_heads*head_dim must be multiples of %d for this dtype", kq);
   REQUIRE(c->vlm_hidden <= 4096 && c->act_hidden <= 4096, DM_ERR_UNSUPPORTED, "hidden sizes above 4096");
+  REQUIRE(c->vlm_mlp_dtype != DM_FP8_E4M3 || (c->vlm_hidden % 128 == 0 && c->vlm_ffn % 128 == 0), DM_ERR_SHAPE,
+          "the FP8 MLP needs vlm_hidden and vlm_ffn to be multiples of 128");
   REQUIRE(c->action_dim >= 4 && c->action_dim <= 64 && c->action_dim % 4 == 0, DM_ERR_UNSUPPORTED,
           "action_dim must be a multiple of 4 in 4..64");
   REQUIRE(c->chunk >= 1 && c->chunk <= 64, DM_ERR_UNSUPPORTED, "chunk must be 1..64");
@@ -270,18 +277,27 @@ const char *layer_ptr(const void *base, size_t layer_elems, int l, size_t es) {
 struct Expert {
   const float *attn_norm, *mlp_norm;
   const void *w_qkv, *w_o, *w_gate, *w_up, *w_down;
+  const float *s_gate = nullptr, *s_up = nullptr, *s_down = nullptr;  // FP8 MLP only
 };
 
-Expert expert_layer(const dm_config &c, const dm_expert_weights &w, int l, int H, int F, size_t es) {
+// Layer l of a stacked expert; fp8: the MLP matrices are one-byte E4M3 codes with scales.
+Expert expert_layer(const dm_config &c, const dm_expert_weights &w, int l, int H, int F, size_t es,
+                    bool fp8 = false) {
   const int QKV = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, QD = c.n_q_heads * c.head_dim;
+  const size_t mes = fp8 ? 1 : es;
   Expert e;
   e.attn_norm = w.attn_norm + (size_t)l * H;
   e.mlp_norm = w.mlp_norm + (size_t)l * H;
   e.w_qkv = layer_ptr(w.w_qkv, (size_t)QKV * H, l, es);
   e.w_o = layer_ptr(w.w_o, (size_t)H * QD, l, es);
-  e.w_gate = layer_ptr(w.w_gate, (size_t)F * H, l, es);
-  e.w_up = layer_ptr(w.w_up, (size_t)F * H, l, es);
-  e.w_down = layer_ptr(w.w_down, (size_t)H * F, l, es);
+  e.w_gate = layer_ptr(w.w_gate, (size_t)F * H, l, mes);
+  e.w_up = layer_ptr(w.w_up, (size_t)F * H, l, mes);
+  e.w_down = layer_ptr(w.w_down, (size_t)H * F, l, mes);
+  if (fp8) {
+    e.s_gate = w.s_gate + (size_t)l * F;
+    e.s_up = w.s_up + (size_t)l * F;
+    e.s_down = w.s_down + (size_t)l * H;
+  }
   return e;
 }
 
@@ -306,6 +322,27 @@ void enqueue_finish(const dm_ctx *ctx, const Layout &L, void *ws, const ExpertPl
   launch_swiglu(ctx->dt, sg, pg, s);
   ResidArgs rd{act, M, F, e.w_down, hid, next_attn_norm, rows};
   launch_resid(ctx->dt, rd, pd, s);
+}
+
+// The same with the MLP in FP8 E4M3 (page "DM0.5: High-Performance Embodied VLA ...", section
+// 6.3): the normalised MLP input and the SwiGLU activation are quantised per token, the three
+// MLP GEMMs run on FP8 MFMA with fp32 accumulation, scales applied in the epilogues.
+void enqueue_finish_fp8(const dm_ctx *ctx, const Layout &L, void *ws, const ExpertPlans &pl, const Expert &e,
+                        const Hidden &hid, const void *o, void *act, int M, int F, RowMap rows,
+                        const float *next_attn_norm, hipStream_t s) {
+  const dm_config &c = ctx->cfg;
+  GemmPlan po = pl.o;
+  po.sk = splitk(L, ws, pl.o);
+  ResidArgs ro{o, M, c.n_q_heads * c.head_dim, e.w_o, hid, e.mlp_norm, rows};
+  launch_resid(ctx->dt, ro, po, s);
+  uint8_t *q8 = at<uint8_t>(ws, L.q8_p);
+  float *qs = at<float>(ws, L.qs_p);
+  launch_fp8_quantize_rows(hid.hg, q8, qs, M, hid.H, s);
+  SwigluArgs sg{hid, M, F, c.rms_eps, e.w_gate, e.w_up, act, rows, q8, qs, e.s_gate, e.s_up};
+  launch_swiglu_fp8(sg, s);
+  launch_fp8_quantize_rows(act, q8, qs, M, F, s);
+  ResidArgs rd{q8, M, F, e.w_down, hid, next_attn_norm, rows, qs, e.s_down};
+  launch_resid_fp8(rd, s);
 }
 
 dm_status enqueue_denoise(const dm_ctx *ctx, const dm_action_weights *aw, const void *k_cache, const void *v_cache,
@@ -531,8 +568,8 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *
                         size_t ws_bytes, void *stream) {
   TRY(check_common(ctx, prefix_lens, B, P_cap, ws, ws_bytes, DM_OP_PREFILL));
   const dm_config &c = ctx->cfg;
-  REQUIRE(c.vlm_mlp_dtype == c.dtype, DM_ERR_UNSUPPORTED, "the FP8 VLM MLP is not built yet");
-  TRY(check_expert(vlm, false, "VLM"));
+  const bool fp8 = c.vlm_mlp_dtype == DM_FP8_E4M3;
+  TRY(check_expert(vlm, fp8, "VLM"));
   REQUIRE(prefix_embeds && k_cache && v_cache, DM_ERR_INVALID_ARG, "prefix_embeds / k_cache / v_cache is NULL");
   REQUIRE(aligned16(prefix_embeds) && aligned16(k_cache) && aligned16(v_cache), DM_ERR_INVALID_ARG,
           "prefix_embeds and caches must be 16-byte aligned");
@@ -549,7 +586,7 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *
   launch_rope_table(rope, P_cap, D, c.rope_base, s);
   launch_norm_prep(ctx->dt, prefix_embeds, hp, vlm->attn_norm, Mp, s);
   for (int l = 0; l < c.n_layers; ++l) {
-    const Expert e = expert_layer(c, *vlm, l, Hv, c.vlm_ffn, ctx->es);
+    const Expert e = expert_layer(c, *vlm, l, Hv, c.vlm_ffn, ctx->es, fp8);
     void *kc = (void *)layer_ptr(k_cache, layer_cache, l, ctx->es);
     void *vc = (void *)layer_ptr(v_cache, layer_cache, l, ctx->es);
     QkvArgs qv{hp, Mp, c.rms_eps, e.w_qkv, at<void>(ws, L.q_p), kc, vc, P_cap, prow, rope, Hq, Hkv, D};
@@ -559,8 +596,8 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *
                 L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),
                 L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr};
     launch_attention(ctx->dt, ap, s);
-    enqueue_finish(ctx, L, ws, L.pv, e, hp, at<void>(ws, L.o_p), at<void>(ws, L.act_p), Mp, c.vlm_ffn, prow,
-                   vlm->attn_norm + (size_t)(l + 1) * Hv, s);
+    (fp8 ? enqueue_finish_fp8 : enqueue_finish)(ctx, L, ws, L.pv, e, hp, at<void>(ws, L.o_p), at<void>(ws, L.act_p),
+                                                Mp, c.vlm_ffn, prow, vlm->attn_norm + (size_t)(l + 1) * Hv, s);
   }
   HIP_TRY(hipGetLastError());
   return DM_OK;
@@ -569,6 +606,7 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *
 dm_status dm_quantize_fp8_rows(const void *src, uint8_t *dst, float *scales, int rows, int cols, void *stream) {
   REQUIRE(src && dst && scales, DM_ERR_INVALID_ARG, "src / dst / scales is NULL");
   REQUIRE(rows >= 1 && cols >= 1, DM_ERR_SHAPE, "rows and cols must be positive");
+  REQUIRE(aligned16(src) && aligned16(dst), DM_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
   launch_fp8_quantize_rows(src, dst, scales, rows, cols, (hipStream_t)stream);
   HIP_TRY(hipGetLastError());
   return DM_OK;

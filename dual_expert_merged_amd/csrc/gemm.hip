@@ -33,7 +33,8 @@ namespace dm {
 // 1/rms of rows m0..m0+rows-1 into inv[], from per-16-column sums of squares: 4 threads per row
 // (64 rows per pass of 256 threads), each summing a contiguous quarter of the row's partials with
 // all its loads in flight, then a fixed-order exchange.  Rows past M use row M-1 (never read).
-__device__ __forceinline__ void rms_prepare(const Hidden &in, int M, float eps, int m0, int rows, float *inv) {
+__device__ __forceinline__ void rms_prepare(const Hidden &in, int M, float eps, int m0, int rows, float *inv,
+                                            const float *row_scale = nullptr) {
   const int nt = in.H >> 4;
   for (int base = 0; base < rows; base += 64) {
     const int t = threadIdx.x, row = base + (t >> 2), part = t & 3;
@@ -52,7 +53,8 @@ __device__ __forceinline__ void rms_prepare(const Hidden &in, int M, float eps, 
       for (int i = part; i < nt; i += 4) s += p[i];
     }
     s = sum4(s);
-    if (part == 0) inv[row] = rsqrtf(s / (float)in.H + eps);
+    const float rs = row_scale ? row_scale[min(m0 + row, M - 1)] : 1.0f;
+    if (part == 0) inv[row] = rsqrtf(s / (float)in.H + eps) * rs;
   }
 }
 
@@ -149,30 +151,37 @@ template <typename T> struct EpiQkv {
   }
 };
 
-template <typename T> struct EpiResid {
+// W: operand type (T, or fp8 with a per-row scale of A and a per-column scale of W).
+template <typename T, typename W = T> struct EpiResid {
+  static constexpr bool Q = !std::is_same<T, W>::value;
   ResidArgs a;
   struct St {
     float hv[4];
-    float gain;
+    float gain, s;
   };
   __device__ __forceinline__ const RowMap &rows() const { return a.rows; }
-  __device__ __forceinline__ const T *wrow(int c) const { return (const T *)a.w + (size_t)c * a.K; }
-  __device__ __forceinline__ void prepare(int, int, float *) const {}
+  __device__ __forceinline__ const W *wrow(int c) const { return (const W *)a.w + (size_t)c * a.K; }
+  __device__ __forceinline__ void prepare(int m0, int rows, float *inv) const {
+    if constexpr (Q)
+      for (int t = threadIdx.x; t < rows; t += blockDim.x) inv[t] = a.a_scale[min(m0 + t, a.M - 1)];
+  }
   __device__ __forceinline__ St load(const RowInfo &ri, int c) const {
     St st;
 #pragma unroll
     for (int r = 0; r < 4; ++r) st.hv[r] = a.out.h[(size_t)ri.rc[r] * a.out.H + c];
     st.gain = a.next_gain ? a.next_gain[c] : 0.f;
+    st.s = Q ? a.s_w[c] : 1.0f;
     return st;
   }
-  __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *,
-                                        int) const {
+  __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
+                                        int m0) const {
     const int H = a.out.H;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + r;
       const bool ok = ri.ok[r];
-      const float hn = ok ? st.hv[r] + acc[r] : 0.f;
+      const float y = Q ? acc[r] * inv[row - m0] * st.s : acc[r];
+      const float hn = ok ? st.hv[r] + y : 0.f;
       if (ok) {
         a.out.h[(size_t)row * H + c] = hn;
         if (a.next_gain) ((T *)a.out.hg)[(size_t)row * H + c] = from_f32<T>(hn * st.gain);
@@ -185,25 +194,33 @@ template <typename T> struct EpiResid {
   }
 };
 
-template <typename T> struct EpiSwiglu {
+template <typename T, typename W = T> struct EpiSwiglu {
+  static constexpr bool Q = !std::is_same<T, W>::value;
   SwigluArgs a;
-  struct St {};
+  struct St {
+    float s;
+  };
   __device__ __forceinline__ const RowMap &rows() const { return a.rows; }
-  __device__ __forceinline__ const T *wrow(int c) const {
+  __device__ __forceinline__ const W *wrow(int c) const {
     const int f = (c >> 4) * 8 + (c & 7);
-    return (const T *)((c >> 3) & 1 ? a.wu : a.wg) + (size_t)f * a.in.H;
+    return (const W *)((c >> 3) & 1 ? a.wu : a.wg) + (size_t)f * a.in.H;
   }
   __device__ __forceinline__ void prepare(int m0, int rows, float *inv) const {
-    rms_prepare(a.in, a.M, a.eps, m0, rows, inv);
+    rms_prepare(a.in, a.M, a.eps, m0, rows, inv, Q ? a.a_scale : nullptr);
   }
-  __device__ __forceinline__ St load(const RowInfo &, int) const { return St{}; }
-  __device__ __forceinline__ void store(const St &, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
+  __device__ __forceinline__ St load(const RowInfo &, int c) const {
+    St st;
+    st.s = 1.0f;
+    if constexpr (Q) st.s = ((c >> 3) & 1 ? a.s_up : a.s_gate)[(c >> 4) * 8 + (c & 7)];
+    return st;
+  }
+  __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
                                         int m0) const {
     const int f = (c >> 4) * 8 + (c & 7);
     const int up = (c >> 3) & 1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float g = acc[r] * inv[row0 + r - m0];
+      const float g = acc[r] * inv[row0 + r - m0] * st.s;
       const float u = lane_xor8(g);
       if (up || !ri.ok[r]) continue;
       ((T *)a.act)[(size_t)(row0 + r) * a.F + f] = from_f32<T>(silu(g) * u);
@@ -346,22 +363,24 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
   }
 }
 
-// ------------------------------------------------------------------------ big kernel (bf16, M > 64)
+// ------------------------------------------------------------------------ big kernel (M > 64)
 // Workgroup tile 128 x BN (BN = 256 or 128); four waves as 2 x 2, each 64 x BN/2, i.e. 4 x BN/32
-// MFMA 16x16 tiles, so every 16-byte LDS fragment read feeds several MFMAs.  K advances 64 at a
-// time through two LDS buffers: the next k-step is loaded into registers while the current one
-// is multiplied, then stored to the other buffer, one barrier per k-step.  Rows are padded to 144
-// bytes, which spreads the 16 rows of a fragment read over all LDS banks.  grid.z splits K (the
-// narrow residual projections), each split writing fp32 partial sums for resid_reduce_kernel.
-template <int BN, class Epi>
-__global__ __launch_bounds__(256) void big_kernel(const bf16 *__restrict__ A, int M, int K, Epi epi, SplitK sk) {
-  typedef Mfma<bf16> MF;
-  typedef MF::frag frag;
-  constexpr int BM = 128, BK = 64, LD = BK + 8;
+// MFMA 16x16 tiles, so every LDS fragment read feeds several MFMAs.  Each k-step moves 128 bytes
+// of every row (64 bf16 or 128 FP8 codes) through two LDS buffers: the next k-step is loaded into
+// registers while the current one is multiplied, then stored to the other buffer, one barrier per
+// k-step.  Rows are padded to 144 bytes, which spreads the 16 rows of a fragment read over all
+// LDS banks.  grid.z splits K (the narrow residual projections), each split writing fp32 partial
+// sums for resid_reduce_kernel.  Op: bf16 (two 16x16x32 MFMAs per k-step) or fp8 (one
+// 16x16x128 MFMA per k-step).
+template <typename Op, int BN, class Epi>
+__global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int M, int K, Epi epi, SplitK sk) {
+  constexpr int EB = sizeof(Op);       // bytes per element
+  constexpr int BM = 128, RB = 128, LDB = RB + 16;
+  constexpr int BK = RB / EB, VE = 16 / EB;
   constexpr int TN = BN / 32;
-  constexpr int AV = BM * BK / 8 / 256, WV = BN * BK / 8 / 256;
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LD];
-  __shared__ __attribute__((aligned(16))) bf16 Ws[2][BN * LD];
+  constexpr int AV = BM * 8 / 256, WV = BN * 8 / 256;
+  __shared__ __attribute__((aligned(16))) char As[2][BM * LDB];
+  __shared__ __attribute__((aligned(16))) char Ws[2][BN * LDB];
   __shared__ float rinv[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -370,34 +389,34 @@ __global__ __launch_bounds__(256) void big_kernel(const bf16 *__restrict__ A, in
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM, split = blockIdx.z;
   const int Ks = K / sk.k_split, kb = split * Ks, nkt = Ks / BK;
 
-  const bf16 *asrc[AV];
+  const Op *asrc[AV];
   int adst[AV];
 #pragma unroll
   for (int v = 0; v < AV; ++v) {
     const int idx = tid + v * 256, r = idx >> 3, cv = idx & 7;
-    asrc[v] = A + (size_t)min(m0 + r, M - 1) * K + kb + cv * 8;  // rows past M: never stored
-    adst[v] = r * LD + cv * 8;
+    asrc[v] = A + (size_t)min(m0 + r, M - 1) * K + kb + cv * VE;  // rows past M: never stored
+    adst[v] = r * LDB + cv * 16;
   }
-  const bf16 *wsrc[WV];
+  const Op *wsrc[WV];
   int wdst[WV];
 #pragma unroll
   for (int v = 0; v < WV; ++v) {
     const int idx = tid + v * 256, r = idx >> 3, cv = idx & 7;
-    wsrc[v] = epi.wrow(n0 + r) + kb + cv * 8;
-    wdst[v] = r * LD + cv * 8;
+    wsrc[v] = epi.wrow(n0 + r) + kb + cv * VE;
+    wdst[v] = r * LDB + cv * 16;
   }
-  frag ra[AV], rw[WV];
+  i32x4 ra[AV], rw[WV];
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int v = 0; v < AV; ++v) ra[v] = load_frag<bf16>(asrc[v] + kt * BK);
+    for (int v = 0; v < AV; ++v) ra[v] = *reinterpret_cast<const i32x4 *>(asrc[v] + kt * BK);
 #pragma unroll
-    for (int v = 0; v < WV; ++v) rw[v] = load_frag<bf16>(wsrc[v] + kt * BK);
+    for (int v = 0; v < WV; ++v) rw[v] = *reinterpret_cast<const i32x4 *>(wsrc[v] + kt * BK);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int v = 0; v < AV; ++v) *reinterpret_cast<frag *>(&As[buf][adst[v]]) = ra[v];
+    for (int v = 0; v < AV; ++v) *reinterpret_cast<i32x4 *>(&As[buf][adst[v]]) = ra[v];
 #pragma unroll
-    for (int v = 0; v < WV; ++v) *reinterpret_cast<frag *>(&Ws[buf][wdst[v]]) = rw[v];
+    for (int v = 0; v < WV; ++v) *reinterpret_cast<i32x4 *>(&Ws[buf][wdst[v]]) = rw[v];
   };
 
   f32x4 acc[4][TN];
@@ -413,19 +432,39 @@ __global__ __launch_bounds__(256) void big_kernel(const bf16 *__restrict__ A, in
   for (int kt = 0; kt < nkt; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nkt) gload(kt + 1);
+    const char *ab = &As[cur][(wm * 64 + c16) * LDB];
+    const char *wb = &Ws[cur][(wn * (BN / 2) + c16) * LDB];
+    if constexpr (EB == 2) {
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      frag fa[4], fb[TN];
+      for (int kc = 0; kc < 2; ++kc) {
+        bf16x8 fa[4], fb[TN];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(ab + i * 16 * LDB + kc * 64 + g * 16);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const bf16x8 *>(wb + j * 16 * LDB + kc * 64 + g * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<bf16>::mma(fa[i], fb[j], acc[i][j]);
+      }
+    } else {
+      i32x8 fa[4], fb[TN];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(ab + i * 16 * LDB + g * 32);
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(ab + i * 16 * LDB + g * 32 + 16);
+        fa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(wb + j * 16 * LDB + g * 32);
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(wb + j * 16 * LDB + g * 32 + 16);
+        fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const frag *>(&As[cur][(wm * 64 + i * 16 + c16) * LD + kc * 32 + g * 8]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[j] = *reinterpret_cast<const frag *>(&Ws[cur][(wn * (BN / 2) + j * 16 + c16) * LD + kc * 32 + g * 8]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = Mfma8::mma(fa[i], fb[j], acc[i][j]);
     }
     if (kt + 1 < nkt) lstore(cur ^ 1);
     __syncthreads();
@@ -576,9 +615,9 @@ static void run_gemm(const T *A, int M, int N, int K, const Epi &epi, const Gemm
     if constexpr (std::is_same<T, bf16>::value) {
       dim3 grid(N / p.nt, (M + 127) / 128, p.sk.k_split);
       if (p.nt == 256)
-        hipLaunchKernelGGL((big_kernel<256, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk);
+        hipLaunchKernelGGL((big_kernel<bf16, 256, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk);
       else
-        hipLaunchKernelGGL((big_kernel<128, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk);
+        hipLaunchKernelGGL((big_kernel<bf16, 128, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk);
     }
   } else {
     dim3 grid(N / 64, (M + 63) / 64);
@@ -598,6 +637,21 @@ template <typename T> static void resid_t(const ResidArgs &a, const GemmPlan &p,
 }
 template <typename T> static void swiglu_t(const SwigluArgs &a, const GemmPlan &p, hipStream_t s) {
   run_gemm<T>((const T *)a.in.hg, a.M, 2 * a.F, a.in.H, EpiSwiglu<T>{a}, p, s);
+}
+
+// FP8: one launch of the large-tile kernel, 256 columns per workgroup when N allows it.
+template <class Epi> static void run_fp8(const fp8 *A, int M, int N, int K, const Epi &epi, hipStream_t s) {
+  const SplitK none{1, nullptr};
+  if (N % 256 == 0)
+    hipLaunchKernelGGL((big_kernel<fp8, 256, Epi>), dim3(N / 256, (M + 127) / 128), dim3(256), 0, s, A, M, K, epi, none);
+  else
+    hipLaunchKernelGGL((big_kernel<fp8, 128, Epi>), dim3(N / 128, (M + 127) / 128), dim3(256), 0, s, A, M, K, epi, none);
+}
+void launch_resid_fp8(const ResidArgs &a, hipStream_t s) {
+  run_fp8((const fp8 *)a.a, a.M, a.out.H, a.K, EpiResid<bf16, fp8>{a}, s);
+}
+void launch_swiglu_fp8(const SwigluArgs &a, hipStream_t s) {
+  run_fp8((const fp8 *)a.a8, a.M, 2 * a.F, a.in.H, EpiSwiglu<bf16, fp8>{a}, s);
 }
 
 int gemm_k_quantum(Dt dt) { return 4 * 4 * (dt == DT_BF16 ? Mfma<bf16>::EPL : Mfma<float>::EPL); }

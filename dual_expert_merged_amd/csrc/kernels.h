@@ -48,19 +48,25 @@ struct QkvArgs {
 };
 // out.h += A W^T, then out.hg = (h * next_gain) and out.ssq for the next sublayer
 // (next_gain NULL: skip them).  Rows outside RowMap untouched.
+// FP8 operands (a and w E4M3 codes): C = a_scale[m] * s_w[n] * (A_q W_q^T); both NULL otherwise.
 struct ResidArgs {
   const void *a; int M, K;       // A [M][K]
   const void *w;                 // [H][K]
   Hidden out;
   const float *next_gain;
   RowMap rows;
+  const float *a_scale = nullptr, *s_w = nullptr;
 };
 // act[M x F] = silu(n Wg^T) * (n Wu^T), n = RMSNorm(h) from in.hg / in.ssq.
+// FP8 operands: a8 holds the E4M3 codes of in.hg per row with scales a_scale (so the normalised
+// row is a_scale[m] * a8[m] / rms), wg / wu hold E4M3 codes with per-channel scales s_gate / s_up.
 struct SwigluArgs {
   Hidden in; int M, F; float eps;
   const void *wg, *wu;           // [F][H] each
   void *act;                     // [M][F]
   RowMap rows;
+  const void *a8 = nullptr;
+  const float *a_scale = nullptr, *s_gate = nullptr, *s_up = nullptr;
 };
 
 // Tile plan of one GEMM launch, chosen by the host.
@@ -73,6 +79,9 @@ struct GemmPlan {
 void launch_qkv(Dt dt, const QkvArgs &a, const GemmPlan &p, hipStream_t s);
 void launch_resid(Dt dt, const ResidArgs &a, const GemmPlan &p, hipStream_t s);
 void launch_swiglu(Dt dt, const SwigluArgs &a, const GemmPlan &p, hipStream_t s);
+// FP8 variants (large-tile kernel, any M; N a multiple of 128 and K of 128).
+void launch_resid_fp8(const ResidArgs &a, hipStream_t s);
+void launch_swiglu_fp8(const SwigluArgs &a, hipStream_t s);
 // Splits that the skinny kernel supports for K (multiple of 4 waves x one MFMA k-chunk).
 int gemm_k_quantum(Dt dt);
 
@@ -102,6 +111,8 @@ void launch_embed(Dt dt, const float *x, const float *w_in, const float *b_in, c
 void launch_velocity_euler(const float *h, const float *gain, const float *w_out,
                            const float *b_out, float *x, int M, int H, int A, float eps,
                            int num_steps, hipStream_t s);
+// dst[r][:] = e4m3(src[r][:] / scales[r]), scales[r] = max|src[r][:]| / 448 (1 for a zero row);
+// src bf16 [rows][cols].
 void launch_fp8_quantize_rows(const void *src, uint8_t *dst, float *scales, int rows, int cols,
                               hipStream_t s);
 

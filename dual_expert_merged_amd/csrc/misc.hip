@@ -200,50 +200,90 @@ void launch_velocity_euler(const float *h, const float *gain, const float *w_out
 }
 
 // Nearest E4M3 (OCP e4m3fn) code of a float32 value, ties to even, saturating at +-448:
-// 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; subnormal step 2^-9.
-__device__ __forceinline__ uint8_t e4m3_encode(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+// 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; subnormal step 2^-9.  Normal range:
+// round the float32 mantissa to 3 bits on the bit pattern (a carry moves into the exponent);
+// below 2^-6: round a * 2^9 to an integer, which is the subnormal code (8 = smallest normal).
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
   const float a = fabsf(x);
-  if (!(a > 0.f)) return (uint8_t)sign;
-  if (a >= 448.f) return (uint8_t)(sign | 0x7Eu);
-  int e;
-  frexpf(a, &e);                    // a = f * 2^e, f in [0.5, 1)
-  int E = e - 1;                    // binade exponent
-  if (E < -6) E = -6;               // subnormals share the smallest normal's step
-  const float step = ldexpf(1.0f, E - 3);
-  float r = rintf(a / step) * step; // exact division by a power of two; ties to even
-  if (r > 448.f) r = 448.f;
-  if (r == 0.f) return (uint8_t)sign;
-  int er;
-  frexpf(r, &er);
-  const int Er = er - 1;
   uint32_t code;
-  if (Er < -6) {
-    code = (uint32_t)(r * 512.0f);  // subnormal: r = m * 2^-9
+  if (a >= 0.015625f) {  // 2^-6
+    const uint32_t au = u & 0x7FFFFFFFu;
+    const uint32_t r = au + 0x7FFFFu + ((au >> 20) & 1u);  // RNE at mantissa bit 20
+    const int e = (int)(r >> 23) - 127 + 7;
+    code = ((uint32_t)e << 3) | ((r >> 20) & 7u);
+    if (!(a < 448.f) || code > 0x7Eu) code = 0x7Eu;     // saturate (also catches e > 15)
   } else {
-    const uint32_t mant = (uint32_t)((r / ldexpf(1.0f, Er) - 1.0f) * 8.0f);
-    code = ((uint32_t)(Er + 7) << 3) | mant;
+    code = (uint32_t)rintf(a * 512.0f);                 // 0..8, ties to even
   }
-  return (uint8_t)(sign | code);
+  return sign | code;
 }
 
-__global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const bf16 *__restrict__ src, uint8_t *__restrict__ dst,
-                                                             float *__restrict__ scales, int cols) {
+// One wave per row (four rows per workgroup); the row is VPL 16-byte vectors per lane, all loaded
+// before the row maximum is reduced.  Codes are e4m3(x / s) with s = max|x| / 448, both divisions
+// correctly rounded float32.
+template <int VPL>
+__global__ __launch_bounds__(256) void fp8_rows_kernel(const bf16 *__restrict__ src, uint8_t *__restrict__ dst,
+                                                       float *__restrict__ scales, int rows) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;  // uniform per wave; no workgroup barrier below
+  constexpr int cols = 512 * VPL;
+  const bf16x8 *p = reinterpret_cast<const bf16x8 *>(src + (size_t)row * cols);
+  bf16x8 v[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) v[i] = p[i * 64 + lane];
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(to_f32(v[i][e])));
+  mx = wave_max(mx);
+  const float s = mx > 0.f ? mx / 448.0f : 1.0f;
+  if (lane == 0) scales[row] = s;
+  uint2 *q = reinterpret_cast<uint2 *>(dst + (size_t)row * cols);
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo |= e4m3_encode(to_f32(v[i][e]) / s) << (8 * e);
+      hi |= e4m3_encode(to_f32(v[i][e + 4]) / s) << (8 * e);
+    }
+    q[i * 64 + lane] = make_uint2(lo, hi);
+  }
+}
+
+// Any column count: one workgroup per row.
+__global__ __launch_bounds__(256) void fp8_rows_any_kernel(const bf16 *__restrict__ src, uint8_t *__restrict__ dst,
+                                                           float *__restrict__ scales, int cols) {
   __shared__ float red[4];
   const bf16 *row = src + (size_t)blockIdx.x * cols;
   float mx = 0.f;
   for (int c = threadIdx.x; c < cols; c += 256) mx = fmaxf(mx, fabsf(to_f32(row[c])));
   mx = wave_max(mx);
-  __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = mx > 0.f ? mx / 448.0f : 1.0f;
   if (threadIdx.x == 0) scales[blockIdx.x] = s;
-  for (int c = threadIdx.x; c < cols; c += 256) dst[(size_t)blockIdx.x * cols + c] = e4m3_encode(to_f32(row[c]) / s);
+  for (int c = threadIdx.x; c < cols; c += 256) dst[(size_t)blockIdx.x * cols + c] = (uint8_t)e4m3_encode(to_f32(row[c]) / s);
 }
+
 void launch_fp8_quantize_rows(const void *src, uint8_t *dst, float *scales, int rows, int cols, hipStream_t s) {
-  hipLaunchKernelGGL(fp8_quant_rows_kernel, dim3(rows), dim3(256), 0, s, (const bf16 *)src, dst, scales, cols);
+  const bf16 *x = (const bf16 *)src;
+  const dim3 g4((rows + 3) / 4), blk(256);
+  switch (cols % 512 == 0 ? cols / 512 : 0) {
+    case 1: hipLaunchKernelGGL(fp8_rows_kernel<1>, g4, blk, 0, s, x, dst, scales, rows); break;
+    case 2: hipLaunchKernelGGL(fp8_rows_kernel<2>, g4, blk, 0, s, x, dst, scales, rows); break;
+    case 4: hipLaunchKernelGGL(fp8_rows_kernel<4>, g4, blk, 0, s, x, dst, scales, rows); break;
+    case 6: hipLaunchKernelGGL(fp8_rows_kernel<6>, g4, blk, 0, s, x, dst, scales, rows); break;
+    case 8: hipLaunchKernelGGL(fp8_rows_kernel<8>, g4, blk, 0, s, x, dst, scales, rows); break;
+    case 12: hipLaunchKernelGGL(fp8_rows_kernel<12>, g4, blk, 0, s, x, dst, scales, rows); break;
+    case 16: hipLaunchKernelGGL(fp8_rows_kernel<16>, g4, blk, 0, s, x, dst, scales, rows); break;
+    default: hipLaunchKernelGGL(fp8_rows_any_kernel, dim3(rows), blk, 0, s, x, dst, scales, cols); break;
+  }
 }
 
 }  // namespace dm

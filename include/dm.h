@@ -127,7 +127,11 @@ size_t dm_workspace_bytes(const dm_ctx *ctx, dm_op op, int B, int P_cap);
 /* Prefix encoding once (page section 5.1): runs the L VLM-expert layers over prefix_embeds
  * [B][P_cap][Hv] (float32, rows >= P_b ignored) with a bidirectional mask among each sample's
  * P_b tokens, and writes every layer's post-RoPE K and V into k_cache / v_cache
- * [L][B][Hkv][P_cap][D] (rows >= P_b left untouched).  prefix_embeds is not modified. */
+ * [L][B][Hkv][P_cap][D] (rows >= P_b left untouched).  prefix_embeds is not modified.
+ * With vlm_mlp_dtype = DM_FP8_E4M3 (page section 6.3) the MLP gate/up/down weights are E4M3
+ * codes with per-output-channel scales (see dm_quantize_fp8_rows); each MLP input row
+ * (RMSNorm output) and each SwiGLU activation row is quantised per token the same way, and
+ * y[m][n] = r_m * s_n * sum_k a_q[m][k] w_q[n][k] accumulates in float32. */
 dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm /* (host) */,
                         const float *prefix_embeds, const int32_t *prefix_lens, int B, int P_cap,
                         void *k_cache, void *v_cache, void *ws, size_t ws_bytes, void *stream);
@@ -164,10 +168,12 @@ dm_status dm_denoise_plan_create(dm_ctx *ctx, const dm_action_weights *aw /* (ho
 dm_status dm_denoise_plan_launch(dm_plan *plan, int num_steps, void *stream);
 void dm_denoise_plan_destroy(dm_plan *plan);
 
-/* FP8 E4M3 (OCP e4m3fn) weight quantisation (page section 6.3), per output channel:
+/* FP8 E4M3 (OCP e4m3fn) row quantisation (page section 6.3), used for weights (one row per
+ * output channel) and, inside dm_prefill_kv, for activations (one row per token):
  * scales[r] = max_c |src[r][c]| / 448 (1 for an all-zero row) and
- * dst[r][c] = e4m3(src[r][c] / scales[r]) rounded to nearest even, saturating at +-448.
- * src [rows][cols] bf16, dst [rows][cols] bytes, scales [rows] float32. */
+ * dst[r][c] = e4m3(src[r][c] / scales[r]) rounded to nearest even, saturating at +-448; both
+ * divisions are correctly rounded float32.  src [rows][cols] bf16, dst [rows][cols] bytes,
+ * scales [rows] float32; src and dst 16-byte aligned.  Asynchronous on `stream`. */
 dm_status dm_quantize_fp8_rows(const void *src, uint8_t *dst, float *scales, int rows, int cols,
                                void *stream);
 

@@ -22,7 +22,8 @@ class Gpu:
         self.shape = wl.shape
         self.ctx = bd.Context(wl.shape)
         self.td = bd.torch_dtype(wl.shape.dtype)
-        self.vlm = bd.DeviceExpert(vlm, wl.shape.dtype) if vlm is not None else None
+        fp8 = wl.shape.vlm_mlp_dtype != wl.shape.dtype
+        self.vlm = bd.DeviceExpert(vlm, wl.shape.dtype, fp8_mlp=fp8) if vlm is not None else None
         self.aw = bd.DeviceAction(aw, wl.shape.dtype) if aw is not None else None
 
     def cache_to_device(self, k, v):

@@ -1,0 +1,147 @@
+"""GPU parity of the FP8 E4M3 prefix MLP (page "DM0.5: High-Performance Embodied VLA and OpenDM
+Open Source Introduction", section 6.3: the prefix MLP gate/up/down GEMMs in FP8 with scales).
+
+Row quantisation is integer work decided by floating point: the oracle takes the same decision
+in the kernel's precision (scale max|x|/448 and x/scale as correctly rounded float32 divisions)
+and the E4M3 values must then match exactly.
+
+The prefill with the FP8 MLP is compared with the oracle's FP8 emulation (per-token activation
+scales, per-channel weight scales, exact sums).  Three mantissa bits make every code sensitive to
+the last bits of its input: where the GPU's bf16 intermediates and the oracle's float64 ones fall
+on two sides of an E4M3 rounding boundary the two codes differ by a whole step (1/8 to 1/16 of
+the value), and from the first FP8 layer on the two runs quantise diverging inputs.  Two correct
+FP8 implementations therefore differ by about as much as FP8 differs from bf16.  Bounds:
+  * small model (2 layers, hidden 256): the bf16 drift bounds, which a wrong scale, operand
+    layout or epilogue exceeds by orders of magnitude;
+  * DM0-base (28 layers): layer 0 (no FP8 upstream) under the bf16 drift bounds; every later
+    layer and the final chunk no further from the FP8 emulation than the FP8 emulation is from
+    the bf16 oracle (mean absolute error x 1, max error x 1.25).
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dual_expert_merged_amd import binding as bd
+from dual_expert_merged_amd import inputs
+from dual_expert_merged_amd.configs import BF16, FP8, ModelShape, workload
+from tests.gpu_harness import Gpu, err_stats, np32, rel_inf
+
+pytestmark = pytest.mark.gpu
+CHUNK_MAX, CHUNK_MEAN, DEEP_REL, DEEP_MEAN = 2e-2, 2e-3, 2e-2, 1e-2
+
+
+def _ties_row(cols):
+    """A row whose maximum is 448 (scale exactly 1), holding E4M3 round-to-even ties, subnormal
+    ties and values past the largest binade."""
+    vals = [448.0, -448.0, 1.0625, 1.1875, -2.125, 3.25 + 0.125, 0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -10,
+            5 * 2.0 ** -11, 2.0 ** -7 + 2.0 ** -10, 240.0, 232.0, 424.0, 440.0, 0.015625, 0.01171875]
+    row = np.zeros(cols, dtype=np.float32)
+    row[:len(vals)] = vals
+    return row
+
+
+@pytest.mark.parametrize("rows,cols", [(37, 2048), (5, 6144), (9, 100), (6, 512)])
+def test_quantize_rows_matches_oracle_codes(rows, cols):
+    print(f"case: dm_quantize_fp8_rows rows={rows} cols={cols}", flush=True)
+    rng = np.random.default_rng([9, rows, cols])
+    x = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(10.0) ** rng.integers(-4, 4, (rows, 1))
+    x[1] = 0.0                                   # all-zero row: scale 1, codes 0
+    x[2] = _ties_row(cols) if cols >= 18 else x[2]
+    x = inputs.round_to(x, BF16)
+    src = bd.to_device(x, torch.bfloat16)
+    codes, scales = bd.quantize_fp8_rows(src)
+    torch.cuda.synchronize()
+    got = codes.cpu().view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    # the oracle's decision in the kernel's precision: float32 scale and float32 quotient
+    amax = np.max(np.abs(x), axis=1)
+    s32 = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    ref = O.e4m3_round((x / s32[:, None]).astype(np.float32))
+    assert np.array_equal(scales.cpu().numpy(), s32), "row scales differ"
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}: gpu {got[tuple(bad[0])]} oracle {ref[tuple(bad[0])]}"
+
+
+def _fp8_tuples(vlm):
+    """The oracle's per-layer FP8 weights: (codes' values, scales) of gate, up and down."""
+    out = []
+    for l in range(vlm.w_qkv.shape[0]):
+        gq, gs = O.fp8_quantize_rows(vlm.w_gate[l])
+        uq, us = O.fp8_quantize_rows(vlm.w_up[l])
+        dq, ds = O.fp8_quantize_rows(vlm.w_down[l])
+        out.append((gq, gs, uq, us, dq, ds))
+    return out
+
+
+def _check_cache(kn, vn, b, rk, rv, n_layers, what, rel_bound=DEEP_REL, mean_bound=DEEP_MEAN):
+    bad = []
+    for l in range(n_layers):
+        for name, g, r in (("K", kn[l, b], rk[l]), ("V", vn[l, b], rv[l])):
+            e = rel_inf(g, r)
+            mean_rel = err_stats(g, r)[1] / float(np.sqrt(np.mean(r * r)))
+            print(f"{what} layer {l} {name}: rel inf err {e:.3e}, mean abs / rms {mean_rel:.3e}", flush=True)
+            if not (e <= rel_bound and mean_rel <= mean_bound):
+                bad.append((l, name, e, mean_rel))
+    assert not bad, (what, bad)
+
+
+def test_prefill_fp8_small_ragged():
+    shape = ModelShape(n_layers=2, vlm_hidden=256, act_hidden=128, vlm_ffn=768, act_ffn=384, n_q_heads=4,
+                       n_kv_heads=2, head_dim=32, action_dim=32, chunk=50, dtype=BF16, vlm_mlp_dtype=FP8)
+    wl = replace(workload(5), shape=shape, batch=3, prefix_len=64)
+    lens = np.array([64, 41, 7], dtype=np.int32)
+    print(f"case: 2-layer FP8-MLP prefill, B=3, lens {lens.tolist()}", flush=True)
+    vlm = inputs.make_vlm_weights(wl)
+    emb = inputs.make_prefix_embeds(wl)
+    gpu = Gpu(wl, vlm, None)
+    k, v = gpu.prefill(emb, lens)
+    kn, vn = np32(k), np32(v)
+    fp8 = _fp8_tuples(vlm)
+    for b in range(3):
+        P = int(lens[b])
+        rk, rv, _ = O.prefill_kv(emb[b, :P], vlm, shape, fp8_mlp=fp8)
+        _check_cache(kn[:, :, :, :P], vn[:, :, :, :P], b, rk, rv, shape.n_layers, f"fp8 prefill sample {b}")
+        bk, _, _ = O.prefill_kv(emb[b, :P], vlm, shape)
+        print(f"sample {b}: layer-1 K vs bf16-MLP oracle rel inf {rel_inf(kn[1, b, :, :P], bk[1]):.3e}", flush=True)
+
+
+def test_prefill_fp8_then_denoise_dm0():
+    s = replace(workload(5).shape, vlm_mlp_dtype=FP8)
+    wl = replace(workload(5), shape=s)
+    print("case: 28-layer VLM prefill with FP8 MLP, B=8 P=816, then suffix denoise", flush=True)
+    vlm = inputs.make_vlm_weights(wl)
+    aw = inputs.make_action_weights(wl)
+    emb = inputs.make_prefix_embeds(wl)
+    x1 = inputs.make_noise(wl)
+    lens = inputs.make_prefix_lens(wl)
+    gpu = Gpu(wl, vlm, aw)
+    k, v = gpu.prefill(emb, lens)
+    got = gpu.denoise(k, v, lens, x1, wl.steps)
+    kn, vn = np32(k), np32(v)
+    b = 2
+    rk, rv, _ = O.prefill_kv(emb[b], vlm, s, fp8_mlp=_fp8_tuples(vlm))
+    ref = O.suffix_denoise(x1[b], aw, rk, rv, s, wl.steps)
+    mx, mean = err_stats(got[b], ref)
+    print(f"config-5 FP8 sample {b} chunk vs FP8 oracle: max abs err {mx:.3e}, mean abs err {mean:.3e}", flush=True)
+    bk, bv, _ = O.prefill_kv(emb[b], vlm, replace(s, vlm_mlp_dtype=BF16))
+    ref16 = O.suffix_denoise(x1[b], aw, bk, bv, s, wl.steps)
+    mx16, mean16 = err_stats(got[b], ref16)
+    print(f"config-5 FP8 sample {b} chunk vs bf16 oracle (accuracy cost of FP8): max {mx16:.3e}, mean {mean16:.3e}",
+          flush=True)
+    mxo, meano = err_stats(ref, ref16)
+    print(f"oracle FP8 vs oracle bf16 chunk: max {mxo:.3e}, mean {meano:.3e}", flush=True)
+    bad = []
+    _check_cache(kn, vn, b, rk, rv, 1, f"fp8 prefill sample {b}")
+    for l in range(1, s.n_layers):
+        for name, g, r8, r16 in (("K", kn[l, b], rk[l], bk[l]), ("V", vn[l, b], rv[l], bv[l])):
+            rms = float(np.sqrt(np.mean(r8 * r8)))
+            e, m = rel_inf(g, r8), err_stats(g, r8)[1] / rms
+            e8, m8 = rel_inf(r16, r8), err_stats(r16, r8)[1] / rms
+            print(f"layer {l} {name}: gpu vs FP8 oracle rel inf {e:.3e} mean/rms {m:.3e}; "
+                  f"FP8 oracle vs bf16 oracle rel inf {e8:.3e} mean/rms {m8:.3e}", flush=True)
+            if not (e <= 1.25 * e8 and m <= m8):
+                bad.append((l, name, e, e8, m, m8))
+    assert not bad, bad
+    assert mx <= 1.25 * mxo and mean <= meano, (mx, mxo, mean, meano)
