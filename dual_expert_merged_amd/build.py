@@ -10,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdm.so")
 SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip"]
+# attention rescales its MFMA accumulators with VALU every key tile: keep them in VGPRs rather
+# than accumulation registers, which would cost a copy out and back per element
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -37,7 +40,7 @@ def build(verbose=False):
         obj = os.path.join(tmpdir, src + ".o")
         flags = [f for f in HIPCC_FLAGS if f != "-shared"]
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [hipcc()] + flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc()] + flags + EXTRA.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         objs.append(obj)
     failed = False

@@ -9,12 +9,14 @@
 // One 256-thread workgroup takes one (sample, KV head, query block, key chunk): 128 query
 // slots = the G query heads of the KV head x 128/G query rows, 32 slots per wave.  Keys stage
 // through LDS 128 at a time (K row-major, V transposed), every load of a stage issued before the
-// first is consumed.  Scores are formed transposed, S^T = K Q^T, so every lane owns one query
-// column: the online-softmax statistics stay in-lane (plus two cross-lane-group exchanges) and
-// the probabilities already sit in the B-operand layout of O^T = V^T P^T.  The key rows of each
-// 16-key score tile are permuted so a lane's probabilities are consecutive keys of the next
-// MFMA's contraction chunk.  Softmax is float32 with base-2 exponentials (scores pre-scaled by
-// log2(e)/sqrt(D)).
+// first is consumed, the next stage loaded while the current one is multiplied.  Scores are
+// formed transposed, S^T = K Q^T, so every lane owns one query column: the online-softmax
+// statistics stay in-lane (plus two cross-lane-group exchanges) and the probabilities already
+// sit in the B-operand layout of O^T = V^T P^T.  The key rows of each 16-key score tile are
+// permuted so a lane's probabilities are consecutive keys of the next MFMA's contraction chunk.
+// Softmax is float32 with base-2 exponentials, updated once per 64 keys; the running output is
+// rescaled only when some column's maximum grew.  Every K and V fragment read from LDS feeds
+// both 16-slot halves of the wave.
 // With several key chunks, each workgroup stores its normalised partial output (weight dtype)
 // with its running max and sum, and attn_combine_kernel merges them in chunk order.
 #include "common.h"
@@ -23,7 +25,7 @@
 namespace dm {
 
 constexpr int ATT_SLOTS = 128;
-constexpr int ATT_KT = 32;   // keys per MFMA score tile pair
+constexpr int ATT_KT = 64;   // keys per softmax update
 constexpr int ATT_CH = 128;  // keys staged in LDS per pass
 
 int attn_qblocks(int q_rows, int Hq, int Hkv) {
@@ -39,6 +41,18 @@ size_t attn_partial_bytes(Dt dt, int B, int Hkv, int nqb, int n_chunks, int D) {
   return ((o + 255) & ~(size_t)255) + ml;
 }
 
+// 4 consecutive output values of one lane: one 8-byte (bf16) or 16-byte (fp32) store.
+template <typename T> __device__ __forceinline__ void store4(T *p, f32x4 v, float s);
+template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, f32x4 v, float s) {
+  bf16x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (bf16)(v[i] * s);
+  *reinterpret_cast<bf16x4 *>(p) = o;
+}
+template <> __device__ __forceinline__ void store4<float>(float *p, f32x4 v, float s) {
+  *reinterpret_cast<f32x4 *>(p) = v * s;
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   typedef Mfma<T> MF;
@@ -46,8 +60,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int EPL = MF::EPL, KC = 4 * EPL;
   constexpr int DC = D / KC;       // contraction chunks of Q K^T
   constexpr int DT = D / 16;       // 16-row tiles of O^T
-  constexpr int NPV = ATT_KT / KC; // contraction chunks of V^T P^T per 32-key tile
+  constexpr int NPV = ATT_KT / KC; // contraction chunks of V^T P^T per tile
   constexpr int SUB = EPL / 4;     // 16-key score tiles per P^T chunk
+  constexpr int NS = ATT_KT / 16;  // 16-key score tiles per tile
   constexpr int RPH = ATT_SLOTS / G;
   constexpr int KLD = D + EPL, VLD = ATT_CH + EPL;
   constexpr int VPRW = D / EPL;                     // 16-byte vectors per key row
@@ -78,9 +93,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int r0 = qb * RPH + (slot0 % RPH);
   const int HD = a.Hq * D;
   const size_t grp = (size_t)bk * nqb + qb;
-  T *part_o = (T *)a.part;
-  float *part_ml = (float *)((char *)a.part + ((part_o_elems(a.B, a.Hkv, nqb, a.n_chunks, D) * sizeof(T) + 255) &
-                                               ~(size_t)255));
 
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   f32x4 o[2][DT];
@@ -99,13 +111,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) qf[qt][dc] = load_frag<T>(qrow + dc * KC + g * EPL);
     }
-    const float sc = 1.4426950408889634f / sqrtf((float)D);
+    const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(D)
     const size_t pre_base = (size_t)(b * a.Hkv + kvh) * a.kp_rows * D;
     const size_t suf_base = (size_t)(b * a.Hkv + kvh) * a.S * D;
 
     // K: 16-byte vectors, lanes along a row (coalesced).  V: lanes along keys, so the transposed
-    // LDS stores of a wave hit consecutive addresses.  The next stage is loaded into registers
-    // while the current one is multiplied.
+    // LDS stores of a wave hit consecutive addresses.  Keys past k_end re-read key k_end-1: their
+    // scores are masked to -inf and their V rows are finite, so they add exactly 0.
     frag kv[LPT], vv[LPT];
     auto stage_load = [&](int ks0) {
 #pragma unroll
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const int r = idx / VPRW, cv = idx - r * VPRW;
         const int kc = min(ks0 + r, k_end - 1);
         const size_t off = kc < P ? pre_base + (size_t)kc * D : suf_base + (size_t)(kc - P) * D;
-        kv[v] = load_frag<T>((kc < P ? kp : ks) + off + cv * EPL);  // keys past k_end: score -inf
+        kv[v] = load_frag<T>((kc < P ? kp : ks) + off + cv * EPL);
       }
 #pragma unroll
       for (int v = 0; v < LPT; ++v) {
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const int cv = idx / ATT_CH, r = idx - cv * ATT_CH;
         const int kc = min(ks0 + r, k_end - 1);
         const size_t off = kc < P ? pre_base + (size_t)kc * D : suf_base + (size_t)(kc - P) * D;
-        vv[v] = load_frag<T>((kc < P ? vp : vs) + off + cv * EPL);  // finite rows, weight 0
+        vv[v] = load_frag<T>((kc < P ? vp : vs) + off + cv * EPL);
       }
     };
     stage_load(k_begin);
@@ -146,67 +158,82 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
       const int stage_keys = min(ATT_CH, k_end - ks0);
       for (int t0 = 0; t0 < stage_keys; t0 += ATT_KT) {
+        // scores S^T for NS 16-key tiles x both 16-slot halves; each K fragment read once
+        f32x4 st[2][NS];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          f32x4 st[2];
+        for (int s = 0; s < NS; ++s) {
+          const int pv = s / SUB, kk = s % SUB;
+          const int krow = t0 + pv * KC + (c16 >> 2) * EPL + 4 * kk + (c16 & 3);
+          frag kf[DC];
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const int pv = s / SUB, kk = s % SUB;
-            const int krow = t0 + pv * KC + (c16 >> 2) * EPL + 4 * kk + (c16 & 3);
+          for (int dc = 0; dc < DC; ++dc) kf[dc] = *reinterpret_cast<const frag *>(&Ks[krow * KLD + dc * KC + g * EPL]);
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dc = 0; dc < DC; ++dc)
-              acc = MF::mma(*reinterpret_cast<const frag *>(&Ks[krow * KLD + dc * KC + g * EPL]), qf[qt][dc], acc);
-            st[s] = acc;
+            for (int dc = 0; dc < DC; ++dc) acc = MF::mma(kf[dc], qf[qt][dc], acc);
+            st[qt][s] = acc;
           }
-          float mx = -INFINITY;
-          const bool partial = ks0 + t0 + ATT_KT > k_end;  // uniform: only the last tile masks keys
+        }
+        const bool partial = ks0 + t0 + ATT_KT > k_end;  // uniform: only the last tile masks keys
+        frag pf[2][NPV];
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const int pv = s / SUB, kk = s % SUB;
+        for (int qt = 0; qt < 2; ++qt) {
+          if (partial) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float v = st[s][i] * sc;
-              if (partial && ks0 + t0 + pv * KC + g * EPL + 4 * kk + i >= k_end) v = -INFINITY;
-              st[s][i] = v;
-              mx = fmaxf(mx, v);
-            }
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (ks0 + t0 + (s / SUB) * KC + g * EPL + 4 * (s % SUB) + i >= k_end) st[qt][s][i] = -INFINITY;
           }
-          mx = max_xor32(max_xor16(mx));
+          float mx = st[qt][0][0];
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[qt][s][i]);
+          mx = max_xor32(max_xor16(mx)) * sc;
           const float m_new = fmaxf(m[qt], mx);
           const float m_use = m_new == -INFINITY ? 0.f : m_new;
-          const float alpha = exp2f(m[qt] - m_use);
           float sum = 0.f;
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
+          for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float p = exp2f(st[s][i] - m_use);
-              st[s][i] = p;
+              const float p = __builtin_amdgcn_exp2f(fmaf(st[qt][s][i], sc, -m_use));
+              st[qt][s][i] = p;
               sum += p;
             }
           sum = sum_xor32(sum_xor16(sum));
-          l[qt] = l[qt] * alpha + sum;
+          // rescale only when some column's maximum grew (wave-uniform branch)
+          if (__ballot(m_new > m[qt]) != 0) {
+            const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_use);
+            l[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
+          }
+          l[qt] += sum;
           m[qt] = m_new;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
-#pragma unroll
-          for (int pv = 0; pv < NPV; ++pv) {
-            frag pf;
+          for (int pv = 0; pv < NPV; ++pv)
 #pragma unroll
             for (int kk = 0; kk < SUB; ++kk)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) pf[kk * 4 + i] = from_f32<T>(st[pv * SUB + kk][i]);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-              o[qt][dt] = MF::mma(*reinterpret_cast<const frag *>(&Vt[(dt * 16 + c16) * VLD + t0 + pv * KC + g * EPL]),
-                                  pf, o[qt][dt]);
-          }
+              for (int i = 0; i < 4; ++i) pf[qt][pv][kk * 4 + i] = from_f32<T>(st[qt][pv * SUB + kk][i]);
         }
+        // O^T += V^T P^T; each V fragment read once for both halves
+#pragma unroll
+        for (int pv = 0; pv < NPV; ++pv)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const frag vf = *reinterpret_cast<const frag *>(&Vt[(dt * 16 + c16) * VLD + t0 + pv * KC + g * EPL]);
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) o[qt][dt] = MF::mma(vf, pf[qt][pv], o[qt][dt]);
+          }
       }
     }
   }
 
+  // lane (g, c16) holds O^T rows dt*16 + 4g .. +3 of query column c16: 4 consecutive outputs
   if (a.n_chunks == 1) {
     T *out = (T *)a.out;
 #pragma unroll
@@ -214,17 +241,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       const int row = r0 + qt * 16 + c16;
       if (row >= nq) continue;
       const float inv = 1.0f / l[qt];
-      T *orow = out + (size_t)(b * a.q_rows_per_b + row) * HD + h * D;
+      T *orow = out + (size_t)(b * a.q_rows_per_b + row) * HD + h * D + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) orow[dt * 16 + 4 * g + i] = from_f32<T>(o[qt][dt][i] * inv);
+      for (int dt = 0; dt < DT; ++dt) store4<T>(orow + dt * 16, o[qt][dt], inv);
     }
     return;
   }
 
   // several chunks: publish this chunk's normalised output and statistics; attn_combine merges
   if (chunk < nch) {
+    T *part_o = (T *)a.part;
+    float *part_ml = (float *)((char *)a.part + ((part_o_elems(a.B, a.Hkv, nqb, a.n_chunks, D) * sizeof(T) + 255) &
+                                                 ~(size_t)255));
     T *po = part_o + (grp * a.n_chunks + chunk) * ATT_SLOTS * D;
     float *pml = part_ml + (grp * a.n_chunks + chunk) * ATT_SLOTS * 2;
 #pragma unroll
@@ -234,13 +262,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       const int slot = slot0 + qt * 16 + c16;
       const float inv = 1.0f / l[qt];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) po[slot * D + dt * 16 + 4 * g + i] = from_f32<T>(o[qt][dt][i] * inv);
-      if (g == 0) {
-        pml[slot * 2] = m[qt];
-        pml[slot * 2 + 1] = l[qt];
-      }
+      for (int dt = 0; dt < DT; ++dt) store4<T>(po + slot * D + dt * 16 + 4 * g, o[qt][dt], inv);
+      if (g == 0) *reinterpret_cast<float2 *>(&pml[slot * 2]) = make_float2(m[qt], l[qt]);
     }
   }
 }
@@ -248,11 +271,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 // Merge the key chunks of every query slot (a separate launch: the kernel boundary makes the
 // partial results visible, with no device-scope fence inside a kernel):
 //   O = sum_c 2^(m_c - M) l_c O_c / sum_c 2^(m_c - M) l_c, summed in chunk order.
+// One workgroup per (sample, KV head, query block, 16 slots); thread = one 16-byte vector of one
+// slot's output, computing its slot's chunk weights itself (the 16 threads of a slot read the
+// same statistics), every load issued before the first is used.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   typedef Mfma<T> MF;
   constexpr int EPL = MF::EPL, RPH = ATT_SLOTS / G, MAXC = 16;
-  __shared__ float wts[ATT_SLOTS * MAXC];
+  constexpr int VPRW = D / EPL;        // vectors per slot row
+  constexpr int SPW = 256 / VPRW;      // slots per workgroup
   const int tid = threadIdx.x;
   const int bk = blockIdx.x, qb = blockIdx.y, nqb = gridDim.y;
   const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
@@ -260,84 +287,47 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int nq = a.suffix ? a.S : P;
   const int nkeys = P + (a.suffix ? a.S : 0);
   const int nch = (nkeys + a.chunk_keys - 1) / a.chunk_keys;
+  const int slot = blockIdx.z * SPW + tid / VPRW, cv = tid % VPRW;
+  const int srow = qb * RPH + slot % RPH;
   if (qb * RPH >= nq) return;
   const int HD = a.Hq * D;
   const size_t grp = (size_t)bk * nqb + qb;
   const T *part_o = (const T *)a.part;
   const float *part_ml = (const float *)((const char *)a.part +
                                          ((part_o_elems(a.B, a.Hkv, nqb, a.n_chunks, D) * sizeof(T) + 255) & ~(size_t)255));
-  // 1: per query slot the weight 2^(m_c - M) l_c / L of every chunk
-  if (tid < ATT_SLOTS) {
-    const int slot = tid;
-    const float *pml = part_ml + grp * a.n_chunks * ATT_SLOTS * 2;
-    float mc[MAXC], lc[MAXC];
+  const float *pml = part_ml + grp * a.n_chunks * ATT_SLOTS * 2;
+  float2 ml[MAXC];
+  typename MF::frag pv[MAXC];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {  // unconditional loads (clamped chunk) stay in flight together
-      const float2 v = *reinterpret_cast<const float2 *>(&pml[(min(c, nch - 1) * ATT_SLOTS + slot) * 2]);
-      mc[c] = v.x;
-      lc[c] = v.y;
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c)
-      if (c < nch) M = fmaxf(M, mc[c]);
-    float L = 0.f;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      mc[c] = c < nch ? exp2f(mc[c] - M) * lc[c] : 0.f;
-      L += mc[c];
-    }
-    const float invL = 1.0f / L;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) wts[slot * MAXC + c] = mc[c] * invL;
+  for (int c = 0; c < MAXC; ++c) {  // unconditional loads (clamped chunk) stay in flight together
+    const int cc = min(c, nch - 1);
+    ml[c] = *reinterpret_cast<const float2 *>(&pml[(cc * ATT_SLOTS + slot) * 2]);
+    pv[c] = load_frag<T>(part_o + ((grp * a.n_chunks + cc) * ATT_SLOTS + slot) * D + cv * EPL);
   }
-  __syncthreads();
-  // 2: out = sum_c w_c O_c over 16-byte vectors, four chunks of loads in flight at a time
-  constexpr int VPRW = D / EPL;
-  constexpr int ITEMS = ATT_SLOTS * VPRW / 256;
-  float acc[ITEMS][EPL];
-  int srow[ITEMS];
+  float M = -INFINITY;
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it) {
-    const int slot = (tid + it * 256) / VPRW;
-    srow[it] = qb * RPH + slot % RPH;
+  for (int c = 0; c < MAXC; ++c)
+    if (c < nch) M = fmaxf(M, ml[c].x);
+  float w[MAXC], L = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[it][e] = 0.f;
+  for (int c = 0; c < MAXC; ++c) {
+    w[c] = c < nch ? __builtin_amdgcn_exp2f(ml[c].x - M) * ml[c].y : 0.f;
+    L += w[c];
   }
-  for (int c0 = 0; c0 < nch; c0 += 4) {
-    typename MF::frag pv[ITEMS][4];
+  const float invL = 1.0f / L;
+  float acc[EPL];
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int idx = tid + it * 256, slot = idx / VPRW, cv = idx - slot * VPRW;
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const int c = min(c0 + cc, nch - 1);
-        // chunks past nch re-read chunk nch-1 (weight 0); slots past nq are never stored
-        pv[it][cc] = load_frag<T>(part_o + ((grp * a.n_chunks + c) * ATT_SLOTS + slot) * D + cv * EPL);
-      }
-    }
+  for (int c = 0; c < MAXC; ++c)
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int slot = (tid + it * 256) / VPRW;
+    for (int e = 0; e < EPL; ++e) acc[e] += w[c] * to_f32(pv[c][e]);
+  if (srow >= nq) return;
+  const int hh = kvh * G + slot / RPH;
+  typename MF::frag o8;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const float w = wts[slot * MAXC + min(c0 + cc, MAXC - 1)];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[it][e] += w * to_f32(pv[it][cc][e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int it = 0; it < ITEMS; ++it) {
-    if (srow[it] >= nq) continue;
-    const int idx = tid + it * 256, slot = idx / VPRW, cv = idx - slot * VPRW;
-    const int hh = kvh * G + slot / RPH;
-    typename MF::frag o8;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o8[e] = from_f32<T>(acc[it][e]);
-    *reinterpret_cast<typename MF::frag *>((T *)a.out + (size_t)(b * a.q_rows_per_b + srow[it]) * HD + hh * D +
-                                           cv * EPL) = o8;
-  }
+  for (int e = 0; e < EPL; ++e) o8[e] = from_f32<T>(acc[e] * invL);
+  *reinterpret_cast<typename MF::frag *>((T *)a.out + (size_t)(b * a.q_rows_per_b + srow) * HD + hh * D + cv * EPL) = o8;
 }
 
 template <typename T, int D, int G> static void attn_t(const AttnArgs &a, hipStream_t s) {
@@ -347,7 +337,10 @@ template <typename T, int D, int G> static void attn_t(const AttnArgs &a, hipStr
   // chunks of one KV head share an XCD and its L2 holds their partial results for the merge.
   dim3 grid(a.B * a.Hkv, nqb, a.n_chunks);
   hipLaunchKernelGGL((attn_kernel<T, D, G>), grid, dim3(256), 0, s, a);
-  if (a.n_chunks > 1) hipLaunchKernelGGL((attn_combine_kernel<T, D, G>), dim3(a.B * a.Hkv, nqb), dim3(256), 0, s, a);
+  if (a.n_chunks > 1) {
+    constexpr int SPW = 256 / (D / Mfma<T>::EPL);
+    hipLaunchKernelGGL((attn_combine_kernel<T, D, G>), dim3(a.B * a.Hkv, nqb, ATT_SLOTS / SPW), dim3(256), 0, s, a);
+  }
 }
 
 template <typename T, int D> static void attn_g(const AttnArgs &a, hipStream_t s) {
