@@ -6,17 +6,19 @@
 // are the cached VLM K/V, so the kernel streams them straight from the cache layout
 // [B][Hkv][P_cap][D] followed by the action keys [B][Hkv][S][D], never concatenating them.
 //
-// One 256-thread workgroup takes one (sample, KV head, query block, key chunk): 128 query
-// slots = the G query heads of the KV head x 128/G query rows, 32 slots per wave.  Keys stage
-// through LDS 128 at a time (K row-major, V transposed), every load of a stage issued before the
-// first is consumed, the next stage loaded while the current one is multiplied.  Scores are
-// formed transposed, S^T = K Q^T, so every lane owns one query column: the online-softmax
-// statistics stay in-lane (plus two cross-lane-group exchanges) and the probabilities already
-// sit in the B-operand layout of O^T = V^T P^T.  The key rows of each 16-key score tile are
-// permuted so a lane's probabilities are consecutive keys of the next MFMA's contraction chunk.
-// Softmax is float32 with base-2 exponentials, updated once per 64 keys; the running output is
-// rescaled only when some column's maximum grew.  Every K and V fragment read from LDS feeds
-// both 16-slot halves of the wave.
+// One 512-thread workgroup takes one (sample, KV head, query block, key chunk): 128 query
+// slots = the G query heads of the KV head x 128/G query rows.  Its 8 waves form 4 slot groups of
+// 32 slots x 2 key halves: both waves of a pair see every LDS stage, each takes one half of every
+// 64-key tile with its own online softmax, and the pair merges (max, sum, output) through LDS at
+// the end.  Two waves per SIMD hide each other's LDS and MFMA latencies while every K/V byte is
+// still read from LDS only once per slot group.  Keys stage through LDS 128 at a time (K
+// row-major, V transposed), every load of a stage issued before the first is consumed, the next
+// stage loaded while the current one is multiplied.  Scores are formed transposed,
+// S^T = K Q^T, so every lane owns one query column: the online-softmax statistics stay in-lane
+// (plus two cross-lane-group exchanges) and the probabilities already sit in the B-operand
+// layout of O^T = V^T P^T.  The key rows of each 16-key score tile are permuted so a lane's
+// probabilities are consecutive keys of the next MFMA's contraction chunk.  Softmax is float32
+// with base-2 exponentials; the running output is rescaled only when some column's maximum grew.
 // With several key chunks, each workgroup stores its normalised partial output (weight dtype)
 // with its running max and sum, and attn_combine_kernel merges them in chunk order.
 #include "common.h"
@@ -25,8 +27,9 @@
 namespace dm {
 
 constexpr int ATT_SLOTS = 128;
-constexpr int ATT_KT = 64;   // keys per softmax update
-constexpr int ATT_CH = 128;  // keys staged in LDS per pass
+constexpr int ATT_KT = 64;    // keys per tile (32 per wave of a pair)
+constexpr int ATT_CH = 128;   // keys staged in LDS per pass
+constexpr int ATT_THREADS = 512;
 
 int attn_qblocks(int q_rows, int Hq, int Hkv) {
   const int rph = ATT_SLOTS / (Hq / Hkv);
@@ -54,21 +57,26 @@ template <> __device__ __forceinline__ void store4<float>(float *p, f32x4 v, flo
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(ATT_THREADS) void attn_kernel(AttnArgs a) {
   typedef Mfma<T> MF;
   typedef typename MF::frag frag;
   constexpr int EPL = MF::EPL, KC = 4 * EPL;
-  constexpr int DC = D / KC;       // contraction chunks of Q K^T
-  constexpr int DT = D / 16;       // 16-row tiles of O^T
-  constexpr int NPV = ATT_KT / KC; // contraction chunks of V^T P^T per tile
-  constexpr int SUB = EPL / 4;     // 16-key score tiles per P^T chunk
-  constexpr int NS = ATT_KT / 16;  // 16-key score tiles per tile
+  constexpr int DC = D / KC;        // contraction chunks of Q K^T
+  constexpr int DT = D / 16;        // 16-row tiles of O^T
+  constexpr int HK = ATT_KT / 2;    // keys of a tile per wave
+  constexpr int NPV = HK / KC;      // contraction chunks of V^T P^T per half tile
+  constexpr int SUB = EPL / 4;      // 16-key score tiles per P^T chunk
+  constexpr int NS = HK / 16;       // 16-key score tiles per half tile
   constexpr int RPH = ATT_SLOTS / G;
   constexpr int KLD = D + EPL, VLD = ATT_CH + EPL;
-  constexpr int VPRW = D / EPL;                     // 16-byte vectors per key row
-  constexpr int LPT = ATT_CH * VPRW / 256;          // vectors per thread per stage
-  __shared__ __attribute__((aligned(16))) T Ks[ATT_CH * KLD];
-  __shared__ __attribute__((aligned(16))) T Vt[D * VLD];
+  constexpr int VPRW = D / EPL;                      // 16-byte vectors per key row
+  constexpr int LPT = ATT_CH * VPRW / ATT_THREADS;   // vectors per thread per stage
+  constexpr int STAGE_B = (ATT_CH * KLD + D * VLD) * (int)sizeof(T);
+  constexpr int XO = 4 * 2 * DT * 64;                // merge: float4 outputs of the second waves
+  constexpr int MERGE_B = XO * 16 + 2 * 4 * 2 * 64 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[STAGE_B > MERGE_B ? STAGE_B : MERGE_B];
+  T *Ks = reinterpret_cast<T *>(smem);
+  T *Vt = Ks + ATT_CH * KLD;
 
   const T *__restrict__ q = (const T *)a.q;
   const T *__restrict__ kp = (const T *)a.kp;
@@ -77,6 +85,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const T *__restrict__ vs = (const T *)a.vs;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sg = wave & 3, kh = wave >> 2;  // slot group, key half
   const int g = lane >> 4, c16 = lane & 15;
   const int bk = blockIdx.x, qb = blockIdx.y, chunk = blockIdx.z, nqb = gridDim.y;
   const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int k_end = min(nkeys, k_begin + a.chunk_keys);
   if (qb * RPH >= nq) return;  // no query rows here: uniform, and no merge is needed
 
-  const int slot0 = wave * 32;
+  const int slot0 = sg * 32;
   const int h = kvh * G + slot0 / RPH;
   const int r0 = qb * RPH + (slot0 % RPH);
   const int HD = a.Hq * D;
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     auto stage_load = [&](int ks0) {
 #pragma unroll
       for (int v = 0; v < LPT; ++v) {
-        const int idx = tid + v * 256;
+        const int idx = tid + v * ATT_THREADS;
         const int r = idx / VPRW, cv = idx - r * VPRW;
         const int kc = min(ks0 + r, k_end - 1);
         const size_t off = kc < P ? pre_base + (size_t)kc * D : suf_base + (size_t)(kc - P) * D;
@@ -130,7 +139,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int v = 0; v < LPT; ++v) {
-        const int idx = tid + v * 256;
+        const int idx = tid + v * ATT_THREADS;
         const int cv = idx / ATT_CH, r = idx - cv * ATT_CH;
         const int kc = min(ks0 + r, k_end - 1);
         const size_t off = kc < P ? pre_base + (size_t)kc * D : suf_base + (size_t)(kc - P) * D;
@@ -142,13 +151,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       __syncthreads();  // the previous stage is consumed
 #pragma unroll
       for (int v = 0; v < LPT; ++v) {
-        const int idx = tid + v * 256;
+        const int idx = tid + v * ATT_THREADS;
         const int r = idx / VPRW, cv = idx - r * VPRW;
         *reinterpret_cast<frag *>(&Ks[r * KLD + cv * EPL]) = kv[v];
       }
 #pragma unroll
       for (int v = 0; v < LPT; ++v) {
-        const int idx = tid + v * 256;
+        const int idx = tid + v * ATT_THREADS;
         const int cv = idx / ATT_CH, r = idx - cv * ATT_CH;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) Vt[(cv * EPL + e) * VLD + r] = vv[v][e];
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       if (ks0 + ATT_CH < k_end) stage_load(ks0 + ATT_CH);
 
       const int stage_keys = min(ATT_CH, k_end - ks0);
-      for (int t0 = 0; t0 < stage_keys; t0 += ATT_KT) {
+      for (int t0 = kh * HK; t0 < stage_keys; t0 += ATT_KT) {  // this wave's half of every tile
         // scores S^T for NS 16-key tiles x both 16-slot halves; each K fragment read once
         f32x4 st[2][NS];
 #pragma unroll
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             st[qt][s] = acc;
           }
         }
-        const bool partial = ks0 + t0 + ATT_KT > k_end;  // uniform: only the last tile masks keys
+        const bool partial = ks0 + t0 + HK > k_end;  // uniform: only the last tile masks keys
         frag pf[2][NPV];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
@@ -233,6 +242,34 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
   }
 
+  // merge the two key halves of every slot group: the second wave hands its state over in LDS
+  __syncthreads();  // every stage read is done: the LDS is free
+  float *xo = reinterpret_cast<float *>(smem);
+  float *xm = xo + XO * 4, *xl = xm + 4 * 2 * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4 *>(&xo[(((sg * 2 + qt) * DT + dt) * 64 + lane) * 4]) = o[qt][dt];
+      xm[(sg * 2 + qt) * 64 + lane] = m[qt];
+      xl[(sg * 2 + qt) * 64 + lane] = l[qt];
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float m1 = xm[(sg * 2 + qt) * 64 + lane], l1 = xl[(sg * 2 + qt) * 64 + lane];
+    const float M = fmaxf(m[qt], m1);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float a0 = __builtin_amdgcn_exp2f(m[qt] - Mu), a1 = __builtin_amdgcn_exp2f(m1 - Mu);
+    l[qt] = l[qt] * a0 + l1 * a1;
+    m[qt] = M;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      o[qt][dt] = o[qt][dt] * a0 + *reinterpret_cast<const f32x4 *>(&xo[(((sg * 2 + qt) * DT + dt) * 64 + lane) * 4]) * a1;
+  }
+
   // lane (g, c16) holds O^T rows dt*16 + 4g .. +3 of query column c16: 4 consecutive outputs
   if (a.n_chunks == 1) {
     T *out = (T *)a.out;
@@ -248,23 +285,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     return;
   }
 
-  // several chunks: publish this chunk's normalised output and statistics; attn_combine merges
-  if (chunk < nch) {
-    T *part_o = (T *)a.part;
-    float *part_ml = (float *)((char *)a.part + ((part_o_elems(a.B, a.Hkv, nqb, a.n_chunks, D) * sizeof(T) + 255) &
-                                                 ~(size_t)255));
-    T *po = part_o + (grp * a.n_chunks + chunk) * ATT_SLOTS * D;
-    float *pml = part_ml + (grp * a.n_chunks + chunk) * ATT_SLOTS * 2;
+  // several chunks: publish this chunk's normalised output and statistics; a chunk past the
+  // sample's keys publishes max -inf and sum 0 (weight 0 in the merge)
+  T *part_o = (T *)a.part;
+  float *part_ml = (float *)((char *)a.part + ((part_o_elems(a.B, a.Hkv, nqb, a.n_chunks, D) * sizeof(T) + 255) &
+                                               ~(size_t)255));
+  T *po = part_o + (grp * a.n_chunks + chunk) * ATT_SLOTS * D;
+  float *pml = part_ml + (grp * a.n_chunks + chunk) * ATT_SLOTS * 2;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int row = r0 + qt * 16 + c16;
-      if (row >= nq) continue;
-      const int slot = slot0 + qt * 16 + c16;
+  for (int qt = 0; qt < 2; ++qt) {
+    const int row = r0 + qt * 16 + c16;
+    if (row >= nq) continue;
+    const int slot = slot0 + qt * 16 + c16;
+    if (chunk < nch) {
       const float inv = 1.0f / l[qt];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) store4<T>(po + slot * D + dt * 16 + 4 * g, o[qt][dt], inv);
-      if (g == 0) *reinterpret_cast<float2 *>(&pml[slot * 2]) = make_float2(m[qt], l[qt]);
     }
+    if (g == 0) *reinterpret_cast<float2 *>(&pml[slot * 2]) = chunk < nch ? make_float2(m[qt], l[qt]) : make_float2(-INFINITY, 0.f);
   }
 }
 
@@ -283,10 +321,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int bk = blockIdx.x, qb = blockIdx.y, nqb = gridDim.y;
   const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
-  const int P = max(0, min(a.lens[b], a.kp_rows));
-  const int nq = a.suffix ? a.S : P;
-  const int nkeys = P + (a.suffix ? a.S : 0);
-  const int nch = (nkeys + a.chunk_keys - 1) / a.chunk_keys;
+  // action queries: S rows, no wait for the prefix length; chunks past a sample's keys carry
+  // weight 0, so every one of the n_chunks is merged
+  const int nq = a.suffix ? a.S : max(0, min(a.lens[b], a.kp_rows));
+  const int nch = a.n_chunks;
   const int slot = blockIdx.z * SPW + tid / VPRW, cv = tid % VPRW;
   const int srow = qb * RPH + slot % RPH;
   if (qb * RPH >= nq) return;
@@ -311,7 +349,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   float w[MAXC], L = 0.f;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
-    w[c] = c < nch ? __builtin_amdgcn_exp2f(ml[c].x - M) * ml[c].y : 0.f;
+    w[c] = c < nch && ml[c].y > 0.f ? __builtin_amdgcn_exp2f(ml[c].x - M) * ml[c].y : 0.f;
     L += w[c];
   }
   const float invL = 1.0f / L;
@@ -321,7 +359,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < MAXC; ++c)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += w[c] * to_f32(pv[c][e]);
+    for (int e = 0; e < EPL; ++e) {
+      const float t = w[c] * to_f32(pv[c][e]);
+      acc[e] += w[c] > 0.f ? t : 0.f;  // a zero-weight chunk's output was never written
+    }
   if (srow >= nq) return;
   const int hh = kvh * G + slot / RPH;
   typename MF::frag o8;
@@ -336,7 +377,7 @@ template <typename T, int D, int G> static void attn_t(const AttnArgs &a, hipStr
   // (sample, KV head) varies fastest: consecutive workgroups go to consecutive XCDs, so all key
   // chunks of one KV head share an XCD and its L2 holds their partial results for the merge.
   dim3 grid(a.B * a.Hkv, nqb, a.n_chunks);
-  hipLaunchKernelGGL((attn_kernel<T, D, G>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_kernel<T, D, G>), grid, dim3(ATT_THREADS), 0, s, a);
   if (a.n_chunks > 1) {
     constexpr int SPW = 256 / (D / Mfma<T>::EPL);
     hipLaunchKernelGGL((attn_combine_kernel<T, D, G>), dim3(a.B * a.Hkv, nqb, ATT_SLOTS / SPW), dim3(256), 0, s, a);

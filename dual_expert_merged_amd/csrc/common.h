@@ -104,14 +104,25 @@ constexpr int DPP_ROR8 = 0x128;        // lane i <- lane (i+8) mod 16: the same 
 __device__ __forceinline__ float lane_xor8(float v) { return dpp<DPP_ROR8>(v); }
 // Across rows: lane l^16 through ds_swizzle (swap of the 16-lane halves of each 32 lanes), lane
 // l^32 through ds_bpermute.
-__device__ __forceinline__ float lane_xor16(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+// Reductions over lane pairs (l, l^16) and (l, l^32) with gfx950's v_permlane16/32_swap: given
+// the same register twice, the two results hold v[l] and v[l^16] (resp. l^32) in some order, so
+// their sum or max is the pair's, bitwise identical in both lanes; no LDS round trip.
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
-__device__ __forceinline__ float lane_xor32(float v) { return __shfl_xor(v, 32, WAVE); }
-__device__ __forceinline__ float sum_xor16(float v) { return v + lane_xor16(v); }
-__device__ __forceinline__ float sum_xor32(float v) { return v + lane_xor32(v); }
-__device__ __forceinline__ float max_xor16(float v) { return fmaxf(v, lane_xor16(v)); }
-__device__ __forceinline__ float max_xor32(float v) { return fmaxf(v, lane_xor32(v)); }
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
 // Sum over the 4 lanes of a quad, the 16 lanes of a row, and the whole wave.
 __device__ __forceinline__ float sum4(float v) {
   v += dpp<DPP_XOR1>(v);

@@ -74,7 +74,7 @@ struct ExpertPlans {
 };
 
 struct Layout {
-  Region rope;
+  Region rope, rope_rows;
   Region h, hg, ssq, q, ks, vs, o, act, apart, split;          // action side (h: denoise only)
   Region hp, hg_p, ssq_p, q_p, kp, vp, o_p, act_p, apart_p;    // prefix side (hp: prefill only)
   Region q8_p, qs_p;                                           // FP8 MLP operand codes and row scales
@@ -158,6 +158,7 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
   const int Ha = c.act_hidden, Hv = c.vlm_hidden;
   const size_t Ms = (size_t)B * S, Mp = (size_t)B * P_cap;
   L.put(L.rope, (size_t)(P_cap + S) * (D / 2) * sizeof(float2));
+  if (op != DM_OP_PREFILL) L.put(L.rope_rows, (size_t)B * S * (D / 2) * sizeof(float2));
   size_t split = 0;
   if (op == DM_OP_DENOISE || op == DM_OP_MERGED_LAYER) {
     L.pa = plan_expert(c, dt, (int)Ms, Ha, c.act_ffn);
@@ -360,12 +361,14 @@ dm_status enqueue_denoise(const dm_ctx *ctx, const dm_action_weights *aw, const 
   const GemmPlan pq = L.pa.qkv;
 
   launch_rope_table(rope, P_cap + S, D, c.rope_base, s);
+  float2 *rope_rows = at<float2>(ws, L.rope_rows);
+  launch_rope_rows(rope, lens, P_cap, B, S, D, rope_rows, s);
   for (int k = 0; k < num_steps; ++k) {
     const float t = 1.0f - (float)k / (float)num_steps;
     launch_embed(ctx->dt, x, aw->w_in, aw->b_in, hid, aw->body.attn_norm, M, c.action_dim, t, s);
     for (int l = 0; l < c.n_layers; ++l) {
       const Expert e = expert_layer(c, aw->body, l, Ha, Fa, ctx->es);
-      QkvArgs qa{hid, M, c.rms_eps, e.w_qkv, q, ks, vs, S, rows, rope, c.n_q_heads, Hkv, D};
+      QkvArgs qa{hid, M, c.rms_eps, e.w_qkv, q, ks, vs, S, rows, rope, c.n_q_heads, Hkv, D, rope_rows};
       launch_qkv(ctx->dt, qa, pq, s);
       AttnArgs aa{q, S, 1,
                   layer_ptr(k_cache, layer_cache, l, ctx->es), layer_ptr(v_cache, layer_cache, l, ctx->es), P_cap,
@@ -542,12 +545,14 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   const Hidden hs{h_suffix, at<void>(ws, L.hg), at<float>(ws, L.ssq), c.act_hidden};
 
   launch_rope_table(rope, P_cap + S, D, c.rope_base, s);
+  float2 *rope_rows = at<float2>(ws, L.rope_rows);
+  launch_rope_rows(rope, prefix_lens, P_cap, B, S, D, rope_rows, s);
   launch_norm_prep(ctx->dt, h_prefix, hp, ev.attn_norm, Mp, s);
   launch_norm_prep(ctx->dt, h_suffix, hs, ea.attn_norm, Ms, s);
   QkvArgs qv{hp, Mp, c.rms_eps, ev.w_qkv, at<void>(ws, L.q_p), kp, vp, P_cap, prow, rope, Hq, Hkv, D};
   launch_qkv(ctx->dt, qv, L.pv.qkv, s);
   QkvArgs qa{hs, Ms, c.rms_eps, ea.w_qkv, at<void>(ws, L.q), at<void>(ws, L.ks), at<void>(ws, L.vs), S, srow, rope,
-             Hq, Hkv, D};
+             Hq, Hkv, D, rope_rows};
   launch_qkv(ctx->dt, qa, L.pa.qkv, s);
   AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kp, vp, P_cap, nullptr, nullptr, S, prefix_lens, B, Hq, Hkv, D,
               L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),

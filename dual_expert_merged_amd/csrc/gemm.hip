@@ -58,6 +58,41 @@ __device__ __forceinline__ void rms_prepare(const Hidden &in, int M, float eps, 
   }
 }
 
+// The same for the 64 rows of the skinny kernel in two steps: rms_load issues the loads of the
+// sums of squares, rms_finish reduces them once they have arrived, so the operand loads can be
+// issued in between (loads complete in issue order: these small ones first).
+struct RmsPre {
+  float4 v[16];
+};
+__device__ __forceinline__ RmsPre rms_load(const Hidden &in, int M, int m0) {
+  RmsPre p;
+  const int nt = in.H >> 4, t = threadIdx.x, row = t >> 2, part = t & 3;
+  if ((nt & 15) == 0) {
+    const int per = nt >> 4;
+    const float4 *q4 = reinterpret_cast<const float4 *>(in.ssq + (size_t)min(m0 + row, M - 1) * nt) + part * per;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p.v[j] = q4[min(j, per - 1)];
+  }
+  return p;
+}
+__device__ __forceinline__ void rms_finish(const RmsPre &p, const Hidden &in, int M, float eps, int m0, float *inv,
+                                           const float *row_scale = nullptr) {
+  const int nt = in.H >> 4, t = threadIdx.x, row = t >> 2, part = t & 3;
+  float s = 0.f;
+  if ((nt & 15) == 0) {
+    const int per = nt >> 4;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < per) s += (p.v[j].x + p.v[j].y) + (p.v[j].z + p.v[j].w);
+  } else {
+    const float *q = in.ssq + (size_t)min(m0 + row, M - 1) * nt;
+    for (int i = part; i < nt; i += 4) s += q[i];
+  }
+  s = sum4(s);
+  const float rs = row_scale ? row_scale[min(m0 + row, M - 1)] : 1.0f;
+  if (part == 0) inv[row] = rsqrtf(s / (float)in.H + eps) * rs;
+}
+
 // Epilogues run per 16x16 tile in two phases so that their global loads (RoPE table, residual
 // rows) are all issued before any is consumed: load() gathers, store() computes and writes.  The
 // row facts (sample, token, validity) of a 16-row tile are shared by all its column tiles.
@@ -83,12 +118,20 @@ __device__ __forceinline__ RowInfo row_info(const RowMap &rm, int row0, int M) {
     ri.b[r] = b0 + wrap;
     ri.s[r] = s - wrap * rm.rows_per_b;
   }
+  if (rm.is_prefix) {  // uniform; action rows need no prefix length (their RoPE rows are precomputed)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) len[r] = rm.lens[ri.b[r]];
+    for (int r = 0; r < 4; ++r) len[r] = rm.lens[ri.b[r]];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    ri.plen[r] = max(0, min(len[r], rm.cap));
-    ri.ok[r] = (row0 + r < M) && (rm.is_prefix ? ri.s[r] < ri.plen[r] : true);
+    for (int r = 0; r < 4; ++r) {
+      ri.plen[r] = max(0, min(len[r], rm.cap));
+      ri.ok[r] = (row0 + r < M) && ri.s[r] < ri.plen[r];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ri.plen[r] = 0;
+      ri.ok[r] = row0 + r < M;
+    }
   }
   return ri;
 }
@@ -114,17 +157,69 @@ template <typename T> struct EpiQkv {
   __device__ __forceinline__ void prepare(int m0, int rows, float *inv) const {
     rms_prepare(a.in, a.M, a.eps, m0, rows, inv);
   }
+  typedef RmsPre Pre;
+  __device__ __forceinline__ Pre pre_load(int m0) const { return rms_load(a.in, a.M, m0); }
+  __device__ __forceinline__ void pre_finish(const Pre &p, int m0, float *inv) const {
+    rms_finish(p, a.in, a.M, a.eps, m0, inv);
+  }
+  // (cos, sin) of the row's position: prefix token s at s (table by position), action rows from
+  // the per-row table (position P_b + s, filled once per call)
   __device__ __forceinline__ St load(const RowInfo &ri, int c) const {
     St st;
     const int D = a.D, half = D >> 1;
     const int d = col(c) & (D - 1);
     const int i = d & (half - 1);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pos = a.rows.is_prefix ? ri.s[r] : ri.plen[r] + ri.s[r];
-      st.cs[r] = a.rope[(size_t)pos * half + i];  // also read for value columns (unused there)
-    }
+    for (int r = 0; r < 4; ++r)  // also read for value columns (unused there)
+      st.cs[r] = a.rows.is_prefix ? a.rope[(size_t)ri.s[r] * half + i] : a.rope_rows[(size_t)ri.rc[r] * half + i];
     return st;
+  }
+  // Large tiles: a 128 x 256 tile is two whole heads of one section (q, k or v).  to_lds puts
+  // the rotated values at their natural (head, d) position of row (row - m0) of the staging tile;
+  // lds_out then writes each row's two heads as whole 16-byte vectors.
+  static constexpr bool kTile = true;
+  // every tile must lie inside one section: q, k and v widths are multiples of the tile width
+  __device__ __forceinline__ bool tile_ok(int bn) const { return (a.Hq * a.D) % bn == 0 && (a.Hkv * a.D) % bn == 0; }
+  template <int LD>
+  __device__ __forceinline__ void to_lds(const St &st, int row0, int c, f32x4 acc, const float *inv, int m0, int n0,
+                                         T *ot) const {
+    const int gc = col(c), gc0 = col(n0);
+    const int D = a.D;
+    const int local = gc - gc0;  // (head - first head) * D + d
+    const int upper = (gc & (D - 1)) >= (D >> 1);
+    const bool rot = gc < (a.Hq + a.Hkv) * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float u = acc[r] * inv[row0 + r - m0];
+      const float pu = lane_xor8(u);
+      if (rot) u = upper ? (u * st.cs[r].x + pu * st.cs[r].y) : (u * st.cs[r].x - pu * st.cs[r].y);
+      ot[(row0 + r - m0) * LD + local] = from_f32<T>(u);
+    }
+  }
+  template <int LD, int BM, int BN>
+  __device__ __forceinline__ void lds_out(const T *ot, int m0, int n0, int M) const {
+    constexpr int CPR = BN / 8;  // 16-byte chunks per row
+    const int D = a.D, qd = a.Hq * D, kd = a.Hkv * D;
+    const int gc0 = col(n0);
+    const int sec = gc0 < qd ? 0 : (gc0 < qd + kd ? 1 : 2);
+    const int head0 = (gc0 - (sec == 0 ? 0 : (sec == 1 ? qd : qd + kd))) / D;
+    const RowMap &rm = a.rows;
+#pragma unroll 4
+    for (int idx = threadIdx.x; idx < BM * CPR; idx += 256) {
+      const int rl = idx / CPR, ch = idx - rl * CPR, row = m0 + rl;
+      if (row >= M) continue;
+      const int b = row / rm.rows_per_b, s = row - b * rm.rows_per_b;
+      if (rm.is_prefix && s >= max(0, min(rm.lens[b], rm.cap))) continue;
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(&ot[rl * LD + ch * 8]);
+      T *dst;
+      if (sec == 0) {
+        dst = (T *)a.q + (size_t)row * qd + gc0 + ch * 8;
+      } else {
+        const int hl = (ch * 8) / D, d = ch * 8 - hl * D;
+        dst = (T *)(sec == 1 ? a.k : a.v) + ((size_t)(b * a.Hkv + head0 + hl) * a.kv_rows + s) * D + d;
+      }
+      *reinterpret_cast<i32x4 *>(dst) = v;
+    }
   }
   __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
                                         int m0) const {
@@ -165,6 +260,15 @@ template <typename T, typename W = T> struct EpiResid {
     if constexpr (Q)
       for (int t = threadIdx.x; t < rows; t += blockDim.x) inv[t] = a.a_scale[min(m0 + t, a.M - 1)];
   }
+  static constexpr bool kTile = false;
+  __device__ __forceinline__ bool tile_ok(int) const { return false; }
+  template <int LD>
+  __device__ __forceinline__ void to_lds(const St &, int, int, f32x4, const float *, int, int, T *) const {}
+  template <int LD, int BM, int BN>
+  __device__ __forceinline__ void lds_out(const T *, int, int, int) const {}
+  struct Pre {};
+  __device__ __forceinline__ Pre pre_load(int) const { return Pre{}; }
+  __device__ __forceinline__ void pre_finish(const Pre &, int m0, float *inv) const { prepare(m0, 64, inv); }
   __device__ __forceinline__ St load(const RowInfo &ri, int c) const {
     St st;
 #pragma unroll
@@ -208,11 +312,48 @@ template <typename T, typename W = T> struct EpiSwiglu {
   __device__ __forceinline__ void prepare(int m0, int rows, float *inv) const {
     rms_prepare(a.in, a.M, a.eps, m0, rows, inv, Q ? a.a_scale : nullptr);
   }
+  typedef RmsPre Pre;
+  __device__ __forceinline__ Pre pre_load(int m0) const { return rms_load(a.in, a.M, m0); }
+  __device__ __forceinline__ void pre_finish(const Pre &p, int m0, float *inv) const {
+    rms_finish(p, a.in, a.M, a.eps, m0, inv, Q ? a.a_scale : nullptr);
+  }
   __device__ __forceinline__ St load(const RowInfo &, int c) const {
     St st;
     st.s = 1.0f;
     if constexpr (Q) st.s = ((c >> 3) & 1 ? a.s_up : a.s_gate)[(c >> 4) * 8 + (c & 7)];
     return st;
+  }
+  // Large tiles: the 256 columns of a tile are 128 activation columns; to_lds stages them per
+  // row, lds_out writes each row's 128 values as whole 16-byte vectors.
+  static constexpr bool kTile = true;
+  __device__ __forceinline__ bool tile_ok(int) const { return true; }
+  template <int LD>
+  __device__ __forceinline__ void to_lds(const St &st, int row0, int c, f32x4 acc, const float *inv, int m0, int n0,
+                                         T *ot) const {
+    const int fl = ((c - n0) >> 4) * 8 + (c & 7);
+    const int up = (c >> 3) & 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float g = acc[r] * inv[row0 + r - m0] * st.s;
+      const float u = lane_xor8(g);
+      if (!up) ot[(row0 + r - m0) * LD + fl] = from_f32<T>(silu(g) * u);
+    }
+  }
+  template <int LD, int BM, int BN>
+  __device__ __forceinline__ void lds_out(const T *ot, int m0, int n0, int M) const {
+    constexpr int CPR = BN / 16;  // 16-byte chunks of activation per row
+    const RowMap &rm = a.rows;
+#pragma unroll 4
+    for (int idx = threadIdx.x; idx < BM * CPR; idx += 256) {
+      const int rl = idx / CPR, ch = idx - rl * CPR, row = m0 + rl;
+      if (row >= M) continue;
+      if (rm.is_prefix) {
+        const int b = row / rm.rows_per_b, s = row - b * rm.rows_per_b;
+        if (s >= max(0, min(rm.lens[b], rm.cap))) continue;
+      }
+      *reinterpret_cast<i32x4 *>((T *)a.act + (size_t)row * a.F + (n0 >> 1) + ch * 8) =
+          *reinterpret_cast<const i32x4 *>(&ot[rl * LD + ch * 8]);
+    }
   }
   __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
                                         int m0) const {
@@ -254,6 +395,14 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
 #pragma unroll
   for (int i = 0; i < 4; ++i) ap[i] = A + (size_t)min(m0 + i * 16 + c16, M - 1) * K + k0 + g * EPL;
 
+  // The small loads go first (norm statistics, row facts, RoPE / residual rows): loads complete
+  // in issue order, so their consumers run while the operand loads below are still in flight.
+  const typename Epi::Pre pre = epi.pre_load(m0);
+  const RowInfo ri = row_info(epi.rows(), m0 + wave * 16 + 4 * g, M);
+  typename Epi::St st[CT];
+#pragma unroll
+  for (int j = 0; j < CT; ++j) st[j] = epi.load(ri, n0 + j * 16 + c16);
+
   frag wf[NK][CT], af[NK][4];
 #pragma unroll
   for (int u = 0; u < NK; ++u)
@@ -267,12 +416,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) af[u][i] = load_frag<T>(ap[i] + u * KC);
 
-  epi.prepare(m0, 64, rinv);
-  // the epilogue's own loads (row lengths, RoPE table, residual rows) go out with the operands
-  const RowInfo ri = row_info(epi.rows(), m0 + wave * 16 + 4 * g, M);
-  typename Epi::St st[CT];
-#pragma unroll
-  for (int j = 0; j < CT; ++j) st[j] = epi.load(ri, n0 + j * 16 + c16);
+  epi.pre_finish(pre, m0, rinv);
 
   f32x4 acc[4][CT];
 #pragma unroll
@@ -337,9 +481,11 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
     pv[sp] = *reinterpret_cast<const float4 *>(part + ((size_t)min(sp, ks - 1) * a.M + row) * H + c);
   float4 hv = *reinterpret_cast<const float4 *>(a.out.h + (size_t)row * H + c);
   float4 gv = a.next_gain ? *reinterpret_cast<const float4 *>(a.next_gain + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-  const int b = row / a.rows.rows_per_b, s = row - b * a.rows.rows_per_b;
-  const int plen = max(0, min(a.rows.lens[b], a.rows.cap));
-  const bool ok = in_range && (a.rows.is_prefix ? s < plen : true);
+  bool ok = in_range;
+  if (a.rows.is_prefix) {  // uniform: action rows need no prefix length
+    const int b = row / a.rows.rows_per_b, s = row - b * a.rows.rows_per_b;
+    ok = ok && s < max(0, min(a.rows.lens[b], a.rows.cap));
+  }
   float4 t = pv[0];
 #pragma unroll
   for (int sp = 1; sp < 16; ++sp)
@@ -366,57 +512,100 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
 // ------------------------------------------------------------------------ big kernel (M > 64)
 // Workgroup tile 128 x BN (BN = 256 or 128); four waves as 2 x 2, each 64 x BN/2, i.e. 4 x BN/32
 // MFMA 16x16 tiles, so every LDS fragment read feeds several MFMAs.  Each k-step moves 128 bytes
-// of every row (64 bf16 or 128 FP8 codes) through two LDS buffers: the next k-step is loaded into
-// registers while the current one is multiplied, then stored to the other buffer, one barrier per
-// k-step.  Rows are padded to 144 bytes, which spreads the 16 rows of a fragment read over all
-// LDS banks.  grid.z splits K (the narrow residual projections), each split writing fp32 partial
-// sums for resid_reduce_kernel.  Op: bf16 (two 16x16x32 MFMAs per k-step) or fp8 (one
-// 16x16x128 MFMA per k-step).
+// of every row (64 bf16 or 128 FP8 codes).  Operands go from global memory straight into LDS
+// (global_load_lds_dwordx4: no registers, whole 128-byte lines per row), three k-steps in flight:
+// while step k is multiplied, steps k+1 and k+2 are loading.  An LDS row holds its eight 16-byte
+// chunks in XOR-swizzled order (chunk c at position c ^ (row & 7)), so the 16 rows of a fragment
+// read spread over all banks.  grid.z splits K (the narrow residual projections), each split
+// writing fp32 partial sums for resid_reduce_kernel.  Workgroups are numbered so that the tiles
+// sharing an operand column run on the same XCD (blocks go to the 8 XCDs round-robin) and meet in
+// its L2.  Op: bf16 (two 16x16x32 MFMAs per k-step) or fp8 (one 16x16x128 MFMA per k-step).
+constexpr int BIG_NBUF = 3;
+
+__device__ __forceinline__ void vm_wait_12() { __builtin_amdgcn_s_waitcnt((12 & 15) | ((12 >> 4) << 14) | (7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void vm_wait_24() { __builtin_amdgcn_s_waitcnt((24 & 15) | ((24 >> 4) << 14) | (7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void vm_wait_8() { __builtin_amdgcn_s_waitcnt((8 & 15) | ((8 >> 4) << 14) | (7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void vm_wait_16() { __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void vm_wait_0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+// 16-byte LDS reads of NA rows at a + i*2048 and NB rows at b + j*2048 (rows 16 apart at 128 bytes)
+// in one asm block that also waits for them.  Written as asm because the compiler otherwise
+// makes every LDS read wait for all outstanding global->LDS loads, including the prefetches of
+// later k-steps into other buffers; the waits those need are explicit in the loop.
+template <int NA, int NB>
+__device__ __forceinline__ void lds_read_tile(i32x4 (&fa)[NA], i32x4 (&fb)[NB], unsigned a, unsigned b);
+template <>
+__device__ __forceinline__ void lds_read_tile<4, 8>(i32x4 (&fa)[4], i32x4 (&fb)[8], unsigned a, unsigned b) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\t"
+      "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %3, %12 offset:6144\n\t"
+      "ds_read_b128 %4, %13\n\tds_read_b128 %5, %13 offset:2048\n\t"
+      "ds_read_b128 %6, %13 offset:4096\n\tds_read_b128 %7, %13 offset:6144\n\t"
+      "ds_read_b128 %8, %13 offset:8192\n\tds_read_b128 %9, %13 offset:10240\n\t"
+      "ds_read_b128 %10, %13 offset:12288\n\tds_read_b128 %11, %13 offset:14336\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]),
+        "=&v"(fb[3]), "=&v"(fb[4]), "=&v"(fb[5]), "=&v"(fb[6]), "=&v"(fb[7])
+      : "v"(a), "v"(b));
+}
+template <>
+__device__ __forceinline__ void lds_read_tile<4, 4>(i32x4 (&fa)[4], i32x4 (&fb)[4], unsigned a, unsigned b) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:2048\n\t"
+      "ds_read_b128 %2, %8 offset:4096\n\tds_read_b128 %3, %8 offset:6144\n\t"
+      "ds_read_b128 %4, %9\n\tds_read_b128 %5, %9 offset:2048\n\t"
+      "ds_read_b128 %6, %9 offset:4096\n\tds_read_b128 %7, %9 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]),
+        "=&v"(fb[3])
+      : "v"(a), "v"(b));
+}
+
 template <typename Op, int BN, class Epi>
-__global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int M, int K, Epi epi, SplitK sk) {
+__global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int M, int K, Epi epi, SplitK sk, int n_tiles,
+                                                  int m_tiles) {
   constexpr int EB = sizeof(Op);       // bytes per element
-  constexpr int BM = 128, RB = 128, LDB = RB + 16;
+  constexpr int BM = 128, RB = 128;    // rows of A per tile, bytes per row per k-step
   constexpr int BK = RB / EB, VE = 16 / EB;
   constexpr int TN = BN / 32;
-  constexpr int AV = BM * 8 / 256, WV = BN * 8 / 256;
-  __shared__ __attribute__((aligned(16))) char As[2][BM * LDB];
-  __shared__ __attribute__((aligned(16))) char Ws[2][BN * LDB];
+  constexpr int ROWS = BM + BN;                 // LDS rows per stage (A then W)
+  constexpr int LPW = ROWS * RB / 1024 / 4;     // 1 KB DMA instructions per wave per stage
+  constexpr int STAGE = ROWS * RB;
+  static_assert(LPW == 8 || LPW == 12, "stage of 8 or 12 DMA instructions per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[BIG_NBUF * STAGE];
   __shared__ float rinv[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM, split = blockIdx.z;
+  // XCD-aware tile order: the blocks on one XCD (b % 8) take a contiguous run of (split, n, m)
+  const int T = n_tiles * m_tiles * (int)gridDim.z;
+  const int b = blockIdx.x + (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x;
+  const int xcd = b & 7, per = T >> 3, rem = T & 7;
+  const int t = xcd * per + min(xcd, rem) + (b >> 3);
+  const int m_t = t % m_tiles, nsplit = t / m_tiles, n_t = nsplit % n_tiles, split = nsplit / n_tiles;
+  const int n0 = n_t * BN, m0 = m_t * BM;
   const int Ks = K / sk.k_split, kb = split * Ks, nkt = Ks / BK;
 
-  const Op *asrc[AV];
-  int adst[AV];
+  // DMA sources: instruction i of this wave fills LDS rows 8*(wave*LPW + i) .. +7 of the stage;
+  // lane (row r = l/8, position p = l%8) fetches chunk p ^ (r & 7) of its row
+  const Op *src[LPW];
 #pragma unroll
-  for (int v = 0; v < AV; ++v) {
-    const int idx = tid + v * 256, r = idx >> 3, cv = idx & 7;
-    asrc[v] = A + (size_t)min(m0 + r, M - 1) * K + kb + cv * VE;  // rows past M: never stored
-    adst[v] = r * LDB + cv * 16;
+  for (int i = 0; i < LPW; ++i) {
+    const int r = (wave * LPW + i) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (r & 7);
+    const Op *row = r < BM ? A + (size_t)min(m0 + r, M - 1) * K : epi.wrow(n0 + r - BM);  // rows past M: never stored
+    src[i] = row + kb + chunk * VE;
   }
-  const Op *wsrc[WV];
-  int wdst[WV];
+  auto dma = [&](int kt) {
+    char *dst = smem + (kt % BIG_NBUF) * STAGE + wave * LPW * 1024;
 #pragma unroll
-  for (int v = 0; v < WV; ++v) {
-    const int idx = tid + v * 256, r = idx >> 3, cv = idx & 7;
-    wsrc[v] = epi.wrow(n0 + r) + kb + cv * VE;
-    wdst[v] = r * LDB + cv * 16;
-  }
-  i32x4 ra[AV], rw[WV];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int v = 0; v < AV; ++v) ra[v] = *reinterpret_cast<const i32x4 *>(asrc[v] + kt * BK);
-#pragma unroll
-    for (int v = 0; v < WV; ++v) rw[v] = *reinterpret_cast<const i32x4 *>(wsrc[v] + kt * BK);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int v = 0; v < AV; ++v) *reinterpret_cast<i32x4 *>(&As[buf][adst[v]]) = ra[v];
-#pragma unroll
-    for (int v = 0; v < WV; ++v) *reinterpret_cast<i32x4 *>(&Ws[buf][wdst[v]]) = rw[v];
+    for (int i = 0; i < LPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void *)(src[i] + kt * BK),
+                                       (__attribute__((address_space(3))) void *)(dst + i * 1024), 16, 0, 0);
   };
 
   f32x4 acc[4][TN];
@@ -425,53 +614,52 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  epi.prepare(m0, BM, rinv);
-  lstore(0);
-  __syncthreads();
+  dma(0);
+  if (nkt > 1) dma(1);
+  epi.prepare(m0, BM, rinv);  // its loads queue behind the first two stages
+  // fragment rows of this wave: A rows wm*64 + i*16 + c16, W rows BM + wn*BN/2 + j*16 + c16;
+  // (row & 7) == (c16 & 7) for all of them
+  const int sw = c16 & 7;
+  const int arow = (wm * 64 + c16) * RB, wrow = (BM + wn * (BN / 2) + c16) * RB;
   for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-    const char *ab = &As[cur][(wm * 64 + c16) * LDB];
-    const char *wb = &Ws[cur][(wn * (BN / 2) + c16) * LDB];
+    // this wave's DMAs for step kt are done once at most the next step's are outstanding
+    if (kt + 1 < nkt) {
+      if constexpr (LPW == 12) vm_wait_12(); else vm_wait_8();
+    } else {
+      vm_wait_0();
+    }
+    __builtin_amdgcn_s_barrier();  // every wave's step kt has landed; step kt-1 is fully read
+    if (kt + 2 < nkt) dma(kt + 2);
+    const unsigned st = lds_addr(smem) + (kt % BIG_NBUF) * STAGE;
     if constexpr (EB == 2) {
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        bf16x8 fa[4], fb[TN];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(ab + i * 16 * LDB + kc * 64 + g * 16);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const bf16x8 *>(wb + j * 16 * LDB + kc * 64 + g * 16);
+        const int pos = ((kc * 4 + g) ^ sw) * 16;
+        i32x4 fa[4], fb[TN];
+        lds_read_tile<4, TN>(fa, fb, st + arow + pos, st + wrow + pos);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<bf16>::mma(fa[i], fb[j], acc[i][j]);
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = Mfma<bf16>::mma(__builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]), acc[i][j]);
       }
     } else {
-      i32x8 fa[4], fb[TN];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const i32x4 lo = *reinterpret_cast<const i32x4 *>(ab + i * 16 * LDB + g * 32);
-        const i32x4 hi = *reinterpret_cast<const i32x4 *>(ab + i * 16 * LDB + g * 32 + 16);
-        fa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const i32x4 lo = *reinterpret_cast<const i32x4 *>(wb + j * 16 * LDB + g * 32);
-        const i32x4 hi = *reinterpret_cast<const i32x4 *>(wb + j * 16 * LDB + g * 32 + 16);
-        fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      const int p0 = ((2 * g) ^ sw) * 16, p1 = ((2 * g + 1) ^ sw) * 16;
+      i32x4 lo[4], hi[4], wlo[TN], whi[TN];
+      lds_read_tile<4, TN>(lo, wlo, st + arow + p0, st + wrow + p0);
+      lds_read_tile<4, TN>(hi, whi, st + arow + p1, st + wrow + p1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = Mfma8::mma(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = Mfma8::mma(__builtin_shufflevector(lo[i], hi[i], 0, 1, 2, 3, 4, 5, 6, 7),
+                                 __builtin_shufflevector(wlo[j], whi[j], 0, 1, 2, 3, 4, 5, 6, 7), acc[i][j]);
     }
-    if (kt + 1 < nkt) lstore(cur ^ 1);
-    __syncthreads();
   }
+  __syncthreads();  // rinv (written by epi.prepare) visible to every wave
 
   if (sk.k_split > 1) {  // partial sums [split][M][N], row-major; resid_reduce_kernel finishes
-    const int N = gridDim.x * BN;
+    const int N = n_tiles * BN;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -482,6 +670,27 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
           if (row < M) sk.part[((size_t)split * M + row) * N + n0 + wn * (BN / 2) + j * 16 + c16] = acc[i][j][r];
         }
     return;
+  }
+  if constexpr (Epi::kTile && EB == 2) {
+    if (epi.tile_ok(BN)) {  // uniform
+    // stage the finished tile in LDS (the k-step buffers are free now), then store whole rows
+    constexpr int LD = BN + 8;
+    bf16 *ot = reinterpret_cast<bf16 *>(smem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row0 = m0 + wm * 64 + i * 16 + 4 * g;
+      const RowInfo ri = row_info(epi.rows(), row0, M);
+      typename Epi::St st[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) st[j] = epi.load(ri, n0 + wn * (BN / 2) + j * 16 + c16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        epi.template to_lds<LD>(st[j], row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], rinv, m0, n0, ot);
+    }
+    __syncthreads();
+    epi.template lds_out<LD, BM, BN>(ot, m0, n0, M);
+    return;
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -494,6 +703,16 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
 #pragma unroll
     for (int j = 0; j < TN; ++j) epi.store(st[j], ri, row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], rinv, m0);
   }
+}
+
+template <typename Op, class Epi>
+static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, const SplitK &sk, hipStream_t s) {
+  const int nN = N / nt, nM = (M + 127) / 128;
+  dim3 grid(nN, nM, sk.k_split);
+  if (nt == 256)
+    hipLaunchKernelGGL((big_kernel<Op, 256, Epi>), grid, dim3(256), 0, s, A, M, K, epi, sk, nN, nM);
+  else
+    hipLaunchKernelGGL((big_kernel<Op, 128, Epi>), grid, dim3(256), 0, s, A, M, K, epi, sk, nN, nM);
 }
 
 // ------------------------------------------------------------------------ tiled kernel (any M)
@@ -613,11 +832,7 @@ static void run_gemm(const T *A, int M, int N, int K, const Epi &epi, const Gemm
     }
   } else if (p.nt >= 128) {
     if constexpr (std::is_same<T, bf16>::value) {
-      dim3 grid(N / p.nt, (M + 127) / 128, p.sk.k_split);
-      if (p.nt == 256)
-        hipLaunchKernelGGL((big_kernel<bf16, 256, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk);
-      else
-        hipLaunchKernelGGL((big_kernel<bf16, 128, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk);
+      run_big<bf16>(A, M, N, K, epi, p.nt, p.sk, s);
     }
   } else {
     dim3 grid(N / 64, (M + 63) / 64);
@@ -642,10 +857,7 @@ template <typename T> static void swiglu_t(const SwigluArgs &a, const GemmPlan &
 // FP8: one launch of the large-tile kernel, 256 columns per workgroup when N allows it.
 template <class Epi> static void run_fp8(const fp8 *A, int M, int N, int K, const Epi &epi, hipStream_t s) {
   const SplitK none{1, nullptr};
-  if (N % 256 == 0)
-    hipLaunchKernelGGL((big_kernel<fp8, 256, Epi>), dim3(N / 256, (M + 127) / 128), dim3(256), 0, s, A, M, K, epi, none);
-  else
-    hipLaunchKernelGGL((big_kernel<fp8, 128, Epi>), dim3(N / 128, (M + 127) / 128), dim3(256), 0, s, A, M, K, epi, none);
+  run_big<fp8>(A, M, N, K, epi, N % 256 == 0 ? 256 : 128, none, s);
 }
 void launch_resid_fp8(const ResidArgs &a, hipStream_t s) {
   run_fp8((const fp8 *)a.a, a.M, a.out.H, a.K, EpiResid<bf16, fp8>{a}, s);

@@ -45,6 +45,7 @@ struct QkvArgs {
   RowMap rows;
   const float2 *rope;            // [positions][D/2] (cos, sin)
   int Hq, Hkv, D;
+  const float2 *rope_rows = nullptr;  // action rows: [M][D/2] (cos, sin) at position P_b + s
 };
 // out.h += A W^T, then out.hg = (h * next_gain) and out.ssq for the next sublayer
 // (next_gain NULL: skip them).  Rows outside RowMap untouched.
@@ -102,6 +103,9 @@ int attn_qblocks(int q_rows, int Hq, int Hkv);
 void launch_attention(Dt dt, const AttnArgs &a, hipStream_t s);
 
 void launch_rope_table(float2 *table, int n_pos, int D, float base, hipStream_t s);
+// out[b*S + s][i] = table[min(max(lens[b], 0), cap) + s][i]: the RoPE rows of the action tokens.
+void launch_rope_rows(const float2 *table, const int32_t *lens, int cap, int B, int S, int D, float2 *out,
+                      hipStream_t s);
 void launch_zero_u32(unsigned *p, size_t n, hipStream_t s);
 // h = src (if src != h), hg = h * gain, ssq per 16 columns: the entry into the first sublayer.
 void launch_norm_prep(Dt dt, const float *src, const Hidden &hid, const float *gain, int M, hipStream_t s);

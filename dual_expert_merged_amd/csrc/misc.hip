@@ -26,6 +26,20 @@ void launch_rope_table(float2 *table, int n_pos, int D, float base, hipStream_t 
                      (double)base);
 }
 
+__global__ void rope_rows_kernel(const float2 *__restrict__ table, const int32_t *__restrict__ lens, int cap, int S,
+                                 int half, int n, float2 *__restrict__ out) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int i = idx % half, row = idx / half, b = row / S, s = row - b * S;
+  const int pos = max(0, min(lens[b], cap)) + s;
+  out[idx] = table[(size_t)pos * half + i];
+}
+void launch_rope_rows(const float2 *table, const int32_t *lens, int cap, int B, int S, int D, float2 *out,
+                      hipStream_t s) {
+  const int n = B * S * (D / 2);
+  hipLaunchKernelGGL(rope_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, table, lens, cap, S, D / 2, n, out);
+}
+
 __global__ void zero_u32_kernel(unsigned *p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
 }
