@@ -8,7 +8,12 @@ action_out_proj + Euler update) for the batch.  Inputs are resident in HBM befor
 Prints one JSON line: chunks/s (whole job), p50/p90/p99 chunk latency, the roofline of the
 dominant kernel, and the float64 oracle timed on the host cores as a CPU baseline.
 
-  python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config 3|4] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config 3|4] [--no-cpu-baseline] [--prefill]
+
+The roofline unit is one launch of the captured graph (one chunk): achieved = algorithmic bytes
+of the chunk / its mean duration (HIP events on the stream the graph is launched on); traffic =
+HBM bytes of the same chunk from rocprofv3 FETCH_SIZE + WRITE_SIZE counters, scaled against a
+plain copy (profiles/*_hbm_traffic.txt, reported only while the kernel sources are unchanged).
 """
 import argparse
 import json
@@ -67,6 +72,110 @@ def cpu_baseline(wl, aw, kc, vc, x1, lens):
                       f"P={P}) in float64 numpy; {dt:.2f} s on {cores} host cores"}
 
 
+SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip", "common.h", "kernels.h"]
+
+
+def source_hash():
+    """Hash of the kernel sources: HBM traffic measured with counters is only reported while the
+    kernels it was measured on are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in SOURCES:
+        with open(os.path.join(ROOT, "dual_expert_merged_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(config):
+    return os.path.join(ROOT, "profiles", f"denoise_{'b1_p816' if config == 3 else 'b32_ragged'}_hbm_traffic.txt")
+
+
+def read_traffic(config):
+    """HBM bytes per chunk from the committed counter summary, or None when the kernels changed."""
+    path = traffic_file(config)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash():
+        return None
+    return int(float(vals["hbm_bytes_per_chunk"]))
+
+
+def _pmc_sum(run_dir, counter, match):
+    """Sum of one counter over the dispatches whose kernel name contains `match`, and the number
+    of dispatches, from a rocprofv3 --pmc csv run directory."""
+    import csv
+    import glob
+    total, n = 0.0, 0
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and match(r["Kernel_Name"]):
+                    total += float(r["Counter_Value"])
+                    n += 1
+    return total, n
+
+
+def traffic_summary(args):
+    """Writes the HBM-traffic summary of one denoise chunk from four rocprofv3 --pmc runs: the
+    bench with FETCH_SIZE, with WRITE_SIZE, and the copy calibration with each.  FETCH_SIZE and
+    WRITE_SIZE count KiB per dispatch; both are scaled by bytes-moved / counted for a plain copy
+    of known size."""
+    lib = lambda name: "dm::" in name or "_ZN2dm" in name
+    copy = lambda name: "copybuffer" in name.lower()  # the device-to-device copies, not the fill before them
+    cal_bytes = COPY_BYTES * COPY_REPS
+    cf, _ = _pmc_sum(args.cal_fetch, "FETCH_SIZE", copy)
+    cw, _ = _pmc_sum(args.cal_write, "WRITE_SIZE", copy)
+    f_scale, w_scale = cal_bytes / (cf * 1024.0), cal_bytes / (cw * 1024.0)
+    fetch, _ = _pmc_sum(args.fetch, "FETCH_SIZE", lib)
+    write, _ = _pmc_sum(args.write, "WRITE_SIZE", lib)
+    _, n_vel = _pmc_sum(args.fetch, "FETCH_SIZE", lambda n: "velocity_euler" in n)
+    from dual_expert_merged_amd.configs import workload
+    wl = workload(args.config)
+    chunks = n_vel / wl.steps
+    per_chunk = (fetch * 1024.0 * f_scale + write * 1024.0 * w_scale) / chunks
+    with open(traffic_file(args.config), "w") as f:
+        f.write(f"# HBM traffic of one denoise chunk ({wl.name}), rocprofv3 counters\n")
+        f.write("# commands (run from the repository root on the GPU box, each pass its own run):\n")
+        f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -- python3 bench.py "
+                f"--config {args.config} --steps 2 --warmup 0 --no-cpu-baseline\n")
+        f.write("#   rocprofv3 --pmc WRITE_SIZE ... (same)\n")
+        f.write("#   rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE --output-format csv -d <cal> -- python3 bench.py --copy-calibration\n")
+        f.write(f"#   python3 bench.py --traffic-summary --config {args.config} --fetch <fetch> --write <write> "
+                "--cal-fetch <cal-fetch> --cal-write <cal-write>\n")
+        f.write(f"chunks_profiled: {chunks:g}\n")
+        f.write(f"copy_calibration_bytes: {cal_bytes}\n")
+        f.write(f"fetch_scale: {f_scale:.4f}\n")
+        f.write(f"write_scale: {w_scale:.4f}\n")
+        f.write(f"fetch_bytes_per_chunk: {fetch * 1024.0 * f_scale / chunks:.0f}\n")
+        f.write(f"write_bytes_per_chunk: {write * 1024.0 * w_scale / chunks:.0f}\n")
+        f.write(f"hbm_bytes_per_chunk: {per_chunk:.0f}\n")
+        f.write(f"source_hash: {source_hash()}\n")
+    print(open(traffic_file(args.config)).read())
+
+
+COPY_BYTES = 1 << 30
+COPY_REPS = 4
+
+
+def copy_calibration():
+    """A plain device copy of known size (COPY_REPS x 1 GiB, hipMemcpy device to device) for scaling
+    the traffic counters."""
+    import torch
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(COPY_REPS):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {COPY_REPS} x {COPY_BYTES} bytes")
+
+
 def prefill_times(reps=3):
     """Prefix encoding of the prefill workload (B=8, 816 tokens, 28 VLM layers) with the bf16
     MLP and with the FP8 E4M3 MLP: mean ms per call over `reps` calls after one warm-up."""
@@ -118,7 +227,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", action="store_true",
                     help="also time the prefix encoding (B=8, 816 tokens) with the bf16 and the FP8 MLP")
+    ap.add_argument("--copy-calibration", action="store_true", help="run only the plain copy for counter scaling")
+    ap.add_argument("--traffic-summary", action="store_true", help="summarise counter runs (no GPU needed)")
+    for name in ("fetch", "write", "cal-fetch", "cal-write"):
+        ap.add_argument("--" + name)
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the suffix denoise path is built for a single MI355X "
               f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
@@ -173,7 +292,7 @@ def main():
     achieved = alg["bytes"] / chunk_s / 1e9
     roof = {"bound": "hbm", "kernel": "denoise graph replay (all kernels of one chunk)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(args.config),
             "algorithmic_bytes_per_launch": alg["bytes"],
             "mfma_frac": round(alg["flops"] / chunk_s / 1e12 / BF16_PEAK_TFLOPS, 4)}
     out = {
