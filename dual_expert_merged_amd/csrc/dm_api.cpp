@@ -117,6 +117,12 @@ GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
     if (dt != DT_BF16 || N % 128 != 0 || K % 64 != 0) return p;
     const int mt = (M + 127) / 128;
     p.nt = (N % 256 == 0 && (N / 256) * mt >= 128) ? 256 : 128;
+    if (!split_ok && p.nt == 256 && N % 384 == 0) {
+      // one workgroup per CU: compare whole rounds of 256 workgroups, a 384-wide tile costing
+      // about 1.5 times a 256-wide one
+      const int r256 = ((N / 256) * mt + 255) / 256, r384 = ((N / 384) * mt + 255) / 256;
+      if (2 * r384 * 3 < 2 * r256 * 2) p.nt = 384;
+    }
     if (split_ok)
       while ((N / p.nt) * mt * p.sk.k_split < 200 && p.sk.k_split < 8 && K % (2 * p.sk.k_split * 64) == 0 &&
              K / (2 * p.sk.k_split) >= 256)

@@ -180,9 +180,9 @@ template <typename T> struct EpiQkv {
   static constexpr bool kTile = true;
   // every tile must lie inside one section: q, k and v widths are multiples of the tile width
   __device__ __forceinline__ bool tile_ok(int bn) const { return (a.Hq * a.D) % bn == 0 && (a.Hkv * a.D) % bn == 0; }
-  template <int LD>
+  template <class Tile>
   __device__ __forceinline__ void to_lds(const St &st, int row0, int c, f32x4 acc, const float *inv, int m0, int n0,
-                                         T *ot) const {
+                                         const Tile &ot) const {
     const int gc = col(c), gc0 = col(n0);
     const int D = a.D;
     const int local = gc - gc0;  // (head - first head) * D + d
@@ -193,11 +193,11 @@ template <typename T> struct EpiQkv {
       float u = acc[r] * inv[row0 + r - m0];
       const float pu = lane_xor8(u);
       if (rot) u = upper ? (u * st.cs[r].x + pu * st.cs[r].y) : (u * st.cs[r].x - pu * st.cs[r].y);
-      ot[(row0 + r - m0) * LD + local] = from_f32<T>(u);
+      ot.row(row0 + r - m0)[local] = from_f32<T>(u);
     }
   }
-  template <int LD, int BM, int BN>
-  __device__ __forceinline__ void lds_out(const T *ot, int m0, int n0, int M) const {
+  template <int BM, int BN, class Tile>
+  __device__ __forceinline__ void lds_out(const Tile &ot, int m0, int n0, int M) const {
     constexpr int CPR = BN / 8;  // 16-byte chunks per row
     const int D = a.D, qd = a.Hq * D, kd = a.Hkv * D;
     const int gc0 = col(n0);
@@ -210,7 +210,7 @@ template <typename T> struct EpiQkv {
       if (row >= M) continue;
       const int b = row / rm.rows_per_b, s = row - b * rm.rows_per_b;
       if (rm.is_prefix && s >= max(0, min(rm.lens[b], rm.cap))) continue;
-      const i32x4 v = *reinterpret_cast<const i32x4 *>(&ot[rl * LD + ch * 8]);
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(ot.row(rl) + ch * 8);
       T *dst;
       if (sec == 0) {
         dst = (T *)a.q + (size_t)row * qd + gc0 + ch * 8;
@@ -262,10 +262,10 @@ template <typename T, typename W = T> struct EpiResid {
   }
   static constexpr bool kTile = false;
   __device__ __forceinline__ bool tile_ok(int) const { return false; }
-  template <int LD>
-  __device__ __forceinline__ void to_lds(const St &, int, int, f32x4, const float *, int, int, T *) const {}
-  template <int LD, int BM, int BN>
-  __device__ __forceinline__ void lds_out(const T *, int, int, int) const {}
+  template <class Tile>
+  __device__ __forceinline__ void to_lds(const St &, int, int, f32x4, const float *, int, int, const Tile &) const {}
+  template <int BM, int BN, class Tile>
+  __device__ __forceinline__ void lds_out(const Tile &, int, int, int) const {}
   struct Pre {};
   __device__ __forceinline__ Pre pre_load(int) const { return Pre{}; }
   __device__ __forceinline__ void pre_finish(const Pre &, int m0, float *inv) const { prepare(m0, 64, inv); }
@@ -327,20 +327,20 @@ template <typename T, typename W = T> struct EpiSwiglu {
   // row, lds_out writes each row's 128 values as whole 16-byte vectors.
   static constexpr bool kTile = true;
   __device__ __forceinline__ bool tile_ok(int) const { return true; }
-  template <int LD>
+  template <class Tile>
   __device__ __forceinline__ void to_lds(const St &st, int row0, int c, f32x4 acc, const float *inv, int m0, int n0,
-                                         T *ot) const {
+                                         const Tile &ot) const {
     const int fl = ((c - n0) >> 4) * 8 + (c & 7);
     const int up = (c >> 3) & 1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float g = acc[r] * inv[row0 + r - m0] * st.s;
       const float u = lane_xor8(g);
-      if (!up) ot[(row0 + r - m0) * LD + fl] = from_f32<T>(silu(g) * u);
+      if (!up) ot.row(row0 + r - m0)[fl] = from_f32<T>(silu(g) * u);
     }
   }
-  template <int LD, int BM, int BN>
-  __device__ __forceinline__ void lds_out(const T *ot, int m0, int n0, int M) const {
+  template <int BM, int BN, class Tile>
+  __device__ __forceinline__ void lds_out(const Tile &ot, int m0, int n0, int M) const {
     constexpr int CPR = BN / 16;  // 16-byte chunks of activation per row
     const RowMap &rm = a.rows;
 #pragma unroll 4
@@ -352,7 +352,7 @@ template <typename T, typename W = T> struct EpiSwiglu {
         if (s >= max(0, min(rm.lens[b], rm.cap))) continue;
       }
       *reinterpret_cast<i32x4 *>((T *)a.act + (size_t)row * a.F + (n0 >> 1) + ch * 8) =
-          *reinterpret_cast<const i32x4 *>(&ot[rl * LD + ch * 8]);
+          *reinterpret_cast<const i32x4 *>(ot.row(rl) + ch * 8);
     }
   }
   __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
@@ -514,57 +514,52 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
 // MFMA 16x16 tiles, so every LDS fragment read feeds several MFMAs.  Each k-step moves 128 bytes
 // of every row (64 bf16 or 128 FP8 codes).  Operands go from global memory straight into LDS
 // (global_load_lds_dwordx4: no registers, whole 128-byte lines per row), three k-steps in flight:
-// while step k is multiplied, steps k+1 and k+2 are loading.  An LDS row holds its eight 16-byte
-// chunks in XOR-swizzled order (chunk c at position c ^ (row & 7)), so the 16 rows of a fragment
-// read spread over all banks.  grid.z splits K (the narrow residual projections), each split
-// writing fp32 partial sums for resid_reduce_kernel.  Workgroups are numbered so that the tiles
-// sharing an operand column run on the same XCD (blocks go to the 8 XCDs round-robin) and meet in
-// its L2.  Op: bf16 (two 16x16x32 MFMAs per k-step) or fp8 (one 16x16x128 MFMA per k-step).
-constexpr int BIG_NBUF = 3;
+// while step k is multiplied, steps k+1 and k+2 are loading.  The three stage buffers are
+// distinct LDS arrays and the k-loop is unrolled by three, so the compiler can tell that reading
+// one buffer does not wait for the loads into another, and it interleaves the fragment reads with
+// the MFMAs.  An LDS row holds its eight 16-byte chunks in XOR-swizzled order (chunk c at
+// position c ^ (row & 7)), so the 16 rows of a fragment read spread over all banks.  grid.z
+// splits K (the narrow residual projections), each split writing fp32 partial sums for
+// resid_reduce_kernel.  Workgroups are numbered so that the tiles sharing an operand column run
+// on the same XCD (blocks go to the 8 XCDs round-robin) and meet in its L2.  Op: bf16 (two
+// 16x16x32 MFMAs per k-step) or fp8 (one 16x16x128 MFMA per k-step).
+// Workgroup barrier without a global-memory fence (a fence would wait for every outstanding
+// load, prefetches included).  It waits for this wave's LDS reads first, so no wave can start a
+// copy into a buffer another wave is still reading; the memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ void vm_wait_12() { __builtin_amdgcn_s_waitcnt((12 & 15) | ((12 >> 4) << 14) | (7 << 4) | (15 << 8)); }
-__device__ __forceinline__ void vm_wait_24() { __builtin_amdgcn_s_waitcnt((24 & 15) | ((24 >> 4) << 14) | (7 << 4) | (15 << 8)); }
-__device__ __forceinline__ void vm_wait_8() { __builtin_amdgcn_s_waitcnt((8 & 15) | ((8 >> 4) << 14) | (7 << 4) | (15 << 8)); }
-__device__ __forceinline__ void vm_wait_16() { __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8)); }
-__device__ __forceinline__ void vm_wait_0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// The finished tile staged in LDS before the coalesced stores: rows 0..63 in one stage buffer,
+// 64..127 in another, LD elements per row.
+template <typename T, int LD> struct TileRows {
+  T *lo, *hi;
+  __device__ __forceinline__ T *row(int r) const { return (r < 64 ? lo : hi) + (r & 63) * LD; }
+};
 
 __device__ __forceinline__ unsigned lds_addr(const void *p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
-// 16-byte LDS reads of NA rows at a + i*2048 and NB rows at b + j*2048 (rows 16 apart at 128 bytes)
-// in one asm block that also waits for them.  Written as asm because the compiler otherwise
-// makes every LDS read wait for all outstanding global->LDS loads, including the prefetches of
-// later k-steps into other buffers; the waits those need are explicit in the loop.
-template <int NA, int NB>
-__device__ __forceinline__ void lds_read_tile(i32x4 (&fa)[NA], i32x4 (&fb)[NB], unsigned a, unsigned b);
-template <>
-__device__ __forceinline__ void lds_read_tile<4, 8>(i32x4 (&fa)[4], i32x4 (&fb)[8], unsigned a, unsigned b) {
-  asm volatile(
-      "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\t"
-      "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %3, %12 offset:6144\n\t"
-      "ds_read_b128 %4, %13\n\tds_read_b128 %5, %13 offset:2048\n\t"
-      "ds_read_b128 %6, %13 offset:4096\n\tds_read_b128 %7, %13 offset:6144\n\t"
-      "ds_read_b128 %8, %13 offset:8192\n\tds_read_b128 %9, %13 offset:10240\n\t"
-      "ds_read_b128 %10, %13 offset:12288\n\tds_read_b128 %11, %13 offset:14336\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]),
-        "=&v"(fb[3]), "=&v"(fb[4]), "=&v"(fb[5]), "=&v"(fb[6]), "=&v"(fb[7])
-      : "v"(a), "v"(b));
-}
-template <>
-__device__ __forceinline__ void lds_read_tile<4, 4>(i32x4 (&fa)[4], i32x4 (&fb)[4], unsigned a, unsigned b) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:2048\n\t"
-      "ds_read_b128 %2, %8 offset:4096\n\tds_read_b128 %3, %8 offset:6144\n\t"
-      "ds_read_b128 %4, %9\n\tds_read_b128 %5, %9 offset:2048\n\t"
-      "ds_read_b128 %6, %9 offset:4096\n\tds_read_b128 %7, %9 offset:6144\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]),
-        "=&v"(fb[3])
-      : "v"(a), "v"(b));
+// global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes [lds + 16 l, lds + 16 l + 16)
+// (lds is wave-uniform, in M0).  Written as asm so that the compiler does not treat later LDS
+// reads of other buffers as waiting on it; the k-loop waits for these copies explicitly
+// (s_waitcnt vmcnt + barrier).  It has no output register: the data lands in LDS.
+__device__ __forceinline__ void dma16(const void *g, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
 }
 
-template <typename Op, int BN, class Epi>
+// The k-step buffers, one LDS array per buffer and stage size, named statically by the k-step
+// code (only the ones a kernel uses are allocated).
+template <int SZ, int I> __shared__ __attribute__((aligned(1024))) char big_sb[SZ];
+template <int SZ, int B> __device__ __forceinline__ char *big_buf() {
+  return B == 0 ? big_sb<SZ, 0> : (B == 1 ? big_sb<SZ, 1> : big_sb<SZ, 2>);
+}
+template <int N> __device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <typename Op, int BN, int NBUF, class Epi>
 __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int M, int K, Epi epi, SplitK sk, int n_tiles,
                                                   int m_tiles) {
   constexpr int EB = sizeof(Op);       // bytes per element
@@ -574,8 +569,8 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
   constexpr int ROWS = BM + BN;                 // LDS rows per stage (A then W)
   constexpr int LPW = ROWS * RB / 1024 / 4;     // 1 KB DMA instructions per wave per stage
   constexpr int STAGE = ROWS * RB;
-  static_assert(LPW == 8 || LPW == 12, "stage of 8 or 12 DMA instructions per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[BIG_NBUF * STAGE];
+  static_assert(NBUF == 2 || NBUF == 3, "two or three k-step buffers");
+  static_assert(NBUF * STAGE + BM * 4 <= 160 * 1024, "buffers fit the LDS");
   __shared__ float rinv[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -600,12 +595,10 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
     const Op *row = r < BM ? A + (size_t)min(m0 + r, M - 1) * K : epi.wrow(n0 + r - BM);  // rows past M: never stored
     src[i] = row + kb + chunk * VE;
   }
-  auto dma = [&](int kt) {
-    char *dst = smem + (kt % BIG_NBUF) * STAGE + wave * LPW * 1024;
+  auto dma = [&](auto bufc, int kt) {
+    const unsigned dst = lds_addr(big_buf<STAGE, decltype(bufc)::value>()) + wave * LPW * 1024;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i)
-      __builtin_amdgcn_global_load_lds((const void *)(src[i] + kt * BK),
-                                       (__attribute__((address_space(3))) void *)(dst + i * 1024), 16, 0, 0);
+    for (int i = 0; i < LPW; ++i) dma16(src[i] + kt * BK, dst + i * 1024);
   };
 
   f32x4 acc[4][TN];
@@ -614,49 +607,79 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  dma(0);
-  if (nkt > 1) dma(1);
-  epi.prepare(m0, BM, rinv);  // its loads queue behind the first two stages
   // fragment rows of this wave: A rows wm*64 + i*16 + c16, W rows BM + wn*BN/2 + j*16 + c16;
   // (row & 7) == (c16 & 7) for all of them
   const int sw = c16 & 7;
   const int arow = (wm * 64 + c16) * RB, wrow = (BM + wn * (BN / 2) + c16) * RB;
-  for (int kt = 0; kt < nkt; ++kt) {
-    // this wave's DMAs for step kt are done once at most the next step's are outstanding
-    if (kt + 1 < nkt) {
-      if constexpr (LPW == 12) vm_wait_12(); else vm_wait_8();
-    } else {
-      vm_wait_0();
-    }
-    __builtin_amdgcn_s_barrier();  // every wave's step kt has landed; step kt-1 is fully read
-    if (kt + 2 < nkt) dma(kt + 2);
-    const unsigned st = lds_addr(smem) + (kt % BIG_NBUF) * STAGE;
+
+  // one k-step: wait for its loads, start the loads NBUF-1 steps ahead into the buffer read in
+  // the previous step, multiply
+  auto step = [&](auto curc, int kt) {
+    constexpr int CB = decltype(curc)::value;
+    const char *cur = big_buf<STAGE, CB>();
+    if (NBUF == 3 && kt + 1 < nkt) vm_wait<LPW>();  // the next step's copies may stay in flight
+    else vm_wait<0>();
+    wg_barrier();  // every wave's step kt has landed; step kt-1 is fully read
+    if (kt + NBUF - 1 < nkt) dma(std::integral_constant<int, (CB + NBUF - 1) % NBUF>{}, kt + NBUF - 1);
     if constexpr (EB == 2) {
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         const int pos = ((kc * 4 + g) ^ sw) * 16;
-        i32x4 fa[4], fb[TN];
-        lds_read_tile<4, TN>(fa, fb, st + arow + pos, st + wrow + pos);
+        bf16x8 fa[4], fb[TN];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(cur + arow + i * 16 * RB + pos);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const bf16x8 *>(cur + wrow + j * 16 * RB + pos);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = Mfma<bf16>::mma(__builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]), acc[i][j]);
+          for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<bf16>::mma(fa[i], fb[j], acc[i][j]);
       }
     } else {
       const int p0 = ((2 * g) ^ sw) * 16, p1 = ((2 * g + 1) ^ sw) * 16;
-      i32x4 lo[4], hi[4], wlo[TN], whi[TN];
-      lds_read_tile<4, TN>(lo, wlo, st + arow + p0, st + wrow + p0);
-      lds_read_tile<4, TN>(hi, whi, st + arow + p1, st + wrow + p1);
+      i32x8 fa[4], fb[TN];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(cur + arow + i * 16 * RB + p0);
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(cur + arow + i * 16 * RB + p1);
+        fa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(cur + wrow + j * 16 * RB + p0);
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(cur + wrow + j * 16 * RB + p1);
+        fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = Mfma8::mma(__builtin_shufflevector(lo[i], hi[i], 0, 1, 2, 3, 4, 5, 6, 7),
-                                 __builtin_shufflevector(wlo[j], whi[j], 0, 1, 2, 3, 4, 5, 6, 7), acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = Mfma8::mma(fa[i], fb[j], acc[i][j]);
     }
+  };
+
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, 1> B1;
+  typedef std::integral_constant<int, 2> B2;
+  dma(B0{}, 0);
+  if (NBUF == 3 && nkt > 1) dma(B1{}, 1);
+  epi.prepare(m0, BM, rinv);  // its loads queue behind the first stages
+  int kt = 0;
+  if constexpr (NBUF == 3) {
+    for (; kt + 3 <= nkt; kt += 3) {
+      step(B0{}, kt);
+      step(B1{}, kt + 1);
+      step(B2{}, kt + 2);
+    }
+    if (kt < nkt) step(B0{}, kt);
+    if (kt + 1 < nkt) step(B1{}, kt + 1);
+  } else {
+    for (; kt + 2 <= nkt; kt += 2) {
+      step(B0{}, kt);
+      step(B1{}, kt + 1);
+    }
+    if (kt < nkt) step(B0{}, kt);
   }
-  __syncthreads();  // rinv (written by epi.prepare) visible to every wave
+  __syncthreads();  // rinv (written by epi.prepare) visible; every stage read is done
 
   if (sk.k_split > 1) {  // partial sums [split][M][N], row-major; resid_reduce_kernel finishes
     const int N = n_tiles * BN;
@@ -673,23 +696,24 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
   }
   if constexpr (Epi::kTile && EB == 2) {
     if (epi.tile_ok(BN)) {  // uniform
-    // stage the finished tile in LDS (the k-step buffers are free now), then store whole rows
-    constexpr int LD = BN + 8;
-    bf16 *ot = reinterpret_cast<bf16 *>(smem);
+      // stage the finished tile in LDS (the k-step buffers are free now), then store whole rows
+      constexpr int LD = BN + 8;
+      static_assert(64 * LD * 2 <= STAGE, "half a tile fits in one stage buffer");
+      const TileRows<bf16, LD> ot{reinterpret_cast<bf16 *>(big_buf<STAGE, 0>()), reinterpret_cast<bf16 *>(big_buf<STAGE, 1>())};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row0 = m0 + wm * 64 + i * 16 + 4 * g;
-      const RowInfo ri = row_info(epi.rows(), row0, M);
-      typename Epi::St st[TN];
+      for (int i = 0; i < 4; ++i) {
+        const int row0 = m0 + wm * 64 + i * 16 + 4 * g;
+        const RowInfo ri = row_info(epi.rows(), row0, M);
+        typename Epi::St st[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) st[j] = epi.load(ri, n0 + wn * (BN / 2) + j * 16 + c16);
+        for (int j = 0; j < TN; ++j) st[j] = epi.load(ri, n0 + wn * (BN / 2) + j * 16 + c16);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        epi.template to_lds<LD>(st[j], row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], rinv, m0, n0, ot);
-    }
-    __syncthreads();
-    epi.template lds_out<LD, BM, BN>(ot, m0, n0, M);
-    return;
+        for (int j = 0; j < TN; ++j)
+          epi.to_lds(st[j], row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], rinv, m0, n0, ot);
+      }
+      __syncthreads();
+      epi.template lds_out<BM, BN>(ot, m0, n0, M);
+      return;
     }
   }
 #pragma unroll
@@ -705,14 +729,18 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
   }
 }
 
+// nt: 128 or 256 columns per tile with three k-step buffers, or 384 with two (LDS holds only two
+// stages of 512 rows).
 template <typename Op, class Epi>
 static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, const SplitK &sk, hipStream_t s) {
   const int nN = N / nt, nM = (M + 127) / 128;
   dim3 grid(nN, nM, sk.k_split);
-  if (nt == 256)
-    hipLaunchKernelGGL((big_kernel<Op, 256, Epi>), grid, dim3(256), 0, s, A, M, K, epi, sk, nN, nM);
+  if (nt == 384)
+    hipLaunchKernelGGL((big_kernel<Op, 384, 2, Epi>), grid, dim3(256), 0, s, A, M, K, epi, sk, nN, nM);
+  else if (nt == 256)
+    hipLaunchKernelGGL((big_kernel<Op, 256, 3, Epi>), grid, dim3(256), 0, s, A, M, K, epi, sk, nN, nM);
   else
-    hipLaunchKernelGGL((big_kernel<Op, 128, Epi>), grid, dim3(256), 0, s, A, M, K, epi, sk, nN, nM);
+    hipLaunchKernelGGL((big_kernel<Op, 128, 3, Epi>), grid, dim3(256), 0, s, A, M, K, epi, sk, nN, nM);
 }
 
 // ------------------------------------------------------------------------ tiled kernel (any M)
