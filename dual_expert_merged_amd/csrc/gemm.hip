@@ -142,16 +142,16 @@ template <typename T> struct EpiQkv {
     float2 cs[4];
   };
   __device__ __forceinline__ const RowMap &rows() const { return a.rows; }
-  // head_dim is a power of two: divisions by D and D/2 are shifts and masks
+  // head_dim is a power of two: divisions by D are shifts and masks
   __device__ __forceinline__ int dlog() const { return 31 - __builtin_clz(a.D); }
+  // Column permutation: the 16-column tiles of a head come in pairs (2p, 2p+1) holding dims
+  // p*16 + l and D/2 + p*16 + l, so the two halves of every rotate-half RoPE pair sit in one lane.
   __device__ __forceinline__ int col(int c) const {
     const int qd = a.Hq * a.D, kd = a.Hkv * a.D;
     const int base = c < qd ? 0 : (c < qd + kd ? qd : qd + kd);
-    const int local = c - base;
-    const int hl = dlog() - 1, half = a.D >> 1;
-    const int p = (local >> 4) * 8 + (local & 7);
-    const int upper = (local >> 3) & 1;
-    return base + ((p >> hl) << (hl + 1)) + (p & (half - 1)) + upper * half;
+    const int local = c - base, dl = dlog();
+    const int t = (local & (a.D - 1)) >> 4;
+    return base + ((local >> dl) << dl) + (t & 1) * (a.D >> 1) + (t >> 1) * 16 + (local & 15);
   }
   __device__ __forceinline__ const T *wrow(int c) const { return (const T *)a.w + (size_t)col(c) * a.in.H; }
   __device__ __forceinline__ void prepare(int m0, int rows, float *inv) const {
@@ -162,38 +162,44 @@ template <typename T> struct EpiQkv {
   __device__ __forceinline__ void pre_finish(const Pre &p, int m0, float *inv) const {
     rms_finish(p, a.in, a.M, a.eps, m0, inv);
   }
-  // (cos, sin) of the row's position: prefix token s at s (table by position), action rows from
-  // the per-row table (position P_b + s, filled once per call)
+  // (cos, sin) of the row's position for the even tile of a pair (the odd tile shares them):
+  // prefix token s at s (table by position), action rows from the per-row table (position
+  // P_b + s, filled once per call)
   __device__ __forceinline__ St load(const RowInfo &ri, int c) const {
     St st;
-    const int D = a.D, half = D >> 1;
-    const int d = col(c) & (D - 1);
-    const int i = d & (half - 1);
+    if ((c >> 4) & 1) return st;  // uniform per tile
+    const int i = col(c) & ((a.D >> 1) - 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r)  // also read for value columns (unused there)
-      st.cs[r] = a.rows.is_prefix ? a.rope[(size_t)ri.s[r] * half + i] : a.rope_rows[(size_t)ri.rc[r] * half + i];
+      st.cs[r] = a.rows.is_prefix ? a.rope[(size_t)ri.s[r] * (a.D >> 1) + i] : a.rope_rows[(size_t)ri.rc[r] * (a.D >> 1) + i];
     return st;
   }
-  // Large tiles: a 128 x 256 tile is two whole heads of one section (q, k or v).  to_lds puts
+  // rotate-half RoPE of the lane's pair (lo = dim d, hi = dim d + D/2) for rows of the q and k
+  // sections; v passes through
+  __device__ __forceinline__ void rotate(const St &st, int gc, float &lo, float &hi, int r) const {
+    if (gc < (a.Hq + a.Hkv) * a.D) {
+      const float l = lo, h = hi;
+      lo = l * st.cs[r].x - h * st.cs[r].y;
+      hi = h * st.cs[r].x + l * st.cs[r].y;
+    }
+  }
+  // Large tiles: a 128 x 256 tile is two whole heads of one section (q, k or v).  to_lds2 puts
   // the rotated values at their natural (head, d) position of row (row - m0) of the staging tile;
   // lds_out then writes each row's two heads as whole 16-byte vectors.
   static constexpr bool kTile = true;
   // every tile must lie inside one section: q, k and v widths are multiples of the tile width
   __device__ __forceinline__ bool tile_ok(int bn) const { return (a.Hq * a.D) % bn == 0 && (a.Hkv * a.D) % bn == 0; }
   template <class Tile>
-  __device__ __forceinline__ void to_lds(const St &st, int row0, int c, f32x4 acc, const float *inv, int m0, int n0,
-                                         const Tile &ot) const {
-    const int gc = col(c), gc0 = col(n0);
-    const int D = a.D;
-    const int local = gc - gc0;  // (head - first head) * D + d
-    const int upper = (gc & (D - 1)) >= (D >> 1);
-    const bool rot = gc < (a.Hq + a.Hkv) * D;
+  __device__ __forceinline__ void to_lds2(const St &st, const St &, int row0, int c, f32x4 acc0, f32x4 acc1,
+                                          const float *inv, int m0, int n0, const Tile &ot) const {
+    const int gc = col(c), local = gc - col(n0);  // (head - first head) * D + d of the low half
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float u = acc[r] * inv[row0 + r - m0];
-      const float pu = lane_xor8(u);
-      if (rot) u = upper ? (u * st.cs[r].x + pu * st.cs[r].y) : (u * st.cs[r].x - pu * st.cs[r].y);
-      ot.row(row0 + r - m0)[local] = from_f32<T>(u);
+      float lo = acc0[r] * inv[row0 + r - m0], hi = acc1[r] * inv[row0 + r - m0];
+      rotate(st, gc, lo, hi, r);
+      T *orow = ot.row(row0 + r - m0);
+      orow[local] = from_f32<T>(lo);
+      orow[local + (a.D >> 1)] = from_f32<T>(hi);
     }
   }
   template <int BM, int BN, class Tile>
@@ -202,7 +208,7 @@ template <typename T> struct EpiQkv {
     const int D = a.D, qd = a.Hq * D, kd = a.Hkv * D;
     const int gc0 = col(n0);
     const int sec = gc0 < qd ? 0 : (gc0 < qd + kd ? 1 : 2);
-    const int head0 = (gc0 - (sec == 0 ? 0 : (sec == 1 ? qd : qd + kd))) / D;
+    const int head0 = (gc0 - (sec == 0 ? 0 : (sec == 1 ? qd : qd + kd))) >> dlog();
     const RowMap &rm = a.rows;
 #pragma unroll 4
     for (int idx = threadIdx.x; idx < BM * CPR; idx += 256) {
@@ -215,33 +221,29 @@ template <typename T> struct EpiQkv {
       if (sec == 0) {
         dst = (T *)a.q + (size_t)row * qd + gc0 + ch * 8;
       } else {
-        const int hl = (ch * 8) / D, d = ch * 8 - hl * D;
+        const int hl = (ch * 8) >> dlog(), d = ch * 8 - (hl << dlog());
         dst = (T *)(sec == 1 ? a.k : a.v) + ((size_t)(b * a.Hkv + head0 + hl) * a.kv_rows + s) * D + d;
       }
       *reinterpret_cast<i32x4 *>(dst) = v;
     }
   }
-  __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
-                                        int m0) const {
+  // tile pair (c, c + 16): the low and high halves of 16 RoPE pairs
+  __device__ __forceinline__ void store2(const St &st, const St &, const RowInfo &ri, int row0, int c, f32x4 acc0,
+                                         f32x4 acc1, bool, const float *inv, int m0) const {
     const int gc = col(c);
     const int D = a.D, qd = a.Hq * D, kd = a.Hkv * D;
     const int sec = gc < qd ? 0 : (gc < qd + kd ? 1 : 2);
     const int local = gc - (sec == 0 ? 0 : (sec == 1 ? qd : qd + kd));
     const int head = local >> dlog(), d = local & (D - 1);
-    const int upper = d >= (D >> 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float u = acc[r] * inv[row0 + r - m0];
-      const float pu = lane_xor8(u);
-      if (sec < 2) u = upper ? (u * st.cs[r].x + pu * st.cs[r].y) : (u * st.cs[r].x - pu * st.cs[r].y);
+      float lo = acc0[r] * inv[row0 + r - m0], hi = acc1[r] * inv[row0 + r - m0];
+      rotate(st, gc, lo, hi, r);
       if (!ri.ok[r]) continue;
-      const T val = from_f32<T>(u);
-      if (sec == 0) {
-        ((T *)a.q)[(size_t)(row0 + r) * qd + gc] = val;
-      } else {
-        T *dst = (T *)(sec == 1 ? a.k : a.v);
-        dst[((size_t)(ri.b[r] * a.Hkv + head) * a.kv_rows + ri.s[r]) * D + d] = val;
-      }
+      T *dst = sec == 0 ? (T *)a.q + (size_t)(row0 + r) * qd + gc
+                        : (T *)(sec == 1 ? a.k : a.v) + ((size_t)(ri.b[r] * a.Hkv + head) * a.kv_rows + ri.s[r]) * D + d;
+      dst[0] = from_f32<T>(lo);
+      dst[D >> 1] = from_f32<T>(hi);
     }
   }
 };
@@ -263,7 +265,8 @@ template <typename T, typename W = T> struct EpiResid {
   static constexpr bool kTile = false;
   __device__ __forceinline__ bool tile_ok(int) const { return false; }
   template <class Tile>
-  __device__ __forceinline__ void to_lds(const St &, int, int, f32x4, const float *, int, int, const Tile &) const {}
+  __device__ __forceinline__ void to_lds2(const St &, const St &, int, int, f32x4, f32x4, const float *, int, int,
+                                          const Tile &) const {}
   template <int BM, int BN, class Tile>
   __device__ __forceinline__ void lds_out(const Tile &, int, int, int) const {}
   struct Pre {};
@@ -296,6 +299,11 @@ template <typename T, typename W = T> struct EpiResid {
       }
     }
   }
+  __device__ __forceinline__ void store2(const St &st0, const St &st1, const RowInfo &ri, int row0, int c, f32x4 acc0,
+                                         f32x4 acc1, bool has1, const float *inv, int m0) const {
+    store(st0, ri, row0, c, acc0, inv, m0);
+    if (has1) store(st1, ri, row0, c + 16, acc1, inv, m0);
+  }
 };
 
 template <typename T, typename W = T> struct EpiSwiglu {
@@ -305,9 +313,11 @@ template <typename T, typename W = T> struct EpiSwiglu {
     float s;
   };
   __device__ __forceinline__ const RowMap &rows() const { return a.rows; }
+  // Column permutation: 16-column tiles come in pairs (2q, 2q+1) = gate and up rows of the same
+  // 16 activation columns f = 16q + l, so silu(gate) * up is formed within one lane.
+  __device__ __forceinline__ static int act_col(int c) { return (c >> 5) * 16 + (c & 15); }
   __device__ __forceinline__ const W *wrow(int c) const {
-    const int f = (c >> 4) * 8 + (c & 7);
-    return (const W *)((c >> 3) & 1 ? a.wu : a.wg) + (size_t)f * a.in.H;
+    return (const W *)((c >> 4) & 1 ? a.wu : a.wg) + (size_t)act_col(c) * a.in.H;
   }
   __device__ __forceinline__ void prepare(int m0, int rows, float *inv) const {
     rms_prepare(a.in, a.M, a.eps, m0, rows, inv, Q ? a.a_scale : nullptr);
@@ -320,23 +330,21 @@ template <typename T, typename W = T> struct EpiSwiglu {
   __device__ __forceinline__ St load(const RowInfo &, int c) const {
     St st;
     st.s = 1.0f;
-    if constexpr (Q) st.s = ((c >> 3) & 1 ? a.s_up : a.s_gate)[(c >> 4) * 8 + (c & 7)];
+    if constexpr (Q) st.s = ((c >> 4) & 1 ? a.s_up : a.s_gate)[act_col(c)];
     return st;
   }
-  // Large tiles: the 256 columns of a tile are 128 activation columns; to_lds stages them per
-  // row, lds_out writes each row's 128 values as whole 16-byte vectors.
+  // Large tiles: the 2*16 columns of a tile pair are 16 activation columns; to_lds2 stages them
+  // per row, lds_out writes each row's BN/2 values as whole 16-byte vectors.
   static constexpr bool kTile = true;
   __device__ __forceinline__ bool tile_ok(int) const { return true; }
   template <class Tile>
-  __device__ __forceinline__ void to_lds(const St &st, int row0, int c, f32x4 acc, const float *inv, int m0, int n0,
-                                         const Tile &ot) const {
-    const int fl = ((c - n0) >> 4) * 8 + (c & 7);
-    const int up = (c >> 3) & 1;
+  __device__ __forceinline__ void to_lds2(const St &sg, const St &su, int row0, int c, f32x4 accg, f32x4 accu,
+                                          const float *inv, int m0, int n0, const Tile &ot) const {
+    const int fl = act_col(c) - (n0 >> 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float g = acc[r] * inv[row0 + r - m0] * st.s;
-      const float u = lane_xor8(g);
-      if (!up) ot.row(row0 + r - m0)[fl] = from_f32<T>(silu(g) * u);
+      const float sc = inv[row0 + r - m0];
+      ot.row(row0 + r - m0)[fl] = from_f32<T>(silu(accg[r] * sc * sg.s) * (accu[r] * sc * su.s));
     }
   }
   template <int BM, int BN, class Tile>
@@ -355,16 +363,14 @@ template <typename T, typename W = T> struct EpiSwiglu {
           *reinterpret_cast<const i32x4 *>(ot.row(rl) + ch * 8);
     }
   }
-  __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
-                                        int m0) const {
-    const int f = (c >> 4) * 8 + (c & 7);
-    const int up = (c >> 3) & 1;
+  __device__ __forceinline__ void store2(const St &sg, const St &su, const RowInfo &ri, int row0, int c, f32x4 accg,
+                                         f32x4 accu, bool, const float *inv, int m0) const {
+    const int f = act_col(c);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float g = acc[r] * inv[row0 + r - m0] * st.s;
-      const float u = lane_xor8(g);
-      if (up || !ri.ok[r]) continue;
-      ((T *)a.act)[(size_t)(row0 + r) * a.F + f] = from_f32<T>(silu(g) * u);
+      if (!ri.ok[r]) continue;
+      const float sc = inv[row0 + r - m0];
+      ((T *)a.act)[(size_t)(row0 + r) * a.F + f] = from_f32<T>(silu(accg[r] * sc * sg.s) * (accu[r] * sc * su.s));
     }
   }
 };
@@ -462,7 +468,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
   }
   if (wave < nrt) {
 #pragma unroll
-    for (int j = 0; j < CT; ++j) epi.store(st[j], ri, m0 + wave * 16 + 4 * g, n0 + j * 16 + c16, sum[j], rinv, m0);
+    for (int j = 0; j < CT; j += 2) {
+      const int j1 = j + 1 < CT ? j + 1 : j;
+      epi.store2(st[j], st[j1], ri, m0 + wave * 16 + 4 * g, n0 + j * 16 + c16, sum[j], sum[j1], j + 1 < CT, rinv, m0);
+    }
   }
 }
 
@@ -708,8 +717,9 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
 #pragma unroll
         for (int j = 0; j < TN; ++j) st[j] = epi.load(ri, n0 + wn * (BN / 2) + j * 16 + c16);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          epi.to_lds(st[j], row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], rinv, m0, n0, ot);
+        for (int j = 0; j < TN; j += 2)
+          epi.to_lds2(st[j], st[j + 1], row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], acc[i][j + 1], rinv, m0, n0,
+                      ot);
       }
       __syncthreads();
       epi.template lds_out<BM, BN>(ot, m0, n0, M);
@@ -725,7 +735,8 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
 #pragma unroll
     for (int j = 0; j < TN; ++j) st[j] = epi.load(ri, n0 + wn * (BN / 2) + j * 16 + c16);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) epi.store(st[j], ri, row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], rinv, m0);
+    for (int j = 0; j < TN; j += 2)
+      epi.store2(st[j], st[j + 1], ri, row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], acc[i][j + 1], true, rinv, m0);
   }
 }
 
@@ -833,9 +844,9 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      epi.store(st[i][j], ri[i], m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4),
-                n0 + wn * (BN / 2) + j * 16 + (lane & 15), acc[i][j], rinv, m0);
+    for (int j = 0; j < TN; j += 2)
+      epi.store2(st[i][j], st[i][j + 1], ri[i], m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4),
+                 n0 + wn * (BN / 2) + j * 16 + (lane & 15), acc[i][j], acc[i][j + 1], true, rinv, m0);
 }
 
 template <typename T, int NT, class Epi>
