@@ -11,8 +11,10 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdm.so")
 SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip"]
 # attention rescales its MFMA accumulators with VALU every key tile: keep them in VGPRs rather
-# than accumulation registers, which would cost a copy out and back per element
-EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# than accumulation registers, which would cost a copy out and back per element.  Its softmax
+# takes many float maxima of MFMA results that are never NaN: without -fno-honor-nans every
+# fmaxf operand is first canonicalised (an extra instruction each).
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

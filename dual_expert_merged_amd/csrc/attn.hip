@@ -56,6 +56,78 @@ template <> __device__ __forceinline__ void store4<float>(float *p, f32x4 v, flo
   *reinterpret_cast<f32x4 *>(p) = v * s;
 }
 
+// Merge the two key halves of every slot group (the second wave of a pair hands its state over
+// through the LDS, which must be free by now), then write the normalised output, or, with several
+// key chunks, this chunk's normalised partial output and its (max, sum); a chunk past the
+// sample's keys publishes max -inf and sum 0 (weight 0 in the merge).
+// Lane (g, c16) holds O^T rows dt*16 + 4g .. +3 of query column c16: 4 consecutive outputs.
+template <typename T, int D>
+__device__ __forceinline__ void attn_finish(const AttnArgs &a, char *smem, float (&m)[2], float (&l)[2],
+                                            f32x4 (&o)[2][D / 16], int wave, int lane, int b, int h, int r0, int nq,
+                                            size_t grp, int chunk, int nch) {
+  constexpr int DT = D / 16;
+  constexpr int XO = 4 * 2 * DT * 64;  // float4 outputs of the second waves
+  const int sg = wave & 3, kh = wave >> 2, g = lane >> 4, c16 = lane & 15;
+  float *xo = reinterpret_cast<float *>(smem);
+  float *xm = xo + XO * 4, *xl = xm + 4 * 2 * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4 *>(&xo[(((sg * 2 + qt) * DT + dt) * 64 + lane) * 4]) = o[qt][dt];
+      xm[(sg * 2 + qt) * 64 + lane] = m[qt];
+      xl[(sg * 2 + qt) * 64 + lane] = l[qt];
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float m1 = xm[(sg * 2 + qt) * 64 + lane], l1 = xl[(sg * 2 + qt) * 64 + lane];
+    const float M = fmaxf(m[qt], m1);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float a0 = __builtin_amdgcn_exp2f(m[qt] - Mu), a1 = __builtin_amdgcn_exp2f(m1 - Mu);
+    l[qt] = l[qt] * a0 + l1 * a1;
+    m[qt] = M;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      o[qt][dt] = o[qt][dt] * a0 + *reinterpret_cast<const f32x4 *>(&xo[(((sg * 2 + qt) * DT + dt) * 64 + lane) * 4]) * a1;
+  }
+
+  const int HD = a.Hq * D;
+  if (a.n_chunks == 1) {
+    T *out = (T *)a.out;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int row = r0 + qt * 16 + c16;
+      if (row >= nq) continue;
+      const float inv = 1.0f / l[qt];
+      T *orow = out + (size_t)(b * a.q_rows_per_b + row) * HD + h * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) store4<T>(orow + dt * 16, o[qt][dt], inv);
+    }
+    return;
+  }
+  const int nqb = gridDim.y, slot0 = sg * 32;
+  T *part_o = (T *)a.part;
+  float *part_ml = (float *)((char *)a.part + ((part_o_elems(a.B, a.Hkv, nqb, a.n_chunks, D) * sizeof(T) + 255) &
+                                               ~(size_t)255));
+  T *po = part_o + (grp * a.n_chunks + chunk) * ATT_SLOTS * D;
+  float *pml = part_ml + (grp * a.n_chunks + chunk) * ATT_SLOTS * 2;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int row = r0 + qt * 16 + c16;
+    if (row >= nq) continue;
+    const int slot = slot0 + qt * 16 + c16;
+    if (chunk < nch) {
+      const float inv = 1.0f / l[qt];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) store4<T>(po + slot * D + dt * 16 + 4 * g, o[qt][dt], inv);
+    }
+    if (g == 0) *reinterpret_cast<float2 *>(&pml[slot * 2]) = chunk < nch ? make_float2(m[qt], l[qt]) : make_float2(-INFINITY, 0.f);
+  }
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(ATT_THREADS) void attn_kernel(AttnArgs a) {
   typedef Mfma<T> MF;
@@ -242,68 +314,275 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // merge the two key halves of every slot group: the second wave hands its state over in LDS
   __syncthreads();  // every stage read is done: the LDS is free
-  float *xo = reinterpret_cast<float *>(smem);
-  float *xm = xo + XO * 4, *xl = xm + 4 * 2 * 64;
-  if (kh == 1) {
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4 *>(&xo[(((sg * 2 + qt) * DT + dt) * 64 + lane) * 4]) = o[qt][dt];
-      xm[(sg * 2 + qt) * 64 + lane] = m[qt];
-      xl[(sg * 2 + qt) * 64 + lane] = l[qt];
-    }
-  }
-  __syncthreads();
-  if (kh == 1) return;
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float m1 = xm[(sg * 2 + qt) * 64 + lane], l1 = xl[(sg * 2 + qt) * 64 + lane];
-    const float M = fmaxf(m[qt], m1);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    const float a0 = __builtin_amdgcn_exp2f(m[qt] - Mu), a1 = __builtin_amdgcn_exp2f(m1 - Mu);
-    l[qt] = l[qt] * a0 + l1 * a1;
-    m[qt] = M;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      o[qt][dt] = o[qt][dt] * a0 + *reinterpret_cast<const f32x4 *>(&xo[(((sg * 2 + qt) * DT + dt) * 64 + lane) * 4]) * a1;
-  }
+  attn_finish<T, D>(a, smem, m, l, o, wave, lane, b, h, r0, nq, grp, chunk, nch);
+}
 
-  // lane (g, c16) holds O^T rows dt*16 + 4g .. +3 of query column c16: 4 consecutive outputs
-  if (a.n_chunks == 1) {
-    T *out = (T *)a.out;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int row = r0 + qt * 16 + c16;
-      if (row >= nq) continue;
-      const float inv = 1.0f / l[qt];
-      T *orow = out + (size_t)(b * a.q_rows_per_b + row) * HD + h * D + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) store4<T>(orow + dt * 16, o[qt][dt], inv);
-    }
-    return;
-  }
+// ------------------------------------------------------------------ bf16, head_dim 128
+// The same work split (8 waves = 4 slot groups x 2 key halves, 64-key tiles, online softmax per
+// wave, pair merge), with the operands copied global -> LDS by the DMA path
+// (global_load_lds_dwordx4): the query tile and NBUF-1 key stages are in flight before the first
+// tile is multiplied, and every iteration starts the copy of the stage NBUF-1 ahead, so about
+// 96 KB per workgroup stay in flight and the kernel streams the cache at the HBM rate instead of
+// one load round trip per stage.  K and V stay row-major in LDS (256-byte rows): V^T fragments
+// are read with the gfx950 transposing LDS read (ds_read_b64_tr_b16), so no register staging
+// or transposed LDS stores are needed.
+//
+// LDS rows of 256 bytes keep their 16-byte chunks permuted: chunk c of row r sits at position
+// c ^ att_swz(r).  Every read below is then free of bank conflicts: a K fragment read (16 lanes:
+// 16 key rows, one chunk), a transposed V read (32 lanes: 8 key rows x 2 chunks) and a Q
+// fragment read (16 consecutive slots, one chunk).
+__device__ __forceinline__ int att_swz(int r) { return ((r & 3) << 1) | (r & 8) | (((r >> 4) ^ (r >> 2)) & 1); }
 
-  // several chunks: publish this chunk's normalised output and statistics; a chunk past the
-  // sample's keys publishes max -inf and sum 0 (weight 0 in the merge)
-  T *part_o = (T *)a.part;
-  float *part_ml = (float *)((char *)a.part + ((part_o_elems(a.B, a.Hkv, nqb, a.n_chunks, D) * sizeof(T) + 255) &
-                                               ~(size_t)255));
-  T *po = part_o + (grp * a.n_chunks + chunk) * ATT_SLOTS * D;
-  float *pml = part_ml + (grp * a.n_chunks + chunk) * ATT_SLOTS * 2;
+typedef short att_s4 __attribute__((ext_vector_type(4)));
+typedef short att_s8 __attribute__((ext_vector_type(8)));
+// Transposing LDS read, per group of 16 lanes: lane i receives element i % 4 of the 4-element
+// (8-byte) row addressed by lane 4e + i / 4 of its group, for e = 0..3.
+__device__ __forceinline__ att_s4 lds_read_tr16(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) att_s4 *)p);
+}
+__device__ __forceinline__ void vm_wait_upto12(int n) {  // n in {0, 4, 8, 12}
+  if (n >= 12) vm_wait<12>();
+  else if (n >= 8) vm_wait<8>();
+  else if (n >= 4) vm_wait<4>();
+  else vm_wait<0>();
+}
+
+template <int G, int NBUF>
+__global__ __launch_bounds__(ATT_THREADS) void attn_dma_kernel(AttnArgs a) {
+  typedef bf16x8 frag;
+  constexpr int D = 128, DC = 4, DT = 8, RB = D * 2;  // RB: bytes per K / V / Q row
+  constexpr int TK = ATT_KT;                           // keys per stage (32 per wave of a pair)
+  constexpr int KV_B = TK * RB;                        // 16 KB of K, then 16 KB of V
+  constexpr int STAGE = 2 * KV_B;
+  constexpr int LPW = STAGE / 1024 / (ATT_THREADS / 64);  // 1 KB copies per wave per stage
+  constexpr int RPH = ATT_SLOTS / G;
+  static_assert(LPW == 4 && ATT_SLOTS * RB == STAGE, "the query tile fills one stage buffer");
+  static_assert(NBUF >= 3 && NBUF <= 4 && NBUF * STAGE <= 160 * 1024, "stage buffers fit the LDS");
+  static_assert(4 * 2 * DT * 64 * 16 + 2 * 4 * 2 * 64 * 4 <= NBUF * STAGE, "the pair merge fits the LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
+
+  const bf16 *__restrict__ q = (const bf16 *)a.q;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sg = wave & 3, kh = wave >> 2;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bk = blockIdx.x, qb = blockIdx.y, chunk = blockIdx.z, nqb = gridDim.y;
+  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+  const int P = max(0, min(a.lens[b], a.kp_rows));
+  const int nq = a.suffix ? a.S : P;
+  const int nkeys = P + (a.suffix ? a.S : 0);
+  const int nch = (nkeys + a.chunk_keys - 1) / a.chunk_keys;
+  const int k_begin = chunk * a.chunk_keys;
+  const int k_end = min(nkeys, k_begin + a.chunk_keys);
+  if (qb * RPH >= nq) return;  // uniform
+
+  const int slot0 = sg * 32;
+  const int h = kvh * G + slot0 / RPH;
+  const int r0 = qb * RPH + (slot0 % RPH);
+  const int HD = a.Hq * D;
+  const size_t grp = (size_t)bk * nqb + qb;
+
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  f32x4 o[2][DT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int row = r0 + qt * 16 + c16;
-    if (row >= nq) continue;
-    const int slot = slot0 + qt * 16 + c16;
-    if (chunk < nch) {
-      const float inv = 1.0f / l[qt];
+  for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) store4<T>(po + slot * D + dt * 16 + 4 * g, o[qt][dt], inv);
+    for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (k_begin < k_end) {
+    const unsigned sbase = lds_addr(smem);
+    const int crow = lane >> 4, cpos = lane & 15;  // a copy: 4 rows x 16 chunks, one per lane
+    // Stage copies: waves 0-3 copy K, waves 4-7 V; copy i of a wave fills rows 4u .. 4u+3 of the
+    // stage, u = 4 (wave & 3) + i.  Keys past k_end re-read key k_end-1: their scores are masked
+    // to -inf and their V rows are finite, so they add exactly 0.
+    const bf16 *kv_pre = (const bf16 *)(wave < 4 ? a.kp : a.vp) + (size_t)(b * a.Hkv + kvh) * a.kp_rows * D;
+    const bf16 *kv_suf = (const bf16 *)(wave < 4 ? a.ks : a.vs) + (size_t)(b * a.Hkv + kvh) * a.S * D;
+    int coff[4];  // byte offsets of this lane's pieces within a stage's rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * (4 * (wave & 3) + i) + crow;
+      coff[i] = (row * D + ((cpos ^ att_swz(row)) << 3)) * 2;
     }
-    if (g == 0) *reinterpret_cast<float2 *>(&pml[slot * 2]) = chunk < nch ? make_float2(m[qt], l[qt]) : make_float2(-INFINITY, 0.f);
+    const int pre_end = min(P, k_end);
+    auto issue = [&](int stage) {
+      const int ks0 = k_begin + stage * TK;
+      const unsigned dst = sbase + (stage % NBUF) * STAGE + (wave >> 2) * KV_B + (wave & 3) * 4 * 1024;
+      if (ks0 + TK <= pre_end) {  // uniform: 64 consecutive cached keys, one scalar base
+        const char *base = (const char *)(kv_pre + (size_t)ks0 * D);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_sbase(base, coff[i], dst + i * 1024);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * (4 * (wave & 3) + i) + crow;
+          const int kc = min(ks0 + row, k_end - 1);
+          const bf16 *src = kc < P ? kv_pre + (size_t)kc * D : kv_suf + (size_t)(kc - P) * D;
+          dma16(src + ((cpos ^ att_swz(row)) << 3), dst + i * 1024);
+        }
+      }
+    };
+    // Query tile into the last buffer (first overwritten by the stage NBUF-1 copies, which start
+    // after every wave has read its fragments): copy i of a wave fills slots 4u .. 4u+3,
+    // u = 4 wave + i; rows past nq read row nq-1 (their outputs are never stored).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = 4 * (4 * wave + i) + crow;
+      const int row = min(qb * RPH + slot % RPH, nq - 1);
+      const bf16 *src = q + (size_t)(b * a.q_rows_per_b + row) * HD + (kvh * G + slot / RPH) * D;
+      dma16(src + ((cpos ^ att_swz(slot)) << 3), sbase + (NBUF - 1) * STAGE + (4 * wave + i) * 1024);
+    }
+    const int nt = (k_end - k_begin + TK - 1) / TK;
+#pragma unroll
+    for (int st = 0; st < NBUF - 1; ++st)
+      if (st < nt) issue(st);
+    vm_wait_upto12(min(NBUF - 2, nt - 1) * LPW);  // this wave's query and stage-0 copies have landed
+    wg_barrier();
+    frag qf[2][DC];
+    {
+      const char *Qb = smem + (NBUF - 1) * STAGE;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int slot = slot0 + qt * 16 + c16;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+          qf[qt][dc] = *reinterpret_cast<const frag *>(Qb + slot * RB + (((dc * 4 + g) ^ att_swz(slot)) << 4));
+      }
+    }
+    const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(D)
+
+    // per-lane LDS offsets within a stage (the same for every stage):
+    // K fragment rows of score tile s: keys (c16 / 4) * 8 + c16 % 4 + 4 s of this wave's half,
+    // so that output row 4g + i of tile s is key 8g + 4s + i (consecutive keys per lane for P^T)
+    int koff[2][DC];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kr = kh * 32 + (c16 >> 2) * 8 + (c16 & 3) + 4 * s;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) koff[s][dc] = kr * RB + (((dc * 4 + g) ^ att_swz(kr)) << 4);
+    }
+    // V^T fragment (d = 16 dt + c16, keys 8g .. 8g+7 of the half): two transposing reads of the
+    // 8-byte pieces (key 8g + j + 4 half, d = 16 dt + 4 (c16 % 4) .. +3), j = c16 / 4
+    const int vr = kh * 32 + g * 8 + (c16 >> 2);
+    const int vsw0 = att_swz(vr), vsw1 = att_swz(vr + 4);
+    const int vpiece = (c16 >> 1) & 1, vbyte = (c16 & 1) * 8;
+
+    // S^T of this wave's half of tile t (two 16-key score tiles x two 16-slot halves)
+    auto scores = [&](int t, f32x4(&st)[2][2]) {
+      const char *Kb = smem + (t % NBUF) * STAGE;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        frag kf[DC];
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) kf[dc] = *reinterpret_cast<const frag *>(Kb + koff[s][dc]);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) acc = Mfma<bf16>::mma(kf[dc], qf[qt][dc], acc);
+          st[qt][s] = acc;
+        }
+      }
+    };
+    // probabilities of tile t (relative to the column maxima mu), the lane's share of the row sums,
+    // and O^T += V^T P^T
+    auto exp_pv = [&](int t, f32x4(&st)[2][2], const float(&mu)[2]) {
+      frag pf[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float sum = 0.f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(st[qt][s][i], sc, -mu[qt]));
+            sum += p;
+            pf[qt][s * 4 + i] = (bf16)p;
+          }
+        l[qt] += sum;
+      }
+      const char *Vb = smem + (t % NBUF) * STAGE + KV_B;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int piece = dt * 2 + vpiece;
+        const att_s4 lo = lds_read_tr16(Vb + vr * RB + ((piece ^ vsw0) << 4) + vbyte);
+        const att_s4 hi = lds_read_tr16(Vb + (vr + 4) * RB + ((piece ^ vsw1) << 4) + vbyte);
+        const frag vf = __builtin_bit_cast(frag, (att_s8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) o[qt][dt] = Mfma<bf16>::mma(vf, pf[qt], o[qt][dt]);
+      }
+    };
+    // new column maxima from tile t's scores; rescales the running sums and outputs (one
+    // wave-uniform branch, taken only when some column's maximum grew)
+    auto new_max = [&](f32x4(&st)[2][2], float(&mu)[2]) {
+      bool grow = false;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float mx = fmaxf(fmaxf(st[qt][0][0], st[qt][0][1]), fmaxf(st[qt][0][2], st[qt][0][3]));
+        mx = fmaxf(mx, fmaxf(fmaxf(st[qt][1][0], st[qt][1][1]), fmaxf(st[qt][1][2], st[qt][1][3])));
+        mx = max_xor32(max_xor16(mx)) * sc;
+        const float m_new = fmaxf(m[qt], mx);
+        mu[qt] = m_new == -INFINITY ? 0.f : m_new;
+        grow |= m_new > m[qt];
+      }
+      if (__ballot(grow) != 0) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const float alpha = __builtin_amdgcn_exp2f(m[qt] - mu[qt]);
+          l[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) m[qt] = fmaxf(m[qt], mu[qt]);
+    };
+
+    // Software pipeline: iteration t multiplies Q K^T of tile t+1 in the same basic block as the
+    // exponentials and P V of tile t, so a wave's MFMAs overlap its own vector work.  Every tile
+    // but the last is full (no masking, keys in both halves); the last one takes the general
+    // path.  The row sums stay per lane (each lane sums its own keys; the maximum, and so every
+    // rescale, is common to the column) and are reduced once at the end.
+    f32x4 st_next[2][2];
+    scores(0, st_next);  // a half without keys computes values that are never used
+    for (int t = 0; t < nt - 1; ++t) {
+      vm_wait_upto12(min(NBUF - 3, nt - 2 - t) * LPW);  // stage t+1 of this wave has landed
+      wg_barrier();  // ... of every wave; stage t-1 is fully read
+      if (t + NBUF - 1 < nt) issue(t + NBUF - 1);
+      f32x4 st[2][2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) st[qt][s] = st_next[qt][s];
+      float mu[2];
+      new_max(st, mu);
+      scores(t + 1, st_next);
+      exp_pv(t, st, mu);
+    }
+    {
+      const int t = nt - 1;
+      vm_wait<0>();
+      wg_barrier();
+      const int kt0 = k_begin + t * TK + kh * 32;
+      if (kt0 < k_end) {  // wave-uniform
+        if (kt0 + 32 > k_end) {
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (kt0 + g * 8 + 4 * s + i >= k_end) st_next[qt][s][i] = -INFINITY;
+        }
+        float mu[2];
+        new_max(st_next, mu);
+        exp_pv(t, st_next, mu);
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) l[qt] = sum_xor32(sum_xor16(l[qt]));
   }
+  __syncthreads();  // every copy has landed and every stage read is done: the LDS is free
+  attn_finish<bf16, D>(a, smem, m, l, o, wave, lane, b, h, r0, nq, grp, chunk, nch);
 }
 
 // Merge the key chunks of every query slot (a separate launch: the kernel boundary makes the
@@ -377,7 +656,10 @@ template <typename T, int D, int G> static void attn_t(const AttnArgs &a, hipStr
   // (sample, KV head) varies fastest: consecutive workgroups go to consecutive XCDs, so all key
   // chunks of one KV head share an XCD and its L2 holds their partial results for the merge.
   dim3 grid(a.B * a.Hkv, nqb, a.n_chunks);
-  hipLaunchKernelGGL((attn_kernel<T, D, G>), grid, dim3(ATT_THREADS), 0, s, a);
+  if constexpr (std::is_same<T, bf16>::value && D == 128)
+    hipLaunchKernelGGL((attn_dma_kernel<G, 4>), grid, dim3(ATT_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<T, D, G>), grid, dim3(ATT_THREADS), 0, s, a);
   if (a.n_chunks > 1) {
     constexpr int SPW = 256 / (D / Mfma<T>::EPL);
     hipLaunchKernelGGL((attn_combine_kernel<T, D, G>), dim3(a.B * a.Hkv, nqb, ATT_SLOTS / SPW), dim3(256), 0, s, a);

@@ -145,4 +145,42 @@ __device__ __forceinline__ float wave_max(float v) {
 // silu(z) = z / (1 + e^-z), with the hardware exponential and reciprocal (about 1 ulp each).
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
+// ---------------------------------------------------------------- global -> LDS copies
+// Workgroup barrier without a global-memory fence (a fence would wait for every outstanding
+// load, prefetches included).  It waits for this wave's LDS reads first, so no wave can start a
+// copy into a buffer another wave is still reading; the memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+// global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes [lds + 16 l, lds + 16 l + 16)
+// (lds is wave-uniform, in M0).  Written as asm so that the compiler does not treat later LDS
+// reads of other buffers as waiting on it; the consumer waits for these copies explicitly
+// (s_waitcnt vmcnt + barrier).  It has no output register: the data lands in LDS.
+__device__ __forceinline__ void dma16(const void *g, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+// The same copy addressed as a wave-uniform 64-bit base (SGPRs) plus a 32-bit per-lane byte
+// offset, so a stream of copies needs no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16_sbase(const void *base, unsigned off, unsigned lds) {
+  const unsigned long long b = (unsigned long long)(uintptr_t)base;
+  // readfirstlane returns int: widen through unsigned, or an address word >= 2^31 would be
+  // sign-extended into the high word
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  const unsigned long long sb = ((unsigned long long)hi << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(sb),
+               "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+// wait until at most N of this wave's vector-memory operations are outstanding (they complete
+// in issue order)
+template <int N> __device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace dm
+

@@ -532,11 +532,6 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
 // resid_reduce_kernel.  Workgroups are numbered so that the tiles sharing an operand column run
 // on the same XCD (blocks go to the 8 XCDs round-robin) and meet in its L2.  Op: bf16 (two
 // 16x16x32 MFMAs per k-step) or fp8 (one 16x16x128 MFMA per k-step).
-// Workgroup barrier without a global-memory fence (a fence would wait for every outstanding
-// load, prefetches included).  It waits for this wave's LDS reads first, so no wave can start a
-// copy into a buffer another wave is still reading; the memory clobber keeps the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // The finished tile staged in LDS before the coalesced stores: rows 0..63 in one stage buffer,
 // 64..127 in another, LD elements per row.
@@ -545,27 +540,12 @@ template <typename T, int LD> struct TileRows {
   __device__ __forceinline__ T *row(int r) const { return (r < 64 ? lo : hi) + (r & 63) * LD; }
 };
 
-__device__ __forceinline__ unsigned lds_addr(const void *p) {
-  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-// global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes [lds + 16 l, lds + 16 l + 16)
-// (lds is wave-uniform, in M0).  Written as asm so that the compiler does not treat later LDS
-// reads of other buffers as waiting on it; the k-loop waits for these copies explicitly
-// (s_waitcnt vmcnt + barrier).  It has no output register: the data lands in LDS.
-__device__ __forceinline__ void dma16(const void *g, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-}
 
 // The k-step buffers, one LDS array per buffer and stage size, named statically by the k-step
 // code (only the ones a kernel uses are allocated).
 template <int SZ, int I> __shared__ __attribute__((aligned(1024))) char big_sb[SZ];
 template <int SZ, int B> __device__ __forceinline__ char *big_buf() {
   return B == 0 ? big_sb<SZ, 0> : (B == 1 ? big_sb<SZ, 1> : big_sb<SZ, 2>);
-}
-template <int N> __device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <typename Op, int BN, int NBUF, class Epi>

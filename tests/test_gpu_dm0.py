@@ -100,6 +100,26 @@ def test_suffix_denoise_b32_ragged_bf16():
     assert mx <= CHUNK_MAX and mean <= CHUNK_MEAN
 
 
+def test_suffix_denoise_b3_ragged_split_keys_bf16():
+    """Three samples of the batch-32 workload (shortest, longest, one between): few enough
+    workgroups that attention splits every sample's keys into chunks, so the shorter samples
+    have chunks past their keys and chunks straddling the prefix/action boundary."""
+    wl = workload(4)
+    lens_all = inputs.make_prefix_lens(wl)
+    pick = [int(np.argmin(lens_all)), int(np.argmax(lens_all)), 7]
+    lens = lens_all[pick]
+    print(f"case: suffix denoise bf16 B=3 ragged P={list(lens)} cap {wl.prefix_len}", flush=True)
+    aw = inputs.make_action_weights(wl)
+    kc, vc = inputs.make_kv_cache(wl)
+    x1 = inputs.make_noise(wl)
+    gpu = Gpu(wl, None, aw)
+    k, v = gpu.cache_to_device(kc[:, pick], vc[:, pick])
+    got = gpu.denoise(k, v, lens, x1[pick], wl.steps)
+    for i, b in enumerate(pick):
+        ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :lens[i]], vc[:, b, :, :lens[i]], wl.shape, wl.steps)
+        _chunk_ok(got[i], ref, f"config-4 sample {b} (P={lens[i]}) in a batch of 3")
+
+
 def test_prefill_then_denoise_bf16():
     wl = workload(5)
     print("case: 28-layer VLM prefill bf16 B=8 P=816, then suffix denoise", flush=True)
