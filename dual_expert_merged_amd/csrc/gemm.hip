@@ -21,7 +21,8 @@
 //  * big (bf16, larger M): 128 x 256 (or 128 x 128) per workgroup, double-buffered LDS.
 //  * tiled (fp32, larger M): a 64x64 output tile per workgroup, A and W staged through LDS.
 // Column permutations put the two halves of every RoPE pair, and the gate/up pair of every
-// SwiGLU column, in lanes l and l^8 of one MFMA tile, so one cross-lane exchange joins them.
+// SwiGLU column, in the same lane of two adjacent 16-column MFMA tiles, so each lane joins them
+// with no cross-lane exchange.
 #include <type_traits>
 
 #include "common.h"
