@@ -541,12 +541,16 @@ template <typename T, int LD> struct TileRows {
   __device__ __forceinline__ T *row(int r) const { return (r < 64 ? lo : hi) + (r & 63) * LD; }
 };
 
-
 // The k-step buffers, one LDS array per buffer and stage size, named statically by the k-step
 // code (only the ones a kernel uses are allocated).
 template <int SZ, int I> __shared__ __attribute__((aligned(1024))) char big_sb[SZ];
-template <int SZ, int B> __device__ __forceinline__ char *big_buf() {
-  return B == 0 ? big_sb<SZ, 0> : (B == 1 ? big_sb<SZ, 1> : big_sb<SZ, 2>);
+template <int SZ, int B> __device__ __forceinline__ char *big_buf() { return big_sb<SZ, B>; }
+
+template <int I, int N, class F> __device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 template <typename Op, int BN, int NBUF, class Epi>
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
   constexpr int ROWS = BM + BN;                 // LDS rows per stage (A then W)
   constexpr int LPW = ROWS * RB / 1024 / 4;     // 1 KB DMA instructions per wave per stage
   constexpr int STAGE = ROWS * RB;
-  static_assert(NBUF == 2 || NBUF == 3, "two or three k-step buffers");
+  static_assert(NBUF >= 2 && NBUF <= 4, "two to four k-step buffers");
   static_assert(NBUF * STAGE + BM * 4 <= 160 * 1024, "buffers fit the LDS");
   __shared__ float rinv[BM];
 
@@ -607,7 +611,10 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
   auto step = [&](auto curc, int kt) {
     constexpr int CB = decltype(curc)::value;
     const char *cur = big_buf<STAGE, CB>();
-    if (NBUF == 3 && kt + 1 < nkt) vm_wait<LPW>();  // the next step's copies may stay in flight
+    // the copies of the steps after kt (at most NBUF-2 of them) may stay in flight
+    const int after = min(NBUF - 2, nkt - 1 - kt);
+    if (NBUF >= 4 && after >= 2) vm_wait<(NBUF >= 4 ? 2 * LPW : 0)>();
+    else if (NBUF >= 3 && after >= 1) vm_wait<(NBUF >= 3 ? LPW : 0)>();
     else vm_wait<0>();
     wg_barrier();  // every wave's step kt has landed; step kt-1 is fully read
     if (kt + NBUF - 1 < nkt) dma(std::integral_constant<int, (CB + NBUF - 1) % NBUF>{}, kt + NBUF - 1);
@@ -647,28 +654,15 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
     }
   };
 
-  typedef std::integral_constant<int, 0> B0;
-  typedef std::integral_constant<int, 1> B1;
-  typedef std::integral_constant<int, 2> B2;
-  dma(B0{}, 0);
-  if (NBUF == 3 && nkt > 1) dma(B1{}, 1);
+  static_for<0, NBUF - 1>([&](auto I) {
+    if (I < nkt) dma(I, I);
+  });
   epi.prepare(m0, BM, rinv);  // its loads queue behind the first stages
   int kt = 0;
-  if constexpr (NBUF == 3) {
-    for (; kt + 3 <= nkt; kt += 3) {
-      step(B0{}, kt);
-      step(B1{}, kt + 1);
-      step(B2{}, kt + 2);
-    }
-    if (kt < nkt) step(B0{}, kt);
-    if (kt + 1 < nkt) step(B1{}, kt + 1);
-  } else {
-    for (; kt + 2 <= nkt; kt += 2) {
-      step(B0{}, kt);
-      step(B1{}, kt + 1);
-    }
-    if (kt < nkt) step(B0{}, kt);
-  }
+  for (; kt + NBUF <= nkt; kt += NBUF) static_for<0, NBUF>([&](auto I) { step(I, kt + I); });
+  static_for<0, NBUF - 1>([&](auto I) {
+    if (kt + I < nkt) step(I, kt + I);
+  });
   __syncthreads();  // rinv (written by epi.prepare) visible; every stage read is done
 
   if (sk.k_split > 1) {  // partial sums [split][M][N], row-major; resid_reduce_kernel finishes
@@ -690,17 +684,23 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
       constexpr int LD = BN + 8;
       static_assert(64 * LD * 2 <= STAGE, "half a tile fits in one stage buffer");
       const TileRows<bf16, LD> ot{reinterpret_cast<bf16 *>(big_buf<STAGE, 0>()), reinterpret_cast<bf16 *>(big_buf<STAGE, 1>())};
+      // the epilogue's loads of row tile i+1 go out before row tile i is processed, so only the
+      // first ones are waited for
+      typename Epi::St st[2][TN];
+      auto load_row_tile = [&](int i, typename Epi::St(&dst)[TN]) {
+        const RowInfo ri = row_info(epi.rows(), m0 + wm * 64 + i * 16 + 4 * g, M);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) dst[j] = epi.load(ri, n0 + wn * (BN / 2) + j * 16 + c16);
+      };
+      load_row_tile(0, st[0]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if (i + 1 < 4) load_row_tile(i + 1, st[(i + 1) & 1]);
         const int row0 = m0 + wm * 64 + i * 16 + 4 * g;
-        const RowInfo ri = row_info(epi.rows(), row0, M);
-        typename Epi::St st[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) st[j] = epi.load(ri, n0 + wn * (BN / 2) + j * 16 + c16);
 #pragma unroll
         for (int j = 0; j < TN; j += 2)
-          epi.to_lds2(st[j], st[j + 1], row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], acc[i][j + 1], rinv, m0, n0,
-                      ot);
+          epi.to_lds2(st[i & 1][j], st[i & 1][j + 1], row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], acc[i][j + 1],
+                      rinv, m0, n0, ot);
       }
       __syncthreads();
       epi.template lds_out<BM, BN>(ot, m0, n0, M);
