@@ -92,7 +92,7 @@ void attn_split(int B, int Hkv, int nqb, int max_keys, int *n_chunks, int *chunk
   const int blocks = B * Hkv * nqb;
   int want = (256 + blocks - 1) / blocks;
   if (want > 16) want = 16;  // the merge keeps every chunk's statistics in registers
-  const int maxc = (max_keys + 127) / 128;
+  const int maxc = (max_keys + 63) / 64;  // at least one 64-key tile per chunk
   if (want > maxc) want = maxc;
   if (want < 1) want = 1;
   int ck = (max_keys + want - 1) / want;

@@ -171,7 +171,8 @@ template <typename T> struct EpiQkv {
     if ((c >> 4) & 1) return st;  // uniform per tile
     const int i = col(c) & ((a.D >> 1) - 1);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)  // also read for value columns (unused there)
+    for (int r = 0; r < 4; ++r)  // also read for value columns (unused there): a branch here
+      // would make the compiler wait for each load where it is issued
       st.cs[r] = a.rows.is_prefix ? a.rope[(size_t)ri.s[r] * (a.D >> 1) + i] : a.rope_rows[(size_t)ri.rc[r] * (a.D >> 1) + i];
     return st;
   }
