@@ -140,6 +140,9 @@ GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
   p.skinny = 1;
   p.nt = nt;
   p.sk.k_split = ks;
+  // half-height workgroups when twice as many still fit the 256 CUs in one round: each reads
+  // half the activation rows, and twice the CUs pull the weights (QKV at batch 1: 9.2 -> 7.5 us)
+  if (M > 32 && (size_t)(N / nt) * ks * ((M + 31) / 32) <= 256) p.rt = 2;
   return p;
 }
 

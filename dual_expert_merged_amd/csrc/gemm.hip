@@ -380,28 +380,31 @@ template <typename T, typename W = T> struct EpiSwiglu {
 // ------------------------------------------------------------------------ skinny kernel (M <= 64)
 // NK: MFMA k-chunks per wave; every fragment of the workgroup's slice is loaded before the first
 // MFMA, so each wave keeps NK*(CT+4) 16-byte loads per lane in flight.
-template <typename T, int NT, int NK, class Epi>
+// RT: 16-row tiles per workgroup (4, or 2 to spread a narrow GEMM over twice the workgroups,
+// each reading half the activation rows).
+template <typename T, int NT, int NK, int RT, class Epi>
 __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, int M, int K, Epi epi, SplitK sk) {
   typedef Mfma<T> MF;
   typedef typename MF::frag frag;
   constexpr int EPL = MF::EPL, KC = 4 * EPL, CT = NT / 16;
-  __shared__ __attribute__((aligned(16))) f32x4 red[4 * 4 * CT * 64];
+  static_assert(RT == 2 || RT == 4, "2 or 4 row tiles");
+  __shared__ __attribute__((aligned(16))) f32x4 red[4 * RT * CT * 64];
   __shared__ float rinv[64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int tile = blockIdx.x, split = blockIdx.y, mt = blockIdx.z, m0 = mt * 64;
+  const int tile = blockIdx.x, split = blockIdx.y, mt = blockIdx.z, m0 = mt * (16 * RT);
   const int n0 = tile * NT;
   const int Ks = K / sk.k_split;
   const int k0 = split * Ks + wave * (Ks >> 2);
-  const int nrt = min(4, (M - m0 + 15) >> 4);  // row tiles holding valid rows (uniform)
+  const int nrt = min(RT, (M - m0 + 15) >> 4);  // row tiles holding valid rows (uniform)
 
   const T *wp[CT];
 #pragma unroll
   for (int j = 0; j < CT; ++j) wp[j] = epi.wrow(n0 + j * 16 + c16) + k0 + g * EPL;
-  const T *ap[4];
+  const T *ap[RT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ap[i] = A + (size_t)min(m0 + i * 16 + c16, M - 1) * K + k0 + g * EPL;
+  for (int i = 0; i < RT; ++i) ap[i] = A + (size_t)min(m0 + i * 16 + c16, M - 1) * K + k0 + g * EPL;
 
   // The small loads go first (norm statistics, row facts, RoPE / residual rows): loads complete
   // in issue order, so their consumers run while the operand loads below are still in flight.
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
 #pragma unroll
   for (int j = 0; j < CT; ++j) st[j] = epi.load(ri, n0 + j * 16 + c16);
 
-  frag wf[NK][CT], af[NK][4];
+  frag wf[NK][CT], af[NK][RT];
 #pragma unroll
   for (int u = 0; u < NK; ++u)
 #pragma unroll
@@ -422,34 +425,36 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
 #pragma unroll
   for (int u = 0; u < NK; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[u][i] = load_frag<T>(ap[i] + u * KC);
+    for (int i = 0; i < RT; ++i) af[u][i] = load_frag<T>(ap[i] + u * KC);
 
   epi.pre_finish(pre, m0, rinv);
 
-  f32x4 acc[4][CT];
+  f32x4 acc[RT][CT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < CT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < NK; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RT; ++i)
       if (i < nrt)
 #pragma unroll
         for (int j = 0; j < CT; ++j) acc[i][j] = MF::mma(af[u][i], wf[u][j], acc[i][j]);
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int j = 0; j < CT; ++j) red[((wave * 4 + i) * CT + j) * 64 + lane] = acc[i][j];
+    for (int j = 0; j < CT; ++j) red[((wave * RT + i) * CT + j) * 64 + lane] = acc[i][j];
   __syncthreads();
+  // wave w sums row tile w over the 4 K quarters (waves past the row tiles sum nothing)
   f32x4 sum[CT];
+  const int rw = min(wave, RT - 1);
 #pragma unroll
   for (int j = 0; j < CT; ++j) {
-    f32x4 t = red[((0 * 4 + wave) * CT + j) * 64 + lane];
+    f32x4 t = red[((0 * RT + rw) * CT + j) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) t += red[((w * 4 + wave) * CT + j) * 64 + lane];
+    for (int w = 1; w < 4; ++w) t += red[((w * RT + rw) * CT + j) * 64 + lane];
     sum[j] = t;
   }
 
@@ -831,16 +836,21 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
                  n0 + wn * (BN / 2) + j * 16 + (lane & 15), acc[i][j], acc[i][j + 1], true, rinv, m0);
 }
 
-template <typename T, int NT, class Epi>
-static void run_skinny(const T *A, int M, int N, int K, const Epi &epi, const GemmPlan &p, hipStream_t s) {
-  dim3 grid(N / NT, p.sk.k_split, (M + 63) / 64);
+template <typename T, int NT, int RT, class Epi>
+static void run_skinny_rt(const T *A, int M, int N, int K, const Epi &epi, const GemmPlan &p, hipStream_t s) {
+  dim3 grid(N / NT, p.sk.k_split, (M + 16 * RT - 1) / (16 * RT));
   const int nk = K / p.sk.k_split / 4 / (4 * Mfma<T>::EPL);
   switch (nk) {
-#define DM_NK(n) case n: hipLaunchKernelGGL((skinny_kernel<T, NT, n, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk); break;
+#define DM_NK(n) case n: hipLaunchKernelGGL((skinny_kernel<T, NT, n, RT, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk); break;
     DM_NK(1) DM_NK(2) DM_NK(3) DM_NK(4) DM_NK(5) DM_NK(6) DM_NK(7) DM_NK(8)
 #undef DM_NK
     default: break;  // the host plan never asks for more than 8 k-chunks per wave
   }
+}
+template <typename T, int NT, class Epi>
+static void run_skinny(const T *A, int M, int N, int K, const Epi &epi, const GemmPlan &p, hipStream_t s) {
+  if (p.rt == 2) run_skinny_rt<T, NT, 2>(A, M, N, K, epi, p, s);
+  else run_skinny_rt<T, NT, 4>(A, M, N, K, epi, p, s);
 }
 
 template <typename T, class Epi>
