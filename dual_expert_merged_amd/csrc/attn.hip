@@ -11,9 +11,12 @@
 // 32 slots x 2 key halves: both waves of a pair see every LDS stage, each takes one half of every
 // 64-key tile with its own online softmax, and the pair merges (max, sum, output) through LDS at
 // the end.  Two waves per SIMD hide each other's LDS and MFMA latencies while every K/V byte is
-// still read from LDS only once per slot group.  Keys stage through LDS 128 at a time (K
-// row-major, V transposed), every load of a stage issued before the first is consumed, the next
-// stage loaded while the current one is multiplied.  Scores are formed transposed,
+// still read from LDS only once per slot group.  Two kernels share this work split:
+// attn_dma_kernel (bf16, head dim 128, the DM0 shapes; described at its definition) copies the
+// operands into LDS by DMA, several stages ahead; attn_kernel (other head dims, fp32) stages
+// keys through LDS 128 at a time (K row-major, V transposed) from registers, every load of a
+// stage issued before the first is consumed, the next stage loaded while the current one is
+// multiplied.  Scores are formed transposed,
 // S^T = K Q^T, so every lane owns one query column: the online-softmax statistics stay in-lane
 // (plus two cross-lane-group exchanges) and the probabilities already sit in the B-operand
 // layout of O^T = V^T P^T.  The key rows of each 16-key score tile are permuted so a lane's

@@ -11,14 +11,15 @@
 // per-16-column sums of squares; the consumer runs the GEMM on hg and multiplies each output row
 // by 1/sqrt(mean(h^2) + eps), which is RMSNorm(h) W^T up to the rounding of hg.
 //
-// Two kernels share the epilogues:
-//  * skinny (M <= 64, the batch-1 action chunk): one workgroup owns NT output columns for all
-//    rows and one K slice; its 4 waves each take a quarter of the slice and load MFMA fragments
+// Three kernels share the epilogues:
+//  * skinny (M <= 64, the batch-1 action chunk): one workgroup owns NT output columns for 64
+//    (or 32) rows and one K slice; its 4 waves each take a quarter of the slice and load MFMA fragments
 //    straight from global memory (16 bytes per lane, the whole slice in flight at once), then
 //    reduce through LDS.  Narrow-N GEMMs also split K across workgroups: each writes an fp32 partial
 //    tile and a second launch (resid_reduce_kernel) sums them in split order and runs the
 //    residual epilogue; the kernel boundary orders the two, so no device-scope fence is needed.
-//  * big (bf16, larger M): 128 x 256 (or 128 x 128) per workgroup, double-buffered LDS.
+//  * big (bf16 or FP8, larger M): 128 x 128, 128 x 256 or 128 x 384 per workgroup, operands
+//    copied global -> LDS with two (or one) k-steps in flight.
 //  * tiled (fp32, larger M): a 64x64 output tile per workgroup, A and W staged through LDS.
 // Column permutations put the two halves of every RoPE pair, and the gate/up pair of every
 // SwiGLU column, in the same lane of two adjacent 16-column MFMA tiles, so each lane joins them
@@ -526,14 +527,14 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
 }
 
 // ------------------------------------------------------------------------ big kernel (M > 64)
-// Workgroup tile 128 x BN (BN = 256 or 128); four waves as 2 x 2, each 64 x BN/2, i.e. 4 x BN/32
-// MFMA 16x16 tiles, so every LDS fragment read feeds several MFMAs.  Each k-step moves 128 bytes
-// of every row (64 bf16 or 128 FP8 codes).  Operands go from global memory straight into LDS
-// (global_load_lds_dwordx4: no registers, whole 128-byte lines per row), three k-steps in flight:
-// while step k is multiplied, steps k+1 and k+2 are loading.  The three stage buffers are
-// distinct LDS arrays and the k-loop is unrolled by three, so the compiler can tell that reading
-// one buffer does not wait for the loads into another, and it interleaves the fragment reads with
-// the MFMAs.  An LDS row holds its eight 16-byte chunks in XOR-swizzled order (chunk c at
+// Workgroup tile 128 x BN (BN = 128, 256 or 384); four waves as 2 x 2, each 64 x BN/2, i.e.
+// 4 x BN/32 MFMA 16x16 tiles, so every LDS fragment read feeds several MFMAs.  Each k-step moves
+// 128 bytes of every row (64 bf16 or 128 FP8 codes).  Operands go from global memory straight
+// into LDS (global_load_lds_dwordx4: no registers, whole 128-byte lines per row) through NBUF
+// stage buffers (3, or 2 for the 384-wide tile): while step k is multiplied, the next NBUF-1
+// steps are loading.  The stage buffers are distinct LDS arrays and the k-loop is unrolled by
+// NBUF, so the compiler can tell that reading one buffer does not wait for the loads into
+// another, and it interleaves the fragment reads with the MFMAs.  An LDS row holds its eight 16-byte chunks in XOR-swizzled order (chunk c at
 // position c ^ (row & 7)), so the 16 rows of a fragment read spread over all banks.  grid.z
 // splits K (the narrow residual projections), each split writing fp32 partial sums for
 // resid_reduce_kernel.  Workgroups are numbered so that the tiles sharing an operand column run
