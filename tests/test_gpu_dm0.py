@@ -120,6 +120,26 @@ def test_suffix_denoise_b3_ragged_split_keys_bf16():
         _chunk_ok(got[i], ref, f"config-4 sample {b} (P={lens[i]}) in a batch of 3")
 
 
+def test_suffix_denoise_empty_and_longest_prefix_bf16():
+    """Batch of two at the DM0 shapes: one sample with no prefix token (its queries see the 50
+    action keys only; every later key chunk of it is empty) and one with the longest prefix."""
+    wl = workload(4)
+    lens_all = inputs.make_prefix_lens(wl)
+    b_long = int(np.argmax(lens_all))
+    pick = [0, b_long]
+    lens = np.array([0, lens_all[b_long]], dtype=lens_all.dtype)
+    print(f"case: suffix denoise bf16 B=2 P={[int(p) for p in lens]} cap {wl.prefix_len}", flush=True)
+    aw = inputs.make_action_weights(wl)
+    kc, vc = inputs.make_kv_cache(wl)
+    x1 = inputs.make_noise(wl)
+    gpu = Gpu(wl, None, aw)
+    k, v = gpu.cache_to_device(kc[:, pick], vc[:, pick])
+    got = gpu.denoise(k, v, lens, x1[pick], wl.steps)
+    for i, b in enumerate(pick):
+        ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :lens[i]], vc[:, b, :, :lens[i]], wl.shape, wl.steps)
+        _chunk_ok(got[i], ref, f"config-4 sample {b} with P={lens[i]}")
+
+
 def test_prefill_then_denoise_bf16():
     wl = workload(5)
     print("case: 28-layer VLM prefill bf16 B=8 P=816, then suffix denoise", flush=True)

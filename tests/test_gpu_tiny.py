@@ -171,6 +171,26 @@ def test_ragged_denoise_and_batch_invariance(cfg1):
         np.testing.assert_allclose(alone[0], got[b], rtol=0, atol=1e-5)
 
 
+def test_empty_prefix_in_ragged_batch(cfg1):
+    """Samples with no prefix token (P_b = 0) attend to the action chunk only; a batch mixing
+    them with full prefixes matches the oracle per sample."""
+    wl, vlm, aw, gpu = cfg1
+    s = wl.shape
+    lens = [0, 64, 0, 5]
+    print(f"case: ragged denoise with empty prefixes lens={lens}", flush=True)
+    B, P_cap = len(lens), 64
+    rng = np.random.default_rng(105)
+    L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
+    kc = rng.standard_normal((L, B, Hkv, P_cap, D)).astype(np.float32)  # rows past P_b are never read
+    vc = rng.standard_normal((L, B, Hkv, P_cap, D)).astype(np.float32)
+    x1 = rng.standard_normal((B, s.chunk, s.action_dim)).astype(np.float32)
+    k, v = gpu.cache_to_device(kc, vc)
+    got = gpu.denoise(k, v, lens, x1, 3)
+    for b, P in enumerate(lens):
+        ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :P], vc[:, b, :, :P], s, 3)
+        assert rel_inf(got[b], ref) <= TOL, (b, rel_inf(got[b], ref))
+
+
 def test_constant_velocity_closed_form(cfg1):
     """W_out = 0, b_out = c: v = c whatever the layers compute, so x_0 = x_1 - c."""
     wl, vlm, aw, gpu = cfg1
