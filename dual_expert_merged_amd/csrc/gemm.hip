@@ -38,7 +38,8 @@ namespace dm {
 __device__ __forceinline__ void rms_prepare(const Hidden &in, int M, float eps, int m0, int rows, float *inv,
                                             const float *row_scale = nullptr) {
   const int nt = in.H >> 4;
-  for (int base = 0; base < rows; base += 64) {
+  const int step = blockDim.x >> 2;  // rows per pass
+  for (int base = 0; base < rows; base += step) {
     const int t = threadIdx.x, row = base + (t >> 2), part = t & 3;
     const float *p = in.ssq + (size_t)min(m0 + row, M - 1) * nt;
     float s = 0.f;
@@ -56,7 +57,7 @@ __device__ __forceinline__ void rms_prepare(const Hidden &in, int M, float eps, 
     }
     s = sum4(s);
     const float rs = row_scale ? row_scale[min(m0 + row, M - 1)] : 1.0f;
-    if (part == 0) inv[row] = rsqrtf(s / (float)in.H + eps) * rs;
+    if (part == 0 && row < rows) inv[row] = rsqrtf(s / (float)in.H + eps) * rs;
   }
 }
 
@@ -214,7 +215,7 @@ template <typename T> struct EpiQkv {
     const int head0 = (gc0 - (sec == 0 ? 0 : (sec == 1 ? qd : qd + kd))) >> dlog();
     const RowMap &rm = a.rows;
 #pragma unroll 4
-    for (int idx = threadIdx.x; idx < BM * CPR; idx += 256) {
+    for (int idx = threadIdx.x; idx < BM * CPR; idx += blockDim.x) {
       const int rl = idx / CPR, ch = idx - rl * CPR, row = m0 + rl;
       if (row >= M) continue;
       const int b = row / rm.rows_per_b, s = row - b * rm.rows_per_b;
@@ -355,7 +356,7 @@ template <typename T, typename W = T> struct EpiSwiglu {
     constexpr int CPR = BN / 16;  // 16-byte chunks of activation per row
     const RowMap &rm = a.rows;
 #pragma unroll 4
-    for (int idx = threadIdx.x; idx < BM * CPR; idx += 256) {
+    for (int idx = threadIdx.x; idx < BM * CPR; idx += blockDim.x) {
       const int rl = idx / CPR, ch = idx - rl * CPR, row = m0 + rl;
       if (row >= M) continue;
       if (rm.is_prefix) {
@@ -527,8 +528,10 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
 }
 
 // ------------------------------------------------------------------------ big kernel (M > 64)
-// Workgroup tile 128 x BN (BN = 128, 256 or 384); four waves as 2 x 2, each 64 x BN/2, i.e.
-// 4 x BN/32 MFMA 16x16 tiles, so every LDS fragment read feeds several MFMAs.  Each k-step moves
+// Workgroup tile 128 x BN (BN = 128, 256 or 384); eight waves as 2 x 4, each 64 x BN/4, i.e.
+// 4 x BN/64 MFMA 16x16 tiles, so every LDS fragment read feeds several MFMAs, and two waves per
+// SIMD (one LDS-bound workgroup per CU) hide each other's LDS and barrier waits (4 waves of
+// 64 x BN/2: 13-14 % slower at the batch-32 shapes).  Each k-step moves
 // 128 bytes of every row (64 bf16 or 128 FP8 codes).  Operands go from global memory straight
 // into LDS (global_load_lds_dwordx4: no registers, whole 128-byte lines per row) through NBUF
 // stage buffers (3, or 2 for the 384-wide tile): while step k is multiplied, the next NBUF-1
@@ -560,15 +563,17 @@ template <int I, int N, class F> __device__ __forceinline__ void static_for(F &&
   }
 }
 
-template <typename Op, int BN, int NBUF, class Epi>
-__global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int M, int K, Epi epi, SplitK sk, int n_tiles,
+// NW: 4 waves (2 x 2, each 64 x BN/2) or 8 (2 x 4, each 64 x BN/4: two waves per SIMD)
+template <typename Op, int BN, int NBUF, int NW, class Epi>
+__global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, int M, int K, Epi epi, SplitK sk, int n_tiles,
                                                   int m_tiles) {
   constexpr int EB = sizeof(Op);       // bytes per element
   constexpr int BM = 128, RB = 128;    // rows of A per tile, bytes per row per k-step
   constexpr int BK = RB / EB, VE = 16 / EB;
-  constexpr int TN = BN / 32;
+  constexpr int WN = NW / 2, TN = BN / (16 * WN);  // waves along N, 16-column tiles per wave
   constexpr int ROWS = BM + BN;                 // LDS rows per stage (A then W)
-  constexpr int LPW = ROWS * RB / 1024 / 4;     // 1 KB DMA instructions per wave per stage
+  constexpr int LPW = ROWS * RB / 1024 / NW;    // 1 KB DMA instructions per wave per stage
+  static_assert(TN % 2 == 0 && LPW * NW * 1024 == ROWS * RB, "wave tiling");
   constexpr int STAGE = ROWS * RB;
   static_assert(NBUF >= 2 && NBUF <= 4, "two to four k-step buffers");
   static_assert(NBUF * STAGE + BM * 4 <= 160 * 1024, "buffers fit the LDS");
@@ -576,7 +581,7 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   // XCD-aware tile order: the blocks on one XCD (b % 8) take a contiguous run of (split, n, m)
   const int T = n_tiles * m_tiles * (int)gridDim.z;
   const int b = blockIdx.x + (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x;
@@ -608,10 +613,10 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment rows of this wave: A rows wm*64 + i*16 + c16, W rows BM + wn*BN/2 + j*16 + c16;
+  // fragment rows of this wave: A rows wm*64 + i*16 + c16, W rows BM + wn*BN/WN + j*16 + c16;
   // (row & 7) == (c16 & 7) for all of them
   const int sw = c16 & 7;
-  const int arow = (wm * 64 + c16) * RB, wrow = (BM + wn * (BN / 2) + c16) * RB;
+  const int arow = (wm * 64 + c16) * RB, wrow = (BM + wn * (BN / WN) + c16) * RB;
 
   // one k-step: wait for its loads, start the loads NBUF-1 steps ahead into the buffer read in
   // the previous step, multiply
@@ -681,7 +686,7 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = m0 + wm * 64 + i * 16 + 4 * g + r;
-          if (row < M) sk.part[((size_t)split * M + row) * N + n0 + wn * (BN / 2) + j * 16 + c16] = acc[i][j][r];
+          if (row < M) sk.part[((size_t)split * M + row) * N + n0 + wn * (BN / WN) + j * 16 + c16] = acc[i][j][r];
         }
     return;
   }
@@ -697,7 +702,7 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
       auto load_row_tile = [&](int i, typename Epi::St(&dst)[TN]) {
         const RowInfo ri = row_info(epi.rows(), m0 + wm * 64 + i * 16 + 4 * g, M);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) dst[j] = epi.load(ri, n0 + wn * (BN / 2) + j * 16 + c16);
+        for (int j = 0; j < TN; ++j) dst[j] = epi.load(ri, n0 + wn * (BN / WN) + j * 16 + c16);
       };
       load_row_tile(0, st[0]);
 #pragma unroll
@@ -706,7 +711,7 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
         const int row0 = m0 + wm * 64 + i * 16 + 4 * g;
 #pragma unroll
         for (int j = 0; j < TN; j += 2)
-          epi.to_lds2(st[i & 1][j], st[i & 1][j + 1], row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], acc[i][j + 1],
+          epi.to_lds2(st[i & 1][j], st[i & 1][j + 1], row0, n0 + wn * (BN / WN) + j * 16 + c16, acc[i][j], acc[i][j + 1],
                       rinv, m0, n0, ot);
       }
       __syncthreads();
@@ -721,10 +726,10 @@ __global__ __launch_bounds__(256) void big_kernel(const Op *__restrict__ A, int 
     const RowInfo ri = row_info(epi.rows(), row0, M);
     typename Epi::St st[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) st[j] = epi.load(ri, n0 + wn * (BN / 2) + j * 16 + c16);
+    for (int j = 0; j < TN; ++j) st[j] = epi.load(ri, n0 + wn * (BN / WN) + j * 16 + c16);
 #pragma unroll
     for (int j = 0; j < TN; j += 2)
-      epi.store2(st[j], st[j + 1], ri, row0, n0 + wn * (BN / 2) + j * 16 + c16, acc[i][j], acc[i][j + 1], true, rinv, m0);
+      epi.store2(st[j], st[j + 1], ri, row0, n0 + wn * (BN / WN) + j * 16 + c16, acc[i][j], acc[i][j + 1], true, rinv, m0);
   }
 }
 
@@ -734,12 +739,13 @@ template <typename Op, class Epi>
 static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, const SplitK &sk, hipStream_t s) {
   const int nN = N / nt, nM = (M + 127) / 128;
   dim3 grid(nN, nM, sk.k_split);
+  constexpr int NW = 8;  // two waves per SIMD: one multiplies while the other waits on LDS
   if (nt == 384)
-    hipLaunchKernelGGL((big_kernel<Op, 384, 2, Epi>), grid, dim3(256), 0, s, A, M, K, epi, sk, nN, nM);
+    hipLaunchKernelGGL((big_kernel<Op, 384, 2, NW, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
   else if (nt == 256)
-    hipLaunchKernelGGL((big_kernel<Op, 256, 3, Epi>), grid, dim3(256), 0, s, A, M, K, epi, sk, nN, nM);
+    hipLaunchKernelGGL((big_kernel<Op, 256, 3, NW, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
   else
-    hipLaunchKernelGGL((big_kernel<Op, 128, 3, Epi>), grid, dim3(256), 0, s, A, M, K, epi, sk, nN, nM);
+    hipLaunchKernelGGL((big_kernel<Op, 128, 3, NW, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
 }
 
 // ------------------------------------------------------------------------ tiled kernel (any M)
