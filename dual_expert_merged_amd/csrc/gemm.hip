@@ -528,10 +528,10 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
 }
 
 // ------------------------------------------------------------------------ big kernel (M > 64)
-// Workgroup tile 128 x BN (BN = 128, 256 or 384); eight waves as 2 x 4, each 64 x BN/4, i.e.
-// 4 x BN/64 MFMA 16x16 tiles, so every LDS fragment read feeds several MFMAs, and two waves per
-// SIMD (one LDS-bound workgroup per CU) hide each other's LDS and barrier waits (4 waves of
-// 64 x BN/2: 13-14 % slower at the batch-32 shapes).  Each k-step moves
+// Workgroup tile 128 x BN (BN = 128, 256 or 384); NW waves as WM x WN (8 as 2 x 4), each
+// (128/WM) x (BN/WN), i.e. several MFMA 16x16 tiles, so every LDS fragment read feeds several
+// MFMAs, and several waves per SIMD (one LDS-bound workgroup per CU) hide each other's LDS and
+// barrier waits.  Each k-step moves
 // 128 bytes of every row (64 bf16 or 128 FP8 codes).  Operands go from global memory straight
 // into LDS (global_load_lds_dwordx4: no registers, whole 128-byte lines per row) through NBUF
 // stage buffers (3, or 2 for the 384-wide tile): while step k is multiplied, the next NBUF-1
@@ -563,14 +563,15 @@ template <int I, int N, class F> __device__ __forceinline__ void static_for(F &&
   }
 }
 
-// NW: 4 waves (2 x 2, each 64 x BN/2) or 8 (2 x 4, each 64 x BN/4: two waves per SIMD)
-template <typename Op, int BN, int NBUF, int NW, class Epi>
+// NW waves as WM x (NW / WM), each (128 / WM) x (BN * WM / NW)
+template <typename Op, int BN, int NBUF, int NW, int WM, class Epi>
 __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, int M, int K, Epi epi, SplitK sk, int n_tiles,
                                                   int m_tiles) {
   constexpr int EB = sizeof(Op);       // bytes per element
   constexpr int BM = 128, RB = 128;    // rows of A per tile, bytes per row per k-step
   constexpr int BK = RB / EB, VE = 16 / EB;
-  constexpr int WN = NW / 2, TN = BN / (16 * WN);  // waves along N, 16-column tiles per wave
+  constexpr int WN = NW / WM, TN = BN / (16 * WN);  // waves along N, 16-column tiles per wave
+  constexpr int TM = BM / (16 * WM);                // 16-row tiles per wave
   constexpr int ROWS = BM + BN;                 // LDS rows per stage (A then W)
   constexpr int LPW = ROWS * RB / 1024 / NW;    // 1 KB DMA instructions per wave per stage
   static_assert(TN % 2 == 0 && LPW * NW * 1024 == ROWS * RB, "wave tiling");
@@ -607,16 +608,16 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
     for (int i = 0; i < LPW; ++i) dma16(src[i] + kt * BK, dst + i * 1024);
   };
 
-  f32x4 acc[4][TN];
+  f32x4 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // fragment rows of this wave: A rows wm*64 + i*16 + c16, W rows BM + wn*BN/WN + j*16 + c16;
   // (row & 7) == (c16 & 7) for all of them
   const int sw = c16 & 7;
-  const int arow = (wm * 64 + c16) * RB, wrow = (BM + wn * (BN / WN) + c16) * RB;
+  const int arow = (wm * (BM / WM) + c16) * RB, wrow = (BM + wn * (BN / WN) + c16) * RB;
 
   // one k-step: wait for its loads, start the loads NBUF-1 steps ahead into the buffer read in
   // the previous step, multiply
@@ -634,21 +635,21 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         const int pos = ((kc * 4 + g) ^ sw) * 16;
-        bf16x8 fa[4], fb[TN];
+        bf16x8 fa[TM], fb[TN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(cur + arow + i * 16 * RB + pos);
+        for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(cur + arow + i * 16 * RB + pos);
 #pragma unroll
         for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const bf16x8 *>(cur + wrow + j * 16 * RB + pos);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<bf16>::mma(fa[i], fb[j], acc[i][j]);
       }
     } else {
       const int p0 = ((2 * g) ^ sw) * 16, p1 = ((2 * g + 1) ^ sw) * 16;
-      i32x8 fa[4], fb[TN];
+      i32x8 fa[TM], fb[TN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < TM; ++i) {
         const i32x4 lo = *reinterpret_cast<const i32x4 *>(cur + arow + i * 16 * RB + p0);
         const i32x4 hi = *reinterpret_cast<const i32x4 *>(cur + arow + i * 16 * RB + p1);
         fa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -660,7 +661,7 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
         fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = Mfma8::mma(fa[i], fb[j], acc[i][j]);
     }
@@ -680,12 +681,12 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
   if (sk.k_split > 1) {  // partial sums [split][M][N], row-major; resid_reduce_kernel finishes
     const int N = n_tiles * BN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = m0 + wm * 64 + i * 16 + 4 * g + r;
+          const int row = m0 + wm * (BM / WM) + i * 16 + 4 * g + r;
           if (row < M) sk.part[((size_t)split * M + row) * N + n0 + wn * (BN / WN) + j * 16 + c16] = acc[i][j][r];
         }
     return;
@@ -700,15 +701,15 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
       // first ones are waited for
       typename Epi::St st[2][TN];
       auto load_row_tile = [&](int i, typename Epi::St(&dst)[TN]) {
-        const RowInfo ri = row_info(epi.rows(), m0 + wm * 64 + i * 16 + 4 * g, M);
+        const RowInfo ri = row_info(epi.rows(), m0 + wm * (BM / WM) + i * 16 + 4 * g, M);
 #pragma unroll
         for (int j = 0; j < TN; ++j) dst[j] = epi.load(ri, n0 + wn * (BN / WN) + j * 16 + c16);
       };
       load_row_tile(0, st[0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i + 1 < 4) load_row_tile(i + 1, st[(i + 1) & 1]);
-        const int row0 = m0 + wm * 64 + i * 16 + 4 * g;
+      for (int i = 0; i < TM; ++i) {
+        if (i + 1 < TM) load_row_tile(i + 1, st[(i + 1) & 1]);
+        const int row0 = m0 + wm * (BM / WM) + i * 16 + 4 * g;
 #pragma unroll
         for (int j = 0; j < TN; j += 2)
           epi.to_lds2(st[i & 1][j], st[i & 1][j + 1], row0, n0 + wn * (BN / WN) + j * 16 + c16, acc[i][j], acc[i][j + 1],
@@ -720,8 +721,8 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row0 = m0 + wm * 64 + i * 16 + 4 * g;
+  for (int i = 0; i < TM; ++i) {
+    const int row0 = m0 + wm * (BM / WM) + i * 16 + 4 * g;
     if (row0 - 4 * g >= M) break;  // uniform over the wave: the whole 16-row tile is past M
     const RowInfo ri = row_info(epi.rows(), row0, M);
     typename Epi::St st[TN];
@@ -739,13 +740,16 @@ template <typename Op, class Epi>
 static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, const SplitK &sk, hipStream_t s) {
   const int nN = N / nt, nM = (M + 127) / 128;
   dim3 grid(nN, nM, sk.k_split);
-  constexpr int NW = 8;  // two waves per SIMD: one multiplies while the other waits on LDS
+  // 8 waves as 2 x 4 (two per SIMD: while one waits on LDS or the barrier, the other
+  // multiplies).  Measured: 4 waves (2 x 2) 13-14 % slower at the batch-32 shapes; 16 waves
+  // (4 x 4, 128 registers per lane) no faster there and the FP8 prefill 1.8 x slower.
+  constexpr int NW = 8, WM = 2;
   if (nt == 384)
-    hipLaunchKernelGGL((big_kernel<Op, 384, 2, NW, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
+    hipLaunchKernelGGL((big_kernel<Op, 384, 2, NW, WM, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
   else if (nt == 256)
-    hipLaunchKernelGGL((big_kernel<Op, 256, 3, NW, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
+    hipLaunchKernelGGL((big_kernel<Op, 256, 3, NW, WM, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
   else
-    hipLaunchKernelGGL((big_kernel<Op, 128, 3, NW, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
+    hipLaunchKernelGGL((big_kernel<Op, 128, 3, NW, WM, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
 }
 
 // ------------------------------------------------------------------------ tiled kernel (any M)
