@@ -90,8 +90,8 @@ __device__ __forceinline__ float to_f32(bf16 x) {
 }
 
 // --------------------------------------------------------------------------- cross-lane
-// Lane exchanges: DPP within 16-lane rows (no LDS crossbar), ds_swizzle / ds_bpermute across
-// rows.  A row is lanes 16r..16r+15.
+// Lane exchanges: DPP within 16-lane rows (no LDS crossbar), gfx950 permlane swaps across rows.
+// A row is lanes 16r..16r+15.
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
@@ -99,11 +99,7 @@ constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within each 8 lanes
 constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within each row
-constexpr int DPP_ROR8 = 0x128;        // lane i <- lane (i+8) mod 16: the same as i^8
 
-__device__ __forceinline__ float lane_xor8(float v) { return dpp<DPP_ROR8>(v); }
-// Across rows: lane l^16 through ds_swizzle (swap of the 16-lane halves of each 32 lanes), lane
-// l^32 through ds_bpermute.
 // Reductions over lane pairs (l, l^16) and (l, l^32) with gfx950's v_permlane16/32_swap: given
 // the same register twice, the two results hold v[l] and v[l^16] (resp. l^32) in some order, so
 // their sum or max is the pair's, bitwise identical in both lanes; no LDS round trip.

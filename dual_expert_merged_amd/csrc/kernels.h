@@ -107,7 +107,6 @@ void launch_rope_table(float2 *table, int n_pos, int D, float base, hipStream_t 
 // out[b*S + s][i] = table[min(max(lens[b], 0), cap) + s][i]: the RoPE rows of the action tokens.
 void launch_rope_rows(const float2 *table, const int32_t *lens, int cap, int B, int S, int D, float2 *out,
                       hipStream_t s);
-void launch_zero_u32(unsigned *p, size_t n, hipStream_t s);
 // h = src (if src != h), hg = h * gain, ssq per 16 columns: the entry into the first sublayer.
 void launch_norm_prep(Dt dt, const float *src, const Hidden &hid, const float *gain, int M, hipStream_t s);
 // h = x w_in^T + b_in + tau(t), then hg / ssq for the first layer's attention norm.

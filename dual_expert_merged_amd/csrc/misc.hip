@@ -40,16 +40,6 @@ void launch_rope_rows(const float2 *table, const int32_t *lens, int cap, int B, 
   hipLaunchKernelGGL(rope_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, table, lens, cap, S, D / 2, n, out);
 }
 
-__global__ void zero_u32_kernel(unsigned *p, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
-}
-void launch_zero_u32(unsigned *p, size_t n, hipStream_t s) {
-  if (n == 0) return;
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
-}
-
 // Writes 8 consecutive columns c0..c0+7 of row m: h (if a source is given), hg = h*gain and,
 // with the neighbouring lane (c0 ^ 8), the sum of squares of the 16-column group.
 template <typename T>
