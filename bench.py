@@ -142,7 +142,7 @@ def traffic_summary(args):
     per_chunk = (fetch * 1024.0 * f_scale + write * 1024.0 * w_scale) / chunks
     with open(traffic_file(args.config), "w") as f:
         f.write(f"# HBM traffic of one denoise chunk ({wl.name}), rocprofv3 counters\n")
-        f.write("# commands (run from the repository root on the GPU box, each pass its own run):\n")
+        f.write("# commands (run from the repository root on the MI355X host, each pass its own run):\n")
         f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -- python3 bench.py "
                 f"--config {args.config} --steps 2 --warmup 0 --no-cpu-baseline\n")
         f.write("#   rocprofv3 --pmc WRITE_SIZE ... (same)\n")

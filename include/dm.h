@@ -61,7 +61,7 @@ typedef enum {
   DM_OK = 0,
   DM_ERR_INVALID_ARG = -1,   /* null pointer, misaligned pointer, bad enum, non-positive size */
   DM_ERR_SHAPE = -2,         /* sizes inconsistent with the config or outside supported range */
-  DM_ERR_UNSUPPORTED = -3,   /* valid request this build does not implement */
+  DM_ERR_UNSUPPORTED = -3,   /* valid request this library does not implement */
   DM_ERR_WORKSPACE = -4,     /* ws too small (see dm_workspace_bytes) */
   DM_ERR_PLAN_MISMATCH = -5, /* launch differs from what the plan captured */
   DM_ERR_HIP = -6            /* a HIP runtime call failed; message in dm_last_error() */
