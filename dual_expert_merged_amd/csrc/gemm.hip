@@ -93,7 +93,7 @@ __device__ __forceinline__ void rms_finish(const RmsPre &p, const Hidden &in, in
   }
   s = sum4(s);
   const float rs = row_scale ? row_scale[min(m0 + row, M - 1)] : 1.0f;
-  if (part == 0) inv[row] = rsqrtf(s / (float)in.H + eps) * rs;
+  if (part == 0 && row < 64) inv[row] = rsqrtf(s / (float)in.H + eps) * rs;
 }
 
 // Epilogues run per 16x16 tile in two phases so that their global loads (RoPE table, residual
@@ -381,16 +381,18 @@ template <typename T, typename W = T> struct EpiSwiglu {
 
 // ------------------------------------------------------------------------ skinny kernel (M <= 64)
 // NK: MFMA k-chunks per wave; every fragment of the workgroup's slice is loaded before the first
-// MFMA, so each wave keeps NK*(CT+4) 16-byte loads per lane in flight.
-// RT: 16-row tiles per workgroup (4, or 2 to spread a narrow GEMM over twice the workgroups,
-// each reading half the activation rows).
-template <typename T, int NT, int NK, int RT, class Epi>
-__global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, int M, int K, Epi epi, SplitK sk) {
+// MFMA, so each wave keeps NK*(CT+RT) 16-byte loads per lane in flight.
+// RT: 16-row tiles per workgroup (4, or 2 / 1 to spread a narrow GEMM over more workgroups,
+// each reading fewer activation rows).
+// NWV: waves per workgroup, each taking 1/NWV of the K slice (4; 16 lets one workgroup cover a
+// residual projection's whole K with all its loads in flight, so no split and no second launch).
+template <typename T, int NT, int NK, int RT, int NWV, class Epi>
+__global__ __launch_bounds__(NWV * 64) void skinny_kernel(const T *__restrict__ A, int M, int K, Epi epi, SplitK sk) {
   typedef Mfma<T> MF;
   typedef typename MF::frag frag;
   constexpr int EPL = MF::EPL, KC = 4 * EPL, CT = NT / 16;
-  static_assert(RT == 2 || RT == 4, "2 or 4 row tiles");
-  __shared__ __attribute__((aligned(16))) f32x4 red[4 * RT * CT * 64];
+  static_assert(RT == 1 || RT == 2 || RT == 4, "1, 2 or 4 row tiles");
+  __shared__ __attribute__((aligned(16))) f32x4 red[NWV * RT * CT * 64];
   __shared__ float rinv[64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
   const int tile = blockIdx.x, split = blockIdx.y, mt = blockIdx.z, m0 = mt * (16 * RT);
   const int n0 = tile * NT;
   const int Ks = K / sk.k_split;
-  const int k0 = split * Ks + wave * (Ks >> 2);
+  const int k0 = split * Ks + wave * (Ks / NWV);
   const int nrt = min(RT, (M - m0 + 15) >> 4);  // row tiles holding valid rows (uniform)
 
   const T *wp[CT];
@@ -449,38 +451,35 @@ __global__ __launch_bounds__(256) void skinny_kernel(const T *__restrict__ A, in
 #pragma unroll
     for (int j = 0; j < CT; ++j) red[((wave * RT + i) * CT + j) * 64 + lane] = acc[i][j];
   __syncthreads();
-  // wave w sums row tile w over the 4 K quarters (waves past the row tiles sum nothing)
+  // wave w < RT sums row tile w over the NWV K slices; the other waves are done (no barrier
+  // follows)
+  if (wave >= nrt) return;
   f32x4 sum[CT];
-  const int rw = min(wave, RT - 1);
 #pragma unroll
   for (int j = 0; j < CT; ++j) {
-    f32x4 t = red[((0 * RT + rw) * CT + j) * 64 + lane];
+    f32x4 t = red[((0 * RT + wave) * CT + j) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) t += red[((w * RT + rw) * CT + j) * 64 + lane];
+    for (int w = 1; w < NWV; ++w) t += red[((w * RT + wave) * CT + j) * 64 + lane];
     sum[j] = t;
   }
 
   if (sk.k_split > 1) {
     // K split across workgroups: store this slice's partial sums [split][M][N] (row-major) and
     // leave the sum and the epilogue to resid_reduce_kernel, launched next.
-    if (wave < nrt) {
-      const int N = gridDim.x * NT;
+    const int N = gridDim.x * NT;
 #pragma unroll
-      for (int j = 0; j < CT; ++j)
+    for (int j = 0; j < CT; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = m0 + wave * 16 + 4 * g + r;
-          if (row < M) sk.part[((size_t)split * M + row) * N + n0 + j * 16 + c16] = sum[j][r];
-        }
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wave * 16 + 4 * g + r;
+        if (row < M) sk.part[((size_t)split * M + row) * N + n0 + j * 16 + c16] = sum[j][r];
+      }
     return;
   }
-  if (wave < nrt) {
 #pragma unroll
-    for (int j = 0; j < CT; j += 2) {
-      const int j1 = j + 1 < CT ? j + 1 : j;
-      epi.store2(st[j], st[j1], ri, m0 + wave * 16 + 4 * g, n0 + j * 16 + c16, sum[j], sum[j1], j + 1 < CT, rinv, m0);
-    }
+  for (int j = 0; j < CT; j += 2) {
+    const int j1 = j + 1 < CT ? j + 1 : j;
+    epi.store2(st[j], st[j1], ri, m0 + wave * 16 + 4 * g, n0 + j * 16 + c16, sum[j], sum[j1], j + 1 < CT, rinv, m0);
   }
 }
 
@@ -847,12 +846,13 @@ __global__ __launch_bounds__(256) void tiled_kernel(const T *__restrict__ A, int
                  n0 + wn * (BN / 2) + j * 16 + (lane & 15), acc[i][j], acc[i][j + 1], true, rinv, m0);
 }
 
-template <typename T, int NT, int RT, class Epi>
+template <typename T, int NT, int RT, int NWV, class Epi>
 static void run_skinny_rt(const T *A, int M, int N, int K, const Epi &epi, const GemmPlan &p, hipStream_t s) {
   dim3 grid(N / NT, p.sk.k_split, (M + 16 * RT - 1) / (16 * RT));
-  const int nk = K / p.sk.k_split / 4 / (4 * Mfma<T>::EPL);
+  const int nk = K / p.sk.k_split / NWV / (4 * Mfma<T>::EPL);
   switch (nk) {
-#define DM_NK(n) case n: hipLaunchKernelGGL((skinny_kernel<T, NT, n, RT, Epi>), grid, dim3(256), 0, s, A, M, K, epi, p.sk); break;
+#define DM_NK(n) \
+  case n: hipLaunchKernelGGL((skinny_kernel<T, NT, n, RT, NWV, Epi>), grid, dim3(NWV * 64), 0, s, A, M, K, epi, p.sk); break;
     DM_NK(1) DM_NK(2) DM_NK(3) DM_NK(4) DM_NK(5) DM_NK(6) DM_NK(7) DM_NK(8)
 #undef DM_NK
     default: break;  // the host plan never asks for more than 8 k-chunks per wave
@@ -860,8 +860,15 @@ static void run_skinny_rt(const T *A, int M, int N, int K, const Epi &epi, const
 }
 template <typename T, int NT, class Epi>
 static void run_skinny(const T *A, int M, int N, int K, const Epi &epi, const GemmPlan &p, hipStream_t s) {
-  if (p.rt == 2) run_skinny_rt<T, NT, 2>(A, M, N, K, epi, p, s);
-  else run_skinny_rt<T, NT, 4>(A, M, N, K, epi, p, s);
+  if constexpr (NT == 16 && std::is_same<Epi, EpiResid<T>>::value) {
+    if (p.nw == 16) {  // residual projections whole-K per workgroup
+      if (p.rt == 1) run_skinny_rt<T, NT, 1, 16>(A, M, N, K, epi, p, s);
+      else run_skinny_rt<T, NT, 2, 16>(A, M, N, K, epi, p, s);
+      return;
+    }
+  }
+  if (p.rt == 2) run_skinny_rt<T, NT, 2, 4>(A, M, N, K, epi, p, s);
+  else run_skinny_rt<T, NT, 4, 4>(A, M, N, K, epi, p, s);
 }
 
 template <typename T, class Epi>

@@ -75,7 +75,8 @@ struct GemmPlan {
   int skinny;   // 1: M <= 64 kernel (K split across waves and workgroups), 0: tiled kernel
   int nt;       // skinny: output columns per workgroup (16, 32 or 64)
   SplitK sk;
-  int rt = 4;   // skinny: 16-row tiles per workgroup (4: 64 rows, 2: 32 rows)
+  int rt = 4;   // skinny: 16-row tiles per workgroup (4: 64 rows, 2: 32 rows, 1: 16 rows)
+  int nw = 4;   // skinny: waves per workgroup (4, or 16 for whole-K residual projections)
 };
 
 void launch_qkv(Dt dt, const QkvArgs &a, const GemmPlan &p, hipStream_t s);

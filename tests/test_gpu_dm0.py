@@ -87,7 +87,7 @@ def test_suffix_denoise_b32_ragged_bf16():
     for b in samples:
         ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :lens[b]], vc[:, b, :, :lens[b]], wl.shape, wl.steps)
         _chunk_ok(got[b], ref, f"config-4 sample {b} (P={lens[b]})")
-    # Batch invariance: the sample run alone takes the batch-1 kernels (skinny split-K GEMMs,
+    # Batch invariance: the sample run alone takes the batch-1 kernels (skinny GEMMs,
     # split-key attention with bf16 partials), the batch the tiled ones, so the two agree to the
     # bf16 bound rather than bit for bit; each is held to the oracle bound on its own.
     b = samples[0]
