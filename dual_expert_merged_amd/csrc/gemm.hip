@@ -527,18 +527,19 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
 }
 
 // ------------------------------------------------------------------------ big kernel (M > 64)
-// Workgroup tile 128 x BN (BN = 128, 256 or 384); NW waves as WM x WN (8 as 2 x 4), each
-// (128/WM) x (BN/WN), i.e. several MFMA 16x16 tiles, so every LDS fragment read feeds several
-// MFMAs, and several waves per SIMD (one LDS-bound workgroup per CU) hide each other's LDS and
-// barrier waits.  Each k-step moves
-// 128 bytes of every row (64 bf16 or 128 FP8 codes).  Operands go from global memory straight
-// into LDS (global_load_lds_dwordx4: no registers, whole 128-byte lines per row) through NBUF
-// stage buffers (3, or 2 for the 384-wide tile): while step k is multiplied, the next NBUF-1
-// steps are loading.  The stage buffers are distinct LDS arrays and the k-loop is unrolled by
-// NBUF, so the compiler can tell that reading one buffer does not wait for the loads into
-// another, and it interleaves the fragment reads with the MFMAs.  An LDS row holds its eight 16-byte chunks in XOR-swizzled order (chunk c at
-// position c ^ (row & 7)), so the 16 rows of a fragment read spread over all banks.  grid.z
-// splits K (the narrow residual projections), each split writing fp32 partial sums for
+// Workgroup tile 128 x BN (BN = 128, 256 or 384) or 256 x 256; NW waves as WM x WN (8 as 2 x 4,
+// or 4 x 2 for 256 rows), each (BM/WM) x (BN/WN), i.e. several MFMA 16x16 tiles, so every LDS
+// fragment read feeds several MFMAs, and several waves per SIMD (one LDS-bound workgroup per
+// CU) hide each other's LDS and barrier waits.  Each k-step moves 128 bytes of every row (64
+// bf16 or 128 FP8 codes).  Operands go from global memory straight into LDS
+// (global_load_lds_dwordx4: no registers, whole 128-byte lines per row) through NBUF stage
+// buffers (3, or 2 for the 512-row stages of the 128 x 384 and 256 x 256 tiles): while step k
+// is multiplied, the next NBUF-1 steps are loading.  The stage buffers are distinct LDS arrays
+// and the k-loop is unrolled by NBUF, so the compiler can tell that reading one buffer does not
+// wait for the loads into another, and it interleaves the fragment reads with the MFMAs.  An
+// LDS row holds its eight 16-byte chunks in XOR-swizzled order (chunk c at position
+// c ^ (row & 7)), so the 16 rows of a fragment read spread over all banks.  grid.z splits K
+// (the narrow residual projections), each split writing fp32 partial sums for
 // resid_reduce_kernel.  Workgroups are numbered so that the tiles sharing an operand column run
 // on the same XCD (blocks go to the 8 XCDs round-robin) and meet in its L2.  Op: bf16 (two
 // 16x16x32 MFMAs per k-step) or fp8 (one 16x16x128 MFMA per k-step).
@@ -562,12 +563,12 @@ template <int I, int N, class F> __device__ __forceinline__ void static_for(F &&
   }
 }
 
-// NW waves as WM x (NW / WM), each (128 / WM) x (BN * WM / NW)
-template <typename Op, int BN, int NBUF, int NW, int WM, class Epi>
+// NW waves as WM x (NW / WM), each (BM / WM) x (BN * WM / NW); BM = 128 or 256 rows of A
+template <typename Op, int BN, int NBUF, int NW, int WM, int BM, class Epi>
 __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, int M, int K, Epi epi, SplitK sk, int n_tiles,
                                                   int m_tiles) {
   constexpr int EB = sizeof(Op);       // bytes per element
-  constexpr int BM = 128, RB = 128;    // rows of A per tile, bytes per row per k-step
+  constexpr int RB = 128;              // bytes per row per k-step
   constexpr int BK = RB / EB, VE = 16 / EB;
   constexpr int WN = NW / WM, TN = BN / (16 * WN);  // waves along N, 16-column tiles per wave
   constexpr int TM = BM / (16 * WM);                // 16-row tiles per wave
@@ -618,8 +619,12 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
   const int sw = c16 & 7;
   const int arow = (wm * (BM / WM) + c16) * RB, wrow = (BM + wn * (BN / WN) + c16) * RB;
 
-  // one k-step: wait for its loads, start the loads NBUF-1 steps ahead into the buffer read in
-  // the previous step, multiply
+  // one k-step: wait for its loads, multiply, and start the loads NBUF-1 steps ahead into the
+  // buffer read in the previous step.  With three buffers the copies go out half-way through the
+  // step: issued right after the barrier, the copies of all 8 waves meet every wave's first
+  // fragment reads in the LDS, issued half-way they overlap the MFMAs (a probe of this loop:
+  // 58 % -> 71 % of the MFMA rate; the bf16 GEMMs 3-5 % faster).  With two buffers the copy has
+  // only this one step to land, so it goes out first.
   auto step = [&](auto curc, int kt) {
     constexpr int CB = decltype(curc)::value;
     const char *cur = big_buf<STAGE, CB>();
@@ -629,10 +634,13 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
     else if (NBUF >= 3 && after >= 1) vm_wait<(NBUF >= 3 ? LPW : 0)>();
     else vm_wait<0>();
     wg_barrier();  // every wave's step kt has landed; step kt-1 is fully read
-    if (kt + NBUF - 1 < nkt) dma(std::integral_constant<int, (CB + NBUF - 1) % NBUF>{}, kt + NBUF - 1);
+    auto issue = [&] {
+      if (kt + NBUF - 1 < nkt) dma(std::integral_constant<int, (CB + NBUF - 1) % NBUF>{}, kt + NBUF - 1);
+    };
     if constexpr (EB == 2) {
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
+        if (kc == (NBUF >= 3 ? 1 : 0)) issue();
         const int pos = ((kc * 4 + g) ^ sw) * 16;
         bf16x8 fa[TM], fb[TN];
 #pragma unroll
@@ -645,6 +653,7 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
           for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<bf16>::mma(fa[i], fb[j], acc[i][j]);
       }
     } else {
+      issue();  // FP8: one MFMA k-chunk per step; measured slower half-way
       const int p0 = ((2 * g) ^ sw) * 16, p1 = ((2 * g + 1) ^ sw) * 16;
       i32x8 fa[TM], fb[TN];
 #pragma unroll
@@ -692,30 +701,39 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
   }
   if constexpr (Epi::kTile && EB == 2) {
     if (epi.tile_ok(BN)) {  // uniform
-      // stage the finished tile in LDS (the k-step buffers are free now), then store whole rows
+      // stage the finished tile in LDS (the k-step buffers are free now), then store whole rows;
+      // 128 rows per pass (a 256-row tile takes two, each staged by the waves that own its rows)
       constexpr int LD = BN + 8;
-      static_assert(64 * LD * 2 <= STAGE, "half a tile fits in one stage buffer");
+      static_assert(64 * LD * 2 <= STAGE, "half a pass fits in one stage buffer");
+      static_assert(BM % 128 == 0 && (BM / WM) <= 128, "a wave's rows lie in one pass");
       const TileRows<bf16, LD> ot{reinterpret_cast<bf16 *>(big_buf<STAGE, 0>()), reinterpret_cast<bf16 *>(big_buf<STAGE, 1>())};
-      // the epilogue's loads of row tile i+1 go out before row tile i is processed, so only the
-      // first ones are waited for
-      typename Epi::St st[2][TN];
-      auto load_row_tile = [&](int i, typename Epi::St(&dst)[TN]) {
-        const RowInfo ri = row_info(epi.rows(), m0 + wm * (BM / WM) + i * 16 + 4 * g, M);
+      static_for<0, BM / 128>([&](auto P) {
+        constexpr int pass = decltype(P)::value;
+        const int pm0 = m0 + pass * 128;
+        if constexpr (pass > 0) __syncthreads();  // the previous pass's rows are stored
+        if (wm * (BM / WM) / 128 == pass) {  // uniform per wave
+          // the epilogue's loads of row tile i+1 go out before row tile i is processed, so only
+          // the first ones are waited for
+          typename Epi::St st[2][TN];
+          auto load_row_tile = [&](int i, typename Epi::St(&dst)[TN]) {
+            const RowInfo ri = row_info(epi.rows(), m0 + wm * (BM / WM) + i * 16 + 4 * g, M);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) dst[j] = epi.load(ri, n0 + wn * (BN / WN) + j * 16 + c16);
-      };
-      load_row_tile(0, st[0]);
+            for (int j = 0; j < TN; ++j) dst[j] = epi.load(ri, n0 + wn * (BN / WN) + j * 16 + c16);
+          };
+          load_row_tile(0, st[0]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        if (i + 1 < TM) load_row_tile(i + 1, st[(i + 1) & 1]);
-        const int row0 = m0 + wm * (BM / WM) + i * 16 + 4 * g;
+          for (int i = 0; i < TM; ++i) {
+            if (i + 1 < TM) load_row_tile(i + 1, st[(i + 1) & 1]);
+            const int row0 = m0 + wm * (BM / WM) + i * 16 + 4 * g;
 #pragma unroll
-        for (int j = 0; j < TN; j += 2)
-          epi.to_lds2(st[i & 1][j], st[i & 1][j + 1], row0, n0 + wn * (BN / WN) + j * 16 + c16, acc[i][j], acc[i][j + 1],
-                      rinv, m0, n0, ot);
-      }
-      __syncthreads();
-      epi.template lds_out<BM, BN>(ot, m0, n0, M);
+            for (int j = 0; j < TN; j += 2)
+              epi.to_lds2(st[i & 1][j], st[i & 1][j + 1], row0, n0 + wn * (BN / WN) + j * 16 + c16, acc[i][j],
+                          acc[i][j + 1], rinv + pass * 128, pm0, n0, ot);
+          }
+        }
+        __syncthreads();
+        epi.template lds_out<128, BN>(ot, pm0, n0, M);
+      });
       return;
     }
   }
@@ -733,22 +751,32 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
   }
 }
 
-// nt: 128 or 256 columns per tile with three k-step buffers, or 384 with two (LDS holds only two
-// stages of 512 rows).
+// Tiles of 128 rows x nt = 128 or 256 columns with three k-step buffers, or 384 with two (LDS
+// holds only two stages of 512 rows); bf16 also 256 x 256 with two (8 waves as 4 x 2, each
+// 64 x 128: a third fewer copied bytes and LDS fragment reads per MFMA than 128 x 384).
 template <typename Op, class Epi>
-static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, const SplitK &sk, hipStream_t s) {
-  const int nN = N / nt, nM = (M + 127) / 128;
-  dim3 grid(nN, nM, sk.k_split);
-  // 8 waves as 2 x 4 (two per SIMD: while one waits on LDS or the barrier, the other
-  // multiplies).  Measured: 4 waves (2 x 2) 13-14 % slower at the batch-32 shapes; 16 waves
-  // (4 x 4, 128 registers per lane) no faster there and the FP8 prefill 1.8 x slower.
+static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, int bm, const SplitK &sk, hipStream_t s) {
+  // 8 waves (two per SIMD: while one waits on LDS or the barrier, the other multiplies).
+  // Measured: 4 waves (2 x 2) 13-14 % slower at the batch-32 shapes; 16 waves (4 x 4, 128
+  // registers per lane) no faster there and the FP8 prefill 1.8 x slower.
   constexpr int NW = 8, WM = 2;
+  const int nN = N / nt;
+  if constexpr (sizeof(Op) == 2) {
+    if (bm == 256 && nt == 256) {
+      const int nM = (M + 255) / 256;
+      dim3 grid(nN, nM, sk.k_split);
+      hipLaunchKernelGGL((big_kernel<Op, 256, 2, NW, 4, 256, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
+      return;
+    }
+  }
+  const int nM = (M + 127) / 128;
+  dim3 grid(nN, nM, sk.k_split);
   if (nt == 384)
-    hipLaunchKernelGGL((big_kernel<Op, 384, 2, NW, WM, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
+    hipLaunchKernelGGL((big_kernel<Op, 384, 2, NW, WM, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
   else if (nt == 256)
-    hipLaunchKernelGGL((big_kernel<Op, 256, 3, NW, WM, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
+    hipLaunchKernelGGL((big_kernel<Op, 256, 3, NW, WM, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
   else
-    hipLaunchKernelGGL((big_kernel<Op, 128, 3, NW, WM, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
+    hipLaunchKernelGGL((big_kernel<Op, 128, 3, NW, WM, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
 }
 
 // ------------------------------------------------------------------------ tiled kernel (any M)
@@ -881,7 +909,7 @@ static void run_gemm(const T *A, int M, int N, int K, const Epi &epi, const Gemm
     }
   } else if (p.nt >= 128) {
     if constexpr (std::is_same<T, bf16>::value) {
-      run_big<bf16>(A, M, N, K, epi, p.nt, p.sk, s);
+      run_big<bf16>(A, M, N, K, epi, p.nt, p.bm, p.sk, s);
     }
   } else {
     dim3 grid(N / 64, (M + 63) / 64);
@@ -906,7 +934,7 @@ template <typename T> static void swiglu_t(const SwigluArgs &a, const GemmPlan &
 // FP8: one launch of the large-tile kernel, 256 columns per workgroup when N allows it.
 template <class Epi> static void run_fp8(const fp8 *A, int M, int N, int K, const Epi &epi, hipStream_t s) {
   const SplitK none{1, nullptr};
-  run_big<fp8>(A, M, N, K, epi, N % 256 == 0 ? 256 : 128, none, s);
+  run_big<fp8>(A, M, N, K, epi, N % 256 == 0 ? 256 : 128, 128, none, s);
 }
 void launch_resid_fp8(const ResidArgs &a, hipStream_t s) {
   run_fp8((const fp8 *)a.a, a.M, a.out.H, a.K, EpiResid<bf16, fp8>{a}, s);

@@ -77,6 +77,7 @@ struct GemmPlan {
   SplitK sk;
   int rt = 4;   // skinny: 16-row tiles per workgroup (4: 64 rows, 2: 32 rows, 1: 16 rows)
   int nw = 4;   // skinny: waves per workgroup (4, or 16 for whole-K residual projections)
+  int bm = 128; // big: rows per tile (128, or 256 with 256 columns, bf16)
 };
 
 void launch_qkv(Dt dt, const QkvArgs &a, const GemmPlan &p, hipStream_t s);
