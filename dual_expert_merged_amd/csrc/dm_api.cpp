@@ -110,10 +110,10 @@ GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
   GemmPlan p{};
   p.sk.k_split = 1;
   p.skinny = 0;
-  p.nt = 64;
+  p.nt = 0;  // the tiled kernel
   if (M > 64) {
     // bf16: 128-row tiles, 256 columns when that still gives >= 128 workgroups, else 128; narrow
-    // GEMMs split K (multiples of 64) until ~200 workgroups.
+    // GEMMs take 64 columns, or split K (multiples of 64) until ~200 workgroups.
     if (dt != DT_BF16 || N % 128 != 0 || K % 64 != 0) return p;
     if (N % 256 == 0 && (size_t)(N / 256) * ((M + 255) / 256) >= 200) {
       // 256 x 256 tiles while they still make ~200 workgroups (the prefill shapes: a third fewer
@@ -123,6 +123,12 @@ GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
       return p;
     }
     const int mt = (M + 127) / 128;
+    if (split_ok && N % 64 == 0 && (N / 64) * mt >= 200) {
+      // residual projections: 128 x 64 tiles fill the CUs without a K split, so the residual
+      // epilogue runs in the same launch (batch 32, O: 18.1 -> 16.7 us with the reduce)
+      p.nt = 64;
+      return p;
+    }
     p.nt = (N % 256 == 0 && (N / 256) * mt >= 128) ? 256 : 128;
     if (!split_ok && p.nt == 256 && N % 384 == 0) {
       // one workgroup per CU: compare whole rounds of 256 workgroups, a 384-wide tile costing

@@ -485,17 +485,17 @@ __global__ __launch_bounds__(NWV * 64) void skinny_kernel(const T *__restrict__ 
 
 // Sum of the K-split partials of a residual projection plus the residual epilogue:
 // h += sum_s part[s], hg = h * next_gain, per-16-column sums of squares.  Thread = 4 columns of
-// one row; the split sum runs in split order.
-template <typename T>
-__global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const float *__restrict__ part, int ks) {
+// one row; the split sum runs in split order.  KS: the number of splits (all its loads in flight).
+template <typename T, int KS>
+__global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const float *__restrict__ part) {
   const int H = a.out.H, q4 = H >> 2;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const int row = min(idx / q4, a.M - 1), c = (idx - (idx / q4) * q4) * 4;
   const bool in_range = idx < a.M * q4;
-  float4 pv[16];
+  float4 pv[KS];
 #pragma unroll
-  for (int sp = 0; sp < 16; ++sp)  // unconditional (clamped) loads stay in flight together
-    pv[sp] = *reinterpret_cast<const float4 *>(part + ((size_t)min(sp, ks - 1) * a.M + row) * H + c);
+  for (int sp = 0; sp < KS; ++sp)
+    pv[sp] = *reinterpret_cast<const float4 *>(part + ((size_t)sp * a.M + row) * H + c);
   float4 hv = *reinterpret_cast<const float4 *>(a.out.h + (size_t)row * H + c);
   float4 gv = a.next_gain ? *reinterpret_cast<const float4 *>(a.next_gain + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   bool ok = in_range;
@@ -505,10 +505,9 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
   }
   float4 t = pv[0];
 #pragma unroll
-  for (int sp = 1; sp < 16; ++sp)
-    if (sp < ks) {
-      t.x += pv[sp].x; t.y += pv[sp].y; t.z += pv[sp].z; t.w += pv[sp].w;
-    }
+  for (int sp = 1; sp < KS; ++sp) {
+    t.x += pv[sp].x; t.y += pv[sp].y; t.z += pv[sp].z; t.w += pv[sp].w;
+  }
   const float4 hn = make_float4(hv.x + t.x, hv.y + t.y, hv.z + t.z, hv.w + t.w);
   if (ok) {
     *reinterpret_cast<float4 *>(a.out.h + (size_t)row * H + c) = hn;
@@ -761,6 +760,15 @@ static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, in
   // registers per lane) no faster there and the FP8 prefill 1.8 x slower.
   constexpr int NW = 8, WM = 2;
   const int nN = N / nt;
+  if constexpr (sizeof(Op) == 2 && std::is_same<Epi, EpiResid<Op>>::value) {
+    // residual projections only (a 64-column tile would split the RoPE pairs of a QKV head)
+    if (nt == 64) {  // 128 x 64, 8 waves as 4 x 2 (32 x 32 each), four 24 KB stages
+      const int nM = (M + 127) / 128;
+      dim3 grid(nN, nM, sk.k_split);
+      hipLaunchKernelGGL((big_kernel<Op, 64, 4, NW, 4, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM);
+      return;
+    }
+  }
   if constexpr (sizeof(Op) == 2) {
     if (bm == 256 && nt == 256) {
       const int nM = (M + 255) / 256;
@@ -907,7 +915,7 @@ static void run_gemm(const T *A, int M, int N, int K, const Epi &epi, const Gemm
       case 32: run_skinny<T, 32>(A, M, N, K, epi, p, s); break;
       default: run_skinny<T, 64>(A, M, N, K, epi, p, s); break;
     }
-  } else if (p.nt >= 128) {
+  } else if (p.nt >= 64) {
     if constexpr (std::is_same<T, bf16>::value) {
       run_big<bf16>(A, M, N, K, epi, p.nt, p.bm, p.sk, s);
     }
@@ -924,7 +932,13 @@ template <typename T> static void resid_t(const ResidArgs &a, const GemmPlan &p,
   run_gemm<T>((const T *)a.a, a.M, a.out.H, a.K, EpiResid<T>{a}, p, s);
   if (p.sk.k_split > 1) {
     const int n = a.M * (a.out.H / 4);
-    hipLaunchKernelGGL(resid_reduce_kernel<T>, dim3((n + 255) / 256), dim3(256), 0, s, a, p.sk.part, p.sk.k_split);
+    const dim3 grid((n + 255) / 256);
+    switch (p.sk.k_split) {
+      case 2: hipLaunchKernelGGL((resid_reduce_kernel<T, 2>), grid, dim3(256), 0, s, a, p.sk.part); break;
+      case 4: hipLaunchKernelGGL((resid_reduce_kernel<T, 4>), grid, dim3(256), 0, s, a, p.sk.part); break;
+      case 8: hipLaunchKernelGGL((resid_reduce_kernel<T, 8>), grid, dim3(256), 0, s, a, p.sk.part); break;
+      default: hipLaunchKernelGGL((resid_reduce_kernel<T, 16>), grid, dim3(256), 0, s, a, p.sk.part); break;
+    }
   }
 }
 template <typename T> static void swiglu_t(const SwigluArgs &a, const GemmPlan &p, hipStream_t s) {

@@ -72,8 +72,9 @@ struct SwigluArgs {
 
 // Tile plan of one GEMM launch, chosen by the host.
 struct GemmPlan {
-  int skinny;   // 1: M <= 64 kernel (K split across waves and workgroups), 0: tiled kernel
-  int nt;       // skinny: output columns per workgroup (16, 32 or 64)
+  int skinny;   // 1: M <= 64 kernel (K split across waves and workgroups), 0: large-tile or tiled kernel
+  int nt;       // skinny: output columns per workgroup (16, 32 or 64); large-tile kernel: 64, 128,
+                // 256 or 384 columns per tile; 0: the tiled kernel
   SplitK sk;
   int rt = 4;   // skinny: 16-row tiles per workgroup (4: 64 rows, 2: 32 rows, 1: 16 rows)
   int nw = 4;   // skinny: waves per workgroup (4, or 16 for whole-K residual projections)
