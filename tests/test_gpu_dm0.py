@@ -164,3 +164,39 @@ def test_prefill_then_denoise_bf16():
             assert e <= DEEP_REL and mean_rel <= DEEP_MEAN, (l, name, e, mean_rel)
     ref = O.suffix_denoise(x1[b], aw, rk, rv, s, wl.steps)
     _chunk_ok(got[b], ref, f"config-5 sample {b} chunk")
+
+
+def test_prefill_ragged_prefix_bf16():
+    """Ragged prefix lengths through the batch-8 prefill (8 x 816 rows: large GEMM tiles that
+    straddle samples and hold rows past a sample's length, down to a one-token prefix): the K/V
+    rows of the shortest samples against the oracle, every row at or past a length left
+    untouched, then the denoise on that cache."""
+    wl = workload(5)
+    s = wl.shape
+    lens = np.array([816, 613, 700, 1, 816, 655, 777, 802], dtype=np.int32)
+    print(f"case: 28-layer VLM prefill bf16 B=8 ragged P={[int(p) for p in lens]} cap {wl.prefix_len}", flush=True)
+    vlm = inputs.make_vlm_weights(wl)
+    aw = inputs.make_action_weights(wl)
+    emb = inputs.make_prefix_embeds(wl).copy()
+    for b in range(wl.batch):
+        emb[b, lens[b]:] = 0.0
+    x1 = inputs.make_noise(wl)
+    gpu = Gpu(wl, vlm, aw)
+    k, v = gpu.prefill(emb, lens)  # the harness zero-fills the caches first
+    kn, vn = np32(k), np32(v)
+    for b in range(wl.batch):
+        assert not np.any(kn[:, b, :, lens[b]:]) and not np.any(vn[:, b, :, lens[b]:]), f"rows past P={lens[b]} written"
+    refs = {}
+    for b in (3, 1):
+        rk, rv, _ = O.prefill_kv(emb[b, :lens[b]], vlm, s)
+        refs[b] = (rk, rv)
+        for l in range(s.n_layers):
+            for name, g, r in (("K", kn[l, b, :, :lens[b]], rk[l]), ("V", vn[l, b, :, :lens[b]], rv[l])):
+                e = rel_inf(g, r)
+                mean_rel = err_stats(g, r)[1] / float(np.sqrt(np.mean(r * r)))
+                assert e <= DEEP_REL and mean_rel <= DEEP_MEAN, (b, l, name, e, mean_rel)
+        print(f"prefill sample {b} (P={lens[b]}): K/V of all {s.n_layers} layers within bounds", flush=True)
+    got = gpu.denoise(k, v, lens, x1, wl.steps)
+    for b in (3, 1):
+        ref = O.suffix_denoise(x1[b], aw, refs[b][0], refs[b][1], s, wl.steps)
+        _chunk_ok(got[b], ref, f"config-5 ragged sample {b} (P={lens[b]}) chunk")
