@@ -532,8 +532,8 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
 // CU) hide each other's LDS and barrier waits.  Each k-step moves 128 bytes of every row (64
 // bf16 or 128 FP8 codes).  Operands go from global memory straight into LDS
 // (global_load_lds_dwordx4: no registers, whole 128-byte lines per row) through NBUF stage
-// buffers (3, or 2 for the 512-row stages of the 128 x 384 and 256 x 256 tiles): while step k
-// is multiplied, the next NBUF-1 steps are loading.  The stage buffers are distinct LDS arrays
+// buffers (3; 4 for the 192-row stages of the 128 x 64 tile; 2 for the 512-row stages of the
+// 128 x 384 and 256 x 256 tiles): while step k is multiplied, the next NBUF-1 steps are loading.  The stage buffers are distinct LDS arrays
 // and the k-loop is unrolled by NBUF, so the compiler can tell that reading one buffer does not
 // wait for the loads into another, and it interleaves the fragment reads with the MFMAs.  An
 // LDS row holds its eight 16-byte chunks in XOR-swizzled order (chunk c at position
