@@ -769,7 +769,7 @@ static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, in
       return;
     }
   }
-  if constexpr (sizeof(Op) == 2) {
+  if constexpr (sizeof(Op) == 2 || Epi::kTile) {  // FP8 residual tiles of 256 rows spill: not built
     if (bm == 256 && nt == 256) {
       const int nM = (M + 255) / 256;
       dim3 grid(nN, nM, sk.k_split);
@@ -948,7 +948,13 @@ template <typename T> static void swiglu_t(const SwigluArgs &a, const GemmPlan &
 // FP8: one launch of the large-tile kernel, 256 columns per workgroup when N allows it.
 template <class Epi> static void run_fp8(const fp8 *A, int M, int N, int K, const Epi &epi, hipStream_t s) {
   const SplitK none{1, nullptr};
-  run_big<fp8>(A, M, N, K, epi, N % 256 == 0 ? 256 : 128, 128, none, s);
+  const int nt = N % 256 == 0 ? 256 : 128;
+  // gate/up: 256 x 256 while those still make ~200 workgroups (an FP8 k-step's MFMAs take half
+  // the time of bf16's for the same copied bytes, so reuse per byte matters twice as much; the
+  // prefill's gate/up 266 -> 220 us).  The residual epilogue keeps 128 rows (256 rows spill
+  // registers and measured 4 % slower).
+  const int bm = Epi::kTile && nt == 256 && (size_t)(N / 256) * ((M + 255) / 256) >= 200 ? 256 : 128;
+  run_big<fp8>(A, M, N, K, epi, nt, bm, none, s);
 }
 void launch_resid_fp8(const ResidArgs &a, hipStream_t s) {
   run_fp8((const fp8 *)a.a, a.M, a.out.H, a.K, EpiResid<bf16, fp8>{a}, s);
