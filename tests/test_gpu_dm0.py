@@ -120,6 +120,26 @@ def test_suffix_denoise_b3_ragged_split_keys_bf16():
         _chunk_ok(got[i], ref, f"config-4 sample {b} (P={lens[i]}) in a batch of 3")
 
 
+def test_suffix_denoise_b16_ragged_bf16():
+    """Sixteen samples of the batch-32 workload (800 action rows): the mid-size plans, 128 x 128
+    QKV tiles with a partial last row tile, 128 x 256 gate/up tiles, residual projections split
+    four ways over K with the separate reduce, and attention keys split in two chunks."""
+    wl = workload(4)
+    lens_all = inputs.make_prefix_lens(wl)
+    pick = list(range(16))
+    lens = lens_all[pick]
+    print(f"case: suffix denoise bf16 B=16 ragged P in [{lens.min()},{lens.max()}] cap {wl.prefix_len}", flush=True)
+    aw = inputs.make_action_weights(wl)
+    kc, vc = inputs.make_kv_cache(wl)
+    x1 = inputs.make_noise(wl)
+    gpu = Gpu(wl, None, aw)
+    k, v = gpu.cache_to_device(kc[:, pick], vc[:, pick])
+    got = gpu.denoise(k, v, lens, x1[pick], wl.steps)
+    for i in sorted({int(np.argmin(lens)), int(np.argmax(lens)), 15}):
+        ref = O.suffix_denoise(x1[i], aw, kc[:, i, :, :lens[i]], vc[:, i, :, :lens[i]], wl.shape, wl.steps)
+        _chunk_ok(got[i], ref, f"config-4 sample {i} (P={lens[i]}) in a batch of 16")
+
+
 def test_suffix_denoise_empty_and_longest_prefix_bf16():
     """Batch of two at the DM0 shapes: one sample with no prefix token (its queries see the 50
     action keys only; every later key chunk of it is empty) and one with the longest prefix."""
