@@ -594,12 +594,12 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_dma_kernel(AttnArgs a) {
 // One workgroup per (sample, KV head, query block, 16 slots); thread = one 16-byte vector of one
 // slot's output, computing its slot's chunk weights itself (the 16 threads of a slot read the
 // same statistics), every load issued before the first is used.
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+template <typename T, int D, int G, int NT>
+__global__ __launch_bounds__(NT) void attn_combine_kernel(AttnArgs a) {
   typedef Mfma<T> MF;
   constexpr int EPL = MF::EPL, RPH = ATT_SLOTS / G, MAXC = 16;
   constexpr int VPRW = D / EPL;        // vectors per slot row
-  constexpr int SPW = 256 / VPRW;      // slots per workgroup
+  constexpr int SPW = NT / VPRW;       // slots per workgroup
   const int tid = threadIdx.x;
   const int bk = blockIdx.x, qb = blockIdx.y, nqb = gridDim.y;
   const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
@@ -664,8 +664,15 @@ template <typename T, int D, int G> static void attn_t(const AttnArgs &a, hipStr
   else
     hipLaunchKernelGGL((attn_kernel<T, D, G>), grid, dim3(ATT_THREADS), 0, s, a);
   if (a.n_chunks > 1) {
-    constexpr int SPW = 256 / (D / Mfma<T>::EPL);
-    hipLaunchKernelGGL((attn_combine_kernel<T, D, G>), dim3(a.B * a.Hkv, nqb, ATT_SLOTS / SPW), dim3(256), 0, s, a);
+    // 256 threads per workgroup, or 64 when that leaves fewer than 256 workgroups (batch 1: the
+    // merge is a latency chain, so more, smaller workgroups keep more loads in flight per CU)
+    constexpr int VPRW = D / Mfma<T>::EPL;
+    if ((size_t)a.B * a.Hkv * nqb * ATT_SLOTS * VPRW / 256 < 256)
+      hipLaunchKernelGGL((attn_combine_kernel<T, D, G, 64>), dim3(a.B * a.Hkv, nqb, ATT_SLOTS * VPRW / 64), dim3(64), 0, s,
+                         a);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<T, D, G, 256>), dim3(a.B * a.Hkv, nqb, ATT_SLOTS * VPRW / 256), dim3(256), 0,
+                         s, a);
   }
 }
 
