@@ -9,6 +9,7 @@ Prints one JSON line: chunks/s (whole job), p50/p90/p99 chunk latency, the roofl
 dominant kernel, and the float64 oracle timed on the host cores as a CPU baseline.
 
   python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config 3|4] [--no-cpu-baseline] [--prefill]
+  python bench.py --merged-layer            (one merged layer only, its own JSON line)
 
 The roofline unit is one launch of the captured graph (one chunk): achieved = algorithmic bytes
 (batch 1, HBM-bound) or FLOPs (batch 32, MFMA-bound) of the chunk / its mean duration (HIP
@@ -219,6 +220,53 @@ def prefill_times(reps=3):
     return out
 
 
+def merged_layer_times(reps=20):
+    """One DM0-base merged layer at batch 1 (816 prefix and 50 action tokens through both experts
+    with the joint block-masked attention, prefix K/V written out): mean µs per dm_merged_layer
+    call (HIP events around each call on its stream; the inputs are restored between calls,
+    outside the timed spans) and the fraction of dense bf16 MFMA peak over its algorithmic FLOPs."""
+    import torch
+    from dual_expert_merged_amd import binding as bd
+    from dual_expert_merged_amd import inputs
+    from dual_expert_merged_amd.configs import workload
+
+    wl = workload(2)
+    s = wl.shape
+    P, S = wl.prefix_len, s.chunk
+    ctx = bd.Context(s, 0)
+    dv = bd.DeviceExpert(inputs.make_vlm_weights(wl), s.dtype)
+    da = bd.DeviceAction(inputs.make_action_weights(wl), s.dtype)
+    hp0 = torch.from_numpy(inputs.make_prefix_embeds(wl)).cuda()
+    hs0 = torch.from_numpy(inputs.make_suffix_hidden(wl)).cuda()
+    hp, hs = hp0.clone(), hs0.clone()
+    lens = torch.full((1,), P, dtype=torch.int32, device="cuda")
+    ko = torch.empty((1, s.n_kv_heads, P, s.head_dim), dtype=bd.torch_dtype(s.dtype), device="cuda")
+    vo = torch.empty_like(ko)
+    ws = ctx.workspace(bd.OP_MERGED_LAYER, 1, P)
+    stream = torch.cuda.Stream()
+    total = 0.0
+    with torch.cuda.stream(stream):
+        ctx.merged_layer(dv, da.body, 0, hp, hs, lens, ws, ko, vo, stream=stream)  # warm-up
+        for _ in range(reps):
+            hp.copy_(hp0)
+            hs.copy_(hs0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ctx.merged_layer(dv, da.body, 0, hp, hs, lens, ws, ko, vo, stream=stream)
+            e1.record(stream)
+            stream.synchronize()
+            total += e0.elapsed_time(e1)
+    ctx.close()
+    us = total * 1e3 / reps
+    D, Hq = s.head_dim, s.n_q_heads
+    params = lambda h, f: s.qkv_rows * h + h * Hq * D + 3 * f * h
+    flops = (2 * P * params(s.vlm_hidden, s.vlm_ffn) + 2 * S * params(s.act_hidden, s.act_ffn)
+             + 4 * D * Hq * (P * P + S * (P + S)))
+    return {"us": round(us, 2), "algorithmic_gflop": round(flops / 1e9, 2),
+            "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "workload": "DM0-base merged layer, bf16, B=1, 816 prefix + 50 action tokens"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +276,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", action="store_true",
                     help="also time the prefix encoding (B=8, 816 tokens) with the bf16 and the FP8 MLP")
+    ap.add_argument("--merged-layer", action="store_true",
+                    help="time only one merged layer (both experts, B=1, 816 + 50 tokens) and print it")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the plain copy for counter scaling")
     ap.add_argument("--traffic-summary", action="store_true", help="summarise counter runs (no GPU needed)")
     for name in ("fetch", "write", "cal-fetch", "cal-write"):
@@ -235,6 +285,9 @@ def main():
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(args)
+        return
+    if args.merged_layer:
+        print(json.dumps({"merged_layer": merged_layer_times()}), flush=True)
         return
     if args.copy_calibration:
         copy_calibration()

@@ -90,7 +90,10 @@ struct Layout {
 
 void attn_split(int B, int Hkv, int nqb, int max_keys, int *n_chunks, int *chunk_keys) {
   const int blocks = B * Hkv * nqb;
-  int want = (256 + blocks - 1) / blocks;
+  // as many chunks as still fit one round of workgroups on the 256 CUs (one per CU): a partial
+  // second round costs more than the longer chunks (one merged layer's prefix attention, 104
+  // groups: 3 chunks 24.5 + 9.2 us merge)
+  int want = 256 / blocks;
   if (want > 16) want = 16;  // the merge keeps every chunk's statistics in registers
   const int maxc = (max_keys + 63) / 64;  // at least one 64-key tile per chunk
   if (want > maxc) want = maxc;
