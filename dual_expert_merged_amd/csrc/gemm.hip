@@ -566,7 +566,7 @@ template <int I, int N, class F> __device__ __forceinline__ void static_for(F &&
 // NW waves as WM x (NW / WM), each (BM / WM) x (BN * WM / NW); BM = 128 or 256 rows of A
 template <typename Op, int BN, int NBUF, int NW, int WM, int BM, class Epi>
 __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, int M, int K, Epi epi, SplitK sk, int n_tiles,
-                                                  int m_tiles, int n_fast) {
+                                                  int m_tiles, int group_m) {
   constexpr int EB = sizeof(Op);       // bytes per element
   constexpr int RB = 128;              // bytes per row per k-step
   constexpr int BK = RB / EB, VE = 16 / EB;
@@ -583,24 +583,17 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int wm = wave / WN, wn = wave % WN;
-  // XCD-aware tile order: the blocks on one XCD (b % 8) take a contiguous run of (split, n, m)
-  // with m fastest, or of (split, m, n) with n fastest (n_fast, uniform: chosen by the host)
+  // XCD-aware tile order: the blocks on one XCD (b % 8) take a contiguous run of tiles, ordered
+  // in bands of group_m row tiles (uniform, chosen by the host): m fastest within a band, then n,
+  // then the next band, the K split outermost (group_m = m_tiles: m fastest; 1: n fastest)
   const int T = n_tiles * m_tiles * (int)gridDim.z;
   const int b = blockIdx.x + (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x;
   const int xcd = b & 7, per = T >> 3, rem = T & 7;
   const int t = xcd * per + min(xcd, rem) + (b >> 3);
-  int m_t, n_t, split;
-  if (n_fast) {
-    n_t = t % n_tiles;
-    const int r = t / n_tiles;
-    m_t = r % m_tiles;
-    split = r / m_tiles;
-  } else {
-    m_t = t % m_tiles;
-    const int r = t / m_tiles;
-    n_t = r % n_tiles;
-    split = r / n_tiles;
-  }
+  const int mn = m_tiles * n_tiles, split = t / mn, r = t - split * mn;
+  const int band = r / (group_m * n_tiles), gm = min(group_m, m_tiles - band * group_m);
+  const int local = r - band * group_m * n_tiles;
+  const int m_t = band * group_m + local % gm, n_t = local / gm;
   const int n0 = n_t * BN, m0 = m_t * BM;
   const int Ks = K / sk.k_split, kb = split * Ks, nkt = Ks / BK;
 
@@ -773,14 +766,18 @@ static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, in
   // registers per lane) no faster there and the FP8 prefill 1.8 x slower.
   constexpr int NW = 8, WM = 2;
   const int nN = N / nt;
-  // tile order: the one whose run of workgroups resident on one XCD at a time (one per CU, 32
-  // per XCD) touches fewer distinct operand rows, so more of them meet in that XCD's L2
-  // (prefill down 193 -> 167 us with n fastest; the batch-32 QKV and gate/up keep m fastest)
-  auto n_fast = [&](int bm_, int nM) {
+  // tile order: the band height whose run of workgroups resident on one XCD at a time (one per
+  // CU, 32 per XCD) touches the fewest distinct operand rows, so more of them meet in that
+  // XCD's L2 (prefill down 193 -> 167 us with bands of one row tile)
+  auto group_m = [&](int bm_, int nM) {
     const long T = (long)nN * nM * sk.k_split, W = std::min<long>((T + 7) / 8, 32);
-    const long rows_m = std::min<long>(W, nM) * bm_ + (W + nM - 1) / nM * nt;
-    const long rows_n = (W + nN - 1) / nN * bm_ + std::min<long>(W, nN) * nt;
-    return rows_n < rows_m ? 1 : 0;
+    int best = nM;
+    long best_rows = -1;
+    for (int g = nM; g >= 1; --g) {
+      const long rows = std::min<long>(W, g) * bm_ + (W + g - 1) / g * nt;
+      if (best_rows < 0 || rows < best_rows) best = g, best_rows = rows;
+    }
+    return best;
   };
   if constexpr (sizeof(Op) == 2 && std::is_same<Epi, EpiResid<Op>>::value) {
     // residual projections only (a 64-column tile would split the RoPE pairs of a QKV head)
@@ -788,7 +785,7 @@ static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, in
       const int nM = (M + 127) / 128;
       dim3 grid(nN, nM, sk.k_split);
       hipLaunchKernelGGL((big_kernel<Op, 64, 4, NW, 4, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM,
-                         n_fast(128, nM));
+                         group_m(128, nM));
       return;
     }
   }
@@ -797,13 +794,13 @@ static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, in
       const int nM = (M + 255) / 256;
       dim3 grid(nN, nM, sk.k_split);
       hipLaunchKernelGGL((big_kernel<Op, 256, 2, NW, 4, 256, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM,
-                         n_fast(256, nM));
+                         group_m(256, nM));
       return;
     }
   }
   const int nM = (M + 127) / 128;
   dim3 grid(nN, nM, sk.k_split);
-  const int nf = n_fast(128, nM);
+  const int nf = group_m(128, nM);
   if (nt == 384)
     hipLaunchKernelGGL((big_kernel<Op, 384, 2, NW, WM, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM, nf);
   else if (nt == 256)
