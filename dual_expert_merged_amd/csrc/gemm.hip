@@ -800,13 +800,13 @@ static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, in
   }
   const int nM = (M + 127) / 128;
   dim3 grid(nN, nM, sk.k_split);
-  const int nf = group_m(128, nM);
+  const int gm = group_m(128, nM);
   if (nt == 384)
-    hipLaunchKernelGGL((big_kernel<Op, 384, 2, NW, WM, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM, nf);
+    hipLaunchKernelGGL((big_kernel<Op, 384, 2, NW, WM, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM, gm);
   else if (nt == 256)
-    hipLaunchKernelGGL((big_kernel<Op, 256, 3, NW, WM, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM, nf);
+    hipLaunchKernelGGL((big_kernel<Op, 256, 3, NW, WM, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM, gm);
   else
-    hipLaunchKernelGGL((big_kernel<Op, 128, 3, NW, WM, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM, nf);
+    hipLaunchKernelGGL((big_kernel<Op, 128, 3, NW, WM, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM, gm);
 }
 
 // ------------------------------------------------------------------------ tiled kernel (any M)
