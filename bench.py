@@ -74,7 +74,7 @@ def cpu_baseline(wl, aw, kc, vc, x1, lens):
                       f"P={P}) in float64 numpy; {dt:.2f} s on {cores} host cores"}
 
 
-SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip", "common.h", "kernels.h"]
+SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip", "persist.hip", "common.h", "kernels.h", "persist_plan.h"]
 
 
 def source_hash():

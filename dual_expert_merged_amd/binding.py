@@ -20,6 +20,7 @@ DM_OK, DM_ERR_INVALID_ARG, DM_ERR_SHAPE, DM_ERR_UNSUPPORTED, DM_ERR_WORKSPACE, D
 STATUS_NAMES = {0: "DM_OK", -1: "DM_ERR_INVALID_ARG", -2: "DM_ERR_SHAPE", -3: "DM_ERR_UNSUPPORTED",
                 -4: "DM_ERR_WORKSPACE", -5: "DM_ERR_PLAN_MISMATCH", -6: "DM_ERR_HIP"}
 DM_F32, DM_BF16, DM_FP8_E4M3 = 0, 1, 2
+DM_FLAG_MULTI_KERNEL = 1
 OP_PREFILL, OP_MERGED_LAYER, OP_DENOISE = 0, 1, 2
 _DT = {F32: DM_F32, BF16: DM_BF16, FP8: DM_FP8_E4M3}
 EXPORTS = ["dm_version", "dm_last_error", "dm_ctx_create", "dm_ctx_destroy", "dm_workspace_bytes",
@@ -38,7 +39,7 @@ class Config(C.Structure):
                 ("vlm_ffn", C.c_int), ("act_ffn", C.c_int), ("n_q_heads", C.c_int),
                 ("n_kv_heads", C.c_int), ("head_dim", C.c_int), ("action_dim", C.c_int),
                 ("chunk", C.c_int), ("rms_eps", C.c_float), ("rope_base", C.c_float),
-                ("dtype", C.c_int), ("vlm_mlp_dtype", C.c_int)]
+                ("dtype", C.c_int), ("vlm_mlp_dtype", C.c_int), ("flags", C.c_int)]
 
 
 class ExpertWeightsC(C.Structure):
@@ -102,10 +103,10 @@ def stream_handle(stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
-def make_config(shape: ModelShape) -> Config:
+def make_config(shape: ModelShape, flags: int = 0) -> Config:
     return Config(shape.n_layers, shape.vlm_hidden, shape.act_hidden, shape.vlm_ffn, shape.act_ffn,
                   shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.action_dim, shape.chunk,
-                  shape.rms_eps, shape.rope_base, _DT[shape.dtype], _DT[shape.vlm_mlp_dtype])
+                  shape.rms_eps, shape.rope_base, _DT[shape.dtype], _DT[shape.vlm_mlp_dtype], flags)
 
 
 def torch_dtype(dtype: str):
@@ -159,10 +160,10 @@ class DeviceAction:
 class Context:
     """A libdm context for one model shape on one device."""
 
-    def __init__(self, shape: ModelShape, device: int = 0):
+    def __init__(self, shape: ModelShape, device: int = 0, flags: int = 0):
         self.shape = shape
         self.device = device
-        self.cfg = make_config(shape)
+        self.cfg = make_config(shape, flags)
         h = C.c_void_p()
         check(lib().dm_ctx_create(C.byref(self.cfg), device, C.byref(h)))
         self.h = h

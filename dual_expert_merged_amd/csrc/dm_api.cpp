@@ -50,7 +50,8 @@ struct dm_ctx {
   dm_config cfg;
   int device;
   Dt dt;
-  size_t es;  // bytes per element of the weight dtype
+  size_t es;         // bytes per element of the weight dtype
+  bool single_ok;    // the device holds all workgroups of the single-launch batch-1 denoise
 };
 
 struct dm_plan {
@@ -78,6 +79,7 @@ struct Layout {
   Region h, hg, ssq, q, ks, vs, o, act, apart, split;          // action side (h: denoise only)
   Region hp, hg_p, ssq_p, q_p, kp, vp, o_p, act_p, apart_p;    // prefix side (hp: prefill only)
   Region q8_p, qs_p;                                           // FP8 MLP operand codes and row scales
+  Region single;                                               // single-launch batch-1 denoise
   int n_chunks = 1, chunk_keys = 32, n_chunks_p = 1, chunk_keys_p = 32;
   ExpertPlans pa, pv;  // action expert, VLM expert
   size_t total = 0;
@@ -186,6 +188,14 @@ size_t split_bytes(const GemmPlan &p, int M, int N) {
   return p.sk.k_split > 1 ? (size_t)p.sk.k_split * M * N * sizeof(float) : 0;
 }
 
+// The batch-1 denoise runs as one launch per chunk (persist.hip) for the DM0-base action expert
+// shapes, unless the config asks for the multi-kernel sequence.
+bool single_launch_shape(const dm_config &c, int B, int P_cap) {
+  return !(c.flags & DM_FLAG_MULTI_KERNEL) &&
+         persist_supported(c.n_layers, c.act_hidden, c.act_ffn, c.n_q_heads, c.n_kv_heads, c.head_dim, c.chunk, c.action_dim, B,
+                           P_cap, c.dtype == DM_BF16);
+}
+
 Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
   Layout L;
   const Dt dt = es == 2 ? DT_BF16 : DT_F32;
@@ -209,6 +219,7 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
     const int nqb = attn_qblocks(S, Hq, Hkv);
     attn_split(B, Hkv, nqb, P_cap + S, &L.n_chunks, &L.chunk_keys);
     if (L.n_chunks > 1) L.put(L.apart, attn_partial_bytes(dt, B, Hkv, nqb, L.n_chunks, D));
+    if (op == DM_OP_DENOISE && single_launch_shape(c, B, P_cap)) L.put(L.single, persist_ws_bytes(S, c.action_dim));
   }
   if (op == DM_OP_PREFILL || op == DM_OP_MERGED_LAYER) {
     L.pv = plan_expert(c, dt, (int)Mp, Hv, c.vlm_ffn);
@@ -268,6 +279,7 @@ dm_status check_config(const dm_config *c) {
   REQUIRE(c->chunk >= 1 && c->chunk <= 64, DM_ERR_UNSUPPORTED, "chunk must be 1..64");
   REQUIRE(c->rms_eps > 0.f && std::isfinite(c->rms_eps), DM_ERR_INVALID_ARG, "rms_eps must be positive");
   REQUIRE(c->rope_base > 1.f && std::isfinite(c->rope_base), DM_ERR_INVALID_ARG, "rope_base must be > 1");
+  REQUIRE((c->flags & ~DM_FLAG_MULTI_KERNEL) == 0, DM_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
   return DM_OK;
 }
 
@@ -385,6 +397,14 @@ dm_status enqueue_denoise(const dm_ctx *ctx, const dm_action_weights *aw, const 
                           const int32_t *lens, int B, int P_cap, float *x, int num_steps, void *ws, hipStream_t s) {
   const dm_config &c = ctx->cfg;
   const Layout L = make_layout(c, ctx->es, DM_OP_DENOISE, B, P_cap);
+  if (ctx->single_ok && L.single.bytes) {
+    const dm_expert_weights &w = aw->body;
+    PersistLaunch p{w.w_qkv, w.w_o, w.w_gate, w.w_up, w.w_down, w.attn_norm, w.mlp_norm, aw->w_in, aw->b_in,
+                    aw->final_norm, aw->w_out, aw->b_out, k_cache, v_cache, lens, x, c.n_layers, c.chunk,
+                    c.action_dim, P_cap, num_steps, c.rms_eps, c.rope_base, at<void>(ws, L.single)};
+    HIP_TRY(launch_denoise_persistent(p, s));
+    return DM_OK;
+  }
   const int S = c.chunk, Ha = c.act_hidden, Fa = c.act_ffn, D = c.head_dim, Hkv = c.n_kv_heads;
   const int M = B * S;
   float2 *rope = at<float2>(ws, L.rope);
@@ -474,6 +494,14 @@ dm_status dm_ctx_create(const dm_config *cfg, int device, dm_ctx **out) {
   ctx->device = device;
   ctx->dt = cfg->dtype == DM_BF16 ? DT_BF16 : DT_F32;
   ctx->es = cfg->dtype == DM_BF16 ? 2 : 4;
+  // the single-launch denoise needs all of its workgroups resident at once
+  int prev = -1;
+  ctx->single_ok = false;
+  if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(device) == hipSuccess) {
+    ctx->single_ok = persist_check_device(device) == hipSuccess;
+    (void)hipSetDevice(prev);
+  }
+  (void)hipGetLastError();
   *out = ctx;
   return DM_OK;
 }
@@ -511,10 +539,15 @@ dm_status dm_denoise_plan_create(dm_ctx *ctx, const dm_action_weights *aw, const
     (void)hipStreamDestroy(cs);
     return fail(DM_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
   }
-  enqueue_denoise(ctx, aw, k_cache, v_cache, prefix_lens, B, P_cap, x, num_steps, ws, cs);
+  const dm_status st = enqueue_denoise(ctx, aw, k_cache, v_cache, prefix_lens, B, P_cap, x, num_steps, ws, cs);
+  const hipError_t le = hipGetLastError();
   e = hipStreamEndCapture(cs, &graph);
   (void)hipStreamDestroy(cs);
-  if (e != hipSuccess) return fail(DM_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  if (st != DM_OK || le != hipSuccess || e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    if (st != DM_OK) return st;
+    return fail(DM_ERR_HIP, "graph capture: %s", hipGetErrorString(le != hipSuccess ? le : e));
+  }
   hipGraphExec_t exec = nullptr;
   e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
   if (e != hipSuccess) {
@@ -542,6 +575,9 @@ dm_status dm_denoise_plan_launch(dm_plan *plan, int num_steps, void *stream) {
   REQUIRE(plan, DM_ERR_INVALID_ARG, "plan is NULL");
   REQUIRE(num_steps == plan->steps, DM_ERR_PLAN_MISMATCH,
           "num_steps %d differs from the %d steps captured in the plan", num_steps, plan->steps);
+  int cur = -1;
+  HIP_TRY(hipGetDevice(&cur));
+  if (cur != plan->device) HIP_TRY(hipSetDevice(plan->device));
   HIP_TRY(hipGraphLaunch(plan->exec, (hipStream_t)stream));
   return DM_OK;
 }
@@ -647,6 +683,13 @@ dm_status dm_quantize_fp8_rows(const void *src, uint8_t *dst, float *scales, int
   REQUIRE(src && dst && scales, DM_ERR_INVALID_ARG, "src / dst / scales is NULL");
   REQUIRE(rows >= 1 && cols >= 1, DM_ERR_SHAPE, "rows and cols must be positive");
   REQUIRE(aligned16(src) && aligned16(dst), DM_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  // run on the device that holds the data (there is no context to name it)
+  hipPointerAttribute_t attr;
+  HIP_TRY(hipPointerGetAttributes(&attr, src));
+  REQUIRE(attr.type == hipMemoryTypeDevice, DM_ERR_INVALID_ARG, "src is not device memory");
+  int cur = -1;
+  HIP_TRY(hipGetDevice(&cur));
+  if (cur != attr.device) HIP_TRY(hipSetDevice(attr.device));
   launch_fp8_quantize_rows(src, dst, scales, rows, cols, (hipStream_t)stream);
   HIP_TRY(hipGetLastError());
   return DM_OK;

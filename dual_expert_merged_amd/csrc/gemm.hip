@@ -110,17 +110,23 @@ struct RowInfo {
 __device__ __forceinline__ RowInfo row_info(const RowMap &rm, int row0, int M) {
   RowInfo ri;
   int len[4];
-  // one division for the tile; the 4 consecutive rows step across at most one sample boundary
+  // one division for the tile when a sample has at least 4 rows (the 4 consecutive rows then
+  // step across at most one sample boundary); otherwise one per row
   const int r0c = min(row0, M - 1);
   const int b0 = r0c / rm.rows_per_b, s0 = r0c - b0 * rm.rows_per_b;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int rc = min(row0 + r, M - 1);
-    const int s = s0 + (rc - r0c);
-    const int wrap = s >= rm.rows_per_b;
     ri.rc[r] = rc;
-    ri.b[r] = b0 + wrap;
-    ri.s[r] = s - wrap * rm.rows_per_b;
+    if (rm.rows_per_b >= 4) {  // uniform
+      const int s = s0 + (rc - r0c);
+      const int wrap = s >= rm.rows_per_b;
+      ri.b[r] = b0 + wrap;
+      ri.s[r] = s - wrap * rm.rows_per_b;
+    } else {
+      ri.b[r] = rc / rm.rows_per_b;
+      ri.s[r] = rc - ri.b[r] * rm.rows_per_b;
+    }
   }
   if (rm.is_prefix) {  // uniform; action rows need no prefix length (their RoPE rows are precomputed)
 #pragma unroll

@@ -123,4 +123,23 @@ void launch_velocity_euler(const float *h, const float *gain, const float *w_out
 void launch_fp8_quantize_rows(const void *src, uint8_t *dst, float *scales, int rows, int cols,
                               hipStream_t s);
 
+// Single-launch batch-1 suffix denoise (persist.hip): the DM0-base action expert (hidden 1024,
+// FFN 3072, 16 query / 8 KV heads of dim 128, bf16) at batch 1, S <= 64 action tokens,
+// action dim <= 32 (multiple of 4), P_cap <= 960, at most 28 layers.
+struct PersistLaunch {
+  const void *w_qkv, *w_o, *w_gate, *w_up, *w_down;
+  const float *attn_norm, *mlp_norm, *w_in, *b_in, *final_norm, *w_out, *b_out;
+  const void *k_cache, *v_cache;
+  const int32_t *lens;
+  float *x;
+  int L, S, A, P_cap, steps;
+  float eps, rope_base;
+  void *ws;  // persist_ws_bytes(S, A), 256-byte aligned
+};
+bool persist_supported(int L, int H, int F, int Hq, int Hkv, int D, int S, int A, int B, int P_cap, bool bf16_dtype);
+size_t persist_ws_bytes(int S, int A);
+// hipSuccess when the device can hold all 256 workgroups at once
+hipError_t persist_check_device(int device);
+hipError_t launch_denoise_persistent(const PersistLaunch &p, hipStream_t s);
+
 }  // namespace dm

@@ -1,6 +1,6 @@
-// Small kernels of the path: RoPE table, counter clearing, entry into the first sublayer
-// (h*gain and sums of squares), action_in_proj + time embedding, final norm + action_out_proj +
-// Euler update, FP8 E4M3 weight quantisation.
+// Small kernels of the path: RoPE table, entry into the first sublayer (h*gain and sums of
+// squares), action_in_proj + time embedding, final norm + action_out_proj + Euler update, FP8
+// E4M3 row quantisation.
 #include "common.h"
 #include "kernels.h"
 

@@ -36,7 +36,8 @@
  *    dm_config.dtype.  Norm gains and the action head (w_in, b_in, final_norm, w_out, b_out)
  *    are float32.
  *  - KV cache layout [L][B][Hkv][P_cap][D]: one sample's head is P_cap contiguous rows of D.
- *  - prefix_lens [B] int32 on the device, 1 <= P_b <= P_cap.  The host validates only P_cap.
+ *  - prefix_lens [B] int32 on the device, 0 <= P_b <= P_cap (a sample may have no prefix token;
+ *    values outside are clamped into that range).  The host validates only P_cap.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream), never
  *    synchronize, and never allocate device memory, except dm_ctx_create and
  *    dm_denoise_plan_create.  The caller owns every buffer; `ws` is caller-provided scratch of
@@ -86,7 +87,12 @@ typedef struct {
   float rope_base;
   dm_dtype dtype;          /* DM_F32 or DM_BF16: weight matrices, KV cache, intermediates */
   dm_dtype vlm_mlp_dtype;  /* equal to dtype, or DM_FP8_E4M3 with dtype DM_BF16 */
+  int flags;               /* DM_FLAG_* bits; 0 for the defaults */
 } dm_config;
+
+/* dm_config.flags: run the batch-1 suffix denoise as the multi-kernel sequence even where the
+ * single-launch kernel applies (the two agree to rounding; used to compare them). */
+#define DM_FLAG_MULTI_KERNEL 1
 
 /* One expert, every layer stacked.  H = expert hidden, F = expert FFN, QKV = (Hq+2Hkv)*D. */
 typedef struct {
@@ -149,7 +155,14 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm /* (host) */
 
 /* Action-chunk sampling against a cached prefix (page sections 5.2-5.3): x [B][S][A] float32
  * holds the noise at t = 1 on entry and the action chunk at t = 0 on return, after num_steps
- * Euler steps.  Runs eagerly (kernel launches on `stream`). */
+ * Euler steps.  Runs eagerly (kernel launches on `stream`).
+ * At B = 1 with the DM0-base action expert (hidden 1024, FFN 3072, 16 query / 8 KV heads of dim
+ * 128, bf16, S <= 64, A <= 32, P_cap <= 960) the whole chunk is one kernel launch whose 256
+ * workgroups run concurrently and hand results to each other through memory (page section 6.4:
+ * at small batch the cost is in per-step launches and temporaries); it needs those 256 CUs to
+ * itself.  Should its workgroups fail to meet within about two seconds (another kernel occupying
+ * CUs), it gives up and x is filled with NaN.  DM_FLAG_MULTI_KERNEL selects the multi-kernel
+ * sequence instead. */
 dm_status dm_suffix_denoise(dm_ctx *ctx, const dm_action_weights *aw /* (host) */,
                             const void *k_cache, const void *v_cache, const int32_t *prefix_lens,
                             int B, int P_cap, float *x, int num_steps,

@@ -236,3 +236,65 @@ def test_plan_rejects_other_step_count(cfg1):
     with pytest.raises(bd.DMError) as e:
         gpu.ctx.suffix_denoise(gpu.aw, k, v, dev_lens([64]), x, 4, ws[:100])
     assert e.value.status == bd.DM_ERR_WORKSPACE
+
+
+def test_one_action_token_per_sample(cfg1):
+    """chunk = 1: every GEMM row tile of four rows spans four samples (the epilogues' sample and
+    token of each row), ragged prefixes, against the oracle per sample."""
+    wl, vlm, aw, _ = cfg1
+    s = dataclasses.replace(wl.shape, chunk=1)
+    wl1 = dataclasses.replace(wl, shape=s)
+    lens = [64, 3, 0, 17, 40]
+    print(f"case: tiny fp32 chunk=1 B=5 lens={lens}", flush=True)
+    B, P_cap = len(lens), 64
+    rng = np.random.default_rng(106)
+    L, Hkv, D = s.n_layers, s.n_kv_heads, s.head_dim
+    kc = rng.standard_normal((L, B, Hkv, P_cap, D)).astype(np.float32)
+    vc = rng.standard_normal((L, B, Hkv, P_cap, D)).astype(np.float32)
+    x1 = rng.standard_normal((B, 1, s.action_dim)).astype(np.float32)
+    g = Gpu(wl1, vlm, aw)
+    k, v = g.cache_to_device(kc, vc)
+    got = g.denoise(k, v, lens, x1, 3)
+    for b, P in enumerate(lens):
+        ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :P], vc[:, b, :, :P], s, 3)
+        assert rel_inf(got[b], ref) <= TOL, (b, rel_inf(got[b], ref))
+    # one merged layer with one action token per sample
+    h_pre = rng.standard_normal((B, P_cap, s.vlm_hidden)).astype(np.float32)
+    h_suf = rng.standard_normal((B, 1, s.act_hidden)).astype(np.float32)
+    hp, hs, kk, vv = g.merged_layer(0, h_pre, h_suf, lens)
+    for b, P in enumerate(lens):
+        rp, rs, rk, rv = O.merged_layer(h_pre[b, :P], h_suf[b], vlm, aw.body, 0, s)
+        assert rel_inf(hs[b], rs) <= TOL, (b, rel_inf(hs[b], rs))
+        if P:
+            assert rel_inf(hp[b, :P], rp) <= TOL
+            assert rel_inf(kk[b, :, :P], rk.transpose(1, 0, 2)) <= TOL
+
+
+def test_prefix_capacity_one(cfg1):
+    """P_cap = 1: one prefix row per sample (four samples per GEMM row tile), prefill and one
+    merged layer for B = 5 with prefixes of 0 or 1 tokens."""
+    wl, vlm, aw, gpu = cfg1
+    s = wl.shape
+    lens = [1, 0, 1, 1, 0]
+    print(f"case: tiny fp32 P_cap=1 B=5 lens={lens}", flush=True)
+    B = len(lens)
+    rng = np.random.default_rng(107)
+    emb = rng.standard_normal((B, 1, s.vlm_hidden)).astype(np.float32)
+    k, v = gpu.prefill(emb, lens)
+    k, v = np32(k), np32(v)
+    for b, P in enumerate(lens):
+        if P:
+            rk, rv, _ = O.prefill_kv(emb[b, :P], vlm, s)
+            assert rel_inf(k[:, b, :, :P], rk) <= TOL, (b, rel_inf(k[:, b, :, :P], rk))
+            assert rel_inf(v[:, b, :, :P], rv) <= TOL
+        else:
+            assert not np.any(k[:, b]) and not np.any(v[:, b])
+    h_suf = rng.standard_normal((B, s.chunk, s.act_hidden)).astype(np.float32)
+    hp, hs, kk, vv = gpu.merged_layer(1, emb, h_suf, lens)
+    for b, P in enumerate(lens):
+        rp, rs, rk, rv = O.merged_layer(emb[b, :P], h_suf[b], vlm, aw.body, 1, s)
+        assert rel_inf(hs[b], rs) <= TOL, (b, rel_inf(hs[b], rs))
+        if P:
+            assert rel_inf(hp[b, :P], rp) <= TOL
+        else:
+            np.testing.assert_array_equal(hp[b], emb[b])
