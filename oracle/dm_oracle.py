@@ -124,6 +124,14 @@ def e4m3_round(x):
     return np.where(a > 0, np.sign(x) * r, 0.0)
 
 
+def bf16_round(x):
+    """Nearest bfloat16 value of each float64: 8 significant bits, ties to even.  Used where the
+    FP8 branch quantises a tensor that a bf16 model holds (reading below); the values met there
+    are far inside bfloat16's normal range, so subnormals and overflow are not handled."""
+    m, e = np.frexp(f64(x))                        # x = m * 2^e, |m| in [0.5, 1)
+    return np.ldexp(np.round(m * 256.0), e - 8)    # numpy rounds half to even
+
+
 def fp8_quantize_rows(m):
     """Per-row symmetric scale s = max|row| / 448 (1 for an all-zero row) and the E4M3 codes'
     values row / s.  Used for weights (per output channel) and activations (per token)."""
@@ -155,21 +163,39 @@ def expert_qkv(h, w, l, shape, pos):
 
 
 def mlp(m, w, l, fp8=None):
-    """SwiGLU MLP down(silu(gate m) * up m).  fp8: optional (wq_gate, s_gate, wq_up, s_up,
-    wq_down, s_down) for layer l, runs the three GEMMs as in [FP8]."""
+    """SwiGLU MLP down(silu(gate m) * up m) of the normalised input m.  fp8: optional
+    (wq_gate, s_gate, wq_up, s_up, wq_down, s_down) for layer l, runs the three GEMMs as in
+    [FP8] (``mlp_fp8`` with m itself as the quantised operand)."""
     if fp8 is None:
         return linear(silu(linear(m, w.w_gate[l])) * linear(m, w.w_up[l]), w.w_down[l])
+    return mlp_fp8(m, np.ones(f64(m).shape[0]), fp8)
+
+
+def mlp_fp8(n, inv_rms, fp8):
+    """[FP8] SwiGLU MLP of the normalised input m = inv_rms[:, None] * n with the three GEMMs on
+    E4M3 codes: n is quantised per token for gate and up, and their outputs are scaled by
+    inv_rms (a positive factor per token commutes with per-token quantisation, so in exact
+    arithmetic this equals quantising m); the dequantised gate output goes through silu and
+    multiplies the up output; that product is quantised per token for down.
+    reading: the tensors quantised are those a bf16 model holds at those two points: the
+    gain-scaled residual n = h * g, whose 1/rms is applied after the GEMM, and the SwiGLU
+    product; each is rounded to bfloat16 before its scale and E4M3 codes are taken, so every
+    code is decided from the value the model stores."""
     gq, gs, uq, us, dq, ds = fp8
-    act = silu(fp8_linear(m, gq, gs)) * fp8_linear(m, uq, us)
-    return fp8_linear(act, dq, ds)
+    n16 = bf16_round(n)
+    r = f64(inv_rms)[:, None]
+    act = silu(r * fp8_linear(n16, gq, gs)) * (r * fp8_linear(n16, uq, us))
+    return fp8_linear(bf16_round(act), dq, ds)
 
 
 def expert_finish(h, o, w, l, shape, fp8=None):
     """[DM0] section 1: after the joint attention each expert applies its own O-projection and
     residual, then its own pre-norm SwiGLU MLP and residual."""
     h = f64(h) + linear(o, w.w_o[l])
-    m = rms_norm(h, w.mlp_norm[l], shape.rms_eps)
-    return h + mlp(m, w, l, fp8)
+    if fp8 is None:
+        return h + mlp(rms_norm(h, w.mlp_norm[l], shape.rms_eps), w, l)
+    inv_rms = 1.0 / np.sqrt(np.mean(h * h, axis=-1) + shape.rms_eps)
+    return h + mlp_fp8(h * f64(w.mlp_norm[l]), inv_rms, fp8)
 
 
 def merged_layer(h_pre, h_suf, vlm, act, l, shape):
