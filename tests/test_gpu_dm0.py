@@ -6,13 +6,17 @@ Bounds: the final action chunk must satisfy max |gpu - oracle| <= 2e-2 and
 mean |gpu - oracle| <= 2e-3.  One layer's outputs (hidden streams, its K/V) are held to
 ||gpu - oracle||_inf / ||oracle||_inf <= 1e-2 (five bf16 half-ulps: bf16 rounds to 2^-9
 relative, and each stored K/V or hidden update has been rounded once or twice).  The KV cache
-of a 28-layer prefill carries, at layer l, the rounding of l earlier bf16 layers in its hidden
-state, so it is checked for drift only: each layer's K/V within ||.||_inf-relative 2e-2 and a
-mean absolute error within 1e-2 of the reference's RMS (already layer 0 sits near 2e-3: the
-stored value and the normalised GEMM input are each rounded once, mean |delta| ~ 2^-10).  The
-per-layer accuracy of the same kernels is pinned by the one-layer test, and the chunk computed
-from that cache is held to the chunk bounds.
+of a 28-layer prefill carries, at layer l, layer 0's own rounding plus one independent bf16
+perturbation per earlier layer, so its error grows as a random walk, sqrt(e0^2 + l c).  Fitted
+to the measured DM0-base prefill (sample 5 of the batch-8 workload, P = 816, all 28 layers of K
+and V): mean |delta| / RMS(ref) e0 = 1.66e-3, c = 2.15e-6 (every layer within 0.99-1.05 of the
+fit); ||delta||_inf / ||ref||_inf e0 = 2.62e-3, c = 3.55e-6 (within 0.90-1.40: a maximum is
+noisier).  Bounds per layer: 1.25 x the mean fit and 1.75 x the max fit (layer 0: 2.1e-3 and
+4.6e-3; layer 27: 9.8e-3 and 1.8e-2).  The chunk computed from that cache is held to the chunk
+bounds.
 """
+from pathlib import Path
+
 import numpy as np
 import pytest
 import torch
@@ -20,10 +24,18 @@ import torch
 import oracle as O
 from dual_expert_merged_amd import inputs
 from dual_expert_merged_amd.configs import workload
+from tests.golden import make_config4_chunks as make_golden4
 from tests.gpu_harness import Gpu, err_stats, np32, rel_inf
 
 pytestmark = pytest.mark.gpu
-CHUNK_MAX, CHUNK_MEAN, INTER_REL, DEEP_REL, DEEP_MEAN = 2e-2, 2e-3, 1e-2, 2e-2, 1e-2
+CHUNK_MAX, CHUNK_MEAN, INTER_REL = 2e-2, 2e-3, 1e-2
+DRIFT_MEAN_E0, DRIFT_MEAN_C, DRIFT_MAX_E0, DRIFT_MAX_C = 1.66e-3, 2.15e-6, 2.62e-3, 3.55e-6
+
+
+def drift_bounds(layer):
+    """(||.||_inf-relative, mean |delta| / RMS) bounds for layer `layer` of a bf16 prefill cache."""
+    return (1.75 * float(np.sqrt(DRIFT_MAX_E0 ** 2 + layer * DRIFT_MAX_C)),
+            1.25 * float(np.sqrt(DRIFT_MEAN_E0 ** 2 + layer * DRIFT_MEAN_C)))
 
 
 def _chunk_ok(got, ref, what):
@@ -73,91 +85,118 @@ def test_suffix_denoise_b1_bf16(cfg3):
         np.testing.assert_array_equal(r, eager)
 
 
-def test_suffix_denoise_b32_ragged_bf16():
+GOLDEN4 = Path(__file__).with_name("golden") / "config4_chunks.npz"
+
+
+@pytest.fixture(scope="module")
+def cfg4():
+    """The batch-32 ragged workload's inputs and the oracle's chunks for all 32 samples
+    (tests/golden/config4_chunks.npz, written by tests/golden/make_config4_chunks.py from the
+    oracle; checked here against a fingerprint of the regenerated inputs)."""
     wl = workload(4)
-    lens = inputs.make_prefix_lens(wl)
-    print(f"case: suffix denoise bf16 B=32 ragged P in [{lens.min()},{lens.max()}] cap {wl.prefix_len}", flush=True)
     aw = inputs.make_action_weights(wl)
     kc, vc = inputs.make_kv_cache(wl)
     x1 = inputs.make_noise(wl)
+    lens = inputs.make_prefix_lens(wl)
+    assert GOLDEN4.exists(), "run: python -m tests.golden.make_config4_chunks"
+    g = np.load(GOLDEN4)
+    assert np.array_equal(g["lens"], lens), "golden chunks were written for other prefix lengths"
+    np.testing.assert_allclose(g["fingerprint"], make_golden4.fingerprint(x1, kc, vc, lens), rtol=1e-6)
+    return wl, aw, kc, vc, x1, lens, g["chunks"].astype(np.float64)
+
+
+def _oracle4(cfg, b):
+    wl, aw, kc, vc, x1, lens, _ = cfg
+    return O.suffix_denoise(x1[b], aw, kc[:, b, :, :lens[b]], vc[:, b, :, :lens[b]], wl.shape, wl.steps)
+
+
+@pytest.mark.timeout(600)
+def test_suffix_denoise_b32_ragged_bf16(cfg4):
+    wl, aw, kc, vc, x1, lens, gold = cfg4
+    print(f"case: suffix denoise bf16 B=32 ragged P in [{lens.min()},{lens.max()}] cap {wl.prefix_len}", flush=True)
+    # the stored oracle chunks agree with the oracle run now (float32 storage)
+    for b in (int(np.argmin(lens)), int(np.argmax(lens))):
+        d = float(np.max(np.abs(_oracle4(cfg4, b) - gold[b])))
+        print(f"golden sample {b}: live oracle vs stored {d:.2e}", flush=True)
+        assert d <= 1e-5, (b, d)
     gpu = Gpu(wl, None, aw)
     k, v = gpu.cache_to_device(kc, vc)
     got = gpu.denoise(k, v, lens, x1, wl.steps)
-    samples = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 31})
-    for b in samples:
-        ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :lens[b]], vc[:, b, :, :lens[b]], wl.shape, wl.steps)
-        _chunk_ok(got[b], ref, f"config-4 sample {b} (P={lens[b]})")
-    # Batch invariance: the sample run alone takes the batch-1 kernels (skinny GEMMs,
-    # split-key attention with bf16 partials), the batch the tiled ones, so the two agree to the
-    # bf16 bound rather than bit for bit; each is held to the oracle bound on its own.
-    b = samples[0]
+    worst = max(range(wl.batch), key=lambda b: err_stats(got[b], gold[b])[0])
+    for b in range(wl.batch):
+        mx, mean = err_stats(got[b], gold[b])
+        assert mx <= CHUNK_MAX and mean <= CHUNK_MEAN, (b, int(lens[b]), mx, mean)
+    _chunk_ok(got[worst], gold[worst], f"all 32 config-4 samples within bounds; worst sample {worst} (P={lens[worst]})")
+    # Batch invariance: B = 31 takes the same plans as B = 32 (13 row tiles of 128 in every
+    # GEMM: 128 x 256 QKV, 128 x 384 gate/up and 128 x 64 residual tiles, no K split, one key
+    # chunk per sample), so every sample's chunk is the same bit for bit.
+    del k, v
+    k31, v31 = gpu.cache_to_device(kc[:, :31], vc[:, :31])
+    got31 = gpu.denoise(k31, v31, lens[:31], x1[:31], wl.steps)
+    diff = int(np.sum(got31 != got[:31]))
+    print(f"batch invariance B=31 vs B=32: {diff} of {got31.size} values differ", flush=True)
+    assert diff == 0
+    # The sample run alone takes the batch-1 kernels, which sum in other orders: held to the
+    # oracle bound on its own and against the batch run.
+    del k31, v31
+    b = int(np.argmin(lens))
     kb, vb = gpu.cache_to_device(kc[:, b:b + 1], vc[:, b:b + 1])
     alone = gpu.denoise(kb, vb, lens[b:b + 1], x1[b:b + 1], wl.steps)
-    ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :lens[b]], vc[:, b, :, :lens[b]], wl.shape, wl.steps)
-    _chunk_ok(alone[0], ref, f"config-4 sample {b} alone at B=1")
+    _chunk_ok(alone[0], gold[b], f"config-4 sample {b} alone at B=1")
     mx, mean = err_stats(alone[0], got[b])
-    print(f"batch invariance sample {b}: max {mx:.3e} mean {mean:.3e}", flush=True)
+    print(f"batch-1 vs batch-32 sample {b}: max {mx:.3e} mean {mean:.3e}", flush=True)
     assert mx <= CHUNK_MAX and mean <= CHUNK_MEAN
 
 
-def test_suffix_denoise_b3_ragged_split_keys_bf16():
+@pytest.mark.timeout(300)
+def test_suffix_denoise_b3_ragged_split_keys_bf16(cfg4):
     """Three samples of the batch-32 workload (shortest, longest, one between): few enough
     workgroups that attention splits every sample's keys into chunks, so the shorter samples
     have chunks past their keys and chunks straddling the prefix/action boundary."""
-    wl = workload(4)
-    lens_all = inputs.make_prefix_lens(wl)
+    wl, aw, kc, vc, x1, lens_all, gold = cfg4
     pick = [int(np.argmin(lens_all)), int(np.argmax(lens_all)), 7]
     lens = lens_all[pick]
     print(f"case: suffix denoise bf16 B=3 ragged P={list(lens)} cap {wl.prefix_len}", flush=True)
-    aw = inputs.make_action_weights(wl)
-    kc, vc = inputs.make_kv_cache(wl)
-    x1 = inputs.make_noise(wl)
     gpu = Gpu(wl, None, aw)
     k, v = gpu.cache_to_device(kc[:, pick], vc[:, pick])
     got = gpu.denoise(k, v, lens, x1[pick], wl.steps)
     for i, b in enumerate(pick):
-        ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :lens[i]], vc[:, b, :, :lens[i]], wl.shape, wl.steps)
-        _chunk_ok(got[i], ref, f"config-4 sample {b} (P={lens[i]}) in a batch of 3")
+        _chunk_ok(got[i], gold[b], f"config-4 sample {b} (P={lens[i]}) in a batch of 3")
 
 
-def test_suffix_denoise_b16_ragged_bf16():
+@pytest.mark.timeout(300)
+def test_suffix_denoise_b16_ragged_bf16(cfg4):
     """Sixteen samples of the batch-32 workload (800 action rows): the mid-size plans, 128 x 128
     QKV tiles with a partial last row tile, 128 x 256 gate/up tiles, residual projections split
     four ways over K with the separate reduce, and attention keys split in two chunks."""
-    wl = workload(4)
-    lens_all = inputs.make_prefix_lens(wl)
+    wl, aw, kc, vc, x1, lens_all, gold = cfg4
     pick = list(range(16))
     lens = lens_all[pick]
     print(f"case: suffix denoise bf16 B=16 ragged P in [{lens.min()},{lens.max()}] cap {wl.prefix_len}", flush=True)
-    aw = inputs.make_action_weights(wl)
-    kc, vc = inputs.make_kv_cache(wl)
-    x1 = inputs.make_noise(wl)
     gpu = Gpu(wl, None, aw)
     k, v = gpu.cache_to_device(kc[:, pick], vc[:, pick])
     got = gpu.denoise(k, v, lens, x1[pick], wl.steps)
-    for i in sorted({int(np.argmin(lens)), int(np.argmax(lens)), 15}):
-        ref = O.suffix_denoise(x1[i], aw, kc[:, i, :, :lens[i]], vc[:, i, :, :lens[i]], wl.shape, wl.steps)
-        _chunk_ok(got[i], ref, f"config-4 sample {i} (P={lens[i]}) in a batch of 16")
+    for i in range(16):
+        mx, mean = err_stats(got[i], gold[i])
+        assert mx <= CHUNK_MAX and mean <= CHUNK_MEAN, (i, int(lens[i]), mx, mean)
+    print("all 16 samples in a batch of 16 within bounds", flush=True)
 
 
-def test_suffix_denoise_empty_and_longest_prefix_bf16():
+@pytest.mark.timeout(300)
+def test_suffix_denoise_empty_and_longest_prefix_bf16(cfg4):
     """Batch of two at the DM0 shapes: one sample with no prefix token (its queries see the 50
     action keys only; every later key chunk of it is empty) and one with the longest prefix."""
-    wl = workload(4)
-    lens_all = inputs.make_prefix_lens(wl)
+    wl, aw, kc, vc, x1, lens_all, gold = cfg4
     b_long = int(np.argmax(lens_all))
     pick = [0, b_long]
     lens = np.array([0, lens_all[b_long]], dtype=lens_all.dtype)
     print(f"case: suffix denoise bf16 B=2 P={[int(p) for p in lens]} cap {wl.prefix_len}", flush=True)
-    aw = inputs.make_action_weights(wl)
-    kc, vc = inputs.make_kv_cache(wl)
-    x1 = inputs.make_noise(wl)
     gpu = Gpu(wl, None, aw)
     k, v = gpu.cache_to_device(kc[:, pick], vc[:, pick])
     got = gpu.denoise(k, v, lens, x1[pick], wl.steps)
-    for i, b in enumerate(pick):
-        ref = O.suffix_denoise(x1[b], aw, kc[:, b, :, :lens[i]], vc[:, b, :, :lens[i]], wl.shape, wl.steps)
-        _chunk_ok(got[i], ref, f"config-4 sample {b} with P={lens[i]}")
+    ref0 = O.suffix_denoise(x1[0], aw, kc[:, 0, :, :0], vc[:, 0, :, :0], wl.shape, wl.steps)
+    _chunk_ok(got[0], ref0, "config-4 sample 0 with P=0")
+    _chunk_ok(got[1], gold[b_long], f"config-4 sample {b_long} with P={lens[1]}")
 
 
 def test_prefill_then_denoise_bf16():
@@ -179,9 +218,10 @@ def test_prefill_then_denoise_bf16():
         for name, g, r in (("K", kn[l, b], rk[l]), ("V", vn[l, b], rv[l])):
             e = rel_inf(g, r)
             mean_rel = err_stats(g, r)[1] / float(np.sqrt(np.mean(r * r)))
-            print(f"prefill sample {b} layer {l} {name}: rel inf err {e:.3e}, mean abs / rms {mean_rel:.3e}",
-                  flush=True)
-            assert e <= DEEP_REL and mean_rel <= DEEP_MEAN, (l, name, e, mean_rel)
+            rb, mb = drift_bounds(l)
+            print(f"prefill sample {b} layer {l} {name}: rel inf err {e:.3e} (bound {rb:.2e}), "
+                  f"mean abs / rms {mean_rel:.3e} (bound {mb:.2e})", flush=True)
+            assert e <= rb and mean_rel <= mb, (l, name, e, mean_rel)
     ref = O.suffix_denoise(x1[b], aw, rk, rv, s, wl.steps)
     _chunk_ok(got[b], ref, f"config-5 sample {b} chunk")
 
@@ -214,7 +254,10 @@ def test_prefill_ragged_prefix_bf16():
             for name, g, r in (("K", kn[l, b, :, :lens[b]], rk[l]), ("V", vn[l, b, :, :lens[b]], rv[l])):
                 e = rel_inf(g, r)
                 mean_rel = err_stats(g, r)[1] / float(np.sqrt(np.mean(r * r)))
-                assert e <= DEEP_REL and mean_rel <= DEEP_MEAN, (b, l, name, e, mean_rel)
+                rb, mb = drift_bounds(l)
+                print(f"prefill sample {b} (P={lens[b]}) layer {l} {name}: rel inf err {e:.3e}, "
+                      f"mean abs / rms {mean_rel:.3e}", flush=True)
+                assert e <= rb and mean_rel <= mb, (b, l, name, e, mean_rel)
         print(f"prefill sample {b} (P={lens[b]}): K/V of all {s.n_layers} layers within bounds", flush=True)
     got = gpu.denoise(k, v, lens, x1, wl.steps)
     for b in (3, 1):
