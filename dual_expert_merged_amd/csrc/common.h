@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "addr_words.h"
+
 namespace dm {
 
 typedef __bf16 bf16;
@@ -163,11 +165,9 @@ __device__ __forceinline__ void dma16(const void *g, unsigned lds) {
 // offset, so a stream of copies needs no per-lane 64-bit address arithmetic.
 __device__ __forceinline__ void dma16_sbase(const void *base, unsigned off, unsigned lds) {
   const unsigned long long b = (unsigned long long)(uintptr_t)base;
-  // readfirstlane returns int: widen through unsigned, or an address word >= 2^31 would be
-  // sign-extended into the high word
-  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
-  const unsigned long long sb = ((unsigned long long)hi << 32) | lo;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)addr_lo(b));
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)addr_hi(b));
+  const unsigned long long sb = addr_join(lo, hi);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(sb),
                "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
