@@ -8,14 +8,18 @@ action_out_proj + Euler update) for the batch.  Inputs are resident in HBM befor
 Prints one JSON line: chunks/s (whole job), p50/p90/p99 chunk latency, the roofline of the
 dominant kernel, and the float64 oracle timed on the host cores as a CPU baseline.
 
-  python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config 3|4] [--no-cpu-baseline] [--prefill]
+  python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config 3|4] [--no-cpu-baseline] [--no-extras]
   python bench.py --merged-layer            (one merged layer only, its own JSON line)
 
-The roofline unit is one launch of the captured graph (one chunk): achieved = algorithmic bytes
-(batch 1, HBM-bound) or FLOPs (batch 32, MFMA-bound) of the chunk / its mean duration (HIP
-events on the stream the graph is launched on); traffic = HBM bytes of the same chunk from
+Headline (batch 1, HBM-bound): the whole chunk is one launch of the single-launch denoise
+kernel, so its roofline is achieved = algorithmic bytes of the chunk / mean duration of a replay
+(HIP events on the stream the graph is launched on); traffic = HBM bytes of the same chunk from
 rocprofv3 FETCH_SIZE + WRITE_SIZE counters, scaled against a plain copy
 (profiles/*_hbm_traffic.txt, reported only while the kernel sources are unchanged).
+Sub-objects of the same line: "batch32" (the batch-32 ragged workload, MFMA-bound: chunks/s,
+latency, the chunk's MFMA fraction from live events, each GEMM kernel's MFMA fraction from the
+committed kernel statistics) and "prefill_ms" (the B=8, 816-token prefix encoding with the bf16
+and with the FP8 MLP).
 """
 import argparse
 import json
@@ -74,7 +78,8 @@ def cpu_baseline(wl, aw, kc, vc, x1, lens):
                       f"P={P}) in float64 numpy; {dt:.2f} s on {cores} host cores"}
 
 
-SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip", "persist.hip", "common.h", "kernels.h", "persist_plan.h"]
+SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip", "persist.hip", "common.h", "kernels.h", "persist_plan.h",
+           "addr_words.h"]
 
 
 def source_hash():
@@ -123,6 +128,49 @@ def _pmc_sum(run_dir, counter, match):
     return total, n
 
 
+def count_chunks(run_dir, counter, wl):
+    """Chunks in a counter run: one launch of the single-launch kernel per chunk, else one
+    velocity/Euler launch per Euler step."""
+    _, n_single = _pmc_sum(run_dir, counter, lambda n: "denoise_b1_kernel" in n)
+    if n_single:
+        return n_single
+    _, n_vel = _pmc_sum(run_dir, counter, lambda n: "velocity_euler" in n)
+    return n_vel / wl.steps
+
+
+def stats_summary(args):
+    """Writes profiles/<name>_kernel_stats.txt from a rocprofv3 --kernel-trace --stats run: per
+    kernel the calls, calls per unit (chunk or prefill call), mean / min / max duration and share
+    of the library's time, plus the source hash of the kernels profiled."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(args.stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    assert paths, f"no *kernel_stats.csv under {args.stats_dir}"
+    rows = []
+    for path in paths:
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    units = args.units
+    out = os.path.join(ROOT, "profiles", f"{args.name}_kernel_stats.txt")
+    with open(out, "w") as f:
+        f.write(f"# rocprofv3 kernel statistics: {args.title}\n")
+        f.write(f"# command (repository root on the MI355X host): rocprofv3 --kernel-trace --stats --output-format csv "
+                f"-d <dir> -o run -- python3 bench.py {args.bench_args}\n")
+        f.write(f"# summary: python3 bench.py --stats-summary --stats-dir <dir> --name {args.name} --units {units} "
+                f"--title '{args.title}' --bench-args '{args.bench_args}'\n")
+        f.write(f"# {units:g} units profiled; kernels total {total / 1e6:.3f} ms = {total / 1e6 / units:.3f} ms per unit\n")
+        f.write(f"# source_hash: {source_hash()}\n")
+        f.write(f"{'kernel':<96} {'calls':>6} {'per_unit':>9} {'avg_us':>9} {'min_us':>8} {'max_us':>8} {'pct':>6}\n")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            name = r["Name"] if len(r["Name"]) <= 95 else r["Name"][:92] + "..."
+            calls = int(r["Calls"])
+            f.write(f"{name:<96} {calls:>6} {calls / units:>9.4g} {float(r['AverageNs']) / 1e3:>9.2f} "
+                    f"{float(r['MinNs']) / 1e3:>8.2f} {float(r['MaxNs']) / 1e3:>8.2f} "
+                    f"{100 * float(r['TotalDurationNs']) / total:>6.2f}\n")
+    print(open(out).read())
+
+
 def traffic_summary(args):
     """Writes the HBM-traffic summary of one denoise chunk from four rocprofv3 --pmc runs: the
     bench with FETCH_SIZE, with WRITE_SIZE, and the copy calibration with each.  FETCH_SIZE and
@@ -136,16 +184,15 @@ def traffic_summary(args):
     f_scale, w_scale = cal_bytes / (cf * 1024.0), cal_bytes / (cw * 1024.0)
     fetch, _ = _pmc_sum(args.fetch, "FETCH_SIZE", lib)
     write, _ = _pmc_sum(args.write, "WRITE_SIZE", lib)
-    _, n_vel = _pmc_sum(args.fetch, "FETCH_SIZE", lambda n: "velocity_euler" in n)
     from dual_expert_merged_amd.configs import workload
     wl = workload(args.config)
-    chunks = n_vel / wl.steps
+    chunks = count_chunks(args.fetch, "FETCH_SIZE", wl)
     per_chunk = (fetch * 1024.0 * f_scale + write * 1024.0 * w_scale) / chunks
     with open(traffic_file(args.config), "w") as f:
         f.write(f"# HBM traffic of one denoise chunk ({wl.name}), rocprofv3 counters\n")
         f.write("# commands (run from the repository root on the MI355X host, each pass its own run):\n")
         f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -- python3 bench.py "
-                f"--config {args.config} --steps 2 --warmup 0 --no-cpu-baseline\n")
+                f"--config {args.config} --steps 2 --warmup 0 --no-cpu-baseline --no-extras\n")
         f.write("#   rocprofv3 --pmc WRITE_SIZE ... (same)\n")
         f.write("#   rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE --output-format csv -d <cal> -- python3 bench.py --copy-calibration\n")
         f.write(f"#   python3 bench.py --traffic-summary --config {args.config} --fetch <fetch> --write <write> "
@@ -178,7 +225,7 @@ def copy_calibration():
     log(f"[bench] copied {COPY_REPS} x {COPY_BYTES} bytes")
 
 
-def prefill_times(reps=3):
+def prefill_times(reps=3, modes=("bf16", "fp8_mlp")):
     """Prefix encoding of the prefill workload (B=8, 816 tokens, 28 VLM layers) with the bf16
     MLP and with the FP8 E4M3 MLP: mean ms per call over `reps` calls after one warm-up."""
     import torch
@@ -194,6 +241,8 @@ def prefill_times(reps=3):
     s = wl.shape
     out = {}
     for name, shape in (("bf16", s), ("fp8_mlp", replace(s, vlm_mlp_dtype=FP8))):
+        if name not in modes:
+            continue
         ctx = bd.Context(shape, 0)
         dv = bd.DeviceExpert(vlm, s.dtype, fp8_mlp=name == "fp8_mlp")
         cshape = (s.n_layers, wl.batch, s.n_kv_heads, wl.prefix_len, s.head_dim)
@@ -216,7 +265,8 @@ def prefill_times(reps=3):
     flops = 2 * wl.batch * wl.prefix_len * s.n_layers * (s.qkv_rows * s.vlm_hidden + s.vlm_hidden * s.n_q_heads *
                                                          s.head_dim + 3 * s.vlm_ffn * s.vlm_hidden)
     out["workload"] = wl.name
-    out["bf16_mfma_frac_of_gemm_flops"] = round(flops / (out["bf16"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    if "bf16" in out:
+        out["bf16_mfma_frac_of_gemm_flops"] = round(flops / (out["bf16"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
     return out
 
 
@@ -267,42 +317,63 @@ def merged_layer_times(reps=20):
             "workload": "DM0-base merged layer, bf16, B=1, 816 prefix + 50 action tokens"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, choices=[3, 4])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill", action="store_true",
-                    help="also time the prefix encoding (B=8, 816 tokens) with the bf16 and the FP8 MLP")
-    ap.add_argument("--merged-layer", action="store_true",
-                    help="time only one merged layer (both experts, B=1, 816 + 50 tokens) and print it")
-    ap.add_argument("--copy-calibration", action="store_true", help="run only the plain copy for counter scaling")
-    ap.add_argument("--traffic-summary", action="store_true", help="summarise counter runs (no GPU needed)")
-    for name in ("fetch", "write", "cal-fetch", "cal-write"):
-        ap.add_argument("--" + name)
-    args = ap.parse_args()
-    if args.traffic_summary:
-        traffic_summary(args)
-        return
-    if args.merged_layer:
-        print(json.dumps({"merged_layer": merged_layer_times()}), flush=True)
-        return
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the suffix denoise path is built for a single MI355X "
-              f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
-        sys.exit(2)
+def kernel_stats(config):
+    """Per-kernel rows of the committed rocprofv3 summary for a denoise workload: name, calls per
+    chunk, mean duration (us), share of the chunk; and the source hash it was taken at."""
+    path = os.path.join(ROOT, "profiles", f"denoise_{'b1_p816' if config == 3 else 'b32_ragged'}_kernel_stats.txt")
+    rows, src = [], None
+    if not os.path.exists(path):
+        return rows, src
+    with open(path) as f:
+        for line in f:
+            if line.startswith("# source_hash"):
+                src = line.split(":", 1)[1].strip()
+                continue
+            if line.startswith("#") or line.startswith("kernel"):
+                continue
+            parts = line.split()
+            if len(parts) >= 7:
+                try:
+                    rows.append({"kernel": " ".join(parts[:-6]), "per_chunk": float(parts[-5]), "avg_us": float(parts[-4]),
+                                 "pct": float(parts[-1])})
+                except ValueError:
+                    pass
+    return rows, src
 
+
+def b32_kernel_rooflines(wl, lens):
+    """MFMA fraction of each GEMM kernel of the batch-32 chunk from the committed kernel
+    statistics (mean duration per launch) and the algorithmic FLOPs of one launch; reported
+    only while the kernel sources match the summary."""
+    rows, src = kernel_stats(4)
+    if not rows or src != source_hash():
+        return None
+    s = wl.shape
+    M, H, F, Hq, D = wl.batch * s.chunk, s.act_hidden, s.act_ffn, s.n_q_heads, s.head_dim
+    flops = {"EpiQkv": 2 * M * s.qkv_rows * H, "EpiSwiglu": 2 * M * 2 * F * H,
+             "EpiResid": (2 * M * H * Hq * D + 2 * M * H * F) / 2}  # O and down alternate: mean per launch
+    attn_flops = sum(4 * D * Hq * s.chunk * (int(p) + s.chunk) for p in lens)
+    out = []
+    for r in rows:
+        k = next((e for e in flops if e in r["kernel"]), None)
+        if k is None and "attn" not in r["kernel"]:
+            continue
+        f = flops[k] if k else attn_flops
+        out.append({"kernel": r["kernel"][:60], "avg_us": r["avg_us"], "launches_per_chunk": r["per_chunk"],
+                    "share_of_chunk": round(r["pct"] / 100, 4), "gflop_per_launch": round(f / 1e9, 3),
+                    "mfma_frac": round(f / (r["avg_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)})
+    return {"source": "profiles/denoise_b32_ragged_kernel_stats.txt", "kernels": out}
+
+
+def run_denoise(config, steps, warmup):
+    """Replays the captured denoise graph of one workload: HIP events around every replay on
+    its stream, wall clock around the timed replays.  Returns (workload, lens, inputs, result)."""
     import torch
     from dual_expert_merged_amd import binding as bd
     from dual_expert_merged_amd import inputs
     from dual_expert_merged_amd.configs import workload
 
-    wl = workload(args.config)
+    wl = workload(config)
     s = wl.shape
     log(f"[bench] generating inputs for: {wl.name}")
     aw = inputs.make_action_weights(wl)
@@ -317,21 +388,20 @@ def main():
     k = bd.to_device(kc, td)
     v = bd.to_device(vc, td)
     ld = torch.from_numpy(lens).cuda()
-    x0 = torch.from_numpy(x1).cuda()
-    x = x0.clone()
+    x = torch.from_numpy(x1).cuda()
     ws = ctx.workspace(bd.OP_DENOISE, wl.batch, wl.prefix_len)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         plan = ctx.denoise_plan(da, k, v, ld, x, wl.steps, ws, stream=stream)
-        log(f"[bench] plan captured; warmup {args.warmup}")
-        for _ in range(args.warmup):
+        log(f"[bench] {wl.name}: plan captured; warmup {warmup}, timed {steps}")
+        for _ in range(warmup):
             plan.launch(stream=stream)
         stream.synchronize()
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             starts[i].record(stream)
             plan.launch(stream=stream)
             ends[i].record(stream)
@@ -339,42 +409,122 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     lat = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])  # ms per chunk, GPU clock
+    plan.close()
+    del k, v, ws, da
+    ctx.close()
+    torch.cuda.empty_cache()
+    res = {"value": wl.batch * steps / wall, "ms": wall * 1e3 / steps, "lat": lat,
+           "single_launch": config == 3}
+    return wl, lens, (aw, kc, vc, x1), res
+
+
+def latency(lat):
+    return {"p50": round(float(np.percentile(lat, 50)), 4), "p90": round(float(np.percentile(lat, 90)), 4),
+            "p99": round(float(np.percentile(lat, 99)), 4), "mean": round(float(np.mean(lat)), 4)}
+
+
+def b1_roofline(wl, lens, lat):
+    """Batch 1: one launch of the single-launch denoise kernel is one chunk (all 10 Euler steps,
+    28 layers); the graph replay timed around it also holds the small kernel that clears its
+    hand-off counters (a few us of the ~10 ms)."""
     alg = algorithmic(wl, lens)
-    ms = wall * 1e3 / args.steps
-    value = wl.batch * args.steps / wall
     chunk_s = float(np.mean(lat)) * 1e-3
     gbs = alg["bytes"] / chunk_s / 1e9
-    tfs = alg["flops"] / chunk_s / 1e12
-    if args.config == 3:  # batch 1: the weights and the cache stream once per step (55 FLOP/B)
-        roof = {"bound": "hbm", "kernel": "denoise graph replay (all kernels of one chunk)",
-                "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic(args.config),
-                "algorithmic_bytes_per_launch": alg["bytes"], "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4)}
-    else:  # batch 32: the GEMMs dominate (435 FLOP/B over the chunk)
-        roof = {"bound": "mfma", "kernel": "denoise graph replay (all kernels of one chunk)",
-                "achieved": round(tfs, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tfs / BF16_PEAK_TFLOPS, 4), "traffic": read_traffic(args.config),
-                "algorithmic_flops_per_launch": alg["flops"], "algorithmic_bytes_per_launch": alg["bytes"],
-                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return {"bound": "hbm", "kernel": "dm::pk::denoise_b1_kernel (one launch = one chunk)",
+            "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic(3), "algorithmic_bytes_per_launch": alg["bytes"],
+            "launch_us": round(chunk_s * 1e6, 1)}
+
+
+def b32_summary(steps=20, warmup=3):
+    """The batch-32 ragged workload (MFMA-bound): chunks/s, latency, the whole chunk's MFMA and
+    HBM fractions from live HIP events, per-kernel MFMA fractions from the committed profile, and
+    the HBM traffic of one chunk from the committed counter summary."""
+    wl, lens, _, res = run_denoise(4, steps, warmup)
+    alg = algorithmic(wl, lens)
+    chunk_s = float(np.mean(res["lat"])) * 1e-3
+    tfs, gbs = alg["flops"] / chunk_s / 1e12, alg["bytes"] / chunk_s / 1e9
+    return {"workload": wl.name, "value": round(res["value"], 2), "unit": "chunks/s", "steps": steps,
+            "latency_ms": latency(res["lat"]),
+            "roofline": {"bound": "mfma", "kernel": "all kernels of one chunk (graph replay)", "achieved": round(tfs, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tfs / BF16_PEAK_TFLOPS, 4),
+                         "traffic": read_traffic(4), "algorithmic_flops_per_launch": alg["flops"],
+                         "algorithmic_bytes_per_launch": alg["bytes"], "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "per_kernel": b32_kernel_rooflines(wl, lens)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, choices=[3, 4],
+                    help="the workload of the headline value (3: batch 1, 4: batch 32 ragged)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline workload only: no batch-32 and prefill sub-objects")
+    ap.add_argument("--merged-layer", action="store_true",
+                    help="time only one merged layer (both experts, B=1, 816 + 50 tokens) and print it")
+    ap.add_argument("--copy-calibration", action="store_true", help="run only the plain copy for counter scaling")
+    ap.add_argument("--prefill-only", choices=["both", "bf16", "fp8_mlp"],
+                    help="time only the prefix encoding (B=8, 816 tokens) with the bf16 MLP, the FP8 MLP or both")
+    ap.add_argument("--traffic-summary", action="store_true", help="summarise counter runs (no GPU needed)")
+    ap.add_argument("--stats-summary", action="store_true", help="summarise a --kernel-trace --stats run (no GPU)")
+    for name in ("fetch", "write", "cal-fetch", "cal-write", "stats-dir", "name", "title", "bench-args"):
+        ap.add_argument("--" + name)
+    ap.add_argument("--units", type=float, default=1.0)
+    args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
+    if args.stats_summary:
+        stats_summary(args)
+        return
+    if args.prefill_only:
+        modes = ("bf16", "fp8_mlp") if args.prefill_only == "both" else (args.prefill_only,)
+        print(json.dumps({"prefill_ms": prefill_times(modes=modes)}), flush=True)
+        return
+    if args.merged_layer:
+        print(json.dumps({"merged_layer": merged_layer_times()}), flush=True)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the suffix denoise path is built for a single MI355X "
+              f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
+        sys.exit(2)
+
+    wl, lens, (aw, kc, vc, x1), res = run_denoise(args.config, args.steps, args.warmup)
+    s = wl.shape
+    if args.config == 3:
+        roof = b1_roofline(wl, lens, res["lat"])
+    else:
+        alg = algorithmic(wl, lens)
+        tfs = alg["flops"] / (float(np.mean(res["lat"])) * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "all kernels of one chunk (graph replay)", "achieved": round(tfs, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tfs / BF16_PEAK_TFLOPS, 4),
+                "traffic": read_traffic(4), "algorithmic_flops_per_launch": alg["flops"]}
     out = {
         "metric": "action chunks/s + p50 chunk latency (DM0-base suffix, 10 steps); % HBM/MFMA peak",
-        "value": round(value, 2), "unit": "chunks/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": round(res["value"], 2), "unit": "chunks/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": s.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "prefix_len": int(lens.max()),
                    "prefix_len_mean": float(lens.mean()), "chunk": s.chunk, "action_dim": s.action_dim,
                    "euler_steps": wl.steps, "layers": s.n_layers, "parallelism": "single GPU"},
-        "latency_ms": {"p50": round(float(np.percentile(lat, 50)), 4), "p90": round(float(np.percentile(lat, 90)), 4),
-                       "p99": round(float(np.percentile(lat, 99)), 4), "mean": round(float(np.mean(lat)), 4)},
+        "latency_ms": latency(res["lat"]),
         "roofline": roof,
     }
-    plan.close()
-    if args.prefill:
-        log("[bench] timing the prefix encoding (bf16 and FP8 MLP)")
-        out["prefill_ms"] = prefill_times()
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
         out["cpu_baseline"] = cpu_baseline(wl, aw, kc, vc, x1, lens)
+    del kc, vc
+    if not args.no_extras:
+        if args.config == 3:
+            out["batch32"] = b32_summary()
+        log("[bench] timing the prefix encoding (bf16 and FP8 MLP)")
+        out["prefill_ms"] = prefill_times()
     print(json.dumps(out), flush=True)
 
 
