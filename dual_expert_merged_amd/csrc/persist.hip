@@ -667,7 +667,8 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
           const int rg = min(c16, FC - 1), ru = FC + min(c16, FC - 1);
 #pragma unroll
           for (int u = 0; u < 16; ++u) {
-            bf16x8 ag = afrag(L_GU, 24, rg, 16 * hw + u), au = afrag(L_GU, 24, ru, 16 * hw + u);
+            const int kc = 16 * hw + u;
+            bf16x8 ag = afrag(L_GU, 24, rg, kc), au = afrag(L_GU, 24, ru, kc);
             if (!rok) { ag = zero_frag<bf16>(); au = zero_frag<bf16>(); }
             acc0 = Mfma<bf16>::mma(ag, bf[u], acc0);
             acc1 = Mfma<bf16>::mma(au, bf[u], acc1);
