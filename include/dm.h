@@ -135,8 +135,9 @@ size_t dm_workspace_bytes(const dm_ctx *ctx, dm_op op, int B, int P_cap);
  * P_b tokens, and writes every layer's post-RoPE K and V into k_cache / v_cache
  * [L][B][Hkv][P_cap][D] (rows >= P_b left untouched).  prefix_embeds is not modified.
  * With vlm_mlp_dtype = DM_FP8_E4M3 (page section 6.3) the MLP gate/up/down weights are E4M3
- * codes with per-output-channel scales (see dm_quantize_fp8_rows); each MLP input row
- * (RMSNorm output) and each SwiGLU activation row is quantised per token the same way, and
+ * codes with per-output-channel scales (see dm_quantize_fp8_rows); each MLP input row (the
+ * gain-scaled residual h * g in bf16; RMSNorm's 1/rms scales the GEMM output) and each SwiGLU
+ * activation row (bf16) is quantised per token the same way, and
  * y[m][n] = r_m * s_n * sum_k a_q[m][k] w_q[n][k] accumulates in float32. */
 dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm /* (host) */,
                         const float *prefix_embeds, const int32_t *prefix_lens, int B, int P_cap,
