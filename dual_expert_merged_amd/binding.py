@@ -25,7 +25,7 @@ OP_PREFILL, OP_MERGED_LAYER, OP_DENOISE = 0, 1, 2
 _DT = {F32: DM_F32, BF16: DM_BF16, FP8: DM_FP8_E4M3}
 EXPORTS = ["dm_version", "dm_last_error", "dm_ctx_create", "dm_ctx_destroy", "dm_workspace_bytes",
            "dm_prefill_kv", "dm_merged_layer", "dm_suffix_denoise", "dm_denoise_plan_create",
-           "dm_denoise_plan_launch", "dm_denoise_plan_destroy", "dm_quantize_fp8_rows"]
+           "dm_denoise_plan_launch", "dm_denoise_plan_destroy", "dm_quantize_fp8_rows", "dm_suffix_denoise_noalloc"]
 
 
 class DMError(RuntimeError):
@@ -80,6 +80,7 @@ def lib():
         L.dm_denoise_plan_destroy.argtypes = [vp]
         L.dm_denoise_plan_destroy.restype = None
         L.dm_quantize_fp8_rows.argtypes = [vp, vp, vp, i, i, vp]
+        L.dm_suffix_denoise_noalloc.argtypes = [vp, C.POINTER(ActionWeightsC), vp, vp, vp, i, i, vp, i, vp]
         for name in EXPORTS:
             if name not in ("dm_version", "dm_last_error", "dm_ctx_destroy", "dm_workspace_bytes",
                             "dm_denoise_plan_destroy"):
@@ -200,6 +201,11 @@ class Context:
         B, P_cap = k_cache.shape[1], k_cache.shape[3]
         check(lib().dm_suffix_denoise(self.h, C.byref(aw.c), ptr(k_cache), ptr(v_cache), ptr(lens), B, P_cap,
                                       ptr(x), num_steps, ptr(ws), ws.numel(), stream_handle(stream)))
+
+    def suffix_denoise_noalloc(self, aw: DeviceAction, k_cache, v_cache, lens, x, num_steps, stream=None):
+        B, P_cap = k_cache.shape[1], k_cache.shape[3]
+        check(lib().dm_suffix_denoise_noalloc(self.h, C.byref(aw.c), ptr(k_cache), ptr(v_cache), ptr(lens), B, P_cap,
+                                              ptr(x), num_steps, stream_handle(stream)))
 
     def denoise_plan(self, aw: DeviceAction, k_cache, v_cache, lens, x, num_steps, ws, stream=None):
         B, P_cap = k_cache.shape[1], k_cache.shape[3]

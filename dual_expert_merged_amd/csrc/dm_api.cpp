@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -52,7 +53,37 @@ struct dm_ctx {
   Dt dt;
   size_t es;         // bytes per element of the weight dtype
   bool single_ok;    // the device holds all workgroups of the single-launch batch-1 denoise
+  hipError_t scratch_status;  // result of looking up the static scratch buffer on `device`
 };
+
+// ---------------------------------------------------------------- static scratch buffer
+// The workspace of dm_suffix_denoise_noalloc: a file-scope device array that every GPU the
+// library runs on holds until the process ends.  In host code `scratch` names a host-side
+// shadow, not device memory; its address on each device is looked up once (dm_ctx_create, with
+// that device current) and only that address is handed to kernels.
+namespace {
+constexpr size_t kScratchBytes = DM_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Looks up this device's copy of `scratch`; the caller has made `device` current.
+hipError_t scratch_setup(int device) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void *p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e == hipSuccess) g_scratch_ptr[device] = p;
+  return e;
+}
+
+void *scratch_ptr(int device) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return device >= 0 && device < kMaxDevices ? g_scratch_ptr[device] : nullptr;
+}
+}  // namespace
 
 struct dm_plan {
   hipGraph_t graph;
@@ -495,10 +526,13 @@ dm_status dm_ctx_create(const dm_config *cfg, int device, dm_ctx **out) {
   ctx->dt = cfg->dtype == DM_BF16 ? DT_BF16 : DT_F32;
   ctx->es = cfg->dtype == DM_BF16 ? 2 : 4;
   // the single-launch denoise needs all of its workgroups resident at once
+  // and, once per device, the address of the static scratch buffer
   int prev = -1;
   ctx->single_ok = false;
+  ctx->scratch_status = hipErrorNotReady;
   if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(device) == hipSuccess) {
     ctx->single_ok = persist_check_device(device) == hipSuccess;
+    ctx->scratch_status = scratch_setup(device);
     (void)hipSetDevice(prev);
   }
   (void)hipGetLastError();
@@ -520,6 +554,26 @@ dm_status dm_suffix_denoise(dm_ctx *ctx, const dm_action_weights *aw, const void
   TRY(set_device(ctx));
   hipStream_t s = (hipStream_t)stream;
   TRY(enqueue_denoise(ctx, aw, k_cache, v_cache, prefix_lens, B, P_cap, x, num_steps, ws, s));
+  HIP_TRY(hipGetLastError());
+  return DM_OK;
+}
+
+dm_status dm_suffix_denoise_noalloc(dm_ctx *ctx, const dm_action_weights *aw, const void *k_cache,
+                                    const void *v_cache, const int32_t *prefix_lens, int B, int P_cap, float *x,
+                                    int num_steps, void *stream) {
+  REQUIRE(ctx, DM_ERR_INVALID_ARG, "ctx is NULL");
+  REQUIRE(B >= 1 && P_cap >= 1, DM_ERR_INVALID_ARG, "B and P_cap must be >= 1");
+  const size_t need = make_layout(ctx->cfg, ctx->es, DM_OP_DENOISE, B, P_cap).total;
+  REQUIRE(need <= kScratchBytes, DM_ERR_WORKSPACE,
+          "dm_suffix_denoise_noalloc: B=%d, P_cap=%d need %zu bytes of scratch, more than the static %zu-byte "
+          "buffer; use dm_suffix_denoise with a workspace",
+          B, P_cap, need, kScratchBytes);
+  void *ws = scratch_ptr(ctx->device);
+  REQUIRE(ws, DM_ERR_HIP, "no address of the static scratch buffer on device %d: %s", ctx->device,
+          hipGetErrorString(ctx->scratch_status));
+  TRY(check_denoise(ctx, aw, k_cache, v_cache, prefix_lens, B, P_cap, x, num_steps, ws, kScratchBytes));
+  TRY(set_device(ctx));
+  TRY(enqueue_denoise(ctx, aw, k_cache, v_cache, prefix_lens, B, P_cap, x, num_steps, ws, (hipStream_t)stream));
   HIP_TRY(hipGetLastError());
   return DM_OK;
 }

@@ -169,6 +169,21 @@ dm_status dm_suffix_denoise(dm_ctx *ctx, const dm_action_weights *aw /* (host) *
                             int B, int P_cap, float *x, int num_steps,
                             void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): dm_suffix_denoise with its workspace taken from a
+ * static device buffer of DM_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends (its address on a device is looked up by dm_ctx_create).  A B and
+ * P_cap whose dm_workspace_bytes(DM_OP_DENOISE) exceed it return DM_ERR_WORKSPACE and launch
+ * nothing.  Allocates nothing.  All calls on one GPU share that GPU's buffer, which keeps the
+ * previous call's contents (what must start at zero is cleared by the call's own kernels): calls
+ * that overlap on one GPU (two streams, two threads, or two contexts) race and their results
+ * are undefined. */
+#define DM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+dm_status dm_suffix_denoise_noalloc(dm_ctx *ctx, const dm_action_weights *aw /* (host) */,
+                                    const void *k_cache, const void *v_cache,
+                                    const int32_t *prefix_lens, int B, int P_cap, float *x,
+                                    int num_steps, void *stream);
+
 /* Same computation captured once as a hipGraph (page section 6.5): every pointer, B, P_cap
  * and num_steps are fixed at capture; prefix_lens and the contents of x and the caches stay
  * device data read at replay.  Capture runs on `stream` and synchronizes it. */
