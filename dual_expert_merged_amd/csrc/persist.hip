@@ -67,7 +67,8 @@ constexpr int L_TOTAL = L_GAIN + (LMAX * 2 + 1) * HC * 4;
 static_assert(L_TOTAL <= 160 * 1024, "LDS budget");
 constexpr int SEG_LDS[NSEG] = {L_QKV, L_KV, L_O, L_GU, L_D};
 
-constexpr long MAX_POLLS = 1L << 21;  // ~2 s of polling: far beyond any legitimate wait
+constexpr long MAX_POLLS = 1L << 21;     // ~2 s of polling: far beyond any legitimate wait
+constexpr int OUT_OF_RANGE = 0x40000000;  // a buffer offset past every workspace
 
 __device__ __forceinline__ rsrc_t mkrsrc(const void *p, long bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
@@ -97,6 +98,15 @@ __device__ __forceinline__ void stl4f(bool l2, rsrc_t r, int off, float v) {
   if (l2) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, off, 0, 0);
   else __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, off, 0, SC1);
 }
+// dma16 (global -> LDS, 16 bytes per lane) with the non-temporal hint: each weight and cached
+// key is read once per layer-step, so its lines are streamed rather than kept in L2 ahead of the
+// hand-off buffers.
+__device__ __forceinline__ void dma16_stream(const void *g, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+template <int N> using Lines = std::integral_constant<int, N>;
+template <int N> using Ph = std::integral_constant<int, N>;
 __device__ __forceinline__ unsigned xcc_id() {
   unsigned v;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
@@ -224,14 +234,16 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
   const int o_vp = a.off_vpart + x * NG * S * A * 4, o_xs = a.off_xs + x * S * A * 4;
 
   // ------------------------------------------------------------------ copy (DMA) waves
-  // Segment `seg` of layer-step ls: this copy wave's share of its 1 KB lines.
-  auto issue = [&](auto segc, int ls) {
+  // Lines [u0, u1) of this copy wave's share of segment `seg` (1 KB each) for layer-step ls.
+  auto issue = [&](auto segc, int ls, auto u0c, auto u1c) {
     constexpr int seg = decltype(segc)::value;
     const int l = ls % L;
     constexpr int per = SEG_LINES[seg] / NDW;
+    constexpr int u0 = decltype(u0c)::value, u1 = decltype(u1c)::value;
+    static_assert(0 <= u0 && u0 < u1 && u1 <= per, "line range");
     const unsigned base = lds_addr(smem + SEG_LDS[seg]);
 #pragma unroll
-    for (int u = 0; u < per; ++u) {
+    for (int u = u0; u < u1; ++u) {
       const int line = dw * per + u;
       const char *src;
       if constexpr (seg == SEG_KV) {
@@ -249,41 +261,46 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
         else w = a.w_down + (long)l * H * F;
         src = (const char *)(w + e);
       }
-      dma16(src, base + line * 1024);
+      dma16_stream(src, base + line * 1024);
     }
   };
   const int total_ls = N * L;
-  // what a copy wave does at the start of each phase: copy the segment the previous phase freed
-  // (for the next layer-step), then wait until this phase's segment has landed.  The counts are
-  // this wave's copies issued after the awaited segment (copies complete in issue order); in the
-  // last layer-step nothing further is issued, so it waits for everything.
-  enum { PH_QKV, PH_ATT, PH_MRG, PH_OPJ, PH_RDO, PH_GU, PH_DN, PH_RDD, PH_OTHER };
-  auto copy_step = [&](int ph, int ls) {
-    if (cw) return;
-    const bool more = ls + 1 < total_ls;
-    switch (ph) {
-      case PH_QKV: if (more) vm_wait<26>(); else vm_wait<0>(); break;
-      case PH_ATT:
-        if (more) { issue(std::integral_constant<int, SEG_QKV>{}, ls + 1); vm_wait<30>(); } else vm_wait<0>();
-        break;
-      case PH_MRG: if (more) issue(std::integral_constant<int, SEG_KV>{}, ls + 1); break;
-      case PH_OPJ: if (more) vm_wait<30>(); else vm_wait<0>(); break;
-      case PH_RDO: if (more) issue(std::integral_constant<int, SEG_O>{}, ls + 1); break;
-      case PH_GU: if (more) vm_wait<22>(); else vm_wait<0>(); break;
-      case PH_DN:
-        if (more) { issue(std::integral_constant<int, SEG_GU>{}, ls + 1); vm_wait<28>(); } else vm_wait<0>();
-        break;
-      case PH_RDD: if (more) issue(std::integral_constant<int, SEG_D>{}, ls + 1); break;
-      default: break;
+  // What a copy wave does at the start of phase PH of layer-step ls: the pieces and the wait of
+  // COPY_PLAN / COPY_WAIT (persist_plan.h, where the schedule is explained).
+  auto copy_step = [&](auto phc, int ls) {
+    constexpr int ph = decltype(phc)::value;
+    if constexpr (cw || ph >= NPH) {
+      return;
+    } else {
+      const bool more = ls + 1 < total_ls;
+      auto piece = [&](auto kc) {
+        constexpr CopyPiece c = COPY_PLAN[ph][decltype(kc)::value];
+        if constexpr (c.seg >= 0) {
+          if (c.next == 0 || more)
+            issue(std::integral_constant<int, c.seg>{}, ls + c.next, Lines<c.u0>{}, Lines<c.u1>{});
+        }
+      };
+      piece(std::integral_constant<int, 0>{});
+      piece(std::integral_constant<int, 1>{});
+      if constexpr (COPY_WAIT[ph] >= 0) {
+        if (more) vm_wait<COPY_WAIT[ph]>();
+        else vm_wait<0>();
+      }
     }
   };
+  static_assert(COPY_PIECES == 2, "copy_step issues two pieces per phase");
+  using QKVs = std::integral_constant<int, SEG_QKV>;
+  using KVs = std::integral_constant<int, SEG_KV>;
+  using Os = std::integral_constant<int, SEG_O>;
+  using GUs = std::integral_constant<int, SEG_GU>;
+  using Ds = std::integral_constant<int, SEG_D>;
 
   // ------------------------------------------------------------------ synchronisation
   int n_bar = 0;  // group barriers passed
   // Phase entry: lane 0 of wave 0 waits for the phase's inputs (group barrier or the 8 flags of
   // workgroups (x', i)), the copy waves do their copy step; then one workgroup barrier.  Returns
   // false when the chunk is aborted.
-  auto enter = [&](int ph, int ls, int flag_target) {
+  auto enter = [&](auto ph, int ls, int flag_target) {
     lane = opaque(tid) & 63;  // lane-derived addresses are rebuilt in every phase
     wave = opaque(tid) >> 6;
     g = lane >> 4;
@@ -323,10 +340,11 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
     const int chunk = (kc & 1) * 4 + g;
     return *reinterpret_cast<const bf16x8 *>(smem + lds_off + ((kc >> 1) * R + row) * 128 + ((chunk ^ (row & 7)) << 4));
   };
-  // B fragment: activation [S][ld] bf16 (device-coherent), token tile tt, inputs k .. k+31
+  // B fragment: activation [S][ld] bf16 (device-coherent), token tile tt, inputs k .. k+31.  Rows
+  // past S take an offset beyond the workspace: the buffer load returns 0 without a memory access.
   auto bfrag = [&](int off, int ld, int k) {
-    const int tok = min(16 * tt + c16, S - 1);
-    return as_bf16x8(ld16(rw, off + (tok * ld + k + 8 * g) * 2));
+    const int tok = 16 * tt + c16;
+    return as_bf16x8(ld16(rw, tok < S ? off + (tok * ld + k + 8 * g) * 2 : OUT_OF_RANGE));
   };
   // 1/rms of every token from the group's per-16-column sums of squares, into LDS: the loads
   // (issued after the phase's operand loads, so they share one round trip), then the sums
@@ -404,7 +422,11 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
     }
   }
   if (!cw) {  // the first layer-step's segments, in consumption order
-    issue(std::integral_constant<int, SEG_QKV>{}, 0); issue(std::integral_constant<int, SEG_KV>{}, 0); issue(std::integral_constant<int, SEG_O>{}, 0); issue(std::integral_constant<int, SEG_GU>{}, 0); issue(std::integral_constant<int, SEG_D>{}, 0);
+    issue(QKVs{}, 0, Lines<0>{}, Lines<SEG_LINES[SEG_QKV] / NDW>{});
+    issue(KVs{}, 0, Lines<0>{}, Lines<SEG_LINES[SEG_KV] / NDW>{});
+    issue(Os{}, 0, Lines<0>{}, Lines<SEG_LINES[SEG_O] / NDW>{});
+    issue(GUs{}, 0, Lines<0>{}, Lines<SEG_LINES[SEG_GU] / NDW>{});
+    issue(Ds{}, 0, Lines<0>{}, Lines<SEG_LINES[SEG_D] / NDW>{});
   }
 
   // action_in_proj + bias + time embedding of step k (t = 1 - k/N), h*gain of layer 0
@@ -453,7 +475,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
     for (int l = 0; l < L && alive; ++l) {
       const int ls = k * L + l;
       // ================================================================ P1: QKV
-      if (!(alive = enter(PH_QKV, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_QKV>{}, ls, 0))) break;
       {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (cw) {
@@ -489,7 +511,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_group();
 
       // ================================================================ P2: attention chunk i
-      if (!(alive = enter(PH_ATT, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_ATT>{}, ls, 0))) break;
       {
         const int nkp = max(0, min(Pc, P - i * Pc));  // prefix keys of this chunk
         const int s0 = i * Sc, nks = max(0, min(Sc, S - s0));
@@ -579,7 +601,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_group();
 
       // ================================================================ P3: merge the key chunks
-      if (!(alive = enter(PH_MRG, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_MRG>{}, ls, 0))) break;
       {
         const int nvec = 2 * S * (D / 8), per = (nvec + NG - 1) / NG;
         const int v = i * per + (tid >> 3), q = tid & 7;
@@ -627,7 +649,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_group();
 
       // ================================================================ P4: O-projection partial
-      if (!(alive = enter(PH_OPJ, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_OPJ>{}, ls, 0))) break;
       if (cw) {
         bf16x8 bf[8];
 #pragma unroll
@@ -641,7 +663,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_flag(epp * ls + 1);
 
       // ================================================================ P5: residual += O-proj
-      if (!(alive = enter(PH_RDO, ls, epp * ls + 1))) break;
+      if (!(alive = enter(Ph<PH_RDO>{}, ls, epp * ls + 1))) break;
       if (hown) {
         i32x4 pv[NX];
 #pragma unroll
@@ -655,7 +677,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_group();
 
       // ================================================================ P6: gate/up + SwiGLU
-      if (!(alive = enter(PH_GU, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_GU>{}, ls, 0))) break;
       {
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
         if (cw) {
@@ -696,7 +718,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_group();
 
       // ================================================================ P7: down-projection partial
-      if (!(alive = enter(PH_DN, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_DN>{}, ls, 0))) break;
       if (cw) {
         bf16x8 bf[12];
 #pragma unroll
@@ -710,7 +732,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_flag(epp * ls + 2);
 
       // ================================================================ P8: residual += down
-      if (!(alive = enter(PH_RDD, ls, epp * ls + 2))) break;
+      if (!(alive = enter(Ph<PH_RDD>{}, ls, epp * ls + 2))) break;
       if (hown) {
         i32x4 pv[NX];
 #pragma unroll
@@ -740,7 +762,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
     }
     if (!alive) break;
     // ================================================================== velocity + Euler
-    if (!(alive = enter(PH_OTHER, 0, 0))) break;
+    if (!(alive = enter(Ph<NPH>{}, 0, 0))) break;
     if (xown) {
       const int t = xi / A, q = xi - t * A;
       float v = 0.f;
@@ -758,7 +780,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
     if (k + 1 == N) break;
     leave_group();
     // ================================================================== next step's input
-    if (!(alive = enter(PH_OTHER, 0, 0))) break;
+    if (!(alive = enter(Ph<NPH>{}, 0, 0))) break;
     embed(k + 1, false);
     publish_h(gain_attn(0));
     leave_group();

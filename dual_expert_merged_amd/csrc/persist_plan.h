@@ -56,6 +56,36 @@ static_assert(SEG_LINES[0] % NDW == 0 && SEG_LINES[1] % NDW == 0 && SEG_LINES[2]
                   SEG_LINES[3] % NDW == 0 && SEG_LINES[4] % NDW == 0,
               "every segment splits evenly over the copy waves");
 
+// The phases of a layer-step, and the one that reads each segment.
+enum Phase { PH_QKV = 0, PH_ATT, PH_MRG, PH_OPJ, PH_RDO, PH_GU, PH_DN, PH_RDD, NPH };
+constexpr int SEG_READER[NSEG] = {PH_QKV, PH_ATT, PH_OPJ, PH_GU, PH_DN};
+
+// Copy schedule of a copy wave, in 1 KB lines of its share of each segment (SEG_LINES / NDW
+// lines).  At the start of phase ph of layer-step ls the wave issues up to two pieces
+// {segment, layer-step (0: ls, 1: ls + 1), first line, end line} (seg < 0: none), then waits
+// until at most COPY_WAIT[ph] of its copies are in flight (-1: no wait).  Copies complete in
+// issue order, so a wait count is the number of this wave's copies issued after the last line
+// of the segment the phase reads.  A segment is refilled for ls + 1 only after its reader phase
+// of ls, in pieces spread over the following phases, so that no phase starts behind a large
+// burst of copies.  Layer-step 0's segments are all copied before the first phase (the pieces
+// "of ls" in layer-step 0 then repeat identical bytes), and in the last layer-step nothing of a
+// next one is issued and every wait is for all copies.
+struct CopyPiece {
+  int seg, next, u0, u1;
+};
+constexpr int COPY_PIECES = 2;
+constexpr CopyPiece COPY_PLAN[NPH][COPY_PIECES] = {
+    {{SEG_GU, 0, 10, 12}, {SEG_D, 0, 2, 4}},  // QKV
+    {{SEG_QKV, 1, 0, 4}, {-1, 0, 0, 0}},      // ATT
+    {{SEG_QKV, 1, 4, 8}, {-1, 0, 0, 0}},      // MRG
+    {{SEG_KV, 1, 0, 4}, {-1, 0, 0, 0}},       // OPJ
+    {{SEG_O, 1, 0, 4}, {-1, 0, 0, 0}},        // RDO
+    {{SEG_D, 0, 4, 6}, {-1, 0, 0, 0}},        // GU
+    {{SEG_GU, 1, 0, 6}, {-1, 0, 0, 0}},       // DN
+    {{SEG_GU, 1, 6, 10}, {SEG_D, 1, 0, 2}},   // RDD
+};
+constexpr int COPY_WAIT[NPH] = {26, 26, -1, 30, -1, 20, 6, -1};
+
 // Chunk permutation of the 256-byte key / value rows: chunk c of row r sits at position
 // c ^ kv_swz(r), which keeps the score-tile reads and the transposing value reads free of bank
 // conflicts.

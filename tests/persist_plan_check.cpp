@@ -1,7 +1,9 @@
 // Host-side check of the single-launch denoise's copy maps (persist_plan.h), built with g++ by
 // tests/test_persist_plan.py: every 16-byte piece a workgroup copies lies inside its matrix or
 // cache block, every LDS position of a segment is filled exactly once, and the workgroups of a
-// group together copy exactly the weight rows (and key rows) the group owns.
+// group together copy exactly the weight rows (and key rows) the group owns; the copy schedule
+// (COPY_PLAN / COPY_WAIT) delivers every segment before it is read and never overwrites one
+// while it is read.
 #include <algorithm>
 #include <cstdio>
 #include <set>
@@ -116,6 +118,63 @@ int main() {
       const int Sc = action_chunk(SMAX);
       CHECK(Pc + Sc <= KROWS, "P %d: prefix + action keys exceed the key rows\n", P);
     }
+  // The copy schedule, simulated per copy wave over whole chunks of 1..7 layer-steps: copies
+  // complete in issue order and a wait retires the oldest until at most COPY_WAIT remain.  When a
+  // phase reads a segment, every line must hold that layer-step's data with no copy of other data
+  // still in flight to it; a refill for the next layer-step may only start after the segment's
+  // reader phase; at most 63 copies are ever in flight (the counter's range).
+  for (int T = 1; T <= 7; ++T) {
+    struct Copy { int seg, u, ls; };
+    std::vector<Copy> fifo;
+    int holds[NSEG][16];
+    for (auto &h : holds)
+      for (int &v : h) v = -1;
+    auto per = [](int seg) { return SEG_LINES[seg] / NDW; };
+    auto retire_to = [&](int n) {
+      while ((int)fifo.size() > n) {
+        holds[fifo.front().seg][fifo.front().u] = fifo.front().ls;
+        fifo.erase(fifo.begin());
+      }
+    };
+    for (int seg : {SEG_QKV, SEG_KV, SEG_O, SEG_GU, SEG_D})
+      for (int u = 0; u < per(seg); ++u) fifo.push_back({seg, u, 0});
+    CHECK((int)fifo.size() <= 63, "start-up copies exceed the counter\n");
+    for (int ls = 0; ls < T; ++ls) {
+      const bool more = ls + 1 < T;
+      for (int ph = 0; ph < NPH; ++ph) {
+        for (int k = 0; k < COPY_PIECES; ++k) {
+          const CopyPiece c = COPY_PLAN[ph][k];
+          if (c.seg < 0 || (c.next && !more)) continue;
+          CHECK(c.u0 >= 0 && c.u0 < c.u1 && c.u1 <= per(c.seg), "phase %d piece %d: line range\n", ph, k);
+          if (c.next) CHECK(SEG_READER[c.seg] < ph, "phase %d refills segment %d before its reader\n", ph, c.seg);
+          else CHECK(SEG_READER[c.seg] > ph, "phase %d copies segment %d of this layer-step after its reader\n", ph, c.seg);
+          for (int u = c.u0; u < c.u1; ++u) fifo.push_back({c.seg, u, ls + c.next});
+        }
+        CHECK((int)fifo.size() <= 63, "T %d ls %d phase %d: %zu copies in flight\n", T, ls, ph, fifo.size());
+        if (COPY_WAIT[ph] >= 0) retire_to(more ? COPY_WAIT[ph] : 0);
+        for (int seg = 0; seg < NSEG; ++seg) {
+          if (SEG_READER[seg] != ph) continue;
+          for (int u = 0; u < per(seg); ++u) {
+            CHECK(holds[seg][u] == ls, "T %d ls %d: segment %d line %d holds layer-step %d when read\n", T, ls, seg, u,
+                  holds[seg][u]);
+            for (const Copy &f : fifo)
+              CHECK(!(f.seg == seg && f.u == u && f.ls != ls), "T %d ls %d: segment %d line %d overwritten while read\n",
+                    T, ls, seg, u);
+          }
+        }
+      }
+    }
+    retire_to(0);
+  }
+  // each segment is refilled exactly once per layer-step (and the total matches SEG_LINES)
+  for (int seg = 0; seg < NSEG; ++seg) {
+    std::vector<int> n(SEG_LINES[seg] / NDW, 0);
+    for (int ph = 0; ph < NPH; ++ph)
+      for (int k = 0; k < COPY_PIECES; ++k)
+        if (COPY_PLAN[ph][k].seg == seg)
+          for (int u = COPY_PLAN[ph][k].u0; u < COPY_PLAN[ph][k].u1; ++u) n[u] += 1;
+    for (size_t u = 0; u < n.size(); ++u) CHECK(n[u] == 1, "segment %d line %zu copied %d times per layer-step\n", seg, u, n[u]);
+  }
   // the swizzle is a permutation of the 16 chunk positions for every row
   for (int r = 0; r < KROWS; ++r) {
     std::set<int> p;
