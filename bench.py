@@ -171,6 +171,58 @@ def stats_summary(args):
     print(open(out).read())
 
 
+def counter_summary(args):
+    """Writes profiles/<name>_mfma_counters.txt from a rocprofv3 --pmc run (derived counters such
+    as MfmaUtil and MfmaFlopsBF16 / MfmaFlopsF8, with --kernel-trace for the durations): per
+    kernel the dispatches, the mean of every counter per dispatch, the mean duration, and the
+    achieved MFMA rate (counted FLOPs / duration) as a fraction of the dense peak of its dtype."""
+    import csv
+    import glob
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in glob.glob(os.path.join(args.stats_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    durs = collections.defaultdict(list)
+    for path in glob.glob(os.path.join(args.stats_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    assert vals, f"no counter csv under {args.stats_dir}"
+    # FLOPs per dispatch: the derived bf16 metric, or raw MFMA operation counts (units of 512 FLOPs)
+    flop_counters = {"MfmaFlopsBF16": (1, BF16_PEAK_TFLOPS), "SQ_INSTS_VALU_MFMA_MOPS_BF16": (512, BF16_PEAK_TFLOPS),
+                     "SQ_INSTS_VALU_MFMA_MOPS_F8": (512, 2 * BF16_PEAK_TFLOPS)}
+    out = os.path.join(ROOT, "profiles", f"{args.name}_mfma_counters.txt")
+    names = sorted(vals, key=lambda k: -sum(durs.get(k, [0.0])))
+    counters = sorted({c for k in vals for c in vals[k]})
+    with open(out, "w") as f:
+        f.write(f"# rocprofv3 counters per dispatch: {args.title}\n")
+        f.write(f"# command (repository root on the MI355X host): rocprofv3 --kernel-trace --pmc {' '.join(counters)} "
+                f"--output-format csv -d <dir> -o run -- python3 bench.py {args.bench_args}\n")
+        f.write(f"# summary: python3 bench.py --counter-summary --stats-dir <dir> --name {args.name} "
+                f"--title '{args.title}' --bench-args '{args.bench_args}'\n")
+        f.write("# MfmaUtil: % of cycles the MFMA units are busy while the GPU is active (SQ_VALU_MFMA_BUSY_CYCLES over\n"
+                "# GRBM_GUI_ACTIVE x SIMDs); MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOPs (likewise the raw\n"
+                "# F8 operation count); frac_of_peak: those FLOPs over the kernel's mean duration, against the dense\n"
+                "# peak of its dtype (bf16 2.5, FP8 5.0 PFLOP/s)\n")
+        f.write(f"# source_hash: {source_hash()}\n")
+        f.write(f"{'kernel':<70} {'n':>5} {'avg_us':>8} " + " ".join(f"{c:>14}" for c in counters) + f" {'frac_of_peak':>12}\n")
+        for k in names:
+            n = len(next(iter(vals[k].values())))
+            us = float(np.mean(durs[k])) if durs.get(k) else float("nan")
+            row = [float(np.mean(vals[k][c])) if vals[k].get(c) else float("nan") for c in counters]
+            frac = float("nan")
+            for c, (unit, pk) in flop_counters.items():
+                if c in counters and vals[k].get(c) and us == us and us > 0:
+                    fl = float(np.mean(vals[k][c])) * unit
+                    if fl > 0:
+                        frac = fl / (us * 1e-6) / 1e12 / pk
+            name = k if len(k) <= 69 else k[:66] + "..."
+            f.write(f"{name:<70} {n:>5} {us:>8.2f} " + " ".join(f"{v:>14.4g}" for v in row) + f" {frac:>12.4f}\n")
+    print(open(out).read())
+
+
 def traffic_summary(args):
     """Writes the HBM-traffic summary of one denoise chunk from four rocprofv3 --pmc runs: the
     bench with FETCH_SIZE, with WRITE_SIZE, and the copy calibration with each.  FETCH_SIZE and
@@ -470,6 +522,7 @@ def main():
                     help="time only the prefix encoding (B=8, 816 tokens) with the bf16 MLP, the FP8 MLP or both")
     ap.add_argument("--traffic-summary", action="store_true", help="summarise counter runs (no GPU needed)")
     ap.add_argument("--stats-summary", action="store_true", help="summarise a --kernel-trace --stats run (no GPU)")
+    ap.add_argument("--counter-summary", action="store_true", help="summarise a --pmc (+ --kernel-trace) run (no GPU)")
     for name in ("fetch", "write", "cal-fetch", "cal-write", "stats-dir", "name", "title", "bench-args"):
         ap.add_argument("--" + name)
     ap.add_argument("--units", type=float, default=1.0)
@@ -479,6 +532,9 @@ def main():
         return
     if args.stats_summary:
         stats_summary(args)
+        return
+    if args.counter_summary:
+        counter_summary(args)
         return
     if args.prefill_only:
         modes = ("bf16", "fp8_mlp") if args.prefill_only == "both" else (args.prefill_only,)
