@@ -21,18 +21,23 @@
 //   P1 QKV      Q/K/V of head x for all action tokens (RMSNorm row scale, RoPE)   group barrier
 //   P2 attention key chunk i of head x over all 2 x S query slots               group barrier
 //   P3 merge    the 32 chunk partials of head x (log-sum-exp weights)            group barrier
-//   P4 O-part   O-projection of head x's 256 inputs -> a partial of all 1024 cols  8 flags
+//   P4 O-part   O-projection of head x's 256 inputs -> a partial of all 1024 cols  (tagged data)
 //   P5 reduce   workgroup i: h[:, 32i..] += sum of the 8 groups' partials, h*gain  group barrier
 //   P6 gate/up  SwiGLU of FFN columns 384x + 12i .. +11                          group barrier
-//   P7 D-part   down-projection of group x's 384 FFN inputs -> partial of all cols  8 flags
+//   P7 D-part   down-projection of group x's 384 FFN inputs -> partial of all cols  (tagged data)
 //   P8 reduce   as P5 (then the next layer's norm gain)                          group barrier
 // and each Euler step adds the velocity head (its partial in P8 of the last layer, a reduce +
 // Euler update, then action_in_proj + time embedding of the next step).  Only P4->P5 and P7->P8
-// cross groups; there a workgroup waits for the 8 workgroups (x', i) that wrote its columns.
+// cross groups: there a workgroup reads the columns it owns from the 8 workgroups (x', i) that
+// wrote them, and polls those values themselves: every fp32 partial carries the layer-step's
+// epoch in its two low mantissa bits, so no separate signal (and no wait for the writes to
+// complete before it) is needed.
 //
-// Memory model: every value one workgroup hands to another is stored and loaded with device-scope
-// coherent accesses (sc1 buffer loads / stores, no L2 write-back or invalidate), and a
-// producer's stores are complete (s_waitcnt vmcnt(0)) before it signals; weights and the prefix
+// Memory model: every value one workgroup hands to another is loaded with device-coherent (sc1)
+// buffer loads and stored device-coherent or, inside a group placed on one XCD, plainly into that
+// XCD's L2 (no L2 write-back or invalidate is issued); before a group barrier a producer's stores
+// are complete (s_waitcnt vmcnt(0)); a tagged partial needs no ordering at all, since each
+// 4-byte word is checked on its own.  Weights and the prefix
 // K/V are read-only and use ordinary cached copies.  Every wait is bounded: a workgroup that
 // waits longer than its limit (e.g. the 256 workgroups were not all resident) records an error,
 // every workgroup leaves, and the chunk is filled with NaN.  Reductions run in a fixed order, so
@@ -169,11 +174,10 @@ struct PkArgs {
 
 namespace pk {
 
-// sync area (ints): [0, 8*64): group counters (one 256-byte line each); [512, 512 + 256*16):
-// per-workgroup flags (64 bytes each); then the error word, the start-up arrival counter and the
-// placement word, each on its own 256-byte line
-constexpr int SYNC_CNT = 0, SYNC_FLAG = 512, SYNC_ERR = 512 + NWG * 16, SYNC_START = SYNC_ERR + 64,
-              SYNC_MISPLACED = SYNC_START + 64, SYNC_INTS = SYNC_MISPLACED + 64;
+// sync area (ints): [0, 8*64): group counters (one 256-byte line each); then the error word, the
+// start-up arrival counter and the placement word, each on its own 256-byte line
+constexpr int SYNC_CNT = 0, SYNC_ERR = 512, SYNC_START = SYNC_ERR + 64, SYNC_MISPLACED = SYNC_START + 64,
+              SYNC_INTS = SYNC_MISPLACED + 64;
 
 // Waits (one lane) until every int at p[k * stride], k < n, is >= target; bounded.  Returns
 // false on timeout or when another workgroup has recorded an error.
@@ -220,7 +224,6 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
   int *sync = a.sync;
   int *err = sync + SYNC_ERR;
   int *cnt = sync + SYNC_CNT + 64 * x;
-  int *flags = sync + SYNC_FLAG;
   int *abort_lds = reinterpret_cast<int *>(smem + L_FLAG);
   float *inv = reinterpret_cast<float *>(smem + L_INV);
 
@@ -297,10 +300,10 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
 
   // ------------------------------------------------------------------ synchronisation
   int n_bar = 0;  // group barriers passed
-  // Phase entry: lane 0 of wave 0 waits for the phase's inputs (group barrier or the 8 flags of
-  // workgroups (x', i)), the copy waves do their copy step; then one workgroup barrier.  Returns
-  // false when the chunk is aborted.
-  auto enter = [&](auto ph, int ls, int flag_target) {
+  // Phase entry: lane 0 of wave 0 waits for the group barrier (group phases) or only checks the
+  // error word (the two reduces, which poll their tagged inputs themselves), the copy waves do
+  // their copy step; then one workgroup barrier.  Returns false when the chunk is aborted.
+  auto enter = [&](auto ph, int ls, bool group) {
     lane = opaque(tid) & 63;  // lane-derived addresses are rebuilt in every phase
     wave = opaque(tid) >> 6;
     g = lane >> 4;
@@ -311,26 +314,51 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
     hc = HC * i + 4 * (opaque(tid) & 7);
     if (tid == 0) {
       bool ok;
-      if (flag_target > 0) ok = wait_geq(flags + 16 * i * NX, 16, NX, flag_target, err);  // flags of (x', i)
-      else ok = wait_geq(cnt, 0, 1, NG * n_bar, err);
+      if (group) ok = wait_geq(cnt, 0, 1, NG * n_bar, err);
+      else ok = ld_flag(err) == 0;
       *abort_lds = ok ? 0 : 1;
     }
     copy_step(ph, ls);
     __syncthreads();
     return *abort_lds == 0;
   };
-  // Phase exit: the compute waves' stores are complete, then lane 0 signals (arrive at the group
-  // counter, or publish this workgroup's flag).
+  // Phase exit: the compute waves' stores are complete, then lane 0 arrives at the group counter.
   auto leave_group = [&]() {
     if (cw) vm_wait<0>();
     __syncthreads();
     ++n_bar;
     if (tid == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  auto leave_flag = [&](int value) {
-    if (cw) vm_wait<0>();
-    __syncthreads();
-    if (tid == 0) st_flag(flags + 16 * (i * NX + x), value);
+  // Exit of a phase whose outputs are tagged partials: nothing to wait for or signal.
+  auto leave_plain = [&]() { __syncthreads(); };
+  // The partials' epoch: layer-step ls modulo 4 in the two low mantissa bits of every float (a
+  // change of at most 3 ulp).  Every element is rewritten every layer-step by the same lane, so a
+  // reader sees either the previous layer-step's tag or this one's; before the first layer-step
+  // the buffers hold all-ones (tag 3).
+  auto tag_bits = [](f32x4 v, int ls) {
+    i32x4 u = __builtin_bit_cast(i32x4, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u[j] = (u[j] & ~3) | (ls & 3);
+    return u;
+  };
+  auto poll_tagged = [&](i32x4 *pv, int off, int ls) {
+    const int tag = ls & 3;
+    long polls = 0;
+    while (true) {
+      int bad = 0;
+#pragma unroll
+      for (int xx = 0; xx < NX; ++xx) {
+        const bool okx = ((pv[xx][0] & 3) == tag) & ((pv[xx][1] & 3) == tag) & ((pv[xx][2] & 3) == tag) & ((pv[xx][3] & 3) == tag);
+        bad |= okx ? 0 : (1 << xx);
+      }
+      if (!bad) return;
+      if ((++polls & 31) == 0 && ld_flag(err) != 0) return;
+      if (polls >= MAX_POLLS) { st_flag(err, 1); return; }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int xx = 0; xx < NX; ++xx)
+        if (bad & (1 << xx)) pv[xx] = ld16(rw, off + ((xx * S + ht) * H + hc) * 4);
+    }
   };
 
   // ------------------------------------------------------------------ GEMM pieces
@@ -470,12 +498,11 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
   publish_h(gain_attn(0));
   leave_group();
 
-  const int epp = 2;  // flag epochs per layer-step
   for (int k = 0; k < N && alive; ++k) {
     for (int l = 0; l < L && alive; ++l) {
       const int ls = k * L + l;
       // ================================================================ P1: QKV
-      if (!(alive = enter(Ph<PH_QKV>{}, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_QKV>{}, ls, true))) break;
       {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (cw) {
@@ -511,7 +538,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_group();
 
       // ================================================================ P2: attention chunk i
-      if (!(alive = enter(Ph<PH_ATT>{}, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_ATT>{}, ls, true))) break;
       {
         const int nkp = max(0, min(Pc, P - i * Pc));  // prefix keys of this chunk
         const int s0 = i * Sc, nks = max(0, min(Sc, S - s0));
@@ -601,7 +628,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_group();
 
       // ================================================================ P3: merge the key chunks
-      if (!(alive = enter(Ph<PH_MRG>{}, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_MRG>{}, ls, true))) break;
       {
         const int nvec = 2 * S * (D / 8), per = (nvec + NG - 1) / NG;
         const int v = i * per + (tid >> 3), q = tid & 7;
@@ -649,7 +676,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_group();
 
       // ================================================================ P4: O-projection partial
-      if (!(alive = enter(Ph<PH_OPJ>{}, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_OPJ>{}, ls, true))) break;
       if (cw) {
         bf16x8 bf[8];
 #pragma unroll
@@ -658,16 +685,17 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc = Mfma<bf16>::mma(afrag(L_O, 32, 16 * hw + c16, u), bf[u], acc);
         const int t = 16 * tt + c16;
-        if (t < S) st16(rw, o_opart + ((x * S + t) * H + HC * i + 16 * hw + 4 * g) * 4, __builtin_bit_cast(i32x4, acc));
+        if (t < S) st16(rw, o_opart + ((x * S + t) * H + HC * i + 16 * hw + 4 * g) * 4, tag_bits(acc, ls));
       }
-      leave_flag(epp * ls + 1);
+      leave_plain();
 
       // ================================================================ P5: residual += O-proj
-      if (!(alive = enter(Ph<PH_RDO>{}, ls, epp * ls + 1))) break;
+      if (!(alive = enter(Ph<PH_RDO>{}, ls, false))) break;
       if (hown) {
         i32x4 pv[NX];
 #pragma unroll
         for (int xx = 0; xx < NX; ++xx) pv[xx] = ld16(rw, o_opart + ((xx * S + ht) * H + hc) * 4);
+        poll_tagged(pv, o_opart, ls);
         f32x4 s = __builtin_bit_cast(f32x4, pv[0]);
 #pragma unroll
         for (int xx = 1; xx < NX; ++xx) s += __builtin_bit_cast(f32x4, pv[xx]);
@@ -677,7 +705,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_group();
 
       // ================================================================ P6: gate/up + SwiGLU
-      if (!(alive = enter(Ph<PH_GU>{}, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_GU>{}, ls, true))) break;
       {
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
         if (cw) {
@@ -718,7 +746,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
       leave_group();
 
       // ================================================================ P7: down-projection partial
-      if (!(alive = enter(Ph<PH_DN>{}, ls, 0))) break;
+      if (!(alive = enter(Ph<PH_DN>{}, ls, true))) break;
       if (cw) {
         bf16x8 bf[12];
 #pragma unroll
@@ -727,16 +755,17 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
 #pragma unroll
         for (int u = 0; u < 12; ++u) acc = Mfma<bf16>::mma(afrag(L_D, 32, 16 * hw + c16, u), bf[u], acc);
         const int t = 16 * tt + c16;
-        if (t < S) st16(rw, o_dpart + ((x * S + t) * H + HC * i + 16 * hw + 4 * g) * 4, __builtin_bit_cast(i32x4, acc));
+        if (t < S) st16(rw, o_dpart + ((x * S + t) * H + HC * i + 16 * hw + 4 * g) * 4, tag_bits(acc, ls));
       }
-      leave_flag(epp * ls + 2);
+      leave_plain();
 
       // ================================================================ P8: residual += down
-      if (!(alive = enter(Ph<PH_RDD>{}, ls, epp * ls + 2))) break;
+      if (!(alive = enter(Ph<PH_RDD>{}, ls, false))) break;
       if (hown) {
         i32x4 pv[NX];
 #pragma unroll
         for (int xx = 0; xx < NX; ++xx) pv[xx] = ld16(rw, o_dpart + ((xx * S + ht) * H + hc) * 4);
+        poll_tagged(pv, o_dpart, ls);
         f32x4 s = __builtin_bit_cast(f32x4, pv[0]);
 #pragma unroll
         for (int xx = 1; xx < NX; ++xx) s += __builtin_bit_cast(f32x4, pv[xx]);
@@ -762,7 +791,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
     }
     if (!alive) break;
     // ================================================================== velocity + Euler
-    if (!(alive = enter(Ph<NPH>{}, 0, 0))) break;
+    if (!(alive = enter(Ph<NPH>{}, 0, true))) break;
     if (xown) {
       const int t = xi / A, q = xi - t * A;
       float v = 0.f;
@@ -780,7 +809,7 @@ __device__ __forceinline__ void pk_run(const PkArgs &a, char *smem) {
     if (k + 1 == N) break;
     leave_group();
     // ================================================================== next step's input
-    if (!(alive = enter(Ph<NPH>{}, 0, 0))) break;
+    if (!(alive = enter(Ph<NPH>{}, 0, true))) break;
     embed(k + 1, false);
     publish_h(gain_attn(0));
     leave_group();
@@ -797,9 +826,13 @@ __global__ __launch_bounds__(THREADS) void denoise_b1_kernel(PkArgs a) {
   else pk_run<false>(a, smem);
 }
 
-// zero the sync area (run before every launch of the denoise kernel)
-__global__ void sync_clear_kernel(int *sync, int n) {
-  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x) sync[e] = 0;
+// Before every launch: zero the sync area and fill the two tagged partial buffers with all-ones
+// (epoch tag 3, which the first layer-step, tag 0, does not accept).
+__global__ void sync_clear_kernel(int *sync, int n, int *p0, int n0, int *p1, int n1) {
+  const int step = gridDim.x * blockDim.x, e0 = blockIdx.x * blockDim.x + threadIdx.x;
+  for (int e = e0; e < n; e += step) sync[e] = 0;
+  for (int e = e0; e < n0; e += step) p0[e] = -1;
+  for (int e = e0; e < n1; e += step) p1[e] = -1;
 }
 
 }  // namespace pk
@@ -857,7 +890,8 @@ hipError_t launch_denoise_persistent(const PersistLaunch &p, hipStream_t s) {
   a.ws_base = (char *)p.ws;
   a.ws_bytes = (int)w;
   a.sync = (int *)((char *)p.ws + w);
-  hipLaunchKernelGGL(sync_clear_kernel, dim3(8), dim3(256), 0, s, a.sync, (int)SYNC_INTS);
+  hipLaunchKernelGGL(sync_clear_kernel, dim3(256), dim3(256), 0, s, a.sync, (int)SYNC_INTS,
+                     (int *)(a.ws_base + a.off_opart), NX * S * H, (int *)(a.ws_base + a.off_dpart), NX * S * H);
   hipLaunchKernelGGL(denoise_b1_kernel, dim3(NWG), dim3(THREADS), 0, s, a);
   return hipGetLastError();
 }
