@@ -22,6 +22,9 @@ Sources (the pages), cited by title and section:
           diffusion_steps (default 10) to the action chunk.
   [FP8]   same page, section 6.3: the prefix MLP gate/up/down GEMMs run in FP8 E4M3 with
           scales and wider accumulation.
+  [TMOD]  same page, section 5.2 (DM0.5 action expert): time_mlp_in / time_mlp_out turn the
+          flow-matching time into a modulation signal, and a time modulator in every layer tells
+          the action expert where on the noisy trajectory it is.
 Constants the pages leave open are fixed by the workload definitions (RMSNorm eps 1e-6, RoPE
 base 1e6, FFN 6144/3072, block mask "prefix bidirectional, suffix sees prefix and suffix").
 Readings taken where the pages are silent are marked "reading:" below.
@@ -152,9 +155,13 @@ def fp8_linear(a, wq, ws):
 
 def expert_qkv(h, w, l, shape, pos):
     """[DM0] section 1: an expert's own pre-norm and Q/K/V projections, RoPE on Q and K."""
-    T = h.shape[0]
+    return project_qkv(rms_norm(h, w.attn_norm[l], shape.rms_eps), w, l, shape, pos)
+
+
+def project_qkv(n, w, l, shape, pos):
+    """Q/K/V projections of the normalised tokens n, RoPE on Q and K."""
+    T = n.shape[0]
     Hq, Hkv, D = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
-    n = rms_norm(h, w.attn_norm[l], shape.rms_eps)
     qkv = linear(n, w.w_qkv[l])
     q = qkv[:, :Hq * D].reshape(T, Hq, D)
     k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D)
@@ -257,8 +264,11 @@ def velocity_cached(x, t, aw, k_cache, v_cache, shape):
     """v(x_t, t | c) for one sample with the prefix already encoded, [PFX] + [SFX].
 
     k_cache, v_cache: [L, Hkv, P, D] for this sample (P its own prefix length).  Every action
-    layer attends over [cache(l) ; its own K/V]; action rows see all P + S keys.
+    layer attends over [cache(l) ; its own K/V]; action rows see all P + S keys.  Action weights
+    with a ``tmod`` attribute that is not None take the time-modulated expert instead.
     """
+    if getattr(aw, "tmod", None) is not None:
+        return velocity_cached_tmod(x, t, aw, k_cache, v_cache, shape)
     S = x.shape[0]
     P = k_cache.shape[2]
     pos = P + np.arange(S)
@@ -271,6 +281,58 @@ def velocity_cached(x, t, aw, k_cache, v_cache, shape):
         o = gqa_attention(q, K, V, np.ones((S, P + S), dtype=bool))
         h = expert_finish(h, o, body, l, shape)
     return velocity_head(h, aw, shape)
+
+
+# ----------------------------------------------------------------------------- time modulation
+
+def time_condition(t, tm, H, base):
+    """[TMOD] the modulation signal of flow time t: c = time_mlp_out(silu(time_mlp_in(tau(t)))).
+    reading: tau is the sinusoidal embedding of ``time_embedding`` (width H), both MLP layers
+    are H -> H linears with biases and SiLU between them."""
+    return linear(silu(linear(time_embedding(t, H, base), tm.w_in, tm.b_in)), tm.w_out, tm.b_out)
+
+
+def layer_modulation(c, tm, l):
+    """[TMOD] layer l's time modulator.  reading: one linear map of silu(c) gives, for each of the
+    layer's two pre-norms (attention, then MLP), a scale, a shift and a residual gate (6 H
+    values, in that order)."""
+    return np.split(linear(silu(c), tm.w_mod[l], tm.b_mod[l]), 6)
+
+
+def final_modulation(c, tm):
+    """[TMOD] reading: the norm before action_out_proj is modulated the same way (scale, shift)."""
+    return np.split(linear(silu(c), tm.w_fmod, tm.b_fmod), 2)
+
+
+def ada_rms_norm(h, scale, shift, eps):
+    """reading: a time-modulated RMSNorm replaces the learned gain by the modulation:
+    x / sqrt(mean(x^2) + eps) * (1 + scale) + shift."""
+    x = f64(h)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * (1.0 + f64(scale)) + f64(shift)
+
+
+def velocity_cached_tmod(x, t, aw, k_cache, v_cache, shape):
+    """v(x_t, t | c) of the time-modulated action expert ([TMOD], [PFX] + [SFX]): action_in_proj
+    without the additive time embedding (the modulation replaces it); in every layer the two
+    pre-norms are modulated and each sublayer's output enters the residual times its gate,
+    h += gate * sublayer(ada_rms_norm(h)); the final norm is modulated too."""
+    S = x.shape[0]
+    P = k_cache.shape[2]
+    pos = P + np.arange(S)
+    body, tm = aw.body, aw.tmod
+    eps = shape.rms_eps
+    c = time_condition(t, tm, aw.w_in.shape[0], shape.time_base)
+    h = linear(x, aw.w_in, aw.b_in)
+    for l in range(body.w_qkv.shape[0]):
+        s1, b1, g1, s2, b2, g2 = layer_modulation(c, tm, l)
+        q, k, v = project_qkv(ada_rms_norm(h, s1, b1, eps), body, l, shape, pos)
+        K = np.concatenate([f64(k_cache[l]).transpose(1, 0, 2), k])
+        V = np.concatenate([f64(v_cache[l]).transpose(1, 0, 2), v])
+        o = gqa_attention(q, K, V, np.ones((S, P + S), dtype=bool))
+        h = h + g1 * linear(o, body.w_o[l])
+        h = h + g2 * mlp(ada_rms_norm(h, s2, b2, eps), body, l)
+    sf, bf = final_modulation(c, tm)
+    return linear(ada_rms_norm(h, sf, bf, eps), aw.w_out, aw.b_out)
 
 
 def velocity_joint(x, t, aw, vlm, x_pre, shape):

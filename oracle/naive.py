@@ -50,8 +50,12 @@ def heads(row, n, D):
 
 def qkv_token(hrow, W, l, pos, sh):
     """Per-token pre-norm, Q/K/V projections, RoPE on Q and K.  Returns per-head lists."""
+    return qkv_normed(rmsnorm(hrow, W.attn_norm[l], sh.rms_eps), W, l, pos, sh)
+
+
+def qkv_normed(n, W, l, pos, sh):
+    """Q/K/V projections of an already normalised token, RoPE on Q and K."""
     Hq, Hkv, D = sh.n_q_heads, sh.n_kv_heads, sh.head_dim
-    n = rmsnorm(hrow, W.attn_norm[l], sh.rms_eps)
     y = matvec(W.w_qkv[l], n)
     q = [rotate(v, pos, sh.rope_base) for v in heads(y[:Hq * D], Hq, D)]
     k = [rotate(v, pos, sh.rope_base) for v in heads(y[Hq * D:(Hq + Hkv) * D], Hkv, D)]
@@ -149,5 +153,80 @@ def denoise_joint(x1, aw, vlm, x_pre, sh, N):
     for k in range(N):
         t = 1.0 - k / N
         v = velocity_joint(x, t, aw, vlm, x_pre, sh)
+        x = [[x[s][a] - v[s][a] / N for a in range(len(x[s]))] for s in range(len(x))]
+    return x
+
+
+# ---------------------------------------------------------------------- time-modulated action expert
+# Same page, section 5.2 (DM0.5): time_mlp_in / time_mlp_out give a modulation signal c(t); every
+# layer's modulator turns silu(c) into scale, shift and gate for each of its two pre-norms.
+
+def silu(v):
+    return v / (1.0 + math.exp(-v))
+
+
+def time_condition(t, tm, H, base):
+    z = matvec(tm.w_in, time_emb(t, H, base), tm.b_in)
+    return matvec(tm.w_out, [silu(v) for v in z], tm.b_out)
+
+
+def modulation(c, W, b, parts):
+    y = matvec(W, [silu(v) for v in c], b)
+    H = len(c)
+    return [y[j * H:(j + 1) * H] for j in range(parts)]
+
+
+def ada_norm(x, scale, shift, eps):
+    ss = 0.0
+    for v in x:
+        ss += float(v) * float(v)
+    inv = 1.0 / math.sqrt(ss / len(x) + eps)
+    return [float(x[i]) * inv * (1.0 + float(scale[i])) + float(shift[i]) for i in range(len(x))]
+
+
+def finish_token_tmod(hrow, orow, W, l, sh, mods):
+    """Gated O-projection residual, modulated pre-norm, gated SwiGLU MLP residual."""
+    s1, b1, g1, s2, b2, g2 = mods
+    a = matvec(W.w_o[l], orow)
+    h = [float(hrow[i]) + float(g1[i]) * a[i] for i in range(len(hrow))]
+    m = ada_norm(h, s2, b2, sh.rms_eps)
+    g = matvec(W.w_gate[l], m)
+    u = matvec(W.w_up[l], m)
+    act = [g[i] / (1.0 + math.exp(-g[i])) * u[i] for i in range(len(g))]
+    d = matvec(W.w_down[l], act)
+    return [h[i] + float(g2[i]) * d[i] for i in range(len(h))]
+
+
+def velocity_joint_tmod(x, t, aw, vlm, x_pre, sh):
+    """Joint stack (prefix + action tokens) with the time-modulated action expert; the VLM
+    expert is unchanged and no additive time embedding is used."""
+    tm = aw.tmod
+    H = len(aw.w_in)
+    c = time_condition(t, tm, H, sh.time_base)
+    h_suf = [matvec(aw.w_in, x[s], aw.b_in) for s in range(len(x))]
+    h_pre = [[float(v) for v in row] for row in x_pre]
+    P, S = len(h_pre), len(h_suf)
+    for l in range(len(vlm.w_qkv)):
+        mods = modulation(c, tm.w_mod[l], tm.b_mod[l], 6)
+        Q, K, V = [], [], []
+        for j in range(P):
+            q, k, v = qkv_token(h_pre[j], vlm, l, j, sh)
+            Q.append(q); K.append(k); V.append(v)
+        for s in range(S):
+            q, k, v = qkv_normed(ada_norm(h_suf[s], mods[0], mods[1], sh.rms_eps), aw.body, l, P + s, sh)
+            Q.append(q); K.append(k); V.append(v)
+        mask = [[(i >= P) or (j < P) for j in range(P + S)] for i in range(P + S)]
+        O = attend(Q, K, V, mask, sh)
+        h_pre = [finish_token(h_pre[j], O[j], vlm, l, sh) for j in range(P)]
+        h_suf = [finish_token_tmod(h_suf[s], O[P + s], aw.body, l, sh, mods) for s in range(S)]
+    sf, bf = modulation(c, tm.w_fmod, tm.b_fmod, 2)
+    return [matvec(aw.w_out, ada_norm(r, sf, bf, sh.rms_eps), aw.b_out) for r in h_suf]
+
+
+def denoise_joint_tmod(x1, aw, vlm, x_pre, sh, N):
+    x = [[float(v) for v in row] for row in x1]
+    for k in range(N):
+        t = 1.0 - k / N
+        v = velocity_joint_tmod(x, t, aw, vlm, x_pre, sh)
         x = [[x[s][a] - v[s][a] / N for a in range(len(x[s]))] for s in range(len(x))]
     return x

@@ -32,3 +32,13 @@ def action(rng, L, H, F, A, sh, std=0.3):
         w_out=std * rng.standard_normal((A, H)),
         b_out=std * rng.standard_normal(A),
     )
+
+
+def time_mod(rng, L, H, std=0.3):
+    """Time-modulation weights: time MLP (H -> H -> H) and per-layer / final modulators."""
+    return SimpleNamespace(
+        w_in=std * rng.standard_normal((H, H)), b_in=std * rng.standard_normal(H),
+        w_out=std * rng.standard_normal((H, H)), b_out=std * rng.standard_normal(H),
+        w_mod=std * rng.standard_normal((L, 6 * H, H)), b_mod=std * rng.standard_normal((L, 6 * H)),
+        w_fmod=std * rng.standard_normal((2 * H, H)), b_fmod=std * rng.standard_normal(2 * H),
+    )
