@@ -21,6 +21,8 @@ STATUS_NAMES = {0: "DM_OK", -1: "DM_ERR_INVALID_ARG", -2: "DM_ERR_SHAPE", -3: "D
                 -4: "DM_ERR_WORKSPACE", -5: "DM_ERR_PLAN_MISMATCH", -6: "DM_ERR_HIP"}
 DM_F32, DM_BF16, DM_FP8_E4M3 = 0, 1, 2
 DM_FLAG_MULTI_KERNEL = 1
+DM_FLAG_TIME_MODULATION = 2
+DM_TMOD_MAX_STEPS = 16
 OP_PREFILL, OP_MERGED_LAYER, OP_DENOISE = 0, 1, 2
 _DT = {F32: DM_F32, BF16: DM_BF16, FP8: DM_FP8_E4M3}
 EXPORTS = ["dm_version", "dm_last_error", "dm_ctx_create", "dm_ctx_destroy", "dm_workspace_bytes",
@@ -47,9 +49,17 @@ class ExpertWeightsC(C.Structure):
                                           "w_down", "s_gate", "s_up", "s_down")]
 
 
+TMOD_FIELDS = ("w_in", "b_in", "w_out", "b_out", "w_mod", "b_mod", "w_fmod", "b_fmod")
+
+
+class TimeModC(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in TMOD_FIELDS]
+
+
 class ActionWeightsC(C.Structure):
     _fields_ = [("body", ExpertWeightsC)] + [(n, C.c_void_p) for n in ("w_in", "b_in", "final_norm",
-                                                                       "w_out", "b_out")]
+                                                                       "w_out", "b_out")] + \
+               [("tmod", C.POINTER(TimeModC))]
 
 
 _lib = None
@@ -150,12 +160,24 @@ class DeviceExpert:
 
 
 class DeviceAction:
+    """Action-expert weights on the device.  With aw.tmod set (the time-modulated expert) the
+    modulator matrices are kept in the weight dtype, the time MLP and all biases in float32."""
+
     def __init__(self, aw, dtype, device="cuda"):
         self.body = DeviceExpert(aw.body, dtype, device)
         self.t = {k: to_device(getattr(aw, k), torch.float32, device)
                   for k in ("w_in", "b_in", "final_norm", "w_out", "b_out")}
+        tm = getattr(aw, "tmod", None)
+        self.tm = None
+        tmod_c = None
+        if tm is not None:
+            wd = torch_dtype(dtype)
+            self.tm = {k: to_device(getattr(tm, k), wd if k in ("w_mod", "w_fmod") else torch.float32, device)
+                       for k in TMOD_FIELDS}
+            self.tmod_c = TimeModC(*(ptr(self.tm[k]) for k in TMOD_FIELDS))
+            tmod_c = C.pointer(self.tmod_c)
         self.c = ActionWeightsC(self.body.c, *(ptr(self.t[k]) for k in ("w_in", "b_in", "final_norm", "w_out",
-                                                                         "b_out")))
+                                                                         "b_out")), tmod_c)
 
 
 class Context:
@@ -164,6 +186,8 @@ class Context:
     def __init__(self, shape: ModelShape, device: int = 0, flags: int = 0):
         self.shape = shape
         self.device = device
+        if getattr(shape, "time_mod", False):
+            flags |= DM_FLAG_TIME_MODULATION
         self.cfg = make_config(shape, flags)
         h = C.c_void_p()
         check(lib().dm_ctx_create(C.byref(self.cfg), device, C.byref(h)))

@@ -35,6 +35,7 @@ class ModelShape:
     time_base: float = 1e4
     dtype: str = BF16
     vlm_mlp_dtype: str = BF16
+    time_mod: bool = False     # DM0.5-style time-modulated action expert (page 2, section 5.2)
 
     @property
     def group(self) -> int:
@@ -84,6 +85,12 @@ WORKLOADS = {
                 kind="denoise"),
     5: Workload(5, "DM0-base prefill (28 VLM layers, 816 tokens) + suffix denoise, bf16, B=8",
                 DM0_BASE, batch=8, prefix_len=816, steps=10, kind="prefill_denoise"),
+    6: Workload(6, "tiny model with the time-modulated action expert, fp32, B=3 ragged prefix 1-64, "
+                   "4 Euler steps", replace(TINY, time_mod=True), batch=3, prefix_len=64, ragged=(1, 64),
+                steps=4, kind="denoise"),
+    7: Workload(7, "DM0-base suffix denoise with the time-modulated action expert, bf16, B=4, prefix KV 816, "
+                   "10 steps", replace(DM0_BASE, time_mod=True), batch=4, prefix_len=816, steps=10,
+                kind="denoise"),
 }
 
 

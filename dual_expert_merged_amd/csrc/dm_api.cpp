@@ -111,6 +111,7 @@ struct Layout {
   Region hp, hg_p, ssq_p, q_p, kp, vp, o_p, act_p, apart_p;    // prefix side (hp: prefill only)
   Region q8_p, qs_p;                                           // FP8 MLP operand codes and row scales
   Region single;                                               // single-launch batch-1 denoise
+  Region tm_tau, tm_z, tm_c, tm_mod, tm_fmod;                  // time-modulation tables of a chunk
   int n_chunks = 1, chunk_keys = 32, n_chunks_p = 1, chunk_keys_p = 32;
   ExpertPlans pa, pv;  // action expert, VLM expert
   size_t total = 0;
@@ -222,7 +223,7 @@ size_t split_bytes(const GemmPlan &p, int M, int N) {
 // The batch-1 denoise runs as one launch per chunk (persist.hip) for the DM0-base action expert
 // shapes, unless the config asks for the multi-kernel sequence.
 bool single_launch_shape(const dm_config &c, int B, int P_cap) {
-  return !(c.flags & DM_FLAG_MULTI_KERNEL) &&
+  return !(c.flags & (DM_FLAG_MULTI_KERNEL | DM_FLAG_TIME_MODULATION)) &&
          persist_supported(c.n_layers, c.act_hidden, c.act_ffn, c.n_q_heads, c.n_kv_heads, c.head_dim, c.chunk, c.action_dim, B,
                            P_cap, c.dtype == DM_BF16);
 }
@@ -251,6 +252,14 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
     attn_split(B, Hkv, nqb, P_cap + S, &L.n_chunks, &L.chunk_keys);
     if (L.n_chunks > 1) L.put(L.apart, attn_partial_bytes(dt, B, Hkv, nqb, L.n_chunks, D));
     if (op == DM_OP_DENOISE && single_launch_shape(c, B, P_cap)) L.put(L.single, persist_ws_bytes(S, c.action_dim));
+    if (op == DM_OP_DENOISE && (c.flags & DM_FLAG_TIME_MODULATION)) {
+      const size_t rows = DM_TMOD_MAX_STEPS;
+      L.put(L.tm_tau, rows * Ha * sizeof(float));
+      L.put(L.tm_z, rows * Ha * sizeof(float));
+      L.put(L.tm_c, rows * Ha * sizeof(float));
+      L.put(L.tm_mod, rows * c.n_layers * 6 * Ha * sizeof(float));
+      L.put(L.tm_fmod, rows * 2 * Ha * sizeof(float));
+    }
   }
   if (op == DM_OP_PREFILL || op == DM_OP_MERGED_LAYER) {
     L.pv = plan_expert(c, dt, (int)Mp, Hv, c.vlm_ffn);
@@ -310,7 +319,10 @@ dm_status check_config(const dm_config *c) {
   REQUIRE(c->chunk >= 1 && c->chunk <= 64, DM_ERR_UNSUPPORTED, "chunk must be 1..64");
   REQUIRE(c->rms_eps > 0.f && std::isfinite(c->rms_eps), DM_ERR_INVALID_ARG, "rms_eps must be positive");
   REQUIRE(c->rope_base > 1.f && std::isfinite(c->rope_base), DM_ERR_INVALID_ARG, "rope_base must be > 1");
-  REQUIRE((c->flags & ~DM_FLAG_MULTI_KERNEL) == 0, DM_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
+  REQUIRE((c->flags & ~(DM_FLAG_MULTI_KERNEL | DM_FLAG_TIME_MODULATION)) == 0, DM_ERR_INVALID_ARG, "unknown flags 0x%x",
+          c->flags);
+  REQUIRE(!(c->flags & DM_FLAG_TIME_MODULATION) || c->act_hidden <= 1024, DM_ERR_UNSUPPORTED,
+          "the time-modulated action expert supports act_hidden <= 1024");
   return DM_OK;
 }
 
@@ -424,10 +436,76 @@ void enqueue_finish_fp8(const dm_ctx *ctx, const Layout &L, void *ws, const Expe
   launch_resid_fp8(rd, s);
 }
 
+// The time-modulated action expert (page "DM0.5: High-Performance Embodied VLA ...", section 5.2):
+// the chunk's modulation tables first (time MLP and every layer's modulator for all Euler steps:
+// t is shared by the batch, so each modulator weight is read once per chunk), then per layer a
+// modulated norm before each sublayer (its GEMM takes the normalised operand as is) and the
+// residual gates in the O and down epilogues.
+dm_status enqueue_denoise_tmod(const dm_ctx *ctx, const Layout &L, const dm_action_weights *aw, const void *k_cache,
+                               const void *v_cache, const int32_t *lens, int B, int P_cap, float *x, int num_steps,
+                               void *ws, hipStream_t s) {
+  const dm_config &c = ctx->cfg;
+  const dm_time_modulation &tm = *aw->tmod;
+  const int S = c.chunk, Ha = c.act_hidden, Fa = c.act_ffn, D = c.head_dim, Hkv = c.n_kv_heads, NL = c.n_layers;
+  const int M = B * S;
+  const float eps = c.rms_eps;
+  float *tau = at<float>(ws, L.tm_tau), *z = at<float>(ws, L.tm_z), *cc = at<float>(ws, L.tm_c);
+  float *mod = at<float>(ws, L.tm_mod), *fmod = at<float>(ws, L.tm_fmod);
+  launch_tau_table(tau, num_steps, Ha, s);
+  launch_rows_gemv(DT_F32, tau, num_steps, Ha, tm.w_in, tm.b_in, z, Ha, false, s);
+  launch_rows_gemv(DT_F32, z, num_steps, Ha, tm.w_out, tm.b_out, cc, Ha, true, s);
+  launch_rows_gemv(ctx->dt, cc, num_steps, Ha, tm.w_mod, tm.b_mod, mod, NL * 6 * Ha, true, s);
+  launch_rows_gemv(ctx->dt, cc, num_steps, Ha, tm.w_fmod, tm.b_fmod, fmod, 2 * Ha, true, s);
+
+  float2 *rope = at<float2>(ws, L.rope);
+  const Hidden hid{at<float>(ws, L.h), at<void>(ws, L.hg), at<float>(ws, L.ssq), Ha};
+  const Hidden normed{hid.h, hid.hg, nullptr, Ha};  // operand already normalised: no row scale
+  void *q = at<void>(ws, L.q), *ks = at<void>(ws, L.ks), *vs = at<void>(ws, L.vs);
+  void *o = at<void>(ws, L.o), *act = at<void>(ws, L.act);
+  const RowMap rows{S, lens, 0, P_cap};
+  const size_t layer_cache = (size_t)B * Hkv * P_cap * D;
+  launch_rope_table(rope, P_cap + S, D, c.rope_base, s);
+  float2 *rope_rows = at<float2>(ws, L.rope_rows);
+  launch_rope_rows(rope, lens, P_cap, B, S, D, rope_rows, s);
+  GemmPlan po = L.pa.o, pd = L.pa.down;
+  po.sk = splitk(L, ws, L.pa.o);
+  pd.sk = splitk(L, ws, L.pa.down);
+  for (int k = 0; k < num_steps; ++k) {
+    const float t = 1.0f - (float)k / (float)num_steps;
+    launch_embed(ctx->dt, x, aw->w_in, aw->b_in, hid, nullptr, M, c.action_dim, t, s);
+    for (int l = 0; l < NL; ++l) {
+      const float *m = mod + ((size_t)k * NL + l) * 6 * Ha;  // attention scale, shift, gate; MLP scale, shift, gate
+      const Expert e = expert_layer(c, aw->body, l, Ha, Fa, ctx->es);
+      launch_mod_norm(ctx->dt, hid.h, hid.hg, m, m + Ha, M, Ha, eps, s);
+      QkvArgs qa{normed, M, eps, e.w_qkv, q, ks, vs, S, rows, rope, c.n_q_heads, Hkv, D, rope_rows};
+      launch_qkv(ctx->dt, qa, L.pa.qkv, s);
+      AttnArgs aa{q, S, 1,
+                  layer_ptr(k_cache, layer_cache, l, ctx->es), layer_ptr(v_cache, layer_cache, l, ctx->es), P_cap,
+                  ks, vs, S, lens, B, c.n_q_heads, Hkv, D, L.n_chunks, L.chunk_keys, o,
+                  L.n_chunks > 1 ? at<void>(ws, L.apart) : nullptr};
+      launch_attention(ctx->dt, aa, s);
+      ResidArgs ro{o, M, c.n_q_heads * D, e.w_o, hid, nullptr, rows};
+      ro.gate = m + 2 * Ha;
+      launch_resid(ctx->dt, ro, po, s);
+      launch_mod_norm(ctx->dt, hid.h, hid.hg, m + 3 * Ha, m + 4 * Ha, M, Ha, eps, s);
+      SwigluArgs sg{normed, M, Fa, eps, e.w_gate, e.w_up, act, rows};
+      launch_swiglu(ctx->dt, sg, L.pa.gu, s);
+      ResidArgs rd{act, M, Fa, e.w_down, hid, nullptr, rows};
+      rd.gate = m + 5 * Ha;
+      launch_resid(ctx->dt, rd, pd, s);
+    }
+    const float *f = fmod + (size_t)k * 2 * Ha;
+    launch_velocity_euler(hid.h, nullptr, aw->w_out, aw->b_out, x, M, Ha, c.action_dim, eps, num_steps, s, f, f + Ha);
+  }
+  return DM_OK;
+}
+
 dm_status enqueue_denoise(const dm_ctx *ctx, const dm_action_weights *aw, const void *k_cache, const void *v_cache,
                           const int32_t *lens, int B, int P_cap, float *x, int num_steps, void *ws, hipStream_t s) {
   const dm_config &c = ctx->cfg;
   const Layout L = make_layout(c, ctx->es, DM_OP_DENOISE, B, P_cap);
+  if (c.flags & DM_FLAG_TIME_MODULATION)
+    return enqueue_denoise_tmod(ctx, L, aw, k_cache, v_cache, lens, B, P_cap, x, num_steps, ws, s);
   if (ctx->single_ok && L.single.bytes) {
     const dm_expert_weights &w = aw->body;
     PersistLaunch p{w.w_qkv, w.w_o, w.w_gate, w.w_up, w.w_down, w.attn_norm, w.mlp_norm, aw->w_in, aw->b_in,
@@ -478,7 +556,18 @@ dm_status check_action(const dm_ctx *ctx, const dm_action_weights *aw) {
     REQUIRE(p, DM_ERR_INVALID_ARG, "action head: a tensor pointer is NULL");
     REQUIRE(aligned16(p), DM_ERR_INVALID_ARG, "action head: a tensor pointer is not 16-byte aligned");
   }
-  (void)ctx;
+  const bool tmod = (ctx->cfg.flags & DM_FLAG_TIME_MODULATION) != 0;
+  REQUIRE(tmod == (aw->tmod != nullptr), DM_ERR_INVALID_ARG,
+          tmod ? "DM_FLAG_TIME_MODULATION needs action weights with tmod set"
+               : "action weights carry tmod but the config has no DM_FLAG_TIME_MODULATION");
+  if (tmod) {
+    const dm_time_modulation &t = *aw->tmod;
+    const void *tp[] = {t.w_in, t.b_in, t.w_out, t.b_out, t.w_mod, t.b_mod, t.w_fmod, t.b_fmod};
+    for (const void *p : tp) {
+      REQUIRE(p, DM_ERR_INVALID_ARG, "time modulation: a tensor pointer is NULL");
+      REQUIRE(aligned16(p), DM_ERR_INVALID_ARG, "time modulation: a tensor pointer is not 16-byte aligned");
+    }
+  }
   return DM_OK;
 }
 
@@ -491,6 +580,8 @@ dm_status check_denoise(dm_ctx *ctx, const dm_action_weights *aw, const void *k_
   REQUIRE(x, DM_ERR_INVALID_ARG, "x is NULL");
   REQUIRE(aligned16(x), DM_ERR_INVALID_ARG, "x must be 16-byte aligned");
   REQUIRE(num_steps >= 1 && num_steps <= 1000, DM_ERR_SHAPE, "num_steps must be 1..1000 (got %d)", num_steps);
+  REQUIRE(!(ctx->cfg.flags & DM_FLAG_TIME_MODULATION) || num_steps <= DM_TMOD_MAX_STEPS, DM_ERR_UNSUPPORTED,
+          "the time-modulated expert supports at most %d Euler steps (got %d)", DM_TMOD_MAX_STEPS, num_steps);
   return DM_OK;
 }
 
@@ -649,6 +740,8 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   TRY(check_common(ctx, prefix_lens, B, P_cap, ws, ws_bytes, DM_OP_MERGED_LAYER));
   const dm_config &c = ctx->cfg;
   REQUIRE(c.vlm_mlp_dtype == c.dtype, DM_ERR_UNSUPPORTED, "dm_merged_layer runs the VLM MLP in the weight dtype");
+  REQUIRE(!(c.flags & DM_FLAG_TIME_MODULATION), DM_ERR_UNSUPPORTED,
+          "the time-modulated action expert needs the flow time: only dm_suffix_denoise runs it");
   TRY(check_expert(vlm, false, "VLM"));
   TRY(check_expert(act, false, "action"));
   REQUIRE(layer >= 0 && layer < c.n_layers, DM_ERR_SHAPE, "layer %d out of range", layer);

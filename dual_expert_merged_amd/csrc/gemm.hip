@@ -38,6 +38,10 @@ namespace dm {
 // all its loads in flight, then a fixed-order exchange.  Rows past M use row M-1 (never read).
 __device__ __forceinline__ void rms_prepare(const Hidden &in, int M, float eps, int m0, int rows, float *inv,
                                             const float *row_scale = nullptr) {
+  if (!in.ssq) {  // operand already normalised (time-modulated norm): only the row scale
+    for (int t = threadIdx.x; t < rows; t += blockDim.x) inv[t] = row_scale ? row_scale[min(m0 + t, M - 1)] : 1.0f;
+    return;
+  }
   const int nt = in.H >> 4;
   const int step = blockDim.x >> 2;  // rows per pass
   for (int base = 0; base < rows; base += step) {
@@ -71,7 +75,7 @@ struct RmsPre {
 __device__ __forceinline__ RmsPre rms_load(const Hidden &in, int M, int m0) {
   RmsPre p;
   const int nt = in.H >> 4, t = threadIdx.x, row = t >> 2, part = t & 3;
-  if ((nt & 15) == 0) {
+  if (in.ssq && (nt & 15) == 0) {
     const int per = nt >> 4;
     const float4 *q4 = reinterpret_cast<const float4 *>(in.ssq + (size_t)min(m0 + row, M - 1) * nt) + part * per;
 #pragma unroll
@@ -82,6 +86,10 @@ __device__ __forceinline__ RmsPre rms_load(const Hidden &in, int M, int m0) {
 __device__ __forceinline__ void rms_finish(const RmsPre &p, const Hidden &in, int M, float eps, int m0, float *inv,
                                            const float *row_scale = nullptr) {
   const int nt = in.H >> 4, t = threadIdx.x, row = t >> 2, part = t & 3;
+  if (!in.ssq) {  // operand already normalised (time-modulated norm): only the row scale
+    if (part == 0 && row < 64) inv[row] = row_scale ? row_scale[min(m0 + row, M - 1)] : 1.0f;
+    return;
+  }
   float s = 0.f;
   if ((nt & 15) == 0) {
     const int per = nt >> 4;
@@ -265,7 +273,7 @@ template <typename T, typename W = T> struct EpiResid {
   ResidArgs a;
   struct St {
     float hv[4];
-    float gain, s;
+    float gain, s, gate;
   };
   __device__ __forceinline__ const RowMap &rows() const { return a.rows; }
   __device__ __forceinline__ const W *wrow(int c) const { return (const W *)a.w + (size_t)c * a.K; }
@@ -289,6 +297,7 @@ template <typename T, typename W = T> struct EpiResid {
     for (int r = 0; r < 4; ++r) st.hv[r] = a.out.h[(size_t)ri.rc[r] * a.out.H + c];
     st.gain = a.next_gain ? a.next_gain[c] : 0.f;
     st.s = Q ? a.s_w[c] : 1.0f;
+    st.gate = a.gate ? a.gate[c] : 1.0f;
     return st;
   }
   __device__ __forceinline__ void store(const St &st, const RowInfo &ri, int row0, int c, f32x4 acc, const float *inv,
@@ -299,7 +308,7 @@ template <typename T, typename W = T> struct EpiResid {
       const int row = row0 + r;
       const bool ok = ri.ok[r];
       const float y = Q ? acc[r] * inv[row - m0] * st.s : acc[r];
-      const float hn = ok ? st.hv[r] + y : 0.f;
+      const float hn = ok ? st.hv[r] + (a.gate ? st.gate * y : y) : 0.f;
       if (ok) {
         a.out.h[(size_t)row * H + c] = hn;
         if (a.next_gain) ((T *)a.out.hg)[(size_t)row * H + c] = from_f32<T>(hn * st.gain);
@@ -491,7 +500,7 @@ __global__ __launch_bounds__(NWV * 64) void skinny_kernel(const T *__restrict__ 
 }
 
 // Sum of the K-split partials of a residual projection plus the residual epilogue:
-// h += sum_s part[s], hg = h * next_gain, per-16-column sums of squares.  Thread = 4 columns of
+// h += sum_s part[s] (times gate when set), hg = h * next_gain, per-16-column sums of squares.  Thread = 4 columns of
 // one row; the split sum runs in split order.  KS: the number of splits (all its loads in flight).
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const float *__restrict__ part) {
@@ -505,6 +514,7 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
     pv[sp] = *reinterpret_cast<const float4 *>(part + ((size_t)sp * a.M + row) * H + c);
   float4 hv = *reinterpret_cast<const float4 *>(a.out.h + (size_t)row * H + c);
   float4 gv = a.next_gain ? *reinterpret_cast<const float4 *>(a.next_gain + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 gt = a.gate ? *reinterpret_cast<const float4 *>(a.gate + c) : make_float4(1.f, 1.f, 1.f, 1.f);
   bool ok = in_range;
   if (a.rows.is_prefix) {  // uniform: action rows need no prefix length
     const int b = row / a.rows.rows_per_b, s = row - b * a.rows.rows_per_b;
@@ -515,6 +525,7 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
   for (int sp = 1; sp < KS; ++sp) {
     t.x += pv[sp].x; t.y += pv[sp].y; t.z += pv[sp].z; t.w += pv[sp].w;
   }
+  if (a.gate) t = make_float4(gt.x * t.x, gt.y * t.y, gt.z * t.z, gt.w * t.w);
   const float4 hn = make_float4(hv.x + t.x, hv.y + t.y, hv.z + t.z, hv.w + t.w);
   if (ok) {
     *reinterpret_cast<float4 *>(a.out.h + (size_t)row * H + c) = hn;

@@ -20,7 +20,8 @@ struct RowMap {
 // The hidden stream between sublayers.  h is the fp32 residual stream [M][H].  hg holds
 // h * gain of the next RMSNorm rounded to the weight dtype (the next GEMM's operand), and ssq
 // the sums of squares of h over every 16-column group, [M][H/16]: the next GEMM scales its
-// output rows by 1/sqrt(sum(ssq)/H + eps), which completes RMSNorm(h) W^T.
+// output rows by 1/sqrt(sum(ssq)/H + eps), which completes RMSNorm(h) W^T.  With ssq NULL the
+// operand hg is already normalised (the time-modulated norm) and the rows are not scaled.
 struct Hidden {
   float *h;
   void *hg;
@@ -47,8 +48,8 @@ struct QkvArgs {
   int Hq, Hkv, D;
   const float2 *rope_rows = nullptr;  // action rows: [M][D/2] (cos, sin) at position P_b + s
 };
-// out.h += A W^T, then out.hg = (h * next_gain) and out.ssq for the next sublayer
-// (next_gain NULL: skip them).  Rows outside RowMap untouched.
+// out.h += A W^T (times gate[n] when gate is set), then out.hg = (h * next_gain) and out.ssq
+// for the next sublayer (next_gain NULL: skip them).  Rows outside RowMap untouched.
 // FP8 operands (a and w E4M3 codes): C = a_scale[m] * s_w[n] * (A_q W_q^T); both NULL otherwise.
 struct ResidArgs {
   const void *a; int M, K;       // A [M][K]
@@ -57,6 +58,7 @@ struct ResidArgs {
   const float *next_gain;
   RowMap rows;
   const float *a_scale = nullptr, *s_w = nullptr;
+  const float *gate = nullptr;   // [H] residual gate of the time-modulated expert
 };
 // act[M x F] = silu(n Wg^T) * (n Wu^T), n = RMSNorm(h) from in.hg / in.ssq.
 // FP8 operands: a8 holds the E4M3 codes of in.hg per row with scales a_scale (so the normalised
@@ -112,12 +114,27 @@ void launch_rope_rows(const float2 *table, const int32_t *lens, int cap, int B, 
                       hipStream_t s);
 // h = src (if src != h), hg = h * gain, ssq per 16 columns: the entry into the first sublayer.
 void launch_norm_prep(Dt dt, const float *src, const Hidden &hid, const float *gain, int M, hipStream_t s);
-// h = x w_in^T + b_in + tau(t), then hg / ssq for the first layer's attention norm.
+// h = x w_in^T + b_in + tau(t), then hg / ssq for the first layer's attention norm.  gain NULL:
+// h = x w_in^T + b_in only (the time-modulated expert: no additive tau, the norm is its own launch).
 void launch_embed(Dt dt, const float *x, const float *w_in, const float *b_in, const Hidden &hid,
                   const float *gain, int M, int A, float t, hipStream_t s);
+// v = n w_out^T + b_out, x -= v / num_steps, n = RMSNorm(h) * gain, or with fscale set the
+// time-modulated n = h / rms(h) * (1 + fscale) + fshift.
 void launch_velocity_euler(const float *h, const float *gain, const float *w_out,
                            const float *b_out, float *x, int M, int H, int A, float eps,
-                           int num_steps, hipStream_t s);
+                           int num_steps, hipStream_t s, const float *fscale = nullptr,
+                           const float *fshift = nullptr);
+// Time modulation of the action expert: the per-step tables of a chunk.
+// tau[k][i] = sinusoidal time embedding of t_k = 1 - k / num_steps, k < num_steps.
+void launch_tau_table(float *tau, int num_steps, int H, hipStream_t s);
+// Y[m][n] = sum_k f(X[m][k]) W[n][k] + b[n] for m < M <= 16 (f = SiLU when silu_in, else the
+// identity); W [N][K] fp32 or in the weight dtype dt; X, Y fp32.
+void launch_rows_gemv(Dt dt, const float *X, int M, int K, const void *W, const float *b, float *Y, int N,
+                      bool silu_in, hipStream_t s);
+// The time-modulated norm: hg[m][i] = h[m][i] / rms(h[m]) * (1 + scale[i]) + shift[i] in the
+// weight dtype (rms over the row, eps as in RMSNorm).
+void launch_mod_norm(Dt dt, const float *h, void *hg, const float *scale, const float *shift, int M, int H,
+                     float eps, hipStream_t s);
 // dst[r][:] = e4m3(src[r][:] / scales[r]), scales[r] = max|src[r][:]| / 448 (1 for a zero row);
 // src bf16 [rows][cols].
 void launch_fp8_quantize_rows(const void *src, uint8_t *dst, float *scales, int rows, int cols,

@@ -1,6 +1,8 @@
 // Small kernels of the path: RoPE table, entry into the first sublayer (h*gain and sums of
 // squares), action_in_proj + time embedding, final norm + action_out_proj + Euler update, FP8
 // E4M3 row quantisation.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -101,12 +103,12 @@ __global__ __launch_bounds__(256) void embed_kernel(const float *__restrict__ x,
   const int nw4 = A / 4;
 #pragma unroll
   for (int j = 0; j < 16; ++j) w4[j] = wr[min(j, nw4 - 1)];  // unconditional: loads stay in flight
-  const float bias = b_in[i], gn = gain[i];
+  const float bias = b_in[i], gn = gain ? gain[i] : 0.f;
   // tau in float32: t * omega lies in [0, 1], where sinf / cosf / exp2f are within a few ulp
   // (the double-precision versions added about 1 us to the launch at batch 1)
   const int j = i < half ? i : i - half;
   const float w = exp2f(-2.0f * (float)j / (float)H * 13.287712379549449f);  // 10000^(-2j/H)
-  const float tau = i < half ? sinf(t * w) : cosf(t * w);
+  const float tau = gain ? (i < half ? sinf(t * w) : cosf(t * w)) : 0.f;
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -122,8 +124,10 @@ __global__ __launch_bounds__(256) void embed_kernel(const float *__restrict__ x,
     const float sq = sum16(v * v);
     if (m < M && col_ok) {
       hid.h[(size_t)m * H + i] = v;
-      ((T *)hid.hg)[(size_t)m * H + i] = from_f32<T>(v * gn);
-      if ((i & 15) == 0) hid.ssq[(size_t)m * (H >> 4) + (i >> 4)] = sq;
+      if (gain) {
+        ((T *)hid.hg)[(size_t)m * H + i] = from_f32<T>(v * gn);
+        if ((i & 15) == 0) hid.ssq[(size_t)m * (H >> 4) + (i >> 4)] = sq;
+      }
     }
   }
 }
@@ -145,17 +149,26 @@ void launch_embed(Dt dt, const float *x, const float *w_in, const float *b_in, c
 __global__ __launch_bounds__(256) void velocity_euler_kernel(const float *__restrict__ h, const float *__restrict__ gain,
                                                              const float *__restrict__ w_out,
                                                              const float *__restrict__ b_out, float *__restrict__ x,
-                                                             int H, int A, float eps, float inv_steps) {
+                                                             int H, int A, float eps, float inv_steps,
+                                                             const float *__restrict__ fscale,
+                                                             const float *__restrict__ fshift) {
   __shared__ float red[4][64];
   __shared__ float red1[4];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float4 hv[4], gv[4];
+  float4 hv[4], gv[4], sv[4];
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {  // unconditional loads (clamped column) stay in flight together
     const int c = min(4 * tid + 1024 * j, H - 4);
     hv[j] = *reinterpret_cast<const float4 *>(h + (size_t)m * H + c);
-    gv[j] = *reinterpret_cast<const float4 *>(gain + c);
+    if (fscale) {  // uniform: the time-modulated norm, gain 1 + fscale and shift fshift
+      const float4 f = *reinterpret_cast<const float4 *>(fscale + c);
+      gv[j] = make_float4(1.f + f.x, 1.f + f.y, 1.f + f.z, 1.f + f.w);
+      sv[j] = *reinterpret_cast<const float4 *>(fshift + c);
+    } else {
+      gv[j] = *reinterpret_cast<const float4 *>(gain + c);
+      sv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -168,7 +181,9 @@ __global__ __launch_bounds__(256) void velocity_euler_kernel(const float *__rest
   const float inv = rsqrtf((red1[0] + red1[1] + red1[2] + red1[3]) / H + eps);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    hv[j].x *= inv * gv[j].x; hv[j].y *= inv * gv[j].y; hv[j].z *= inv * gv[j].z; hv[j].w *= inv * gv[j].w;
+    if (4 * tid + 1024 * j >= H) continue;  // stays zero: a clamped column must add nothing
+    hv[j].x = hv[j].x * inv * gv[j].x + sv[j].x; hv[j].y = hv[j].y * inv * gv[j].y + sv[j].y;
+    hv[j].z = hv[j].z * inv * gv[j].z + sv[j].z; hv[j].w = hv[j].w * inv * gv[j].w + sv[j].w;
   }
   for (int a0 = 0; a0 < A; a0 += 16) {
     float part[16];
@@ -200,9 +215,120 @@ __global__ __launch_bounds__(256) void velocity_euler_kernel(const float *__rest
   }
 }
 void launch_velocity_euler(const float *h, const float *gain, const float *w_out, const float *b_out, float *x, int M,
-                           int H, int A, float eps, int num_steps, hipStream_t s) {
+                           int H, int A, float eps, int num_steps, hipStream_t s, const float *fscale,
+                           const float *fshift) {
   hipLaunchKernelGGL(velocity_euler_kernel, dim3(M), dim3(256), 0, s, h, gain, w_out, b_out, x, H, A, eps,
-                     1.0f / (float)num_steps);
+                     1.0f / (float)num_steps, fscale, fshift);
+}
+
+// ---------------------------------------------------------------- time modulation of the action expert
+// Page "DM0.5: High-Performance Embodied VLA ...", section 5.2: time_mlp_in / time_mlp_out turn the
+// flow time into a modulation signal and every layer's modulator turns it into the scale, shift
+// and gate of its two norms.  t is shared by the whole batch, so a chunk's tables (all Euler
+// steps, all layers) are computed once before the first step, each weight read once.
+
+// tau[k][i] = sin / cos(t_k * 10000^(-2j/H)) with t_k = 1 - k / num_steps (as in embed_kernel).
+__global__ void tau_table_kernel(float *tau, int num_steps, int H) {
+  const int k = blockIdx.y, i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= H) return;
+  const int half = H / 2, j = i < half ? i : i - half;
+  const float t = 1.0f - (float)k / (float)num_steps;
+  const float w = exp2f(-2.0f * (float)j / (float)H * 13.287712379549449f);
+  tau[(size_t)k * H + i] = i < half ? sinf(t * w) : cosf(t * w);
+}
+void launch_tau_table(float *tau, int num_steps, int H, hipStream_t s) {
+  hipLaunchKernelGGL(tau_table_kernel, dim3((H + 255) / 256, num_steps), dim3(256), 0, s, tau, num_steps, H);
+}
+
+// Y[m][n] = b[n] + sum_k f(X[m][k]) W[n][k], M <= 16, K <= 1024 (a multiple of 8): the M input
+// rows (f applied) sit in LDS; each wave takes one output row n at a time, its lanes 8 consecutive
+// inputs each (one 16- or 32-byte load), then one reduction across the wave per input row.
+constexpr int GEMV_MAX_ROWS = 16, GEMV_MAX_K = 1024;
+template <typename WT>
+__global__ __launch_bounds__(256) void rows_gemv_kernel(const float *__restrict__ X, int M, int K,
+                                                        const WT *__restrict__ W, const float *__restrict__ b,
+                                                        float *__restrict__ Y, int N, int silu_in) {
+  __shared__ float xs[GEMV_MAX_ROWS * GEMV_MAX_K];
+  for (int e = threadIdx.x; e < M * K; e += blockDim.x) {
+    const float v = X[e];
+    xs[e] = silu_in ? silu(v) : v;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  for (int n = blockIdx.x * nwave + wave; n < N; n += gridDim.x * nwave) {
+    float acc[GEMV_MAX_ROWS];
+#pragma unroll
+    for (int m = 0; m < GEMV_MAX_ROWS; ++m) acc[m] = 0.f;
+    const WT *wr = W + (size_t)n * K;
+    for (int c = lane; c < K / 8; c += 64) {
+      float w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = to_f32(wr[8 * c + e]);
+#pragma unroll
+      for (int m = 0; m < GEMV_MAX_ROWS; ++m)
+        if (m < M) {
+          const float *xr = xs + m * K + 8 * c;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[m] += w[e] * xr[e];
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < GEMV_MAX_ROWS; ++m)
+      if (m < M) {
+        const float v = wave_sum(acc[m]);
+        if (lane == 0) Y[(size_t)m * N + n] = v + b[n];
+      }
+  }
+}
+void launch_rows_gemv(Dt dt, const float *X, int M, int K, const void *W, const float *b, float *Y, int N, bool silu_in,
+                      hipStream_t s) {
+  const int blocks = std::min(1024, (N + 3) / 4);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(rows_gemv_kernel<bf16>, dim3(blocks), dim3(256), 0, s, X, M, K, (const bf16 *)W, b, Y, N,
+                       (int)silu_in);
+  else
+    hipLaunchKernelGGL(rows_gemv_kernel<float>, dim3(blocks), dim3(256), 0, s, X, M, K, (const float *)W, b, Y, N,
+                       (int)silu_in);
+}
+
+// hg[m][i] = h[m][i] / rms(h[m]) * (1 + scale[i]) + shift[i]: one workgroup per row, thread t the
+// columns 4t + 1024j (H <= 4096, a multiple of 4).
+template <typename T>
+__global__ __launch_bounds__(256) void mod_norm_kernel(const float *__restrict__ h, T *__restrict__ hg,
+                                                       const float *__restrict__ scale, const float *__restrict__ shift,
+                                                       int H, float eps) {
+  __shared__ float red[4];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float4 hv[4];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 4 * tid + 1024 * j;
+    hv[j] = c < H ? *reinterpret_cast<const float4 *>(h + (size_t)m * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += hv[j].x * hv[j].x + hv[j].y * hv[j].y + hv[j].z * hv[j].z + hv[j].w * hv[j].w;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / H + eps);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 4 * tid + 1024 * j;
+    if (c >= H) continue;
+    const float4 sc = *reinterpret_cast<const float4 *>(scale + c), sh = *reinterpret_cast<const float4 *>(shift + c);
+    T *o = hg + (size_t)m * H + c;
+    o[0] = from_f32<T>(hv[j].x * inv * (1.f + sc.x) + sh.x);
+    o[1] = from_f32<T>(hv[j].y * inv * (1.f + sc.y) + sh.y);
+    o[2] = from_f32<T>(hv[j].z * inv * (1.f + sc.z) + sh.z);
+    o[3] = from_f32<T>(hv[j].w * inv * (1.f + sc.w) + sh.w);
+  }
+}
+void launch_mod_norm(Dt dt, const float *h, void *hg, const float *scale, const float *shift, int M, int H, float eps,
+                     hipStream_t s) {
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(mod_norm_kernel<bf16>, dim3(M), dim3(256), 0, s, h, (bf16 *)hg, scale, shift, H, eps);
+  else
+    hipLaunchKernelGGL(mod_norm_kernel<float>, dim3(M), dim3(256), 0, s, h, (float *)hg, scale, shift, H, eps);
 }
 
 // Nearest E4M3 (OCP e4m3fn) code of a float32 value, ties to even, saturating at +-448:

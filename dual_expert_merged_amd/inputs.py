@@ -15,6 +15,9 @@ Recipe (every draw uses ``numpy.random.default_rng([config_id, stream, layer, te
     in/out projections are float32 tensors of the action head; they are rounded too so every
     input of a bf16 workload is a bf16 value.
   * ragged prefix lengths are integers drawn uniformly from [lo, hi] inclusive.
+  * time-modulated action expert (stream 1, tensors 5..12): time MLP weights N(0, 0.05) and
+    biases N(0, 0.02); modulator weights N(0, 0.005); modulator biases N(0, 0.02) for the scales
+    and shifts and 1 + N(0, 0.02) for the gates; all rounded like the other weights.
 """
 from dataclasses import dataclass
 
@@ -25,6 +28,7 @@ from .configs import BF16, F32, Workload
 VLM_W, ACT_W, PREFIX, KV, NOISE, LENS, SUFFIX_H = range(7)
 T_ATTN_NORM, T_QKV, T_O, T_MLP_NORM, T_GATE, T_UP, T_DOWN = range(7)
 T_W_IN, T_B_IN, T_FINAL_NORM, T_W_OUT, T_B_OUT = range(5)
+T_TM_W_IN, T_TM_B_IN, T_TM_W_OUT, T_TM_B_OUT, T_TM_W_MOD, T_TM_B_MOD, T_TM_W_FMOD, T_TM_B_FMOD = range(5, 13)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -80,6 +84,19 @@ class ExpertWeights:
 
 
 @dataclass
+class TimeModWeights:
+    """Time modulation of the action expert: time MLP and per-layer / final modulators."""
+    w_in: np.ndarray        # [Ha, Ha] time_mlp_in
+    b_in: np.ndarray        # [Ha]
+    w_out: np.ndarray       # [Ha, Ha] time_mlp_out
+    b_out: np.ndarray       # [Ha]
+    w_mod: np.ndarray       # [L, 6 Ha, Ha]: attention scale, shift, gate, MLP scale, shift, gate
+    b_mod: np.ndarray       # [L, 6 Ha]
+    w_fmod: np.ndarray      # [2 Ha, Ha]: final-norm scale, shift
+    b_fmod: np.ndarray      # [2 Ha]
+
+
+@dataclass
 class ActionWeights:
     body: ExpertWeights
     w_in: np.ndarray        # [Ha, A]
@@ -87,6 +104,7 @@ class ActionWeights:
     final_norm: np.ndarray  # [Ha]
     w_out: np.ndarray       # [A, Ha]
     b_out: np.ndarray       # [A]
+    tmod: TimeModWeights = None
 
 
 def make_expert(wl: Workload, stream: int, hidden: int, ffn: int, n_layers=None) -> ExpertWeights:
@@ -120,6 +138,23 @@ def make_action_weights(wl: Workload) -> ActionWeights:
     body = make_expert(wl, ACT_W, s.act_hidden, s.act_ffn)
     L, c, dt = s.n_layers, wl.config_id, s.dtype
     H, A = s.act_hidden, s.action_dim
+    tmod = None
+    if s.time_mod:
+        # modulators: scale and shift biases N(0, 0.02), gate biases 1 + N(0, 0.02), weights
+        # N(0, 0.005) (modulations of about +-0.1 at hidden 1024); the time MLP's weights N(0, 0.05)
+        # so that c(t) varies visibly with t
+        gate_mean = np.tile(np.repeat([0.0, 0.0, 1.0], H), 2).astype(np.float32)
+        tmod = TimeModWeights(
+            w_in=round_to(_normal(c, ACT_W, L, T_TM_W_IN, (H, H), std=0.05), dt),
+            b_in=round_to(_normal(c, ACT_W, L, T_TM_B_IN, (H,), std=0.02), dt),
+            w_out=round_to(_normal(c, ACT_W, L, T_TM_W_OUT, (H, H), std=0.05), dt),
+            b_out=round_to(_normal(c, ACT_W, L, T_TM_B_OUT, (H,), std=0.02), dt),
+            w_mod=np.stack([round_to(_normal(c, ACT_W, l, T_TM_W_MOD, (6 * H, H), std=0.005), dt) for l in range(L)]),
+            b_mod=np.stack([round_to(_normal(c, ACT_W, l, T_TM_B_MOD, (6 * H,), std=0.02) + gate_mean, dt)
+                            for l in range(L)]),
+            w_fmod=round_to(_normal(c, ACT_W, L, T_TM_W_FMOD, (2 * H, H), std=0.005), dt),
+            b_fmod=round_to(_normal(c, ACT_W, L, T_TM_B_FMOD, (2 * H,), std=0.02), dt),
+        )
     return ActionWeights(
         body=body,
         w_in=round_to(_normal(c, ACT_W, L, T_W_IN, (H, A), std=0.02), dt),
@@ -127,6 +162,7 @@ def make_action_weights(wl: Workload) -> ActionWeights:
         final_norm=round_to(_normal(c, ACT_W, L, T_FINAL_NORM, (H,), std=0.02, mean=1.0), dt),
         w_out=round_to(_normal(c, ACT_W, L, T_W_OUT, (A, H), std=0.02), dt),
         b_out=round_to(_normal(c, ACT_W, L, T_B_OUT, (A,), std=0.02), dt),
+        tmod=tmod,
     )
 
 

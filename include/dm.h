@@ -93,6 +93,12 @@ typedef struct {
 /* dm_config.flags: run the batch-1 suffix denoise as the multi-kernel sequence even where the
  * single-launch kernel applies (the two agree to rounding; used to compare them). */
 #define DM_FLAG_MULTI_KERNEL 1
+/* dm_config.flags: the action expert is time-modulated (page "DM0.5: High-Performance Embodied
+ * VLA and OpenDM Open Source Introduction", section 5.2: time_mlp_in / time_mlp_out and a time
+ * modulator in every layer) instead of taking the additive time embedding; the denoise then
+ * needs dm_action_weights.tmod and at most DM_TMOD_MAX_STEPS Euler steps. */
+#define DM_FLAG_TIME_MODULATION 2
+#define DM_TMOD_MAX_STEPS 16
 
 /* One expert, every layer stacked.  H = expert hidden, F = expert FFN, QKV = (Hq+2Hkv)*D. */
 typedef struct {
@@ -108,6 +114,23 @@ typedef struct {
   const float *s_down;    /* [L][H] */
 } dm_expert_weights;
 
+/* Time modulation of the action expert (DM_FLAG_TIME_MODULATION), H = Ha.  Per Euler step with
+ * time t: c = w_out silu(w_in tau(t) + b_in) + b_out (tau: the sinusoidal time embedding of width
+ * H); layer l's modulator m = w_mod[l] silu(c) + b_mod[l] splits into (scale, shift, gate) of the
+ * attention norm, then of the MLP norm; each norm becomes h / rms(h) * (1 + scale) + shift
+ * (replacing its learned gain) and its sublayer enters the residual as h += gate * out; the
+ * final norm is h / rms(h) * (1 + fscale) + fshift with (fscale, fshift) = w_fmod silu(c) + b_fmod. */
+typedef struct {
+  const float *w_in;    /* [H][H] time_mlp_in */
+  const float *b_in;    /* [H] */
+  const float *w_out;   /* [H][H] time_mlp_out */
+  const float *b_out;   /* [H] */
+  const void *w_mod;    /* [L][6H][H], weight dtype: per layer attention scale, shift, gate, MLP scale, shift, gate */
+  const float *b_mod;   /* [L][6H] */
+  const void *w_fmod;   /* [2H][H], weight dtype: final-norm scale, shift */
+  const float *b_fmod;  /* [2H] */
+} dm_time_modulation;
+
 typedef struct {
   dm_expert_weights body; /* H = Ha, F = Fa, never FP8 */
   const float *w_in;      /* [Ha][A]  action_in_proj */
@@ -115,6 +138,8 @@ typedef struct {
   const float *final_norm;/* [Ha] */
   const float *w_out;     /* [A][Ha]  action_out_proj */
   const float *b_out;     /* [A] */
+  const dm_time_modulation *tmod; /* (host) set exactly when the config has DM_FLAG_TIME_MODULATION;
+                                     then attn_norm, mlp_norm and final_norm are not read */
 } dm_action_weights;
 
 typedef struct dm_ctx dm_ctx;

@@ -53,6 +53,7 @@ def _cfg(**kw):
     ("vlm_mlp_dtype", bd.DM_FP8_E4M3, bd.DM_ERR_UNSUPPORTED),  # FP8 MLP needs a bf16 model
     ("rms_eps", 0.0, bd.DM_ERR_INVALID_ARG),
     ("n_layers", 0, bd.DM_ERR_SHAPE),
+    ("flags", 4, bd.DM_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected_before_any_hip_call(field, value, status):
     lib = bd.lib()
@@ -89,3 +90,20 @@ def test_dm0_base_config_is_accepted_by_validation():
     else:
         assert st == bd.DM_ERR_HIP or st == bd.DM_ERR_INVALID_ARG, st
         assert b"hipGetDeviceCount" in lib.dm_last_error() or b"device" in lib.dm_last_error()
+
+
+def test_time_modulation_needs_hidden_at_most_1024():
+    h = C.c_void_p()
+    cfg = _cfg(flags=bd.DM_FLAG_TIME_MODULATION, act_hidden=2048)
+    assert bd.lib().dm_ctx_create(C.byref(cfg), 0, C.byref(h)) == bd.DM_ERR_UNSUPPORTED
+
+
+def test_action_weights_struct_matches_the_header():
+    """dm_action_weights ends with the tmod pointer after the five head tensors."""
+    text = open(HEADER).read()
+    body = text[text.index("dm_expert_weights body;"):text.index("} dm_action_weights;")]
+    names = re.findall(r"\*\s*(\w+);", body)
+    assert names == ["w_in", "b_in", "final_norm", "w_out", "b_out", "tmod"]
+    assert [f[0] for f in bd.ActionWeightsC._fields_] == ["body"] + names
+    tm = text[text.index("typedef struct {\n  const float *w_in;    /* [H][H] time_mlp_in */"):text.index("} dm_time_modulation;")]
+    assert re.findall(r"\*\s*(\w+);", tm) == list(bd.TMOD_FIELDS)
