@@ -18,8 +18,8 @@ rocprofv3 FETCH_SIZE + WRITE_SIZE counters, scaled against a plain copy
 (profiles/*_hbm_traffic.txt, reported only while the kernel sources are unchanged).
 Sub-objects of the same line: "batch32" (the batch-32 ragged workload, MFMA-bound: chunks/s,
 latency, the chunk's MFMA fraction from live events, each GEMM kernel's MFMA fraction from the
-committed kernel statistics) and "prefill_ms" (the B=8, 816-token prefix encoding with the bf16
-and with the FP8 MLP).
+committed kernel statistics), "time_modulated" (the DM0.5-style time-modulated expert, B=4) and
+"prefill_ms" (the B=8, 816-token prefix encoding with the bf16 and with the FP8 MLP).
 """
 import argparse
 import json
@@ -56,7 +56,14 @@ def algorithmic(wl, lens):
     tokens = wl.batch * S
     gemm = 2 * mat * tokens + 2 * (2 * A * H) * tokens
     attn = sum(4 * D * Hq * S * (int(p) + S) for p in lens) * L
-    return {"bytes": per_step_bytes * wl.steps, "flops": (gemm + attn) * wl.steps,
+    chunk_bytes = per_step_bytes * wl.steps
+    chunk_flops = (gemm + attn) * wl.steps
+    if getattr(s, "time_mod", False):
+        # the modulation tables, once per chunk: time MLP (fp32) and every modulator (weight dtype)
+        mod_rows = 6 * H * L + 2 * H
+        chunk_bytes += 2 * H * H * 4 + 2 * H * 4 + mod_rows * (H * es + 4)
+        chunk_flops += 2 * wl.steps * (2 * H * H + mod_rows * H)
+    return {"bytes": chunk_bytes, "flops": chunk_flops,
             "weight_bytes_per_step": mat * es + vec, "kv_bytes_per_step": kv}
 
 
@@ -505,6 +512,20 @@ def b32_summary(steps=20, warmup=3):
             "per_kernel": b32_kernel_rooflines(wl, lens)}
 
 
+def tmod_summary(steps=20, warmup=3):
+    """The time-modulated action expert (workload 7: DM0-base, B=4, 816-token prefix, 10 steps):
+    chunks/s, latency and the chunk's HBM / MFMA fractions from live events."""
+    wl, lens, _, res = run_denoise(7, steps, warmup)
+    alg = algorithmic(wl, lens)
+    chunk_s = float(np.mean(res["lat"])) * 1e-3
+    gbs, tfs = alg["bytes"] / chunk_s / 1e9, alg["flops"] / chunk_s / 1e12
+    return {"workload": wl.name, "value": round(res["value"], 2), "unit": "chunks/s", "steps": steps,
+            "latency_ms": latency(res["lat"]),
+            "roofline": {"bound": "hbm", "kernel": "all kernels of one chunk (graph replay)", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": alg["bytes"], "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -579,6 +600,8 @@ def main():
     if not args.no_extras:
         if args.config == 3:
             out["batch32"] = b32_summary()
+        log("[bench] timing the time-modulated expert")
+        out["time_modulated"] = tmod_summary()
         log("[bench] timing the prefix encoding (bf16 and FP8 MLP)")
         out["prefill_ms"] = prefill_times()
     print(json.dumps(out), flush=True)
