@@ -159,13 +159,19 @@ def expert_qkv(h, w, l, shape, pos):
 
 
 def project_qkv(n, w, l, shape, pos):
-    """Q/K/V projections of the normalised tokens n, RoPE on Q and K."""
+    """Q/K/V projections of the normalised tokens n, RoPE on Q and K.  Experts with per-head
+    QK-norm gains (``q_norm``, ``k_norm`` [L, D], not None) normalise every query and key head
+    vector first: [DM0] names Qwen3 experts, whose attention applies an RMSNorm over each head's
+    D dims (one gain vector per layer shared by the heads, the layers' eps) before RoPE."""
     T = n.shape[0]
     Hq, Hkv, D = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     qkv = linear(n, w.w_qkv[l])
     q = qkv[:, :Hq * D].reshape(T, Hq, D)
     k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D)
     v = qkv[:, (Hq + Hkv) * D:].reshape(T, Hkv, D)
+    if getattr(w, "q_norm", None) is not None:
+        q = rms_norm(q, w.q_norm[l], shape.rms_eps)
+        k = rms_norm(k, w.k_norm[l], shape.rms_eps)
     return rope(q, pos, shape.rope_base), rope(k, pos, shape.rope_base), v
 
 

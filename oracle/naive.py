@@ -54,11 +54,16 @@ def qkv_token(hrow, W, l, pos, sh):
 
 
 def qkv_normed(n, W, l, pos, sh):
-    """Q/K/V projections of an already normalised token, RoPE on Q and K."""
+    """Q/K/V projections of an already normalised token, RoPE on Q and K (after the per-head
+    RMSNorm of q and k when the expert has QK-norm gains)."""
     Hq, Hkv, D = sh.n_q_heads, sh.n_kv_heads, sh.head_dim
     y = matvec(W.w_qkv[l], n)
-    q = [rotate(v, pos, sh.rope_base) for v in heads(y[:Hq * D], Hq, D)]
-    k = [rotate(v, pos, sh.rope_base) for v in heads(y[Hq * D:(Hq + Hkv) * D], Hkv, D)]
+    qh, kh = heads(y[:Hq * D], Hq, D), heads(y[Hq * D:(Hq + Hkv) * D], Hkv, D)
+    if getattr(W, "q_norm", None) is not None:
+        qh = [rmsnorm(v, W.q_norm[l], sh.rms_eps) for v in qh]
+        kh = [rmsnorm(v, W.k_norm[l], sh.rms_eps) for v in kh]
+    q = [rotate(v, pos, sh.rope_base) for v in qh]
+    k = [rotate(v, pos, sh.rope_base) for v in kh]
     v = heads(y[(Hq + Hkv) * D:], Hkv, D)
     return q, k, v
 
