@@ -23,6 +23,7 @@ DM_F32, DM_BF16, DM_FP8_E4M3 = 0, 1, 2
 DM_FLAG_MULTI_KERNEL = 1
 DM_FLAG_TIME_MODULATION = 2
 DM_TMOD_MAX_STEPS = 16
+DM_FLAG_QK_NORM = 4
 OP_PREFILL, OP_MERGED_LAYER, OP_DENOISE = 0, 1, 2
 _DT = {F32: DM_F32, BF16: DM_BF16, FP8: DM_FP8_E4M3}
 EXPORTS = ["dm_version", "dm_last_error", "dm_ctx_create", "dm_ctx_destroy", "dm_workspace_bytes",
@@ -46,7 +47,7 @@ class Config(C.Structure):
 
 class ExpertWeightsC(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate", "w_up",
-                                          "w_down", "s_gate", "s_up", "s_down")]
+                                          "w_down", "s_gate", "s_up", "s_down", "q_norm", "k_norm")]
 
 
 TMOD_FIELDS = ("w_in", "b_in", "w_out", "b_out", "w_mod", "b_mod", "w_fmod", "b_fmod")
@@ -155,8 +156,13 @@ class DeviceExpert:
                 self.t[k], self.t["s" + k[1:]] = codes, s
                 scales[i] = ptr(s)
             torch.cuda.current_stream().synchronize()
+        qk = [None, None]
+        if getattr(w, "q_norm", None) is not None:  # per-head QK-norm gains (float32)
+            for i, k in enumerate(("q_norm", "k_norm")):
+                self.t[k] = to_device(getattr(w, k), torch.float32, device)
+                qk[i] = ptr(self.t[k])
         self.c = ExpertWeightsC(*(ptr(self.t[k]) for k in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate",
-                                                            "w_up", "w_down")), *scales)
+                                                            "w_up", "w_down")), *scales, *qk)
 
 
 class DeviceAction:
@@ -188,6 +194,8 @@ class Context:
         self.device = device
         if getattr(shape, "time_mod", False):
             flags |= DM_FLAG_TIME_MODULATION
+        if getattr(shape, "qk_norm", False):
+            flags |= DM_FLAG_QK_NORM
         self.cfg = make_config(shape, flags)
         h = C.c_void_p()
         check(lib().dm_ctx_create(C.byref(self.cfg), device, C.byref(h)))

@@ -36,6 +36,7 @@ class ModelShape:
     dtype: str = BF16
     vlm_mlp_dtype: str = BF16
     time_mod: bool = False     # DM0.5-style time-modulated action expert (page 2, section 5.2)
+    qk_norm: bool = False      # Qwen3 per-head QK-norm in both experts (page 1, section 1: Qwen3 stacks)
 
     @property
     def group(self) -> int:
@@ -91,6 +92,11 @@ WORKLOADS = {
     7: Workload(7, "DM0-base suffix denoise with the time-modulated action expert, bf16, B=4, prefix KV 816, "
                    "10 steps", replace(DM0_BASE, time_mod=True), batch=4, prefix_len=816, steps=10,
                 kind="denoise"),
+    8: Workload(8, "tiny model with per-head QK-norm in both experts, fp32, B=2 ragged prefix 1-64, 3 Euler steps",
+                replace(TINY, qk_norm=True), batch=2, prefix_len=64, ragged=(1, 64), steps=3,
+                kind="prefill_denoise"),
+    9: Workload(9, "DM0-base suffix denoise with per-head QK-norm, bf16, B=2, prefix KV 816, 10 steps",
+                replace(DM0_BASE, qk_norm=True), batch=2, prefix_len=816, steps=10, kind="denoise"),
 }
 
 

@@ -223,7 +223,7 @@ size_t split_bytes(const GemmPlan &p, int M, int N) {
 // The batch-1 denoise runs as one launch per chunk (persist.hip) for the DM0-base action expert
 // shapes, unless the config asks for the multi-kernel sequence.
 bool single_launch_shape(const dm_config &c, int B, int P_cap) {
-  return !(c.flags & (DM_FLAG_MULTI_KERNEL | DM_FLAG_TIME_MODULATION)) &&
+  return !(c.flags & (DM_FLAG_MULTI_KERNEL | DM_FLAG_TIME_MODULATION | DM_FLAG_QK_NORM)) &&
          persist_supported(c.n_layers, c.act_hidden, c.act_ffn, c.n_q_heads, c.n_kv_heads, c.head_dim, c.chunk, c.action_dim, B,
                            P_cap, c.dtype == DM_BF16);
 }
@@ -319,15 +319,18 @@ dm_status check_config(const dm_config *c) {
   REQUIRE(c->chunk >= 1 && c->chunk <= 64, DM_ERR_UNSUPPORTED, "chunk must be 1..64");
   REQUIRE(c->rms_eps > 0.f && std::isfinite(c->rms_eps), DM_ERR_INVALID_ARG, "rms_eps must be positive");
   REQUIRE(c->rope_base > 1.f && std::isfinite(c->rope_base), DM_ERR_INVALID_ARG, "rope_base must be > 1");
-  REQUIRE((c->flags & ~(DM_FLAG_MULTI_KERNEL | DM_FLAG_TIME_MODULATION)) == 0, DM_ERR_INVALID_ARG, "unknown flags 0x%x",
-          c->flags);
+  REQUIRE((c->flags & ~(DM_FLAG_MULTI_KERNEL | DM_FLAG_TIME_MODULATION | DM_FLAG_QK_NORM)) == 0, DM_ERR_INVALID_ARG,
+          "unknown flags 0x%x", c->flags);
   REQUIRE(!(c->flags & DM_FLAG_TIME_MODULATION) || c->act_hidden <= 1024, DM_ERR_UNSUPPORTED,
           "the time-modulated action expert supports act_hidden <= 1024");
   return DM_OK;
 }
 
-dm_status check_expert(const dm_expert_weights *w, bool fp8, const char *name) {
+dm_status check_expert(const dm_expert_weights *w, bool fp8, const char *name, bool qk) {
   REQUIRE(w, DM_ERR_INVALID_ARG, "%s weights are NULL", name);
+  REQUIRE(qk == (w->q_norm != nullptr) && qk == (w->k_norm != nullptr), DM_ERR_INVALID_ARG,
+          qk ? "%s weights: DM_FLAG_QK_NORM needs q_norm and k_norm" : "%s weights: q_norm / k_norm without DM_FLAG_QK_NORM",
+          name);
   const void *ptrs[] = {w->attn_norm, w->w_qkv, w->w_o, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
   for (const void *p : ptrs) {
     REQUIRE(p, DM_ERR_INVALID_ARG, "%s weights: a tensor pointer is NULL", name);
@@ -369,6 +372,7 @@ struct Expert {
   const float *attn_norm, *mlp_norm;
   const void *w_qkv, *w_o, *w_gate, *w_up, *w_down;
   const float *s_gate = nullptr, *s_up = nullptr, *s_down = nullptr;  // FP8 MLP only
+  const float *q_norm = nullptr, *k_norm = nullptr;                   // QK-norm only
 };
 
 // Layer l of a stacked expert; fp8: the MLP matrices are one-byte E4M3 codes with scales.
@@ -388,6 +392,10 @@ Expert expert_layer(const dm_config &c, const dm_expert_weights &w, int l, int H
     e.s_gate = w.s_gate + (size_t)l * F;
     e.s_up = w.s_up + (size_t)l * F;
     e.s_down = w.s_down + (size_t)l * H;
+  }
+  if (c.flags & DM_FLAG_QK_NORM) {
+    e.q_norm = w.q_norm + (size_t)l * c.head_dim;
+    e.k_norm = w.k_norm + (size_t)l * c.head_dim;
   }
   return e;
 }
@@ -477,7 +485,7 @@ dm_status enqueue_denoise_tmod(const dm_ctx *ctx, const Layout &L, const dm_acti
       const float *m = mod + ((size_t)k * NL + l) * 6 * Ha;  // attention scale, shift, gate; MLP scale, shift, gate
       const Expert e = expert_layer(c, aw->body, l, Ha, Fa, ctx->es);
       launch_mod_norm(ctx->dt, hid.h, hid.hg, m, m + Ha, M, Ha, eps, s);
-      QkvArgs qa{normed, M, eps, e.w_qkv, q, ks, vs, S, rows, rope, c.n_q_heads, Hkv, D, rope_rows};
+      QkvArgs qa{normed, M, eps, e.w_qkv, q, ks, vs, S, rows, rope, c.n_q_heads, Hkv, D, rope_rows, e.q_norm, e.k_norm};
       launch_qkv(ctx->dt, qa, L.pa.qkv, s);
       AttnArgs aa{q, S, 1,
                   layer_ptr(k_cache, layer_cache, l, ctx->es), layer_ptr(v_cache, layer_cache, l, ctx->es), P_cap,
@@ -532,7 +540,7 @@ dm_status enqueue_denoise(const dm_ctx *ctx, const dm_action_weights *aw, const 
     launch_embed(ctx->dt, x, aw->w_in, aw->b_in, hid, aw->body.attn_norm, M, c.action_dim, t, s);
     for (int l = 0; l < c.n_layers; ++l) {
       const Expert e = expert_layer(c, aw->body, l, Ha, Fa, ctx->es);
-      QkvArgs qa{hid, M, c.rms_eps, e.w_qkv, q, ks, vs, S, rows, rope, c.n_q_heads, Hkv, D, rope_rows};
+      QkvArgs qa{hid, M, c.rms_eps, e.w_qkv, q, ks, vs, S, rows, rope, c.n_q_heads, Hkv, D, rope_rows, e.q_norm, e.k_norm};
       launch_qkv(ctx->dt, qa, pq, s);
       AttnArgs aa{q, S, 1,
                   layer_ptr(k_cache, layer_cache, l, ctx->es), layer_ptr(v_cache, layer_cache, l, ctx->es), P_cap,
@@ -550,7 +558,7 @@ dm_status enqueue_denoise(const dm_ctx *ctx, const dm_action_weights *aw, const 
 
 dm_status check_action(const dm_ctx *ctx, const dm_action_weights *aw) {
   REQUIRE(aw, DM_ERR_INVALID_ARG, "action weights are NULL");
-  TRY(check_expert(&aw->body, false, "action"));
+  TRY(check_expert(&aw->body, false, "action", (ctx->cfg.flags & DM_FLAG_QK_NORM) != 0));
   const void *ptrs[] = {aw->w_in, aw->b_in, aw->final_norm, aw->w_out, aw->b_out};
   for (const void *p : ptrs) {
     REQUIRE(p, DM_ERR_INVALID_ARG, "action head: a tensor pointer is NULL");
@@ -742,8 +750,8 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   REQUIRE(c.vlm_mlp_dtype == c.dtype, DM_ERR_UNSUPPORTED, "dm_merged_layer runs the VLM MLP in the weight dtype");
   REQUIRE(!(c.flags & DM_FLAG_TIME_MODULATION), DM_ERR_UNSUPPORTED,
           "the time-modulated action expert needs the flow time: only dm_suffix_denoise runs it");
-  TRY(check_expert(vlm, false, "VLM"));
-  TRY(check_expert(act, false, "action"));
+  TRY(check_expert(vlm, false, "VLM", (c.flags & DM_FLAG_QK_NORM) != 0));
+  TRY(check_expert(act, false, "action", (c.flags & DM_FLAG_QK_NORM) != 0));
   REQUIRE(layer >= 0 && layer < c.n_layers, DM_ERR_SHAPE, "layer %d out of range", layer);
   REQUIRE(h_prefix && h_suffix, DM_ERR_INVALID_ARG, "h_prefix / h_suffix is NULL");
   REQUIRE(aligned16(h_prefix) && aligned16(h_suffix), DM_ERR_INVALID_ARG, "hidden streams must be 16-byte aligned");
@@ -767,10 +775,11 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   launch_rope_rows(rope, prefix_lens, P_cap, B, S, D, rope_rows, s);
   launch_norm_prep(ctx->dt, h_prefix, hp, ev.attn_norm, Mp, s);
   launch_norm_prep(ctx->dt, h_suffix, hs, ea.attn_norm, Ms, s);
-  QkvArgs qv{hp, Mp, c.rms_eps, ev.w_qkv, at<void>(ws, L.q_p), kp, vp, P_cap, prow, rope, Hq, Hkv, D};
+  QkvArgs qv{hp, Mp, c.rms_eps, ev.w_qkv, at<void>(ws, L.q_p), kp, vp, P_cap, prow, rope, Hq, Hkv, D, nullptr,
+             ev.q_norm, ev.k_norm};
   launch_qkv(ctx->dt, qv, L.pv.qkv, s);
   QkvArgs qa{hs, Ms, c.rms_eps, ea.w_qkv, at<void>(ws, L.q), at<void>(ws, L.ks), at<void>(ws, L.vs), S, srow, rope,
-             Hq, Hkv, D, rope_rows};
+             Hq, Hkv, D, rope_rows, ea.q_norm, ea.k_norm};
   launch_qkv(ctx->dt, qa, L.pa.qkv, s);
   AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kp, vp, P_cap, nullptr, nullptr, S, prefix_lens, B, Hq, Hkv, D,
               L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),
@@ -792,7 +801,7 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *
   TRY(check_common(ctx, prefix_lens, B, P_cap, ws, ws_bytes, DM_OP_PREFILL));
   const dm_config &c = ctx->cfg;
   const bool fp8 = c.vlm_mlp_dtype == DM_FP8_E4M3;
-  TRY(check_expert(vlm, fp8, "VLM"));
+  TRY(check_expert(vlm, fp8, "VLM", (c.flags & DM_FLAG_QK_NORM) != 0));
   REQUIRE(prefix_embeds && k_cache && v_cache, DM_ERR_INVALID_ARG, "prefix_embeds / k_cache / v_cache is NULL");
   REQUIRE(aligned16(prefix_embeds) && aligned16(k_cache) && aligned16(v_cache), DM_ERR_INVALID_ARG,
           "prefix_embeds and caches must be 16-byte aligned");
@@ -812,7 +821,8 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *
     const Expert e = expert_layer(c, *vlm, l, Hv, c.vlm_ffn, ctx->es, fp8);
     void *kc = (void *)layer_ptr(k_cache, layer_cache, l, ctx->es);
     void *vc = (void *)layer_ptr(v_cache, layer_cache, l, ctx->es);
-    QkvArgs qv{hp, Mp, c.rms_eps, e.w_qkv, at<void>(ws, L.q_p), kc, vc, P_cap, prow, rope, Hq, Hkv, D};
+    QkvArgs qv{hp, Mp, c.rms_eps, e.w_qkv, at<void>(ws, L.q_p), kc, vc, P_cap, prow, rope, Hq, Hkv, D, nullptr,
+               e.q_norm, e.k_norm};
     launch_qkv(ctx->dt, qv, L.pv.qkv, s);
     if (l == c.n_layers - 1) break;  // the last layer's outputs past its K/V are never read
     AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kc, vc, P_cap, nullptr, nullptr, c.chunk, prefix_lens, B, Hq, Hkv, D,

@@ -196,6 +196,7 @@ template <typename T> struct EpiQkv {
   // rotate-half RoPE of the lane's pair (lo = dim d, hi = dim d + D/2) for rows of the q and k
   // sections; v passes through
   __device__ __forceinline__ void rotate(const St &st, int gc, float &lo, float &hi, int r) const {
+    if (a.q_norm) return;  // QK-norm first: qk_norm_rope_kernel rotates after normalising
     if (gc < (a.Hq + a.Hkv) * a.D) {
       const float l = lo, h = hi;
       lo = l * st.cs[r].x - h * st.cs[r].y;
@@ -1004,8 +1005,39 @@ void launch_swiglu_fp8(const SwigluArgs &a, hipStream_t s) {
 
 int gemm_k_quantum(Dt dt) { return 4 * 4 * (dt == DT_BF16 ? Mfma<bf16>::EPL : Mfma<float>::EPL); }
 
+// Qwen3 per-head QK-norm, then rotate-half RoPE, in place on the Q and K the product wrote
+// unrotated: workgroup = (row, head), lane i < D/2 the pair (i, i + D/2); rows past a sample's
+// prefix are left untouched, as by the product.
+template <typename T> __global__ __launch_bounds__(64) void qk_norm_rope_kernel(QkvArgs a) {
+  const int m = blockIdx.x, h = blockIdx.y, i = threadIdx.x, half = a.D >> 1;
+  const int rpb = a.rows.rows_per_b, b = m / rpb, s = m - b * rpb;
+  if (a.rows.is_prefix && s >= max(0, min(a.rows.lens[b], a.rows.cap))) return;  // uniform
+  T *p;
+  const float *g;
+  if (h < a.Hq) {
+    p = (T *)a.q + (size_t)m * a.Hq * a.D + (size_t)h * a.D;
+    g = a.q_norm;
+  } else {
+    p = (T *)a.k + ((size_t)(b * a.Hkv + h - a.Hq) * a.kv_rows + s) * a.D;
+    g = a.k_norm;
+  }
+  const bool on = i < half;
+  const float x0 = on ? to_f32(p[i]) : 0.f, x1 = on ? to_f32(p[i + half]) : 0.f;
+  const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)a.D + a.eps);
+  if (!on) return;
+  const float n0 = x0 * inv * g[i], n1 = x1 * inv * g[i + half];
+  const float2 cs = a.rows.is_prefix ? a.rope[(size_t)s * half + i] : a.rope_rows[(size_t)m * half + i];
+  p[i] = from_f32<T>(n0 * cs.x - n1 * cs.y);
+  p[i + half] = from_f32<T>(n1 * cs.x + n0 * cs.y);
+}
+
 void launch_qkv(Dt dt, const QkvArgs &a, const GemmPlan &p, hipStream_t s) {
   if (dt == DT_BF16) qkv_t<bf16>(a, p, s); else qkv_t<float>(a, p, s);
+  if (a.q_norm) {
+    const dim3 grid(a.M, a.Hq + a.Hkv);
+    if (dt == DT_BF16) hipLaunchKernelGGL(qk_norm_rope_kernel<bf16>, grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(qk_norm_rope_kernel<float>, grid, dim3(64), 0, s, a);
+  }
 }
 void launch_resid(Dt dt, const ResidArgs &a, const GemmPlan &p, hipStream_t s) {
   if (dt == DT_BF16) resid_t<bf16>(a, p, s); else resid_t<float>(a, p, s);

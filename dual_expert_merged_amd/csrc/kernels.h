@@ -47,6 +47,9 @@ struct QkvArgs {
   const float2 *rope;            // [positions][D/2] (cos, sin)
   int Hq, Hkv, D;
   const float2 *rope_rows = nullptr;  // action rows: [M][D/2] (cos, sin) at position P_b + s
+  // Qwen3 per-head QK-norm gains [D] (NULL: none).  When set, the product writes Q and K
+  // unrotated and a second launch normalises every query / key head vector, then applies RoPE.
+  const float *q_norm = nullptr, *k_norm = nullptr;
 };
 // out.h += A W^T (times gate[n] when gate is set), then out.hg = (h * next_gain) and out.ssq
 // for the next sublayer (next_gain NULL: skip them).  Rows outside RowMap untouched.

@@ -15,6 +15,7 @@ Recipe (every draw uses ``numpy.random.default_rng([config_id, stream, layer, te
     in/out projections are float32 tensors of the action head; they are rounded too so every
     input of a bf16 workload is a bf16 value.
   * ragged prefix lengths are integers drawn uniformly from [lo, hi] inclusive.
+  * per-head QK-norm gains (QK-norm models, tensors 7 and 8 of each expert's stream): 1 + N(0, 0.1).
   * time-modulated action expert (stream 1, tensors 5..12): time MLP weights N(0, 0.05) and
     biases N(0, 0.02); modulator weights N(0, 0.005); modulator biases N(0, 0.02) for the scales
     and shifts and 1 + N(0, 0.02) for the gates; all rounded like the other weights.
@@ -26,7 +27,7 @@ import numpy as np
 from .configs import BF16, F32, Workload
 
 VLM_W, ACT_W, PREFIX, KV, NOISE, LENS, SUFFIX_H = range(7)
-T_ATTN_NORM, T_QKV, T_O, T_MLP_NORM, T_GATE, T_UP, T_DOWN = range(7)
+T_ATTN_NORM, T_QKV, T_O, T_MLP_NORM, T_GATE, T_UP, T_DOWN, T_Q_NORM, T_K_NORM = range(9)
 T_W_IN, T_B_IN, T_FINAL_NORM, T_W_OUT, T_B_OUT = range(5)
 T_TM_W_IN, T_TM_B_IN, T_TM_W_OUT, T_TM_B_OUT, T_TM_W_MOD, T_TM_B_MOD, T_TM_W_FMOD, T_TM_B_FMOD = range(5, 13)
 
@@ -74,9 +75,12 @@ class ExpertWeights:
     w_gate: np.ndarray      # [L, F, H]
     w_up: np.ndarray        # [L, F, H]
     w_down: np.ndarray      # [L, H, F]
+    q_norm: np.ndarray = None   # [L, D] per-head QK-norm gains (QK-norm models only)
+    k_norm: np.ndarray = None   # [L, D]
 
     def layer(self, l):
-        return ExpertWeights(*(getattr(self, f)[l:l + 1] for f in self.__dataclass_fields__))
+        return ExpertWeights(*(None if getattr(self, f) is None else getattr(self, f)[l:l + 1]
+                               for f in self.__dataclass_fields__))
 
     @property
     def n_layers(self):
@@ -126,6 +130,8 @@ def make_expert(wl: Workload, stream: int, hidden: int, ffn: int, n_layers=None)
         w_gate=stack(T_GATE, (ffn, hidden), std=0.02),
         w_up=stack(T_UP, (ffn, hidden), std=0.02),
         w_down=stack(T_DOWN, (hidden, ffn), std=0.02),
+        q_norm=stack(T_Q_NORM, (s.head_dim,), std=0.1, mean=1.0) if s.qk_norm else None,
+        k_norm=stack(T_K_NORM, (s.head_dim,), std=0.1, mean=1.0) if s.qk_norm else None,
     )
 
 

@@ -99,6 +99,11 @@ typedef struct {
  * needs dm_action_weights.tmod and at most DM_TMOD_MAX_STEPS Euler steps. */
 #define DM_FLAG_TIME_MODULATION 2
 #define DM_TMOD_MAX_STEPS 16
+/* dm_config.flags: Qwen3 per-head QK-norm in both experts (page "DM0 paper definition vs.
+ * Dexbotic code", section 1: the experts are Qwen3 stacks): every query and key head vector is
+ * RMS-normalised over its D dims with the layer's gain (dm_expert_weights.q_norm / k_norm) before
+ * RoPE.  The experts' weights then need q_norm and k_norm. */
+#define DM_FLAG_QK_NORM 4
 
 /* One expert, every layer stacked.  H = expert hidden, F = expert FFN, QKV = (Hq+2Hkv)*D. */
 typedef struct {
@@ -112,6 +117,8 @@ typedef struct {
   const float *s_gate;    /* [L][F] per-output-channel dequantisation scales (FP8 only, else NULL) */
   const float *s_up;      /* [L][F] */
   const float *s_down;    /* [L][H] */
+  const float *q_norm;    /* [L][D] per-head query norm gain (DM_FLAG_QK_NORM only, else NULL) */
+  const float *k_norm;    /* [L][D] per-head key norm gain (DM_FLAG_QK_NORM only, else NULL) */
 } dm_expert_weights;
 
 /* Time modulation of the action expert (DM_FLAG_TIME_MODULATION), H = Ha.  Per Euler step with

@@ -53,7 +53,7 @@ def _cfg(**kw):
     ("vlm_mlp_dtype", bd.DM_FP8_E4M3, bd.DM_ERR_UNSUPPORTED),  # FP8 MLP needs a bf16 model
     ("rms_eps", 0.0, bd.DM_ERR_INVALID_ARG),
     ("n_layers", 0, bd.DM_ERR_SHAPE),
-    ("flags", 4, bd.DM_ERR_INVALID_ARG),
+    ("flags", 8, bd.DM_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected_before_any_hip_call(field, value, status):
     lib = bd.lib()
@@ -107,3 +107,11 @@ def test_action_weights_struct_matches_the_header():
     assert [f[0] for f in bd.ActionWeightsC._fields_] == ["body"] + names
     tm = text[text.index("typedef struct {\n  const float *w_in;    /* [H][H] time_mlp_in */"):text.index("} dm_time_modulation;")]
     assert re.findall(r"\*\s*(\w+);", tm) == list(bd.TMOD_FIELDS)
+
+
+def test_expert_weights_struct_matches_the_header():
+    text = open(HEADER).read()
+    body = text[text.index("const float *attn_norm; /* [L][H] */"):text.index("} dm_expert_weights;")]
+    names = re.findall(r"\*\s*(\w+);", body)
+    assert [f[0] for f in bd.ExpertWeightsC._fields_] == names
+    assert names[-2:] == ["q_norm", "k_norm"]
