@@ -198,12 +198,13 @@ class Context:
             flags |= DM_FLAG_QK_NORM
         self.cfg = make_config(shape, flags)
         h = C.c_void_p()
+        self._destroy = lib().dm_ctx_destroy  # bound now: module globals may be gone when __del__ runs at exit
         check(lib().dm_ctx_create(C.byref(self.cfg), device, C.byref(h)))
         self.h = h
 
     def close(self):
-        if self.h:
-            lib().dm_ctx_destroy(self.h)
+        if getattr(self, "h", None):
+            self._destroy(self.h)
             self.h = None
 
     __del__ = close
@@ -252,6 +253,7 @@ class Plan:
     """A captured denoise graph; keeps the tensors it was captured with alive."""
 
     def __init__(self, handle, steps, keep):
+        self._destroy = lib().dm_denoise_plan_destroy  # bound now, as in Context
         self.h = handle
         self.steps = steps
         self.keep = keep
@@ -261,8 +263,8 @@ class Plan:
                                            stream_handle(stream)))
 
     def close(self):
-        if self.h:
-            lib().dm_denoise_plan_destroy(self.h)
+        if getattr(self, "h", None):
+            self._destroy(self.h)
             self.h = None
 
     __del__ = close

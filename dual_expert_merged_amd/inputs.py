@@ -78,9 +78,13 @@ class ExpertWeights:
     q_norm: np.ndarray = None   # [L, D] per-head QK-norm gains (QK-norm models only)
     k_norm: np.ndarray = None   # [L, D]
 
-    def layer(self, l):
-        return ExpertWeights(*(None if getattr(self, f) is None else getattr(self, f)[l:l + 1]
+    def layers(self, lo, hi):
+        """Layers lo .. hi-1 (absent optional gains stay absent)."""
+        return ExpertWeights(*(None if getattr(self, f) is None else getattr(self, f)[lo:hi]
                                for f in self.__dataclass_fields__))
+
+    def layer(self, l):
+        return self.layers(l, l + 1)
 
     @property
     def n_layers(self):

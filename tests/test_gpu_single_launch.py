@@ -82,7 +82,7 @@ def test_single_launch_one_euler_step_and_short_stack(dm0):
     wl, aw = dm0
     s = dataclasses.replace(wl.shape, n_layers=3)
     wl3 = dataclasses.replace(wl, shape=s)
-    body3 = inputs.ExpertWeights(*(getattr(aw.body, f)[:3] for f in aw.body.__dataclass_fields__))
+    body3 = aw.body.layers(0, 3)
     aw3 = dataclasses.replace(aw, body=body3)
     print("case: single-launch denoise, 3 layers, N=1 and N=2", flush=True)
     kc, vc, x1 = _cache(wl3, 816, 5)
