@@ -18,8 +18,10 @@ rocprofv3 FETCH_SIZE + WRITE_SIZE counters, scaled against a plain copy
 (profiles/*_hbm_traffic.txt, reported only while the kernel sources are unchanged).
 Sub-objects of the same line: "batch32" (the batch-32 ragged workload, MFMA-bound: chunks/s,
 latency, the chunk's MFMA fraction from live events, each GEMM kernel's MFMA fraction from the
-committed kernel statistics), "time_modulated" (the DM0.5-style time-modulated expert, B=4) and
-"prefill_ms" (the B=8, 816-token prefix encoding with the bf16 and with the FP8 MLP).
+committed kernel statistics), "time_modulated" (the DM0.5-style time-modulated expert, B=4),
+"prefill_ms" (the B=8, 816-token prefix encoding with the bf16 and with the FP8 MLP) and
+"serving" (the fixed-contract engine on prefill + denoise at B=8: model-core and request
+latency percentiles).
 """
 import argparse
 import json
@@ -284,7 +286,7 @@ def copy_calibration():
     log(f"[bench] copied {COPY_REPS} x {COPY_BYTES} bytes")
 
 
-def prefill_times(reps=3, modes=("bf16", "fp8_mlp")):
+def prefill_times(reps=3, modes=("bf16", "fp8_mlp"), vlm=None):
     """Prefix encoding of the prefill workload (B=8, 816 tokens, 28 VLM layers) with the bf16
     MLP and with the FP8 E4M3 MLP: mean ms per call over `reps` calls after one warm-up."""
     import torch
@@ -294,7 +296,8 @@ def prefill_times(reps=3, modes=("bf16", "fp8_mlp")):
     from dual_expert_merged_amd.configs import FP8, workload
 
     wl = workload(5)
-    vlm = inputs.make_vlm_weights(wl)
+    if vlm is None:
+        vlm = inputs.make_vlm_weights(wl)
     emb = torch.from_numpy(inputs.make_prefix_embeds(wl)).cuda()
     lens = torch.from_numpy(inputs.make_prefix_lens(wl)).cuda()
     s = wl.shape
@@ -327,6 +330,63 @@ def prefill_times(reps=3, modes=("bf16", "fp8_mlp")):
     if "bf16" in out:
         out["bf16_mfma_frac_of_gemm_flops"] = round(flops / (out["bf16"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
     return out
+
+
+def serving_summary(vlm=None, reps=20, warmup=3):
+    """The fixed-contract engine on the prefill + denoise workload (B=8, 816-token prefix, 28 VLM
+    and 28 action layers, 10 Euler steps): model-core latency (one replay of the captured prefix
+    encoding + denoise over the resident static buffers, HIP events on its stream) and request
+    latency (host wall clock around dm_engine_run: copy of the embeddings, lengths and noise
+    from pinned host buffers into the static ones, the replay, the chunk copied back)."""
+    import torch
+    from dual_expert_merged_amd import binding as bd
+    from dual_expert_merged_amd import inputs
+    from dual_expert_merged_amd.configs import workload
+
+    wl = workload(5)
+    s = wl.shape
+    if vlm is None:
+        vlm = inputs.make_vlm_weights(wl)
+    aw = inputs.make_action_weights(wl)
+
+    def pinned(a):
+        t = torch.empty(a.shape, dtype=torch.from_numpy(a).dtype, pin_memory=True)
+        t.numpy()[...] = a
+        return t
+
+    emb, lens, x1 = (pinned(a) for a in (inputs.make_prefix_embeds(wl), inputs.make_prefix_lens(wl),
+                                         inputs.make_noise(wl)))
+    actions = torch.empty(x1.shape, dtype=torch.float32, pin_memory=True)
+    ctx = bd.Context(s, 0)
+    dv, da = bd.DeviceExpert(vlm, s.dtype), bd.DeviceAction(aw, s.dtype)
+    stream = torch.cuda.Stream()
+    eng = bd.Engine(ctx, dv, da, wl.batch, wl.prefix_len, wl.steps, stream=stream)
+    args = (emb.numpy(), lens.numpy(), x1.numpy(), actions.numpy())
+    for _ in range(warmup):
+        eng.run(*args, stream=stream)
+    req = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        eng.run(*args, stream=stream)
+        req.append((time.perf_counter() - t0) * 1e3)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record(stream)
+        eng.replay(stream=stream)
+        ends[i].record(stream)
+    stream.synchronize()
+    core = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    contract = eng.contract()
+    eng.close()
+    del dv, da
+    ctx.close()
+    torch.cuda.empty_cache()
+    h2d = emb.numel() * 4 + lens.numel() * 4 + x1.numel() * 4
+    return {"workload": wl.name, "contract": contract, "model_core_ms": latency(core),
+            "request_ms": latency(np.array(req)), "requests_per_s": round(1e3 / float(np.mean(req)), 2),
+            "chunks_per_s": round(wl.batch * 1e3 / float(np.mean(req)), 2), "copied_in_bytes": int(h2d),
+            "copied_out_bytes": int(x1.numel() * 4), "host_buffers": "pinned"}
 
 
 def merged_layer_times(reps=20):
@@ -539,6 +599,8 @@ def main():
     ap.add_argument("--merged-layer", action="store_true",
                     help="time only one merged layer (both experts, B=1, 816 + 50 tokens) and print it")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the plain copy for counter scaling")
+    ap.add_argument("--serving-only", action="store_true",
+                    help="time only the fixed-contract engine (prefill + denoise, B=8) and print it")
     ap.add_argument("--prefill-only", choices=["both", "bf16", "fp8_mlp"],
                     help="time only the prefix encoding (B=8, 816 tokens) with the bf16 MLP, the FP8 MLP or both")
     ap.add_argument("--traffic-summary", action="store_true", help="summarise counter runs (no GPU needed)")
@@ -563,6 +625,9 @@ def main():
         return
     if args.merged_layer:
         print(json.dumps({"merged_layer": merged_layer_times()}), flush=True)
+        return
+    if args.serving_only:
+        print(json.dumps({"serving": serving_summary()}), flush=True)
         return
     if args.copy_calibration:
         copy_calibration()
@@ -602,8 +667,14 @@ def main():
             out["batch32"] = b32_summary()
         log("[bench] timing the time-modulated expert")
         out["time_modulated"] = tmod_summary()
+        from dual_expert_merged_amd import inputs
+        from dual_expert_merged_amd.configs import workload
+        log("[bench] generating the VLM expert of the prefill workload")
+        vlm = inputs.make_vlm_weights(workload(5))
         log("[bench] timing the prefix encoding (bf16 and FP8 MLP)")
-        out["prefill_ms"] = prefill_times()
+        out["prefill_ms"] = prefill_times(vlm=vlm)
+        log("[bench] timing the fixed-contract engine (prefill + denoise, B=8)")
+        out["serving"] = serving_summary(vlm=vlm)
     print(json.dumps(out), flush=True)
 
 

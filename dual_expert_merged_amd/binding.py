@@ -28,7 +28,22 @@ OP_PREFILL, OP_MERGED_LAYER, OP_DENOISE = 0, 1, 2
 _DT = {F32: DM_F32, BF16: DM_BF16, FP8: DM_FP8_E4M3}
 EXPORTS = ["dm_version", "dm_last_error", "dm_ctx_create", "dm_ctx_destroy", "dm_workspace_bytes",
            "dm_prefill_kv", "dm_merged_layer", "dm_suffix_denoise", "dm_denoise_plan_create",
-           "dm_denoise_plan_launch", "dm_denoise_plan_destroy", "dm_quantize_fp8_rows", "dm_suffix_denoise_noalloc"]
+           "dm_denoise_plan_launch", "dm_denoise_plan_destroy", "dm_quantize_fp8_rows", "dm_suffix_denoise_noalloc",
+           "dm_engine_create", "dm_engine_contract_get", "dm_engine_run", "dm_engine_replay", "dm_engine_buffers",
+           "dm_engine_destroy"]
+
+
+ENGINE_CONTRACT_FIELDS = ("batch", "prefix_cap", "num_steps", "chunk", "action_dim", "vlm_hidden")
+
+
+class EngineContractC(C.Structure):
+    _fields_ = [(n, C.c_int) for n in ENGINE_CONTRACT_FIELDS]
+
+
+class EngineRequestC(C.Structure):
+    _fields_ = [("batch", C.c_int), ("prefix_cap", C.c_int), ("num_steps", C.c_int),
+                ("prefix_embeds", C.c_void_p), ("prefix_lens", C.c_void_p), ("noise", C.c_void_p),
+                ("actions", C.c_void_p)]
 
 
 class DMError(RuntimeError):
@@ -92,9 +107,17 @@ def lib():
         L.dm_denoise_plan_destroy.restype = None
         L.dm_quantize_fp8_rows.argtypes = [vp, vp, vp, i, i, vp]
         L.dm_suffix_denoise_noalloc.argtypes = [vp, C.POINTER(ActionWeightsC), vp, vp, vp, i, i, vp, i, vp]
+        L.dm_engine_create.argtypes = [vp, C.POINTER(ExpertWeightsC), C.POINTER(ActionWeightsC), i, i, i, vp,
+                                       C.POINTER(vp)]
+        L.dm_engine_contract_get.argtypes = [vp, C.POINTER(EngineContractC)]
+        L.dm_engine_run.argtypes = [vp, C.POINTER(EngineRequestC), vp]
+        L.dm_engine_replay.argtypes = [vp, vp]
+        L.dm_engine_buffers.argtypes = [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp)]
+        L.dm_engine_destroy.argtypes = [vp]
+        L.dm_engine_destroy.restype = None
         for name in EXPORTS:
             if name not in ("dm_version", "dm_last_error", "dm_ctx_destroy", "dm_workspace_bytes",
-                            "dm_denoise_plan_destroy"):
+                            "dm_denoise_plan_destroy", "dm_engine_destroy"):
                 getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -261,6 +284,56 @@ class Plan:
     def launch(self, num_steps=None, stream=None):
         check(lib().dm_denoise_plan_launch(self.h, self.steps if num_steps is None else num_steps,
                                            stream_handle(stream)))
+
+    def close(self):
+        if getattr(self, "h", None):
+            self._destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+
+class Engine:
+    """A fixed-contract engine: static device buffers and one captured prefill + denoise graph.
+    Keeps the weight objects it was created from alive."""
+
+    def __init__(self, ctx: "Context", vlm: "DeviceExpert", aw: "DeviceAction", B, P_cap, num_steps, stream=None):
+        self._destroy = lib().dm_engine_destroy  # bound now, as in Context
+        self.h = None
+        h = C.c_void_p()
+        check(lib().dm_engine_create(ctx.h, C.byref(vlm.c), C.byref(aw.c), B, P_cap, num_steps,
+                                     stream_handle(stream), C.byref(h)))
+        self.h = h
+        self.keep = (ctx, vlm, aw)
+
+    def contract(self):
+        c = EngineContractC()
+        check(lib().dm_engine_contract_get(self.h, C.byref(c)))
+        return {n: getattr(c, n) for n in ENGINE_CONTRACT_FIELDS}
+
+    def run(self, prefix_embeds, prefix_lens, noise, actions, batch=None, prefix_cap=None, num_steps=None,
+            stream=None):
+        """One request from host numpy arrays (float32 embeds / noise / actions, int32 lengths);
+        the claimed shape defaults to the arrays' own, num_steps to the contract's."""
+        for a, dt in ((prefix_embeds, np.float32), (prefix_lens, np.int32), (noise, np.float32), (actions, np.float32)):
+            if a is not None and (a.dtype != dt or not a.flags.c_contiguous):
+                raise ValueError("request arrays must be C-contiguous float32 (lengths int32)")
+        k = self.contract()
+        req = EngineRequestC(
+            prefix_embeds.shape[0] if batch is None else batch,
+            prefix_embeds.shape[1] if prefix_cap is None else prefix_cap,
+            k["num_steps"] if num_steps is None else num_steps,
+            *(None if a is None else C.c_void_p(a.ctypes.data) for a in (prefix_embeds, prefix_lens, noise, actions)))
+        check(lib().dm_engine_run(self.h, C.byref(req), stream_handle(stream)))
+
+    def replay(self, stream=None):
+        check(lib().dm_engine_replay(self.h, stream_handle(stream)))
+
+    def buffers(self):
+        """Device addresses (ints) of the static prefix embeddings, prefix lengths and x."""
+        e, l, x = C.c_void_p(), C.c_void_p(), C.c_void_p()
+        check(lib().dm_engine_buffers(self.h, C.byref(e), C.byref(l), C.byref(x)))
+        return e.value, l.value, x.value
 
     def close(self):
         if getattr(self, "h", None):

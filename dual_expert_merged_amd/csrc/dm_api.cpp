@@ -593,6 +593,50 @@ dm_status check_denoise(dm_ctx *ctx, const dm_action_weights *aw, const void *k_
   return DM_OK;
 }
 
+dm_status check_prefill(dm_ctx *ctx, const dm_expert_weights *vlm, const float *prefix_embeds, const int32_t *lens,
+                        int B, int P_cap, void *k_cache, void *v_cache, void *ws, size_t ws_bytes) {
+  TRY(check_common(ctx, lens, B, P_cap, ws, ws_bytes, DM_OP_PREFILL));
+  const dm_config &c = ctx->cfg;
+  TRY(check_expert(vlm, c.vlm_mlp_dtype == DM_FP8_E4M3, "VLM", (c.flags & DM_FLAG_QK_NORM) != 0));
+  REQUIRE(prefix_embeds && k_cache && v_cache, DM_ERR_INVALID_ARG, "prefix_embeds / k_cache / v_cache is NULL");
+  REQUIRE(aligned16(prefix_embeds) && aligned16(k_cache) && aligned16(v_cache), DM_ERR_INVALID_ARG,
+          "prefix_embeds and caches must be 16-byte aligned");
+  return DM_OK;
+}
+
+// The prefix encoding's launches on `s` (arguments already checked).
+void enqueue_prefill(const dm_ctx *ctx, const dm_expert_weights *vlm, const float *prefix_embeds,
+                     const int32_t *prefix_lens, int B, int P_cap, void *k_cache, void *v_cache, void *ws,
+                     hipStream_t s) {
+  const dm_config &c = ctx->cfg;
+  const bool fp8 = c.vlm_mlp_dtype == DM_FP8_E4M3;
+  const Layout L = make_layout(c, ctx->es, DM_OP_PREFILL, B, P_cap);
+  const int D = c.head_dim, Hkv = c.n_kv_heads, Hq = c.n_q_heads, Hv = c.vlm_hidden;
+  const int Mp = B * P_cap;
+  float2 *rope = at<float2>(ws, L.rope);
+  const Hidden hp{at<float>(ws, L.hp), at<void>(ws, L.hg_p), at<float>(ws, L.ssq_p), Hv};
+  const RowMap prow{P_cap, prefix_lens, 1, P_cap};
+  const size_t layer_cache = (size_t)B * Hkv * P_cap * D;
+
+  launch_rope_table(rope, P_cap, D, c.rope_base, s);
+  launch_norm_prep(ctx->dt, prefix_embeds, hp, vlm->attn_norm, Mp, s);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const Expert e = expert_layer(c, *vlm, l, Hv, c.vlm_ffn, ctx->es, fp8);
+    void *kc = (void *)layer_ptr(k_cache, layer_cache, l, ctx->es);
+    void *vc = (void *)layer_ptr(v_cache, layer_cache, l, ctx->es);
+    QkvArgs qv{hp, Mp, c.rms_eps, e.w_qkv, at<void>(ws, L.q_p), kc, vc, P_cap, prow, rope, Hq, Hkv, D, nullptr,
+               e.q_norm, e.k_norm};
+    launch_qkv(ctx->dt, qv, L.pv.qkv, s);
+    if (l == c.n_layers - 1) break;  // the last layer's outputs past its K/V are never read
+    AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kc, vc, P_cap, nullptr, nullptr, c.chunk, prefix_lens, B, Hq, Hkv, D,
+                L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),
+                L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr};
+    launch_attention(ctx->dt, ap, s);
+    (fp8 ? enqueue_finish_fp8 : enqueue_finish)(ctx, L, ws, L.pv, e, hp, at<void>(ws, L.o_p), at<void>(ws, L.act_p),
+                                                Mp, c.vlm_ffn, prow, vlm->attn_norm + (size_t)(l + 1) * Hv, s);
+  }
+}
+
 dm_status set_device(const dm_ctx *ctx) {
   int cur = -1;
   HIP_TRY(hipGetDevice(&cur));
@@ -600,7 +644,61 @@ dm_status set_device(const dm_ctx *ctx) {
   return DM_OK;
 }
 
+// Captures what `enqueue(capture_stream)` launches into a graph on a private stream, then
+// instantiates it and uploads it on `stream` (which is synchronised).  On failure nothing is
+// kept and the enqueue's own status, or DM_ERR_HIP, is returned.
+template <class F>
+dm_status capture_graph(hipStream_t stream, F &&enqueue, hipGraph_t *graph_out, hipGraphExec_t *exec_out) {
+  hipStream_t cs = nullptr;
+  HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return fail(DM_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
+  }
+  const dm_status st = enqueue(cs);
+  const hipError_t le = hipGetLastError();
+  e = hipStreamEndCapture(cs, &graph);
+  (void)hipStreamDestroy(cs);
+  if (st != DM_OK || le != hipSuccess || e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    if (st != DM_OK) return st;
+    return fail(DM_ERR_HIP, "graph capture: %s", hipGetErrorString(le != hipSuccess ? le : e));
+  }
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return fail(DM_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+  }
+  e = hipGraphUpload(exec, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return fail(DM_ERR_HIP, "hipGraphUpload: %s", hipGetErrorString(e));
+  }
+  *graph_out = graph;
+  *exec_out = exec;
+  return DM_OK;
+}
+
 }  // namespace
+
+// A fixed-contract engine: one device allocation holding the static buffers, and the captured
+// graph of the prefix encoding followed by the denoise over them.
+struct dm_engine {
+  int device;
+  dm_engine_contract contract;
+  void *mem;
+  float *embeds;
+  int32_t *lens;
+  float *x;
+  size_t embeds_bytes, x_bytes;
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
 
 // ============================================================================= exported C ABI
 
@@ -684,36 +782,12 @@ dm_status dm_denoise_plan_create(dm_ctx *ctx, const dm_action_weights *aw, const
   *out = nullptr;
   TRY(check_denoise(ctx, aw, k_cache, v_cache, prefix_lens, B, P_cap, x, num_steps, ws, ws_bytes));
   TRY(set_device(ctx));
-  hipStream_t cs = nullptr;
-  HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
   hipGraph_t graph = nullptr;
-  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
-  if (e != hipSuccess) {
-    (void)hipStreamDestroy(cs);
-    return fail(DM_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
-  }
-  const dm_status st = enqueue_denoise(ctx, aw, k_cache, v_cache, prefix_lens, B, P_cap, x, num_steps, ws, cs);
-  const hipError_t le = hipGetLastError();
-  e = hipStreamEndCapture(cs, &graph);
-  (void)hipStreamDestroy(cs);
-  if (st != DM_OK || le != hipSuccess || e != hipSuccess) {
-    if (graph) (void)hipGraphDestroy(graph);
-    if (st != DM_OK) return st;
-    return fail(DM_ERR_HIP, "graph capture: %s", hipGetErrorString(le != hipSuccess ? le : e));
-  }
   hipGraphExec_t exec = nullptr;
-  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-  if (e != hipSuccess) {
-    (void)hipGraphDestroy(graph);
-    return fail(DM_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
-  }
-  e = hipGraphUpload(exec, (hipStream_t)stream);
-  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
-  if (e != hipSuccess) {
-    (void)hipGraphExecDestroy(exec);
-    (void)hipGraphDestroy(graph);
-    return fail(DM_ERR_HIP, "hipGraphUpload: %s", hipGetErrorString(e));
-  }
+  TRY(capture_graph(
+      (hipStream_t)stream,
+      [&](hipStream_t cs) { return enqueue_denoise(ctx, aw, k_cache, v_cache, prefix_lens, B, P_cap, x, num_steps, ws, cs); },
+      &graph, &exec));
   dm_plan *p = new (std::nothrow) dm_plan{graph, exec, num_steps, ctx->device};
   if (!p) {
     (void)hipGraphExecDestroy(exec);
@@ -740,6 +814,137 @@ void dm_denoise_plan_destroy(dm_plan *plan) {
   (void)hipGraphExecDestroy(plan->exec);
   (void)hipGraphDestroy(plan->graph);
   delete plan;
+}
+
+dm_status dm_engine_create(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_action_weights *aw, int B, int P_cap,
+                           int num_steps, void *stream, dm_engine **out) {
+  REQUIRE(out, DM_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  REQUIRE(ctx, DM_ERR_INVALID_ARG, "ctx is NULL");
+  REQUIRE(B >= 1 && B <= 4096, DM_ERR_SHAPE, "B must be 1..4096 (got %d)", B);
+  REQUIRE(P_cap >= 1 && P_cap <= 65536, DM_ERR_SHAPE, "P_cap must be 1..65536 (got %d)", P_cap);
+  REQUIRE(num_steps >= 1 && num_steps <= 1000, DM_ERR_SHAPE, "num_steps must be 1..1000 (got %d)", num_steps);
+  const dm_config &c = ctx->cfg;
+  TRY(check_expert(vlm, c.vlm_mlp_dtype == DM_FP8_E4M3, "VLM", (c.flags & DM_FLAG_QK_NORM) != 0));
+  TRY(check_action(ctx, aw));
+  REQUIRE(!(c.flags & DM_FLAG_TIME_MODULATION) || num_steps <= DM_TMOD_MAX_STEPS, DM_ERR_UNSUPPORTED,
+          "the time-modulated expert supports at most %d Euler steps (got %d)", DM_TMOD_MAX_STEPS, num_steps);
+  // one allocation: embeddings, lengths, x, K cache, V cache, workspace (each 256-byte aligned)
+  const size_t embeds_bytes = (size_t)B * P_cap * c.vlm_hidden * sizeof(float);
+  const size_t lens_bytes = (size_t)B * sizeof(int32_t);
+  const size_t x_bytes = (size_t)B * c.chunk * c.action_dim * sizeof(float);
+  const size_t cache_bytes = (size_t)c.n_layers * B * c.n_kv_heads * P_cap * c.head_dim * ctx->es;
+  const size_t ws_bytes = std::max(make_layout(c, ctx->es, DM_OP_PREFILL, B, P_cap).total,
+                                   make_layout(c, ctx->es, DM_OP_DENOISE, B, P_cap).total);
+  const size_t o_lens = up256(embeds_bytes), o_x = o_lens + up256(lens_bytes), o_k = o_x + up256(x_bytes);
+  const size_t o_v = o_k + up256(cache_bytes), o_ws = o_v + up256(cache_bytes), total = o_ws + up256(ws_bytes);
+  TRY(set_device(ctx));
+  hipStream_t s = (hipStream_t)stream;
+  void *mem = nullptr;
+  HIP_TRY(hipMalloc(&mem, total));
+  char *base = (char *)mem;
+  float *embeds = (float *)base;
+  int32_t *lens = (int32_t *)(base + o_lens);
+  float *x = (float *)(base + o_x);
+  void *kc = base + o_k, *vc = base + o_v, *ws = base + o_ws;
+  hipError_t e = hipMemsetAsync(mem, 0, total, s);  // before capture, never inside the graph
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(mem);
+    return fail(DM_ERR_HIP, "clearing the engine buffers: %s", hipGetErrorString(e));
+  }
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  const dm_status st = capture_graph(
+      s,
+      [&](hipStream_t cs) {
+        enqueue_prefill(ctx, vlm, embeds, lens, B, P_cap, kc, vc, ws, cs);
+        return enqueue_denoise(ctx, aw, kc, vc, lens, B, P_cap, x, num_steps, ws, cs);
+      },
+      &graph, &exec);
+  if (st != DM_OK) {
+    (void)hipFree(mem);
+    return st;
+  }
+  dm_engine *eng = new (std::nothrow) dm_engine;
+  if (!eng) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    (void)hipFree(mem);
+    return fail(DM_ERR_INVALID_ARG, "out of host memory");
+  }
+  eng->device = ctx->device;
+  eng->contract = dm_engine_contract{B, P_cap, num_steps, c.chunk, c.action_dim, c.vlm_hidden};
+  eng->mem = mem;
+  eng->embeds = embeds;
+  eng->lens = lens;
+  eng->x = x;
+  eng->embeds_bytes = embeds_bytes;
+  eng->x_bytes = x_bytes;
+  eng->graph = graph;
+  eng->exec = exec;
+  *out = eng;
+  return DM_OK;
+}
+
+dm_status dm_engine_contract_get(const dm_engine *eng, dm_engine_contract *out) {
+  REQUIRE(eng && out, DM_ERR_INVALID_ARG, "engine / out is NULL");
+  *out = eng->contract;
+  return DM_OK;
+}
+
+dm_status dm_engine_run(dm_engine *eng, const dm_engine_request *req, void *stream) {
+  REQUIRE(eng && req, DM_ERR_INVALID_ARG, "engine / request is NULL");
+  const dm_engine_contract &k = eng->contract;
+  REQUIRE(req->batch == k.batch && req->prefix_cap == k.prefix_cap && req->num_steps == k.num_steps,
+          DM_ERR_PLAN_MISMATCH,
+          "request (batch %d, prefix_cap %d, num_steps %d) differs from the engine's contract (batch %d, prefix_cap "
+          "%d, num_steps %d)",
+          req->batch, req->prefix_cap, req->num_steps, k.batch, k.prefix_cap, k.num_steps);
+  REQUIRE(req->prefix_embeds && req->prefix_lens && req->noise && req->actions, DM_ERR_INVALID_ARG,
+          "a request buffer is NULL");
+  for (int b = 0; b < k.batch; ++b)
+    REQUIRE(req->prefix_lens[b] >= 0 && req->prefix_lens[b] <= k.prefix_cap, DM_ERR_SHAPE,
+            "prefix_lens[%d] = %d lies outside 0..%d", b, req->prefix_lens[b], k.prefix_cap);
+  int cur = -1;
+  HIP_TRY(hipGetDevice(&cur));
+  if (cur != eng->device) HIP_TRY(hipSetDevice(eng->device));
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipMemcpyAsync(eng->embeds, req->prefix_embeds, eng->embeds_bytes, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemcpyAsync(eng->lens, req->prefix_lens, (size_t)k.batch * sizeof(int32_t), hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemcpyAsync(eng->x, req->noise, eng->x_bytes, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipGraphLaunch(eng->exec, s));
+  HIP_TRY(hipMemcpyAsync(req->actions, eng->x, eng->x_bytes, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return DM_OK;
+}
+
+dm_status dm_engine_replay(dm_engine *eng, void *stream) {
+  REQUIRE(eng, DM_ERR_INVALID_ARG, "engine is NULL");
+  int cur = -1;
+  HIP_TRY(hipGetDevice(&cur));
+  if (cur != eng->device) HIP_TRY(hipSetDevice(eng->device));
+  HIP_TRY(hipGraphLaunch(eng->exec, (hipStream_t)stream));
+  return DM_OK;
+}
+
+dm_status dm_engine_buffers(const dm_engine *eng, float **prefix_embeds, int32_t **prefix_lens, float **x) {
+  REQUIRE(eng, DM_ERR_INVALID_ARG, "engine is NULL");
+  if (prefix_embeds) *prefix_embeds = eng->embeds;
+  if (prefix_lens) *prefix_lens = eng->lens;
+  if (x) *x = eng->x;
+  return DM_OK;
+}
+
+void dm_engine_destroy(dm_engine *eng) {
+  if (!eng) return;
+  int cur = -1;
+  const bool back = hipGetDevice(&cur) == hipSuccess && cur != eng->device && hipSetDevice(eng->device) == hipSuccess;
+  (void)hipGraphExecDestroy(eng->exec);
+  (void)hipGraphDestroy(eng->graph);
+  (void)hipFree(eng->mem);
+  if (back) (void)hipSetDevice(cur);
+  delete eng;
 }
 
 dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_expert_weights *act, int layer,
@@ -798,40 +1003,9 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
 dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *prefix_embeds,
                         const int32_t *prefix_lens, int B, int P_cap, void *k_cache, void *v_cache, void *ws,
                         size_t ws_bytes, void *stream) {
-  TRY(check_common(ctx, prefix_lens, B, P_cap, ws, ws_bytes, DM_OP_PREFILL));
-  const dm_config &c = ctx->cfg;
-  const bool fp8 = c.vlm_mlp_dtype == DM_FP8_E4M3;
-  TRY(check_expert(vlm, fp8, "VLM", (c.flags & DM_FLAG_QK_NORM) != 0));
-  REQUIRE(prefix_embeds && k_cache && v_cache, DM_ERR_INVALID_ARG, "prefix_embeds / k_cache / v_cache is NULL");
-  REQUIRE(aligned16(prefix_embeds) && aligned16(k_cache) && aligned16(v_cache), DM_ERR_INVALID_ARG,
-          "prefix_embeds and caches must be 16-byte aligned");
+  TRY(check_prefill(ctx, vlm, prefix_embeds, prefix_lens, B, P_cap, k_cache, v_cache, ws, ws_bytes));
   TRY(set_device(ctx));
-  hipStream_t s = (hipStream_t)stream;
-  const Layout L = make_layout(c, ctx->es, DM_OP_PREFILL, B, P_cap);
-  const int D = c.head_dim, Hkv = c.n_kv_heads, Hq = c.n_q_heads, Hv = c.vlm_hidden;
-  const int Mp = B * P_cap;
-  float2 *rope = at<float2>(ws, L.rope);
-  const Hidden hp{at<float>(ws, L.hp), at<void>(ws, L.hg_p), at<float>(ws, L.ssq_p), Hv};
-  const RowMap prow{P_cap, prefix_lens, 1, P_cap};
-  const size_t layer_cache = (size_t)B * Hkv * P_cap * D;
-
-  launch_rope_table(rope, P_cap, D, c.rope_base, s);
-  launch_norm_prep(ctx->dt, prefix_embeds, hp, vlm->attn_norm, Mp, s);
-  for (int l = 0; l < c.n_layers; ++l) {
-    const Expert e = expert_layer(c, *vlm, l, Hv, c.vlm_ffn, ctx->es, fp8);
-    void *kc = (void *)layer_ptr(k_cache, layer_cache, l, ctx->es);
-    void *vc = (void *)layer_ptr(v_cache, layer_cache, l, ctx->es);
-    QkvArgs qv{hp, Mp, c.rms_eps, e.w_qkv, at<void>(ws, L.q_p), kc, vc, P_cap, prow, rope, Hq, Hkv, D, nullptr,
-               e.q_norm, e.k_norm};
-    launch_qkv(ctx->dt, qv, L.pv.qkv, s);
-    if (l == c.n_layers - 1) break;  // the last layer's outputs past its K/V are never read
-    AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kc, vc, P_cap, nullptr, nullptr, c.chunk, prefix_lens, B, Hq, Hkv, D,
-                L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),
-                L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr};
-    launch_attention(ctx->dt, ap, s);
-    (fp8 ? enqueue_finish_fp8 : enqueue_finish)(ctx, L, ws, L.pv, e, hp, at<void>(ws, L.o_p), at<void>(ws, L.act_p),
-                                                Mp, c.vlm_ffn, prow, vlm->attn_norm + (size_t)(l + 1) * Hv, s);
-  }
+  enqueue_prefill(ctx, vlm, prefix_embeds, prefix_lens, B, P_cap, k_cache, v_cache, ws, (hipStream_t)stream);
   HIP_TRY(hipGetLastError());
   return DM_OK;
 }

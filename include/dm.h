@@ -39,10 +39,11 @@
  *  - prefix_lens [B] int32 on the device, 0 <= P_b <= P_cap (a sample may have no prefix token;
  *    values outside are clamped into that range).  The host validates only P_cap.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream), never
- *    synchronize, and never allocate device memory, except dm_ctx_create and
- *    dm_denoise_plan_create.  The caller owns every buffer; `ws` is caller-provided scratch of
- *    at least dm_workspace_bytes() bytes, 256-byte aligned; the library keeps no pointer
- *    after a call returns (a plan keeps the ones it was created with).
+ *    synchronize, and never allocate device memory, except dm_ctx_create,
+ *    dm_denoise_plan_create and dm_engine_create (and dm_engine_run synchronizes).  The
+ *    caller owns every buffer it passes; `ws` is caller-provided scratch of at least
+ *    dm_workspace_bytes() bytes, 256-byte aligned; the library keeps no pointer after a call
+ *    returns (a plan or an engine keeps the ones it was created with).
  *  - Errors: every call returns a dm_status; arguments are fully validated before any HIP
  *    call; no exception crosses the ABI and nothing aborts.  dm_last_error() gives a
  *    thread-local message for the last failure on the calling thread.
@@ -228,6 +229,56 @@ dm_status dm_denoise_plan_create(dm_ctx *ctx, const dm_action_weights *aw /* (ho
  * (else DM_ERR_PLAN_MISMATCH and nothing is launched). */
 dm_status dm_denoise_plan_launch(dm_plan *plan, int num_steps, void *stream);
 void dm_denoise_plan_destroy(dm_plan *plan);
+/* Fixed-contract engine (page "DM0.5: High-Performance Embodied VLA and OpenDM Open Source
+ * Introduction", section 6.5: at start-up the computation is captured once over static buffers
+ * of fixed shape; online a new observation is copied into those buffers and the graph is
+ * replayed once; batch, prompt length, chunk shape and step count are fixed, and another step
+ * count needs another capture; section 9.1: model-core latency, the GPU computation alone, is a
+ * different figure from request latency, which adds the data movement).
+ * An engine owns, on the context's device, the prefix embeddings [B][P_cap][Hv] float32, the
+ * prefix lengths [B] int32, x [B][S][A] float32, both KV caches [L][B][Hkv][P_cap][D] and one
+ * workspace, and a hipGraph of dm_prefill_kv followed by dm_suffix_denoise over them.  The
+ * weights passed at creation must stay valid and unchanged while the engine lives. */
+typedef struct dm_engine dm_engine;
+/* What every request must match (the engine's "capabilities"). */
+typedef struct {
+  int batch;       /* B */
+  int prefix_cap;  /* P_cap: token slots per sample; each request's P_b lies in 0..P_cap */
+  int num_steps;   /* Euler steps captured */
+  int chunk;       /* S, from the config */
+  int action_dim;  /* A, from the config */
+  int vlm_hidden;  /* Hv: floats per prefix embedding row, from the config */
+} dm_engine_contract;
+/* One request: the shape it claims, and host buffers in and out. */
+typedef struct {
+  int batch, prefix_cap, num_steps;  /* must equal the contract's */
+  const float *prefix_embeds;        /* (host) [B][P_cap][Hv]; rows >= P_b are copied, never read */
+  const int32_t *prefix_lens;        /* (host) [B] */
+  const float *noise;                /* (host) [B][S][A]: x at t = 1 */
+  float *actions;                    /* (host) [B][S][A]: receives the chunk at t = 0 */
+} dm_engine_request;
+/* Allocates the static buffers (zero-filled), captures the graph for B, P_cap and num_steps
+ * (the same ranges as dm_prefill_kv and dm_suffix_denoise) and uploads it; `stream` is
+ * synchronised.  Allocates device memory. */
+dm_status dm_engine_create(dm_ctx *ctx, const dm_expert_weights *vlm /* (host) */,
+                           const dm_action_weights *aw /* (host) */, int B, int P_cap, int num_steps,
+                           void *stream, dm_engine **out /* (host) */);
+dm_status dm_engine_contract_get(const dm_engine *eng, dm_engine_contract *out /* (host) */);
+/* Serves one request: a request whose batch, prefix_cap or num_steps differ from the contract
+ * returns DM_ERR_PLAN_MISMATCH, a prefix length outside 0..P_cap DM_ERR_SHAPE, a NULL buffer
+ * DM_ERR_INVALID_ARG; a rejected request copies and launches nothing.  Otherwise: the three
+ * inputs are copied into the static buffers, the graph is replayed once, the chunk is copied
+ * to `actions`, and `stream` is synchronised before the call returns.  Requests on one engine
+ * must not overlap. */
+dm_status dm_engine_run(dm_engine *eng, const dm_engine_request *req /* (host) */, void *stream);
+/* The model-core part alone: one replay over the static buffers as they stand (x is denoised
+ * in place, so a second replay starts from the previous chunk).  Asynchronous on `stream`. */
+dm_status dm_engine_replay(dm_engine *eng, void *stream);
+/* Device addresses of the static input / output buffers (any out pointer may be NULL), for
+ * callers whose inputs are already on the device. */
+dm_status dm_engine_buffers(const dm_engine *eng, float **prefix_embeds /* (host) */,
+                            int32_t **prefix_lens /* (host) */, float **x /* (host) */);
+void dm_engine_destroy(dm_engine *eng);
 
 /* FP8 E4M3 (OCP e4m3fn) row quantisation (page section 6.3), used for weights (one row per
  * output channel) and, inside dm_prefill_kv, for activations (one row per token):

@@ -79,6 +79,28 @@ def test_null_arguments_rejected():
     lib.dm_denoise_plan_destroy(None)
 
 
+def test_engine_null_arguments_rejected():
+    lib = bd.lib()
+    h = C.c_void_p()
+    assert lib.dm_engine_create(None, None, None, 8, 816, 10, None, None) == bd.DM_ERR_INVALID_ARG
+    assert lib.dm_engine_create(None, None, None, 8, 816, 10, None, C.byref(h)) == bd.DM_ERR_INVALID_ARG
+    assert h.value is None
+    assert lib.dm_engine_contract_get(None, C.byref(bd.EngineContractC())) == bd.DM_ERR_INVALID_ARG
+    assert lib.dm_engine_run(None, C.byref(bd.EngineRequestC()), None) == bd.DM_ERR_INVALID_ARG
+    assert lib.dm_engine_replay(None, None) == bd.DM_ERR_INVALID_ARG
+    assert lib.dm_engine_buffers(None, None, None, None) == bd.DM_ERR_INVALID_ARG
+    lib.dm_engine_destroy(None)
+
+
+def test_engine_structs_match_the_header():
+    text = open(HEADER).read()
+    con = text[text.index("int batch;       /* B */"):text.index("} dm_engine_contract;")]
+    assert tuple(re.findall(r"int (\w+);", con)) == bd.ENGINE_CONTRACT_FIELDS
+    req = text[text.index("int batch, prefix_cap, num_steps;"):text.index("} dm_engine_request;")]
+    names = ["batch", "prefix_cap", "num_steps"] + re.findall(r"\*\s*(\w+);", req)
+    assert [f[0] for f in bd.EngineRequestC._fields_] == names
+
+
 def test_dm0_base_config_is_accepted_by_validation():
     # a good config fails only at the device query on a machine without a GPU
     lib = bd.lib()
