@@ -19,6 +19,12 @@ Recipe (every draw uses ``numpy.random.default_rng([config_id, stream, layer, te
   * time-modulated action expert (stream 1, tensors 5..12): time MLP weights N(0, 0.05) and
     biases N(0, 0.02); modulator weights N(0, 0.005); modulator biases N(0, 0.02) for the scales
     and shifts and 1 + N(0, 0.02) for the gates; all rounded like the other weights.
+  * a training batch (stream 7, ``make_train_batch``): the prefix hidden input of the merged
+    layer N(0, 1) in the rows below each sample's prefix length (zero past it), the real action
+    chunk a uniform in [-1, 1], the noise eps N(0, 1), one time t per sample uniform in [0, 1],
+    and an action mask that keeps the first S_b time slices and the first A_b action dims of
+    sample b, with S_b uniform in [S/2, S] and A_b uniform in [A/2, A] (the last sample keeps
+    all of them); float32, rounded like the other inputs of the workload.
 """
 from dataclasses import dataclass
 
@@ -26,7 +32,7 @@ import numpy as np
 
 from .configs import BF16, F32, Workload
 
-VLM_W, ACT_W, PREFIX, KV, NOISE, LENS, SUFFIX_H = range(7)
+VLM_W, ACT_W, PREFIX, KV, NOISE, LENS, SUFFIX_H, TRAIN = range(8)
 T_ATTN_NORM, T_QKV, T_O, T_MLP_NORM, T_GATE, T_UP, T_DOWN, T_Q_NORM, T_K_NORM = range(9)
 T_W_IN, T_B_IN, T_FINAL_NORM, T_W_OUT, T_B_OUT = range(5)
 T_TM_W_IN, T_TM_B_IN, T_TM_W_OUT, T_TM_B_OUT, T_TM_W_MOD, T_TM_B_MOD, T_TM_W_FMOD, T_TM_B_FMOD = range(5, 13)
@@ -223,3 +229,35 @@ def make_suffix_hidden(wl: Workload) -> np.ndarray:
     s = wl.shape
     return round_to(_normal(wl.config_id, SUFFIX_H, 0, 0, (wl.batch, s.chunk, s.act_hidden)),
                     s.dtype)
+
+
+@dataclass
+class TrainBatch:
+    """Inputs of one flow-matching training step on a merged layer."""
+    h_pre: np.ndarray   # [B, P_cap, Hv] prefix hidden entering the layer (zero past lens[b])
+    lens: np.ndarray    # [B] int32 prefix lengths
+    a: np.ndarray       # [B, S, A] real action chunk
+    eps: np.ndarray     # [B, S, A] noise
+    t: np.ndarray       # [B] flow-matching time per sample
+    mask: np.ndarray    # [B, S, A] 1 on valid (time slice, action dim), else 0
+
+
+def make_train_batch(wl: Workload) -> TrainBatch:
+    s = wl.shape
+    B, S, A, P = wl.batch, s.chunk, s.action_dim, wl.prefix_len
+    c = wl.config_id
+    lens = make_prefix_lens(wl)
+    h_pre = np.zeros((B, P, s.vlm_hidden), dtype=np.float32)
+    for b in range(B):
+        h_pre[b, :lens[b]] = round_to(_normal(c, TRAIN, b, 0, (lens[b], s.vlm_hidden)), s.dtype)
+    a = round_to(_rng(c, TRAIN, 0, 1).uniform(-1.0, 1.0, (B, S, A)).astype(np.float32), s.dtype)
+    eps = round_to(_normal(c, TRAIN, 0, 2, (B, S, A)), s.dtype)
+    t = _rng(c, TRAIN, 0, 3).uniform(0.0, 1.0, B).astype(np.float32)
+    lim = _rng(c, TRAIN, 0, 4)
+    s_b = lim.integers(S // 2, S + 1, size=B)
+    a_b = lim.integers(A // 2, A + 1, size=B)
+    s_b[-1], a_b[-1] = S, A
+    mask = np.zeros((B, S, A), dtype=np.float32)
+    for b in range(B):
+        mask[b, :s_b[b], :a_b[b]] = 1.0
+    return TrainBatch(h_pre, lens, a, eps, t, mask)
