@@ -21,7 +21,8 @@ latency, the chunk's MFMA fraction from live events, each GEMM kernel's MFMA fra
 committed kernel statistics), "time_modulated" (the DM0.5-style time-modulated expert, B=4),
 "prefill_ms" (the B=8, 816-token prefix encoding with the bf16 and with the FP8 MLP) and
 "serving" (the fixed-contract engine on prefill + denoise at B=8: model-core and request
-latency percentiles).
+latency percentiles) and "training" (one flow-matching training step on one merged layer:
+ms per step and its fp32 matrix-core fraction).
 """
 import argparse
 import json
@@ -87,7 +88,7 @@ def cpu_baseline(wl, aw, kc, vc, x1, lens):
                       f"P={P}) in float64 numpy; {dt:.2f} s on {cores} host cores"}
 
 
-SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip", "persist.hip", "common.h", "kernels.h", "persist_plan.h",
+SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip", "persist.hip", "train.hip", "common.h", "kernels.h", "persist_plan.h",
            "addr_words.h"]
 
 
@@ -389,6 +390,78 @@ def serving_summary(vlm=None, reps=20, warmup=3):
             "copied_out_bytes": int(x1.numel() * 4), "host_buffers": "pinned"}
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak, TFLOP/s
+
+
+def train_flops(s, lens, ki):
+    """Algorithmic FLOPs of one training step on one merged layer: every product of the forward
+    (prefix K/V projection, action-row Q/K/V, scores and P V over P_b + S keys, O, gate, up, down,
+    action_in / out projections) once, and twice again in the backward (input and weight
+    gradients; the attention backward's four products); without knowledge insulation the prefix
+    K/V projection's two backward products too."""
+    S, A, D, Hq, Hkv = s.chunk, s.action_dim, s.head_dim, s.n_q_heads, s.n_kv_heads
+    Ha, Hv, F, QKV = s.act_hidden, s.vlm_hidden, s.act_ffn, s.qkv_rows
+    total = 0
+    for P in (int(p) for p in lens):
+        T = P + S
+        dense = 2 * S * (Ha * QKV + Hq * D * Ha + 3 * Ha * F + 2 * Ha * A)
+        attn = 2 * 2 * S * Hq * T * D
+        kv = 2 * P * Hv * 2 * Hkv * D
+        total += 3 * dense + attn + 2 * attn + kv + (0 if ki else 2 * kv)
+    return total
+
+
+def train_summary(reps=20, warmup=3, ki=False):
+    """One flow-matching training step on the one-layer DM0-base merged layer (B=1, 816-token
+    prefix + 50 action tokens, bf16 weights, float32 arithmetic), without knowledge insulation:
+    ms per step from HIP events around every call, and the step's fp32 matrix-core fraction."""
+    import torch
+    from dual_expert_merged_amd import binding as bd
+    from dual_expert_merged_amd import inputs
+    from dual_expert_merged_amd.configs import workload
+
+    wl = workload(2)
+    s = wl.shape
+    vlm, aw, tb = inputs.make_vlm_weights(wl), inputs.make_action_weights(wl), inputs.make_train_batch(wl)
+    ctx = bd.Context(s, 0)
+    dvlm, daw = bd.DeviceExpert(vlm, s.dtype), bd.DeviceAction(aw, s.dtype)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    args = (dev(tb.h_pre), torch.from_numpy(tb.lens).cuda(), dev(tb.a), dev(tb.eps), dev(tb.t), dev(tb.mask))
+    z = lambda shp: torch.empty(tuple(shp), dtype=torch.float32, device="cuda")
+    grads = {"attn_norm": z(aw.body.attn_norm.shape[1:]), "w_qkv": z(aw.body.w_qkv.shape[1:]),
+             "w_o": z(aw.body.w_o.shape[1:]), "mlp_norm": z(aw.body.mlp_norm.shape[1:]),
+             "w_gate": z(aw.body.w_gate.shape[1:]), "w_up": z(aw.body.w_up.shape[1:]),
+             "w_down": z(aw.body.w_down.shape[1:]), "w_in": z(aw.w_in.shape), "b_in": z(aw.b_in.shape),
+             "final_norm": z(aw.final_norm.shape), "w_out": z(aw.w_out.shape), "b_out": z(aw.b_out.shape),
+             "vlm_attn_norm": z(vlm.attn_norm.shape[1:]), "vlm_w_qkv": z(vlm.w_qkv.shape[1:]),
+             "h_prefix": z(tb.h_pre.shape)}
+    loss = z((1,))
+    ws = ctx.workspace(bd.OP_TRAIN, wl.batch, wl.prefix_len)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            ctx.train_merged_layer(dvlm, daw, 0, *args, ki, loss, grads, ws, stream=stream)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        for i in range(reps):
+            starts[i].record(stream)
+            ctx.train_merged_layer(dvlm, daw, 0, *args, ki, loss, grads, ws, stream=stream)
+            ends[i].record(stream)
+        stream.synchronize()
+    lat = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    flops = train_flops(s, tb.lens, ki)
+    tfs = flops / (float(np.mean(lat)) * 1e-3) / 1e12
+    del dvlm, daw, grads, ws
+    ctx.close()
+    torch.cuda.empty_cache()
+    return {"workload": "flow-matching training step on one DM0-base merged layer, B=1, prefix 816 + 50 action "
+                        "tokens, bf16 weights, fp32 arithmetic, no knowledge insulation",
+            "ms_per_step": latency(lat), "steps_per_s": round(1e3 / float(np.mean(lat)), 2),
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tfs / FP32_MFMA_PEAK_TFLOPS, 4), "algorithmic_flops_per_step": int(flops)},
+            "dtype": "f32"}
+
+
 def merged_layer_times(reps=20):
     """One DM0-base merged layer at batch 1 (816 prefix and 50 action tokens through both experts
     with the joint block-masked attention, prefix K/V written out): mean µs per dm_merged_layer
@@ -599,6 +672,8 @@ def main():
     ap.add_argument("--merged-layer", action="store_true",
                     help="time only one merged layer (both experts, B=1, 816 + 50 tokens) and print it")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the plain copy for counter scaling")
+    ap.add_argument("--train-only", action="store_true",
+                    help="time only the flow-matching training step on one merged layer and print it")
     ap.add_argument("--serving-only", action="store_true",
                     help="time only the fixed-contract engine (prefill + denoise, B=8) and print it")
     ap.add_argument("--prefill-only", choices=["both", "bf16", "fp8_mlp"],
@@ -628,6 +703,9 @@ def main():
         return
     if args.serving_only:
         print(json.dumps({"serving": serving_summary()}), flush=True)
+        return
+    if args.train_only:
+        print(json.dumps({"training": train_summary()}), flush=True)
         return
     if args.copy_calibration:
         copy_calibration()
@@ -675,6 +753,9 @@ def main():
         out["prefill_ms"] = prefill_times(vlm=vlm)
         log("[bench] timing the fixed-contract engine (prefill + denoise, B=8)")
         out["serving"] = serving_summary(vlm=vlm)
+        del vlm
+        log("[bench] timing the training step (one merged layer)")
+        out["training"] = train_summary()
     print(json.dumps(out), flush=True)
 
 

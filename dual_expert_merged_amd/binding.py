@@ -24,13 +24,21 @@ DM_FLAG_MULTI_KERNEL = 1
 DM_FLAG_TIME_MODULATION = 2
 DM_TMOD_MAX_STEPS = 16
 DM_FLAG_QK_NORM = 4
-OP_PREFILL, OP_MERGED_LAYER, OP_DENOISE = 0, 1, 2
+OP_PREFILL, OP_MERGED_LAYER, OP_DENOISE, OP_TRAIN = 0, 1, 2, 3
 _DT = {F32: DM_F32, BF16: DM_BF16, FP8: DM_FP8_E4M3}
 EXPORTS = ["dm_version", "dm_last_error", "dm_ctx_create", "dm_ctx_destroy", "dm_workspace_bytes",
            "dm_prefill_kv", "dm_merged_layer", "dm_suffix_denoise", "dm_denoise_plan_create",
            "dm_denoise_plan_launch", "dm_denoise_plan_destroy", "dm_quantize_fp8_rows", "dm_suffix_denoise_noalloc",
            "dm_engine_create", "dm_engine_contract_get", "dm_engine_run", "dm_engine_replay", "dm_engine_buffers",
-           "dm_engine_destroy"]
+           "dm_engine_destroy", "dm_train_merged_layer"]
+
+
+TRAIN_GRAD_FIELDS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate", "w_up", "w_down", "w_in", "b_in",
+                     "final_norm", "w_out", "b_out", "vlm_attn_norm", "vlm_w_qkv", "h_prefix")
+
+
+class TrainGradsC(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in TRAIN_GRAD_FIELDS]
 
 
 ENGINE_CONTRACT_FIELDS = ("batch", "prefix_cap", "num_steps", "chunk", "action_dim", "vlm_hidden")
@@ -113,6 +121,8 @@ def lib():
         L.dm_engine_run.argtypes = [vp, C.POINTER(EngineRequestC), vp]
         L.dm_engine_replay.argtypes = [vp, vp]
         L.dm_engine_buffers.argtypes = [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp)]
+        L.dm_train_merged_layer.argtypes = [vp, C.POINTER(ExpertWeightsC), C.POINTER(ActionWeightsC), i, vp, vp, i,
+                                            i, vp, vp, vp, vp, i, vp, C.POINTER(TrainGradsC), vp, sz, vp]
         L.dm_engine_destroy.argtypes = [vp]
         L.dm_engine_destroy.restype = None
         for name in EXPORTS:
@@ -262,6 +272,18 @@ class Context:
         B, P_cap = k_cache.shape[1], k_cache.shape[3]
         check(lib().dm_suffix_denoise_noalloc(self.h, C.byref(aw.c), ptr(k_cache), ptr(v_cache), ptr(lens), B, P_cap,
                                               ptr(x), num_steps, stream_handle(stream)))
+
+    def train_merged_layer(self, vlm: DeviceExpert, aw: DeviceAction, layer, h_prefix, lens, actions, noise, t, mask,
+                           knowledge_insulation, loss, grads, ws, stream=None):
+        """One flow-matching training step on merged layer `layer`; `grads` maps the names in
+        TRAIN_GRAD_FIELDS to float32 device tensors (absent names pass NULL); `loss` is a
+        one-element float32 device tensor."""
+        B, P_cap = h_prefix.shape[0], h_prefix.shape[1]
+        gc = TrainGradsC(*(ptr(grads.get(n)) for n in TRAIN_GRAD_FIELDS))
+        check(lib().dm_train_merged_layer(self.h, C.byref(vlm.c), C.byref(aw.c), layer, ptr(h_prefix), ptr(lens), B,
+                                          P_cap, ptr(actions), ptr(noise), ptr(t), ptr(mask),
+                                          1 if knowledge_insulation else 0, ptr(loss), C.byref(gc), ptr(ws),
+                                          ws.numel(), stream_handle(stream)))
 
     def denoise_plan(self, aw: DeviceAction, k_cache, v_cache, lens, x, num_steps, ws, stream=None):
         B, P_cap = k_cache.shape[1], k_cache.shape[3]

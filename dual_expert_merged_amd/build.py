@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdm.so")
-SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip", "persist.hip"]
+SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip", "persist.hip", "train.hip"]
 # attention rescales its MFMA accumulators with VALU every key tile: keep them in VGPRs rather
 # than accumulation registers, which would cost a copy out and back per element.  Its softmax
 # takes many float maxima of MFMA results that are never NaN: without -fno-honor-nans every

@@ -288,6 +288,39 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
 
 template <typename P> P *at(void *ws, const Region &r) { return (P *)((char *)ws + r.off); }
 
+// fp32 buffers of one training step (dm_train_merged_layer): M = B*S action rows, Mp = B*P_cap
+// prefix rows, T = P_cap + S joined keys.
+struct TrainLayout {
+  Region x, u, v, dv, h0, n1, r1, qkv, dqkv, K, V, dK, dV, sc, dp, o, dO, h1, n2, r2, gt, up, act, dgt, dup, dact, h2,
+      nf, rf, dnf, dh2, dn2, dh1, dn1, dh0, np, rp, kvp, dkvp, dnp;
+  size_t total = 0;
+  void put(Region &r, size_t floats) {
+    r.off = total;
+    r.bytes = floats * sizeof(float);
+    total += up256(r.bytes);
+  }
+};
+
+TrainLayout train_layout(const dm_config &c, int B, int P_cap) {
+  TrainLayout L;
+  const size_t S = c.chunk, A = c.action_dim, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const size_t Ha = c.act_hidden, Hv = c.vlm_hidden, F = c.act_ffn, QKV = (Hq + 2 * Hkv) * D;
+  const size_t M = (size_t)B * S, Mp = (size_t)B * P_cap, T = P_cap + S;
+  for (Region *r : {&L.x, &L.u, &L.v, &L.dv}) L.put(*r, M * A);
+  for (Region *r : {&L.h0, &L.n1, &L.h1, &L.n2, &L.h2, &L.nf, &L.dnf, &L.dh2, &L.dn2, &L.dh1, &L.dn1, &L.dh0})
+    L.put(*r, M * Ha);
+  for (Region *r : {&L.r1, &L.r2, &L.rf}) L.put(*r, M);
+  for (Region *r : {&L.qkv, &L.dqkv}) L.put(*r, M * QKV);
+  for (Region *r : {&L.K, &L.V, &L.dK, &L.dV}) L.put(*r, (size_t)B * Hkv * T * D);
+  for (Region *r : {&L.sc, &L.dp}) L.put(*r, (size_t)B * Hq * S * T);
+  for (Region *r : {&L.o, &L.dO}) L.put(*r, M * Hq * D);
+  for (Region *r : {&L.gt, &L.up, &L.act, &L.dgt, &L.dup, &L.dact}) L.put(*r, M * F);
+  for (Region *r : {&L.np, &L.dnp}) L.put(*r, Mp * Hv);
+  L.put(L.rp, Mp);
+  for (Region *r : {&L.kvp, &L.dkvp}) L.put(*r, Mp * 2 * Hkv * D);
+  return L;
+}
+
 dm_status check_config(const dm_config *c) {
   REQUIRE(c, DM_ERR_INVALID_ARG, "config is NULL");
   REQUIRE(c->dtype == DM_F32 || c->dtype == DM_BF16, DM_ERR_UNSUPPORTED, "dtype must be DM_F32 or DM_BF16");
@@ -740,7 +773,9 @@ dm_status dm_ctx_create(const dm_config *cfg, int device, dm_ctx **out) {
 void dm_ctx_destroy(dm_ctx *ctx) { delete ctx; }
 
 size_t dm_workspace_bytes(const dm_ctx *ctx, dm_op op, int B, int P_cap) {
-  if (!ctx || B < 1 || P_cap < 1 || (op != DM_OP_PREFILL && op != DM_OP_MERGED_LAYER && op != DM_OP_DENOISE)) return 0;
+  if (!ctx || B < 1 || P_cap < 1) return 0;
+  if (op == DM_OP_TRAIN) return train_layout(ctx->cfg, B, P_cap).total;
+  if (op != DM_OP_PREFILL && op != DM_OP_MERGED_LAYER && op != DM_OP_DENOISE) return 0;
   return make_layout(ctx->cfg, ctx->es, op, B, P_cap).total;
 }
 
@@ -1006,6 +1041,191 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm, const float *
   TRY(check_prefill(ctx, vlm, prefix_embeds, prefix_lens, B, P_cap, k_cache, v_cache, ws, ws_bytes));
   TRY(set_device(ctx));
   enqueue_prefill(ctx, vlm, prefix_embeds, prefix_lens, B, P_cap, k_cache, v_cache, ws, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return DM_OK;
+}
+
+dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_action_weights *aw, int layer,
+                                const float *h_prefix, const int32_t *prefix_lens, int B, int P_cap,
+                                const float *actions, const float *noise, const float *t, const float *mask,
+                                int knowledge_insulation, float *loss, const dm_train_grads *grads, void *ws,
+                                size_t ws_bytes, void *stream) {
+  REQUIRE(ctx, DM_ERR_INVALID_ARG, "ctx is NULL");
+  const dm_config &c = ctx->cfg;
+  REQUIRE(!(c.flags & (DM_FLAG_TIME_MODULATION | DM_FLAG_QK_NORM)), DM_ERR_UNSUPPORTED,
+          "the training step covers the additive-time, plain-QK model (no DM_FLAG_TIME_MODULATION / DM_FLAG_QK_NORM)");
+  REQUIRE(prefix_lens, DM_ERR_INVALID_ARG, "prefix_lens is NULL");
+  REQUIRE(B >= 1 && B <= 4096, DM_ERR_SHAPE, "B must be 1..4096 (got %d)", B);
+  REQUIRE(P_cap >= 1 && P_cap <= 65536, DM_ERR_SHAPE, "P_cap must be 1..65536 (got %d)", P_cap);
+  REQUIRE(layer >= 0 && layer < c.n_layers, DM_ERR_SHAPE, "layer %d outside 0..%d", layer, c.n_layers - 1);
+  TRY(check_expert(vlm, c.vlm_mlp_dtype == DM_FP8_E4M3, "VLM", false));
+  TRY(check_action(ctx, aw));
+  REQUIRE(h_prefix && actions && noise && t && mask && loss && grads, DM_ERR_INVALID_ARG,
+          "h_prefix / actions / noise / t / mask / loss / grads is NULL");
+  const dm_train_grads &G = *grads;
+  const float *need[] = {G.attn_norm, G.w_qkv, G.w_o, G.mlp_norm, G.w_gate, G.w_up, G.w_down,
+                         G.w_in, G.b_in, G.final_norm, G.w_out, G.b_out};
+  for (const float *p : need) REQUIRE(p, DM_ERR_INVALID_ARG, "an action-side gradient pointer is NULL");
+  const bool ki = knowledge_insulation != 0;
+  REQUIRE(ki || (G.vlm_attn_norm && G.vlm_w_qkv), DM_ERR_INVALID_ARG,
+          "without knowledge insulation vlm_attn_norm and vlm_w_qkv gradients are required");
+  REQUIRE(ws, DM_ERR_INVALID_ARG, "workspace is NULL");
+  REQUIRE(((uintptr_t)ws & 255u) == 0, DM_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const TrainLayout L = train_layout(c, B, P_cap);
+  REQUIRE(ws_bytes >= L.total, DM_ERR_WORKSPACE, "workspace too small: %zu bytes, need %zu", ws_bytes, L.total);
+  TRY(set_device(ctx));
+  hipStream_t s = (hipStream_t)stream;
+
+  const int S = c.chunk, A = c.action_dim, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, grp = Hq / Hkv;
+  const int Ha = c.act_hidden, Hv = c.vlm_hidden, F = c.act_ffn, QKV = (Hq + 2 * Hkv) * D, HqD = Hq * D, KV2 = 2 * Hkv * D;
+  const int M = B * S, Mp = B * P_cap, T = P_cap + S, l = layer;
+  const Dt dt = ctx->dt;
+  const size_t es = ctx->es;
+  const float eps = c.rms_eps, isd = 1.0f / sqrtf((float)D);
+  const double base = c.rope_base;
+  const int *lens = prefix_lens;
+  auto F32 = [&](const Region &r) { return at<float>(ws, r); };
+  float *x = F32(L.x), *u = F32(L.u), *v = F32(L.v), *dv = F32(L.dv), *h0 = F32(L.h0), *n1 = F32(L.n1),
+        *r1 = F32(L.r1), *qkv = F32(L.qkv), *dqkv = F32(L.dqkv), *K = F32(L.K), *V = F32(L.V), *dK = F32(L.dK),
+        *dV = F32(L.dV), *sc = F32(L.sc), *dp = F32(L.dp), *o = F32(L.o), *dO = F32(L.dO), *h1 = F32(L.h1),
+        *n2 = F32(L.n2), *r2 = F32(L.r2), *gt = F32(L.gt), *up = F32(L.up), *act = F32(L.act), *dgt = F32(L.dgt),
+        *dup = F32(L.dup), *dact = F32(L.dact), *h2 = F32(L.h2), *nf = F32(L.nf), *rf = F32(L.rf), *dnf = F32(L.dnf),
+        *dh2 = F32(L.dh2), *dn2 = F32(L.dn2), *dh1 = F32(L.dh1), *dn1 = F32(L.dn1), *dh0 = F32(L.dh0),
+        *np_ = F32(L.np), *rp = F32(L.rp), *kvp = F32(L.kvp), *dkvp = F32(L.dkvp), *dnp = F32(L.dnp);
+  const dm_expert_weights &W = aw->body;
+  const char *wq = layer_ptr(W.w_qkv, (size_t)QKV * Ha, l, es), *wo = layer_ptr(W.w_o, (size_t)Ha * HqD, l, es);
+  const char *wg = layer_ptr(W.w_gate, (size_t)F * Ha, l, es), *wu = layer_ptr(W.w_up, (size_t)F * Ha, l, es);
+  const char *wd = layer_ptr(W.w_down, (size_t)Ha * F, l, es);
+  const char *wv_kv = layer_ptr(vlm->w_qkv, (size_t)QKV * Hv, l, es) + (size_t)HqD * Hv * es;  // K/V rows
+  const float *g1 = W.attn_norm + (size_t)l * Ha, *g2 = W.mlp_norm + (size_t)l * Ha, *gv = vlm->attn_norm + (size_t)l * Hv;
+  // C[M][N] = A(m, k) B(n, k) (+ C with beta 1); operands by element strides {so, si, sm, sk}
+  const TOperand ROW_K = {0, 0, 0, 1};
+  auto rows = [&](long ld) { TOperand t = ROW_K; t.sm = ld; return t; };     // X[m][k] row-major, row length ld
+  auto cols = [&](long ld) { return TOperand{0, 0, 1, ld}; };                 // X[k][m] read as (m, k)
+  auto mm = [&](int Mm, int Nn, int Kk, TOperand a, Dt ta, const void *pa, TOperand b, Dt tb, const void *pb,
+                float *C, long ldc, float beta = 0.f) {
+    TGemm g{};
+    g.M = Mm, g.N = Nn, g.K = Kk, g.a = a, g.b = b, g.bdiv = 1, g.C = C, g.ldc = ldc, g.zo_n = 1, g.zi_n = 1;
+    g.alpha = 1.f, g.beta = beta;
+    launch_tgemm(g, ta, pa, tb, pb, s);
+  };
+
+  // ---- forward
+  launch_fm_embed(actions, noise, t, aw->w_in, aw->b_in, B, S, A, Ha, 10000.0f, x, u, h0, s);
+  // prefix: the VLM expert's pre-norm and K/V rows (rows past each prefix are zero), RoPE on K
+  launch_rms_fwd(h_prefix, DT_F32, gv, eps, Mp, Hv, lens, P_cap, np_, rp, s);
+  mm(Mp, KV2, Hv, rows(Hv), DT_F32, np_, rows(Hv), dt, wv_kv, kvp, KV2);
+  launch_rope_rows(kvp, Mp, P_cap, KV2, 0, Hkv, D, base, lens, false, 1.0f, s);
+  // action rows: pre-norm, Q/K/V, RoPE on Q and K at positions P_b + s
+  launch_rms_fwd(h0, DT_F32, g1, eps, M, Ha, nullptr, 1, n1, r1, s);
+  mm(M, QKV, Ha, rows(Ha), DT_F32, n1, rows(Ha), dt, wq, qkv, QKV);
+  launch_rope_rows(qkv, M, S, QKV, 0, Hq + Hkv, D, base, lens, true, 1.0f, s);
+  launch_gather_kv(kvp, qkv, lens, B, P_cap, S, Hq, Hkv, D, K, V, s);
+  // scores[b][h][s][j] = q . k / sqrt(D), softmax over the visible keys, O = P V
+  TGemm at_{};
+  at_.zo_n = B, at_.zi_n = Hq, at_.bdiv = grp, at_.alpha = 1.f;
+  {
+    TGemm g = at_;
+    g.M = S, g.N = T, g.K = D, g.alpha = isd;
+    g.a = {(long)S * QKV, D, QKV, 1};
+    g.b = {(long)Hkv * T * D, (long)T * D, D, 1};
+    g.C = sc, g.ldc = T, g.c_so = (long)Hq * S * T, g.c_si = (long)S * T;
+    launch_tgemm(g, DT_F32, qkv, DT_F32, K, s);
+  }
+  launch_softmax_rows(sc, lens, B, Hq, S, P_cap, s);
+  {
+    TGemm g = at_;
+    g.M = S, g.N = D, g.K = T;
+    g.a = {(long)Hq * S * T, (long)S * T, T, 1};
+    g.b = {(long)Hkv * T * D, (long)T * D, 1, D};
+    g.C = o, g.ldc = HqD, g.c_so = (long)S * HqD, g.c_si = D;
+    launch_tgemm(g, DT_F32, sc, DT_F32, V, s);
+  }
+  launch_copy_bias(h0, nullptr, M, Ha, h1, s);
+  mm(M, Ha, HqD, rows(HqD), DT_F32, o, rows(HqD), dt, wo, h1, Ha, 1.f);
+  launch_rms_fwd(h1, DT_F32, g2, eps, M, Ha, nullptr, 1, n2, r2, s);
+  mm(M, F, Ha, rows(Ha), DT_F32, n2, rows(Ha), dt, wg, gt, F);
+  mm(M, F, Ha, rows(Ha), DT_F32, n2, rows(Ha), dt, wu, up, F);
+  launch_swiglu_fwd(gt, up, (long)M * F, act, s);
+  launch_copy_bias(h1, nullptr, M, Ha, h2, s);
+  mm(M, Ha, F, rows(F), DT_F32, act, rows(F), dt, wd, h2, Ha, 1.f);
+  launch_rms_fwd(h2, DT_F32, aw->final_norm, eps, M, Ha, nullptr, 1, nf, rf, s);
+  launch_copy_bias(nullptr, aw->b_out, M, A, v, s);
+  mm(M, A, Ha, rows(Ha), DT_F32, nf, rows(Ha), DT_F32, aw->w_out, v, A, 1.f);
+  launch_fm_loss(v, u, mask, (long)M * A, loss, dv, s);
+
+  // ---- backward: head, final norm
+  mm(A, Ha, M, cols(A), DT_F32, dv, cols(Ha), DT_F32, nf, G.w_out, Ha);
+  launch_colsum(dv, nullptr, nullptr, M, A, G.b_out, s);
+  mm(M, Ha, A, rows(A), DT_F32, dv, cols(Ha), DT_F32, aw->w_out, dnf, Ha);
+  launch_rms_bwd(h2, DT_F32, aw->final_norm, dnf, rf, nullptr, M, Ha, dh2, s);
+  launch_colsum(dnf, h2, rf, M, Ha, G.final_norm, s);
+  // MLP
+  mm(Ha, F, M, cols(Ha), DT_F32, dh2, cols(F), DT_F32, act, G.w_down, F);
+  mm(M, F, Ha, rows(Ha), DT_F32, dh2, cols(F), dt, wd, dact, F);
+  launch_swiglu_bwd(gt, up, dact, (long)M * F, dgt, dup, s);
+  mm(F, Ha, M, cols(F), DT_F32, dgt, cols(Ha), DT_F32, n2, G.w_gate, Ha);
+  mm(F, Ha, M, cols(F), DT_F32, dup, cols(Ha), DT_F32, n2, G.w_up, Ha);
+  mm(M, Ha, F, rows(F), DT_F32, dgt, cols(Ha), dt, wg, dn2, Ha);
+  mm(M, Ha, F, rows(F), DT_F32, dup, cols(Ha), dt, wu, dn2, Ha, 1.f);
+  launch_rms_bwd(h1, DT_F32, g2, dn2, r2, dh2, M, Ha, dh1, s);
+  launch_colsum(dn2, h1, r2, M, Ha, G.mlp_norm, s);
+  // O-projection
+  mm(Ha, HqD, M, cols(Ha), DT_F32, dh1, cols(HqD), DT_F32, o, G.w_o, HqD);
+  mm(M, HqD, Ha, rows(Ha), DT_F32, dh1, cols(HqD), dt, wo, dO, HqD);
+  // attention: dP = dO V^T, dS = P (dP - rowsum(P dP)) / sqrt(D), dQ = dS K, dK = dS^T Q, dV = P^T dO
+  {
+    TGemm g = at_;
+    g.M = S, g.N = T, g.K = D;
+    g.a = {(long)S * HqD, D, HqD, 1};
+    g.b = {(long)Hkv * T * D, (long)T * D, D, 1};
+    g.C = dp, g.ldc = T, g.c_so = (long)Hq * S * T, g.c_si = (long)S * T;
+    launch_tgemm(g, DT_F32, dO, DT_F32, V, s);
+  }
+  launch_softmax_bwd(sc, dp, (long)B * Hq * S, T, isd, s);
+  {
+    TGemm g = at_;
+    g.M = S, g.N = D, g.K = T;
+    g.a = {(long)Hq * S * T, (long)S * T, T, 1};
+    g.b = {(long)Hkv * T * D, (long)T * D, 1, D};
+    g.C = dqkv, g.ldc = QKV, g.c_so = (long)S * QKV, g.c_si = D;
+    launch_tgemm(g, DT_F32, dp, DT_F32, K, s);
+  }
+  for (int r = 0; r < grp; ++r) {  // the grp query heads of a KV head add into its dK / dV
+    TGemm g{};
+    g.M = T, g.N = D, g.K = S, g.bdiv = 1, g.zo_n = B, g.zi_n = Hkv, g.alpha = 1.f, g.beta = r ? 1.f : 0.f;
+    g.ldc = D, g.c_so = (long)Hkv * T * D, g.c_si = (long)T * D;
+    g.a = {(long)Hq * S * T, (long)grp * S * T, 1, T};
+    g.b = {(long)S * QKV, (long)grp * D, 1, QKV};
+    g.C = dK;
+    launch_tgemm(g, DT_F32, dp + (size_t)r * S * T, DT_F32, qkv + (size_t)r * D, s);
+    g.b = {(long)S * HqD, (long)grp * D, 1, HqD};
+    g.C = dV;
+    launch_tgemm(g, DT_F32, sc + (size_t)r * S * T, DT_F32, dO + (size_t)r * D, s);
+  }
+  launch_scatter_kv(dK, dV, lens, B, P_cap, S, Hq, Hkv, D, dqkv, ki ? nullptr : dkvp, s);
+  launch_rope_rows(dqkv, M, S, QKV, 0, Hq + Hkv, D, base, lens, true, -1.0f, s);
+  // Q/K/V projection and the attention pre-norm
+  mm(QKV, Ha, M, cols(QKV), DT_F32, dqkv, cols(Ha), DT_F32, n1, G.w_qkv, Ha);
+  mm(M, Ha, QKV, rows(QKV), DT_F32, dqkv, cols(Ha), dt, wq, dn1, Ha);
+  launch_rms_bwd(h0, DT_F32, g1, dn1, r1, dh1, M, Ha, dh0, s);
+  launch_colsum(dn1, h0, r1, M, Ha, G.attn_norm, s);
+  // action_in_proj
+  mm(Ha, A, M, cols(Ha), DT_F32, dh0, cols(A), DT_F32, x, G.w_in, A);
+  launch_colsum(dh0, nullptr, nullptr, M, Ha, G.b_in, s);
+  // the VLM side: through the prefix K/V, or nothing with knowledge insulation
+  if (ki) {
+    if (G.vlm_attn_norm) launch_fill(G.vlm_attn_norm, Hv, 0.f, s);
+    if (G.vlm_w_qkv) launch_fill(G.vlm_w_qkv, (long)QKV * Hv, 0.f, s);
+    if (G.h_prefix) launch_fill(G.h_prefix, (long)Mp * Hv, 0.f, s);
+  } else {
+    launch_rope_rows(dkvp, Mp, P_cap, KV2, 0, Hkv, D, base, lens, false, -1.0f, s);
+    launch_fill(G.vlm_w_qkv, (long)HqD * Hv, 0.f, s);  // the query rows do not reach the loss
+    mm(KV2, Hv, Mp, cols(KV2), DT_F32, dkvp, cols(Hv), DT_F32, np_, G.vlm_w_qkv + (size_t)HqD * Hv, Hv);
+    mm(Mp, Hv, KV2, rows(KV2), DT_F32, dkvp, cols(Hv), dt, wv_kv, dnp, Hv);
+    if (G.h_prefix) launch_rms_bwd(h_prefix, DT_F32, gv, dnp, rp, nullptr, Mp, Hv, G.h_prefix, s);
+    launch_colsum(dnp, h_prefix, rp, Mp, Hv, G.vlm_attn_norm, s);
+  }
   HIP_TRY(hipGetLastError());
   return DM_OK;
 }

@@ -143,6 +143,45 @@ void launch_mod_norm(Dt dt, const float *h, void *hg, const float *scale, const 
 void launch_fp8_quantize_rows(const void *src, uint8_t *dst, float *scales, int rows, int cols,
                               hipStream_t s);
 
+// ------------------------------------------------------------- training step (train.hip)
+// Element strides of a GEMM operand X(row, k) = X[zo*so + zi'*si + row*sm + k*sk] (zi' = zi for
+// A, zi / bdiv for B).
+struct TOperand {
+  long so, si, sm, sk;
+};
+// C[m][n] = alpha * sum_k A(m, k) B(n, k) + beta * C[m][n] over a zo_n x zi_n batch, fp32 math on
+// the matrix cores; C = C + zo*c_so + zi*c_si, rows ldc apart.
+struct TGemm {
+  int M, N, K;
+  TOperand a, b;
+  int bdiv;
+  float *C;
+  long ldc, c_so, c_si;
+  int zo_n, zi_n;
+  float alpha, beta;
+};
+void launch_tgemm(const TGemm &g, Dt ta, const void *A, Dt tb, const void *B, hipStream_t s);
+void launch_rms_fwd(const float *x, Dt gt, const void *g, float eps, long rows, int H, const int *lens, int rows_per_b,
+                    float *y, float *rstd, hipStream_t s);
+void launch_rms_bwd(const float *x, Dt gt, const void *g, const float *dy, const float *rstd, const float *add, long rows,
+                    int H, float *out, hipStream_t s);
+void launch_colsum(const float *dy, const float *x, const float *rstd, int M, int N, float *out, hipStream_t s);
+void launch_rope_rows(float *p, long rows, int rows_per_b, int ld, int col0, int heads, int D, double base,
+                      const int *lens, bool after_prefix, float sign, hipStream_t s);
+void launch_gather_kv(const float *kvp, const float *qkv, const int *lens, int B, int P_cap, int S, int Hq, int Hkv,
+                      int D, float *K, float *V, hipStream_t s);
+void launch_scatter_kv(const float *dK, const float *dV, const int *lens, int B, int P_cap, int S, int Hq, int Hkv,
+                       int D, float *dqkv, float *dkvp, hipStream_t s);
+void launch_softmax_rows(float *sc, const int *lens, int B, int Hq, int S, int P_cap, hipStream_t s);
+void launch_softmax_bwd(const float *p, float *dp, long rows, int T, float scale, hipStream_t s);
+void launch_fm_embed(const float *a, const float *eps, const float *t, const float *w_in, const float *b_in, int B, int S,
+                     int A, int H, float time_base, float *x, float *u, float *h0, hipStream_t s);
+void launch_copy_bias(const float *src, const float *bias, long M, int N, float *dst, hipStream_t s);
+void launch_fill(float *p, long n, float v, hipStream_t s);
+void launch_swiglu_fwd(const float *gt, const float *up, long n, float *act, hipStream_t s);
+void launch_swiglu_bwd(const float *gt, const float *up, const float *dact, long n, float *dgt, float *dup, hipStream_t s);
+void launch_fm_loss(const float *v, const float *u, const float *mask, long n, float *loss, float *dv, hipStream_t s);
+
 // Single-launch batch-1 suffix denoise (persist.hip): the DM0-base action expert (hidden 1024,
 // FFN 3072, 16 query / 8 KV heads of dim 128, bf16) at batch 1, S <= 64 action tokens,
 // action dim <= 32 (multiple of 4), P_cap <= 960, at most 28 layers.

@@ -71,7 +71,7 @@ typedef enum {
 
 typedef enum { DM_F32 = 0, DM_BF16 = 1, DM_FP8_E4M3 = 2 } dm_dtype;
 
-typedef enum { DM_OP_PREFILL = 0, DM_OP_MERGED_LAYER = 1, DM_OP_DENOISE = 2 } dm_op;
+typedef enum { DM_OP_PREFILL = 0, DM_OP_MERGED_LAYER = 1, DM_OP_DENOISE = 2, DM_OP_TRAIN = 3 } dm_op;
 
 typedef struct {
   int n_layers;      /* L */
@@ -280,6 +280,41 @@ dm_status dm_engine_buffers(const dm_engine *eng, float **prefix_embeds /* (host
                             int32_t **prefix_lens /* (host) */, float **x /* (host) */);
 void dm_engine_destroy(dm_engine *eng);
 
+/* Gradients written by dm_train_merged_layer, all float32 and overwritten (not accumulated);
+ * shapes are one layer's: the action expert's layer tensors, the action head, and the VLM
+ * expert's layer-l attention-norm gain [Hv] and Q/K/V projection [QKV][Hv] (its query rows are
+ * zero: in one layer they do not reach the loss) plus the prefix hidden [B][P_cap][Hv] (rows
+ * >= P_b zero).  The VLM entries and h_prefix may be NULL with knowledge insulation (then they
+ * are zero-filled when set); h_prefix may always be NULL. */
+typedef struct {
+  float *attn_norm, *w_qkv, *w_o, *mlp_norm, *w_gate, *w_up, *w_down; /* action expert, layer l */
+  float *w_in, *b_in, *final_norm, *w_out, *b_out;                    /* action head */
+  float *vlm_attn_norm, *vlm_w_qkv;                                   /* VLM expert, layer l */
+  float *h_prefix;                                                    /* input gradient of h_prefix */
+} dm_train_grads;
+/* One flow-matching training step on merged layer `layer` (page "DM0.5: High-Performance
+ * Embodied VLA and OpenDM Open Source Introduction", section 5.3: x_t = t eps + (1 - t) a, target
+ * u_t = eps - a, loss = mean squared error between the velocity and u_t over the valid action
+ * dimensions and time slices only; page "DM0 paper definition vs. Dexbotic code", section 1:
+ * knowledge insulation keeps the action expert's gradient out of the VLM, which the public code
+ * does not).  Per sample b with time t[b]: the action tokens h0 = x_t W_in^T + b_in + tau(t[b])
+ * pass layer `layer` of the action expert, attending to its own tokens and to the prefix keys /
+ * values that the VLM expert's layer `layer` makes from h_prefix[b] (rows < P_b; the prefix
+ * queries, O-projection and MLP do not reach the action tokens in one layer and are not
+ * formed), then the final norm and action_out_proj give v.  *loss (device float) =
+ * sum(mask (v - u_t)^2) / sum(mask) over the batch (0 if the mask is empty), and `grads`
+ * receives its gradients; with knowledge_insulation != 0 the prefix K/V are constants.
+ * h_prefix [B][P_cap][Hv], actions / noise / mask [B][S][A] (mask 0 or 1), t [B]: float32.
+ * Arithmetic is float32 (bf16 weights are widened exactly); the model must have neither
+ * DM_FLAG_TIME_MODULATION nor DM_FLAG_QK_NORM (else DM_ERR_UNSUPPORTED).  ws: at least
+ * dm_workspace_bytes(ctx, DM_OP_TRAIN, B, P_cap) bytes. */
+dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm /* (host) */,
+                                const dm_action_weights *aw /* (host) */, int layer,
+                                const float *h_prefix, const int32_t *prefix_lens, int B, int P_cap,
+                                const float *actions, const float *noise, const float *t,
+                                const float *mask, int knowledge_insulation, float *loss,
+                                const dm_train_grads *grads /* (host) */, void *ws, size_t ws_bytes,
+                                void *stream);
 /* FP8 E4M3 (OCP e4m3fn) row quantisation (page section 6.3), used for weights (one row per
  * output channel) and, inside dm_prefill_kv, for activations (one row per token):
  * scales[r] = max_c |src[r][c]| / 448 (1 for an all-zero row) and

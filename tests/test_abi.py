@@ -101,6 +101,20 @@ def test_engine_structs_match_the_header():
     assert [f[0] for f in bd.EngineRequestC._fields_] == names
 
 
+def test_train_null_arguments_rejected_and_grads_struct_matches_the_header():
+    lib = bd.lib()
+    g = bd.TrainGradsC()
+    assert lib.dm_train_merged_layer(None, None, None, 0, None, None, 1, 816, None, None, None, None, 1, None,
+                                     C.byref(g), None, 0, None) == bd.DM_ERR_INVALID_ARG
+    assert lib.dm_workspace_bytes(None, bd.OP_TRAIN, 1, 816) == 0
+    text = open(HEADER).read()
+    body = text[text.index("float *attn_norm, *w_qkv, *w_o"):text.index("} dm_train_grads;")]
+    body = re.sub(r"/\*.*?\*/", "", body)
+    names = re.findall(r"\*(\w+)", body)
+    assert tuple(names) == bd.TRAIN_GRAD_FIELDS
+    assert [f[0] for f in bd.TrainGradsC._fields_] == list(names)
+
+
 def test_dm0_base_config_is_accepted_by_validation():
     # a good config fails only at the device query on a machine without a GPU
     lib = bd.lib()
