@@ -288,11 +288,13 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
 
 template <typename P> P *at(void *ws, const Region &r) { return (P *)((char *)ws + r.off); }
 
+constexpr size_t kTrainSplitFloats = (size_t)4 << 20;
+
 // fp32 buffers of one training step (dm_train_merged_layer): M = B*S action rows, Mp = B*P_cap
 // prefix rows, T = P_cap + S joined keys.
 struct TrainLayout {
   Region x, u, v, dv, h0, n1, r1, qkv, dqkv, K, V, dK, dV, sc, dp, o, dO, h1, n2, r2, gt, up, act, dgt, dup, dact, h2,
-      nf, rf, dnf, dh2, dn2, dh1, dn1, dh0, np, rp, kvp, dkvp, dnp;
+      nf, rf, dnf, dh2, dn2, dh1, dn1, dh0, np, rp, kvp, dkvp, dnp, split, cpart;
   size_t total = 0;
   void put(Region &r, size_t floats) {
     r.off = total;
@@ -318,6 +320,8 @@ TrainLayout train_layout(const dm_config &c, int B, int P_cap) {
   for (Region *r : {&L.np, &L.dnp}) L.put(*r, Mp * Hv);
   L.put(L.rp, Mp);
   for (Region *r : {&L.kvp, &L.dkvp}) L.put(*r, Mp * 2 * Hkv * D);
+  L.put(L.split, kTrainSplitFloats);  // split-K partial sums of the products with few tiles
+  L.put(L.cpart, std::max(colsum_part_floats((int)M, (int)std::max(Ha, A)), colsum_part_floats((int)Mp, (int)Hv)));
   return L;
 }
 
@@ -1091,7 +1095,8 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
         *n2 = F32(L.n2), *r2 = F32(L.r2), *gt = F32(L.gt), *up = F32(L.up), *act = F32(L.act), *dgt = F32(L.dgt),
         *dup = F32(L.dup), *dact = F32(L.dact), *h2 = F32(L.h2), *nf = F32(L.nf), *rf = F32(L.rf), *dnf = F32(L.dnf),
         *dh2 = F32(L.dh2), *dn2 = F32(L.dn2), *dh1 = F32(L.dh1), *dn1 = F32(L.dn1), *dh0 = F32(L.dh0),
-        *np_ = F32(L.np), *rp = F32(L.rp), *kvp = F32(L.kvp), *dkvp = F32(L.dkvp), *dnp = F32(L.dnp);
+        *np_ = F32(L.np), *rp = F32(L.rp), *kvp = F32(L.kvp), *dkvp = F32(L.dkvp), *dnp = F32(L.dnp),
+        *split = F32(L.split), *cpart = F32(L.cpart);
   const dm_expert_weights &W = aw->body;
   const char *wq = layer_ptr(W.w_qkv, (size_t)QKV * Ha, l, es), *wo = layer_ptr(W.w_o, (size_t)Ha * HqD, l, es);
   const char *wg = layer_ptr(W.w_gate, (size_t)F * Ha, l, es), *wu = layer_ptr(W.w_up, (size_t)F * Ha, l, es);
@@ -1106,8 +1111,11 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
                 float *C, long ldc, float beta = 0.f) {
     TGemm g{};
     g.M = Mm, g.N = Nn, g.K = Kk, g.a = a, g.b = b, g.bdiv = 1, g.C = C, g.ldc = ldc, g.zo_n = 1, g.zi_n = 1;
-    g.alpha = 1.f, g.beta = beta;
+    g.alpha = 1.f, g.beta = beta, g.part = split, g.part_floats = kTrainSplitFloats;
     launch_tgemm(g, ta, pa, tb, pb, s);
+  };
+  auto colsum = [&](const float *dy, const float *xx, const float *rr, int Mm, int Nn, float *out) {
+    launch_colsum(dy, xx, rr, Mm, Nn, out, cpart, s);
   };
 
   // ---- forward
@@ -1156,10 +1164,10 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
 
   // ---- backward: head, final norm
   mm(A, Ha, M, cols(A), DT_F32, dv, cols(Ha), DT_F32, nf, G.w_out, Ha);
-  launch_colsum(dv, nullptr, nullptr, M, A, G.b_out, s);
+  colsum(dv, nullptr, nullptr, M, A, G.b_out);
   mm(M, Ha, A, rows(A), DT_F32, dv, cols(Ha), DT_F32, aw->w_out, dnf, Ha);
   launch_rms_bwd(h2, DT_F32, aw->final_norm, dnf, rf, nullptr, M, Ha, dh2, s);
-  launch_colsum(dnf, h2, rf, M, Ha, G.final_norm, s);
+  colsum(dnf, h2, rf, M, Ha, G.final_norm);
   // MLP
   mm(Ha, F, M, cols(Ha), DT_F32, dh2, cols(F), DT_F32, act, G.w_down, F);
   mm(M, F, Ha, rows(Ha), DT_F32, dh2, cols(F), dt, wd, dact, F);
@@ -1169,7 +1177,7 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
   mm(M, Ha, F, rows(F), DT_F32, dgt, cols(Ha), dt, wg, dn2, Ha);
   mm(M, Ha, F, rows(F), DT_F32, dup, cols(Ha), dt, wu, dn2, Ha, 1.f);
   launch_rms_bwd(h1, DT_F32, g2, dn2, r2, dh2, M, Ha, dh1, s);
-  launch_colsum(dn2, h1, r2, M, Ha, G.mlp_norm, s);
+  colsum(dn2, h1, r2, M, Ha, G.mlp_norm);
   // O-projection
   mm(Ha, HqD, M, cols(Ha), DT_F32, dh1, cols(HqD), DT_F32, o, G.w_o, HqD);
   mm(M, HqD, Ha, rows(Ha), DT_F32, dh1, cols(HqD), dt, wo, dO, HqD);
@@ -1209,10 +1217,10 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
   mm(QKV, Ha, M, cols(QKV), DT_F32, dqkv, cols(Ha), DT_F32, n1, G.w_qkv, Ha);
   mm(M, Ha, QKV, rows(QKV), DT_F32, dqkv, cols(Ha), dt, wq, dn1, Ha);
   launch_rms_bwd(h0, DT_F32, g1, dn1, r1, dh1, M, Ha, dh0, s);
-  launch_colsum(dn1, h0, r1, M, Ha, G.attn_norm, s);
+  colsum(dn1, h0, r1, M, Ha, G.attn_norm);
   // action_in_proj
   mm(Ha, A, M, cols(Ha), DT_F32, dh0, cols(A), DT_F32, x, G.w_in, A);
-  launch_colsum(dh0, nullptr, nullptr, M, Ha, G.b_in, s);
+  colsum(dh0, nullptr, nullptr, M, Ha, G.b_in);
   // the VLM side: through the prefix K/V, or nothing with knowledge insulation
   if (ki) {
     if (G.vlm_attn_norm) launch_fill(G.vlm_attn_norm, Hv, 0.f, s);
@@ -1224,7 +1232,7 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
     mm(KV2, Hv, Mp, cols(KV2), DT_F32, dkvp, cols(Hv), DT_F32, np_, G.vlm_w_qkv + (size_t)HqD * Hv, Hv);
     mm(Mp, Hv, KV2, rows(KV2), DT_F32, dkvp, cols(Hv), dt, wv_kv, dnp, Hv);
     if (G.h_prefix) launch_rms_bwd(h_prefix, DT_F32, gv, dnp, rp, nullptr, Mp, Hv, G.h_prefix, s);
-    launch_colsum(dnp, h_prefix, rp, Mp, Hv, G.vlm_attn_norm, s);
+    colsum(dnp, h_prefix, rp, Mp, Hv, G.vlm_attn_norm);
   }
   HIP_TRY(hipGetLastError());
   return DM_OK;

@@ -159,13 +159,19 @@ struct TGemm {
   long ldc, c_so, c_si;
   int zo_n, zi_n;
   float alpha, beta;
+  float *part;         // optional split-K scratch (unbatched products only) of part_floats floats
+  size_t part_floats;
+  int splits, k_per_split;  // set by launch_tgemm
 };
 void launch_tgemm(const TGemm &g, Dt ta, const void *A, Dt tb, const void *B, hipStream_t s);
 void launch_rms_fwd(const float *x, Dt gt, const void *g, float eps, long rows, int H, const int *lens, int rows_per_b,
                     float *y, float *rstd, hipStream_t s);
 void launch_rms_bwd(const float *x, Dt gt, const void *g, const float *dy, const float *rstd, const float *add, long rows,
                     int H, float *out, hipStream_t s);
-void launch_colsum(const float *dy, const float *x, const float *rstd, int M, int N, float *out, hipStream_t s);
+// part: colsum_part_floats(M, N) floats of scratch
+void launch_colsum(const float *dy, const float *x, const float *rstd, int M, int N, float *out, float *part,
+                   hipStream_t s);
+size_t colsum_part_floats(int M, int N);
 void launch_rope_rows(float *p, long rows, int rows_per_b, int ld, int col0, int heads, int D, double base,
                       const int *lens, bool after_prefix, float sign, hipStream_t s);
 void launch_gather_kv(const float *kvp, const float *qkv, const int *lens, int B, int P_cap, int S, int Hq, int Hkv,

@@ -18,69 +18,154 @@ template <typename T> __device__ __forceinline__ float ld(const T *p, long i) { 
 // ------------------------------------------------------------------------------------- GEMM
 // C[m][n] = alpha * sum_k A(m, k) B(n, k) + beta * C[m][n] for a 2-level batch z = (zo, zi):
 // A(m, k) = A[zo*a.so + zi*a.si + m*a.sm + k*a.sk], B(n, k) = B[zo*b.so + (zi / bdiv)*b.si +
-// n*b.sm + k*b.sk], C[m][n] = C[zo*c.so + zi*c.si + m*ldc + n].  64 x 64 tiles, four waves of
-// 32 x 32 (2 x 2 MFMA 16x16x4 tiles), k-steps of 16 staged in LDS (k-major, padded rows);
-// out-of-range elements load as 0, so any M, N, K works.
-constexpr int GT = 64, GK = 16, GLD = GT + 4;
+// n*b.sm + k*b.sk], C[m][n] = C[zo*c.so + zi*c.si + m*ldc + n].  BM x BN tiles (64 or 128
+// each), four waves of BM/2 x BN/2 (MFMA 16x16x4 fp32 tiles), k-steps of 16 in two LDS buffers
+// (k-major, padded rows): the next k-step's operands are loaded into registers while the
+// current one multiplies, then stored into the other buffer, one barrier per k-step.  Each
+// thread loads runs of 4 elements along the operand's unit-stride axis (one 16- or 8-byte load
+// when the run is in range and aligned, else element by element with zero fill), so any M, N,
+// K works.
+constexpr int GK = 16;
 
-template <typename TA, typename TB_>
+template <typename T> struct Run4 {
+  float v[4];
+};
+// Loads elements (r0 + e) along `fast` (e = 0..3) of operand X at (row, k) coordinates, with
+// zero outside [0, R) x [0, K); `kfast` says the run goes along k (else along the rows).
+template <typename T>
+__device__ __forceinline__ Run4<T> load_run(const T *__restrict__ x, long sm, long sk, int row, int k, bool kfast,
+                                            int R, int K) {
+  Run4<T> o;
+  const long base = (long)row * sm + (long)k * sk;
+  const bool full = kfast ? (row < R && k + 3 < K) : (k < K && row + 3 < R);
+  const T *p = x + base;
+  constexpr int VB = 4 * sizeof(T);
+  if (full && ((uintptr_t)p & (VB - 1)) == 0) {
+    if constexpr (sizeof(T) == 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+      o.v[0] = v[0], o.v[1] = v[1], o.v[2] = v[2], o.v[3] = v[3];
+    } else {
+      const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+      o.v[0] = to_f32(v[0]), o.v[1] = to_f32(v[1]), o.v[2] = to_f32(v[2]), o.v[3] = to_f32(v[3]);
+    }
+    return o;
+  }
+  const long step = kfast ? sk : sm;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int rr = kfast ? row : row + e, kk = kfast ? k + e : k;
+    o.v[e] = (rr < R && kk < K) ? to_f32(x[base + e * step]) : 0.f;
+  }
+  return o;
+}
+
+template <int BM, int BN, typename TA, typename TB_>
 __global__ __launch_bounds__(256) void tgemm_kernel(TGemm g, const TA *__restrict__ A, const TB_ *__restrict__ B) {
-  __shared__ float As[GK][GLD], Bs[GK][GLD];
+  constexpr int NA = BM * GK / 1024, NB = BN * GK / 1024;  // 4-element runs per thread per k-step
+  constexpr int TM = BM / 32, TN = BN / 32;                // 16x16 tiles per wave
+  __shared__ float As[2][GK][BM + 4], Bs[2][GK][BN + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, c16 = lane & 15, gq = lane >> 4;
-  const int n0 = blockIdx.x * GT, m0 = blockIdx.y * GT;
-  const int zo = blockIdx.z / g.zi_n, zi = blockIdx.z - zo * g.zi_n;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  // blockIdx.z = batch index * splits + split; a split takes its own k range and writes raw sums
+  // to its slice of g.part (tgemm_reduce_kernel finishes)
+  const int split = blockIdx.z % g.splits, zb = blockIdx.z / g.splits;
+  const int zo = zb / g.zi_n, zi = zb - zo * g.zi_n;
   const TA *a = A + zo * g.a.so + zi * g.a.si;
   const TB_ *b = B + zo * g.b.so + (zi / g.bdiv) * g.b.si;
-  float *c = g.C + zo * g.c_so + zi * g.c_si;
-  f32x4 acc[2][2];
+  float *c = g.splits > 1 ? g.part + (long)split * g.M * g.N : g.C + zo * g.c_so + zi * g.c_si;
+  const long ldc = g.splits > 1 ? g.N : g.ldc;
+  const float alpha = g.splits > 1 ? 1.f : g.alpha, beta = g.splits > 1 ? 0.f : g.beta;
+  const int kb = split * g.k_per_split, ke = min(g.K, kb + g.k_per_split);  // multiple of GK apart
+  const bool a_kf = g.a.sk == 1, b_kf = g.b.sk == 1;
+  // run q of this thread covers (row, k..k+3) when k-fast, else (row..row+3, k)
+  auto coord = [&](int q, bool kf, int rows, int &r, int &k) {
+    const int id = q * 256 + tid;
+    if (kf) r = id / (GK / 4), k = (id % (GK / 4)) * 4;
+    else k = id / (rows / 4), r = (id % (rows / 4)) * 4;
+  };
+  Run4<TA> ra[NA];
+  Run4<TB_> rb[NB];
+  auto load = [&](int k0) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // 1024 elements per operand tile: 4 per thread, the fast index along the operand's unit stride
-  const bool a_kfast = g.a.sk == 1, b_kfast = g.b.sk == 1;
-  for (int k0 = 0; k0 < g.K; k0 += GK) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int id = tid * 4 + e;
+    for (int q = 0; q < NA; ++q) {
       int r, k;
-      if (a_kfast) r = id >> 4, k = id & 15;
-      else k = id >> 6, r = id & 63;
-      const int m = m0 + r, kk = k0 + k;
-      As[k][r] = (m < g.M && kk < g.K) ? ld(a, (long)m * g.a.sm + (long)kk * g.a.sk) : 0.f;
-      if (b_kfast) r = id >> 4, k = id & 15;
-      else k = id >> 6, r = id & 63;
-      const int n = n0 + r, kb = k0 + k;
-      Bs[k][r] = (n < g.N && kb < g.K) ? ld(b, (long)n * g.b.sm + (long)kb * g.b.sk) : 0.f;
+      coord(q, a_kf, BM, r, k);
+      ra[q] = load_run(a, g.a.sm, g.a.sk, m0 + r, k0 + k, a_kf, g.M, ke);
     }
-    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      int r, k;
+      coord(q, b_kf, BN, r, k);
+      rb[q] = load_run(b, g.b.sm, g.b.sk, n0 + r, k0 + k, b_kf, g.N, ke);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      int r, k;
+      coord(q, a_kf, BM, r, k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[buf][a_kf ? k + e : k][a_kf ? r : r + e] = ra[q].v[e];
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      int r, k;
+      coord(q, b_kf, BN, r, k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Bs[buf][b_kf ? k + e : k][b_kf ? r : r + e] = rb[q].v[e];
+    }
+  };
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = ke > kb ? (ke - kb + GK - 1) / GK : 0;
+  load(kb);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load(kb + (kt + 1) * GK);  // in flight during this k-step's MFMAs
 #pragma unroll
     for (int kc = 0; kc < GK / 4; ++kc) {
-      float fa[2], fb[2];
+      float fa[TM], fb[TN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = As[kc * 4 + gq][wm * 32 + i * 16 + c16];
+      for (int i = 0; i < TM; ++i) fa[i] = As[cur][kc * 4 + gq][wm * (BM / 2) + i * 16 + c16];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = Bs[kc * 4 + gq][wn * 32 + j * 16 + c16];
+      for (int j = 0; j < TN; ++j) fb[j] = Bs[cur][kc * 4 + gq][wn * (BN / 2) + j * 16 + c16];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
+    if (kt + 1 < nk) store(cur ^ 1);  // the other buffer was last read before the previous barrier
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 32 + i * 16 + 4 * gq + r, n = n0 + wn * 32 + j * 16 + c16;
+        const int m = m0 + wm * (BM / 2) + i * 16 + 4 * gq + r, n = n0 + wn * (BN / 2) + j * 16 + c16;
         if (m < g.M && n < g.N) {
-          float *p = c + (long)m * g.ldc + n;
-          *p = g.alpha * acc[i][j][r] + (g.beta != 0.f ? g.beta * *p : 0.f);
+          float *p = c + (long)m * ldc + n;
+          *p = alpha * acc[i][j][r] + (beta != 0.f ? beta * *p : 0.f);
         }
       }
+}
+
+// C[m][n] = alpha * sum over splits (in order) of part[s][m][n] + beta * C[m][n] (one batch entry)
+__global__ __launch_bounds__(256) void tgemm_reduce_kernel(TGemm g) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)g.M * g.N) return;
+  const int m = (int)(idx / g.N), n = (int)(idx - (long)m * g.N);
+  float acc = 0.f;
+  for (int sp = 0; sp < g.splits; ++sp) acc += g.part[(long)sp * g.M * g.N + idx];
+  float *p = g.C + (long)m * g.ldc + n;
+  *p = g.alpha * acc + (g.beta != 0.f ? g.beta * *p : 0.f);
 }
 
 // ------------------------------------------------------------------------- row kernels
@@ -140,19 +225,30 @@ __global__ __launch_bounds__(TB) void rms_bwd_kernel(const float *__restrict__ x
   }
 }
 
-// out[n] = sum over rows m of dy[m][n] (* x[m][n] * r[m] when x is set, skipping rows with
-// r = 0), rows in order
-__global__ __launch_bounds__(TB) void colsum_kernel(const float *__restrict__ dy, const float *__restrict__ x,
-                                                    const float *__restrict__ rstd, int M, int N,
-                                                    float *__restrict__ out) {
+// Column sums in two passes: partial[c][n] = sum over rows m in chunk c (CS rows) of dy[m][n]
+// (* x[m][n] * r[m] when x is set, skipping rows with r = 0), then out[n] = sum over chunks in
+// order; deterministic.
+constexpr int CS = 64;
+__global__ __launch_bounds__(TB) void colsum_part_kernel(const float *__restrict__ dy, const float *__restrict__ x,
+                                                         const float *__restrict__ rstd, int M, int N,
+                                                         float *__restrict__ part) {
   const int n = blockIdx.x * TB + threadIdx.x;
   if (n >= N) return;
+  const int m0 = blockIdx.y * CS, m1 = min(M, m0 + CS);
   float s = 0.f;
-  for (int m = 0; m < M; ++m) {
+  for (int m = m0; m < m1; ++m) {
     const long k = (long)m * N + n;
     if (!x) s += dy[k];
     else if (rstd[m] != 0.f) s += dy[k] * x[k] * rstd[m];
   }
+  part[(long)blockIdx.y * N + n] = s;
+}
+__global__ __launch_bounds__(TB) void colsum_final_kernel(const float *__restrict__ part, int chunks, int N,
+                                                          float *__restrict__ out) {
+  const int n = blockIdx.x * TB + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int c = 0; c < chunks; ++c) s += part[(long)c * N + n];
   out[n] = s;
 }
 
@@ -366,10 +462,36 @@ unsigned blocks(long n) { return (unsigned)((n + TB - 1) / TB); }
 
 // ------------------------------------------------------------------------------- launchers
 
+// Tile shape: the largest of 128 x 128, 128 x 64, 64 x 128 whose grid still gives about one
+// workgroup per CU (>= 200), else 64 x 64.  An unbatched product that still fills fewer than
+// half the CUs splits K (at least 128 per split) until about 256 workgroups, when g.part holds
+// the partial sums (splits x M x N floats, g.part_floats); the reduce runs in split order.
+// Measured on the one-layer DM0-base step (1.15 ms): sizing for two workgroups per CU instead
+// (>= 512 workgroups, splits up to 512) 1.41 ms, k-steps of 32 instead of 16 1.47 ms.
 template <typename TA, typename TB_>
-static void tgemm_t(const TGemm &g, const void *A, const void *B, hipStream_t s) {
-  dim3 grid((g.N + GT - 1) / GT, (g.M + GT - 1) / GT, g.zo_n * g.zi_n);
-  hipLaunchKernelGGL((tgemm_kernel<TA, TB_>), grid, dim3(256), 0, s, g, (const TA *)A, (const TB_ *)B);
+static void tgemm_t(TGemm g, const void *A, const void *B, hipStream_t s) {
+  const long z = (long)g.zo_n * g.zi_n;
+  auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * (long)((g.N + bn - 1) / bn); };
+  int bm = 64, bn = 64;
+  if (g.M > 64 && g.N > 64 && z * tiles(128, 128) >= 200) bm = 128, bn = 128;
+  else if (g.M > 64 && z * tiles(128, 64) >= 200) bm = 128;
+  else if (g.N > 64 && z * tiles(64, 128) >= 200) bn = 128;
+  const long t = z * tiles(bm, bn);
+  int splits = 1;
+  if (z == 1 && g.part && t < 128)
+    while (t * splits * 2 <= 256 && g.K / (splits * 2) >= 128 &&
+           (size_t)(splits * 2) * g.M * g.N <= g.part_floats)
+      splits *= 2;
+  g.splits = splits;
+  g.k_per_split = (((g.K + splits - 1) / splits) + GK - 1) / GK * GK;
+  dim3 grid((g.N + bn - 1) / bn, (g.M + bm - 1) / bm, (unsigned)(z * splits));
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, g, (const TA *)A, (const TB_ *)B); };
+  if (bm == 128 && bn == 128) go(tgemm_kernel<128, 128, TA, TB_>);
+  else if (bm == 128) go(tgemm_kernel<128, 64, TA, TB_>);
+  else if (bn == 128) go(tgemm_kernel<64, 128, TA, TB_>);
+  else go(tgemm_kernel<64, 64, TA, TB_>);
+  if (splits > 1)
+    hipLaunchKernelGGL(tgemm_reduce_kernel, dim3(blocks((long)g.M * g.N)), dim3(256), 0, s, g);
 }
 void launch_tgemm(const TGemm &g, Dt ta, const void *A, Dt tb, const void *B, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.zo_n <= 0 || g.zi_n <= 0) return;
@@ -394,9 +516,13 @@ void launch_rms_bwd(const float *x, Dt gt, const void *g, const float *dy, const
   else
     hipLaunchKernelGGL(rms_bwd_kernel<float>, dim3(rows), dim3(TB), 0, s, x, (const float *)g, dy, rstd, add, H, out);
 }
-void launch_colsum(const float *dy, const float *x, const float *rstd, int M, int N, float *out, hipStream_t s) {
-  hipLaunchKernelGGL(colsum_kernel, dim3(blocks(N)), dim3(TB), 0, s, dy, x, rstd, M, N, out);
+void launch_colsum(const float *dy, const float *x, const float *rstd, int M, int N, float *out, float *part,
+                   hipStream_t s) {
+  const int chunks = (M + CS - 1) / CS;
+  hipLaunchKernelGGL(colsum_part_kernel, dim3(blocks(N), chunks), dim3(TB), 0, s, dy, x, rstd, M, N, part);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3(blocks(N)), dim3(TB), 0, s, part, chunks, N, out);
 }
+size_t colsum_part_floats(int M, int N) { return (size_t)((M + CS - 1) / CS) * N; }
 void launch_rope_rows(float *p, long rows, int rows_per_b, int ld, int col0, int heads, int D, double base,
                       const int *lens, bool after_prefix, float sign, hipStream_t s) {
   hipLaunchKernelGGL(rope_kernel, dim3(blocks(rows * heads * (D / 2))), dim3(TB), 0, s, p, rows, rows_per_b, ld, col0,
