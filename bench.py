@@ -19,6 +19,7 @@ rocprofv3 FETCH_SIZE + WRITE_SIZE counters, scaled against a plain copy
 Sub-objects of the same line: "batch32" (the batch-32 ragged workload, MFMA-bound: chunks/s,
 latency, the chunk's MFMA fraction from live events, each GEMM kernel's MFMA fraction from the
 committed kernel statistics), "time_modulated" (the DM0.5-style time-modulated expert, B=4),
+"qk_norm" (the per-head QK-norm switch, B=2),
 "prefill_ms" (the B=8, 816-token prefix encoding with the bf16 and with the FP8 MLP) and
 "serving" (the fixed-contract engine on prefill + denoise at B=8: model-core and request
 latency percentiles) and "training" (one flow-matching training step on one merged layer:
@@ -659,6 +660,20 @@ def tmod_summary(steps=20, warmup=3):
                          "algorithmic_bytes_per_launch": alg["bytes"], "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4)}}
 
 
+def qknorm_summary(steps=20, warmup=3):
+    """The per-head QK-norm switch in both experts (workload 9: DM0-base, B=2, 816-token prefix,
+    10 steps; the kernel sequence): chunks/s, latency and the chunk's HBM / MFMA fractions."""
+    wl, lens, _, res = run_denoise(9, steps, warmup)
+    alg = algorithmic(wl, lens)
+    chunk_s = float(np.mean(res["lat"])) * 1e-3
+    gbs, tfs = alg["bytes"] / chunk_s / 1e9, alg["flops"] / chunk_s / 1e12
+    return {"workload": wl.name, "value": round(res["value"], 2), "unit": "chunks/s", "steps": steps,
+            "latency_ms": latency(res["lat"]),
+            "roofline": {"bound": "hbm", "kernel": "all kernels of one chunk (graph replay)", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": alg["bytes"], "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -745,6 +760,8 @@ def main():
             out["batch32"] = b32_summary()
         log("[bench] timing the time-modulated expert")
         out["time_modulated"] = tmod_summary()
+        log("[bench] timing the QK-norm switch")
+        out["qk_norm"] = qknorm_summary()
         from dual_expert_merged_amd import inputs
         from dual_expert_merged_amd.configs import workload
         log("[bench] generating the VLM expert of the prefill workload")

@@ -7,8 +7,8 @@ The step computes in float32 throughout, so the bounds are float32 ones:
   - tiny fp32 model, B = 3 with prefix lengths 0, 17 and 24 (P_cap 24), layer 1, with and
     without knowledge insulation: the loss within 1e-5 relative, every gradient tensor within
     1e-4 of the oracle relative to that tensor's largest magnitude;
-  - DM0-base shapes (one layer, bf16 weights widened exactly), B = 2 with prefixes 816 and 431:
-    the loss and every gradient within 1e-4 of the oracle relative to the tensor's largest
+  - DM0-base shapes (one layer, bf16 weights widened exactly), B = 2 with prefixes 816 and 431,
+    with and without knowledge insulation: the loss and every gradient within 1e-4 of the oracle relative to the tensor's largest
     magnitude, the bound stated for float32 paths (measured: at most 1.6e-6, from float32 sums
     over up to 6528 rows and softmax rows of up to 866 keys);
   - an empty mask gives loss 0 and all-zero gradients; argument checks.
@@ -83,15 +83,17 @@ def test_train_step_tiny_fp32(ki):
 
 
 @pytest.mark.timeout(600)
-def test_train_step_dm0_base_one_layer_bf16():
+@pytest.mark.parametrize("ki", [False, True])
+def test_train_step_dm0_base_one_layer_bf16(ki):
     wl = dataclasses.replace(workload(2), batch=2)
-    print("case: training step, DM0-base one layer (bf16 weights), B=2 prefixes 816 / 431, no insulation", flush=True)
+    print(f"case: training step, DM0-base one layer (bf16 weights), B=2 prefixes 816 / 431, knowledge insulation {ki}",
+          flush=True)
     vlm = inputs.make_vlm_weights(wl)
     aw = inputs.make_action_weights(wl)
     tb = inputs.make_train_batch(wl)
     tb.lens[:] = [816, 431]
     tb.h_pre[1, 431:] = 0.0
-    _compare(wl, vlm, aw, tb, 0, False, 1e-4, 1e-4)
+    _compare(wl, vlm, aw, tb, 0, ki, 1e-4, 1e-4)
 
 
 def test_train_step_empty_mask_and_argument_checks():
