@@ -19,7 +19,8 @@ rocprofv3 FETCH_SIZE + WRITE_SIZE counters, scaled against a plain copy
 Sub-objects of the same line: "batch32" (the batch-32 ragged workload, MFMA-bound: chunks/s,
 latency, the chunk's MFMA fraction from live events, each GEMM kernel's MFMA fraction from the
 committed kernel statistics), "time_modulated" (the DM0.5-style time-modulated expert, B=4),
-"qk_norm" (the per-head QK-norm switch, B=2),
+"qk_norm" (the per-head QK-norm switch, B=2), "merged_layer" (one joint layer of both experts at
+B=1, 816 + 50 tokens: us per call and its MFMA fraction),
 "prefill_ms" (the B=8, 816-token prefix encoding with the bf16 and with the FP8 MLP) and
 "serving" (the fixed-contract engine on prefill + denoise at B=8: model-core and request
 latency percentiles) and "training" (one flow-matching training step on one merged layer:
@@ -762,6 +763,8 @@ def main():
         out["time_modulated"] = tmod_summary()
         log("[bench] timing the QK-norm switch")
         out["qk_norm"] = qknorm_summary()
+        log("[bench] timing one merged layer (both experts, B=1)")
+        out["merged_layer"] = merged_layer_times()
         from dual_expert_merged_amd import inputs
         from dual_expert_merged_amd.configs import workload
         log("[bench] generating the VLM expert of the prefill workload")
