@@ -10,7 +10,9 @@ new observation in, replay once; section 9.1: model-core against request latency
 - DM0-base bf16, B=2, prefix 816 / 523: two successive requests with different inputs, each
   bitwise equal to dm_prefill_kv followed by dm_suffix_denoise on the same inputs (the calls the
   other GPU tests hold to the oracle), and model-core replays between them changing nothing
-  the next request sees.
+  the next request sees;
+- the FP8-MLP prefill (DM0-base, B = 2) and the time-modulated expert (tiny, B = 3): two
+  requests each, bitwise equal to the separate calls.
 """
 import dataclasses
 
@@ -21,7 +23,7 @@ import torch
 import oracle as O
 from dual_expert_merged_amd import binding as bd
 from dual_expert_merged_amd import inputs
-from dual_expert_merged_amd.configs import workload
+from dual_expert_merged_amd.configs import FP8, workload
 from tests.gpu_harness import Gpu, rel_inf
 
 pytestmark = pytest.mark.gpu
@@ -131,4 +133,40 @@ def test_engine_dm0_base_bf16_equals_separate_calls_over_two_requests():
         for _ in range(2):  # model-core replays over whatever the buffers hold
             eng.replay()
         torch.cuda.synchronize()
+    eng.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("variant", ["fp8_mlp", "time_modulation"])
+def test_engine_equals_separate_calls_for_model_variants(variant):
+    """The engine captures whatever the context's model is: the FP8-MLP prefill (DM0-base, B=2,
+    prefixes 816 / 300) and the time-modulated action expert (tiny fp32, B=3 ragged); two
+    requests each, bitwise equal to dm_prefill_kv followed by dm_suffix_denoise."""
+    if variant == "fp8_mlp":
+        wl = dataclasses.replace(workload(5), batch=2,
+                                 shape=dataclasses.replace(workload(5).shape, vlm_mlp_dtype=FP8))
+        lens_a = np.array([816, 300], dtype=np.int32)
+    else:
+        wl = dataclasses.replace(workload(6), kind="prefill_denoise")
+        lens_a = inputs.make_prefix_lens(wl)
+    print(f"case: engine, {variant}, B={wl.batch} P_cap={wl.prefix_len} lens {lens_a.tolist()}", flush=True)
+    vlm = inputs.make_vlm_weights(wl)
+    aw = inputs.make_action_weights(wl)
+    emb_a = inputs.make_prefix_embeds(wl)
+    x_a = inputs.make_noise(wl)
+    emb_b = np.ascontiguousarray(emb_a[::-1])
+    lens_b = np.ascontiguousarray(lens_a[::-1])
+    x_b = np.random.default_rng(9).standard_normal(x_a.shape).astype(np.float32)
+    gpu = Gpu(wl, vlm, aw)
+    eng = _engine(gpu, wl)
+    for name, emb, lens, x in (("A", emb_a, lens_a, x_a), ("B", emb_b, lens_b, x_b)):
+        got = np.zeros_like(x)
+        eng.run(emb, lens, x, got)
+        k, v = gpu.prefill(emb, lens)
+        ref = gpu.denoise(k, v, lens, x, wl.steps)
+        del k, v
+        torch.cuda.empty_cache()
+        print(f"request {name}: max |engine - separate calls| = {float(np.abs(got - ref).max()):.3e}", flush=True)
+        np.testing.assert_array_equal(got, ref)
+        assert np.isfinite(got).all()
     eng.close()
