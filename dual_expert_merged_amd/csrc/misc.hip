@@ -1,6 +1,7 @@
 // Small kernels of the path: RoPE table, entry into the first sublayer (h*gain and sums of
 // squares), action_in_proj + time embedding, final norm + action_out_proj + Euler update, FP8
-// E4M3 row quantisation.
+// E4M3 row quantisation, and the time-modulated expert's pieces (the chunk's sinusoid table,
+// a rows-times-matrix GEMV for its time MLP and modulators, the modulated RMSNorm).
 #include <algorithm>
 
 #include "common.h"
