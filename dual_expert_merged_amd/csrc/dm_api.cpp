@@ -288,7 +288,7 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
 
 template <typename P> P *at(void *ws, const Region &r) { return (P *)((char *)ws + r.off); }
 
-constexpr size_t kTrainSplitFloats = (size_t)4 << 20;
+constexpr size_t kTrainSplitFloats = (size_t)24 << 20;
 
 // fp32 buffers of one training step (dm_train_merged_layer): M = B*S action rows, Mp = B*P_cap
 // prefix rows, T = P_cap + S joined keys.
@@ -1131,7 +1131,7 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
   launch_gather_kv(kvp, qkv, lens, B, P_cap, S, Hq, Hkv, D, K, V, s);
   // scores[b][h][s][j] = q . k / sqrt(D), softmax over the visible keys, O = P V
   TGemm at_{};
-  at_.zo_n = B, at_.zi_n = Hq, at_.bdiv = grp, at_.alpha = 1.f;
+  at_.zo_n = B, at_.zi_n = Hq, at_.bdiv = grp, at_.alpha = 1.f, at_.part = split, at_.part_floats = kTrainSplitFloats;
   {
     TGemm g = at_;
     g.M = S, g.N = T, g.K = D, g.alpha = isd;
@@ -1202,6 +1202,7 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
   for (int r = 0; r < grp; ++r) {  // the grp query heads of a KV head add into its dK / dV
     TGemm g{};
     g.M = T, g.N = D, g.K = S, g.bdiv = 1, g.zo_n = B, g.zi_n = Hkv, g.alpha = 1.f, g.beta = r ? 1.f : 0.f;
+    g.part = split, g.part_floats = kTrainSplitFloats;
     g.ldc = D, g.c_so = (long)Hkv * T * D, g.c_si = (long)T * D;
     g.a = {(long)Hq * S * T, (long)grp * S * T, 1, T};
     g.b = {(long)S * QKV, (long)grp * D, 1, QKV};

@@ -68,12 +68,12 @@ __global__ __launch_bounds__(256) void tgemm_kernel(TGemm g, const TA *__restric
   const int wm = wave >> 1, wn = wave & 1, c16 = lane & 15, gq = lane >> 4;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   // blockIdx.z = batch index * splits + split; a split takes its own k range and writes raw sums
-  // to its slice of g.part (tgemm_reduce_kernel finishes)
+  // to its slice [batch index][split] of g.part (tgemm_reduce_kernel finishes)
   const int split = blockIdx.z % g.splits, zb = blockIdx.z / g.splits;
   const int zo = zb / g.zi_n, zi = zb - zo * g.zi_n;
   const TA *a = A + zo * g.a.so + zi * g.a.si;
   const TB_ *b = B + zo * g.b.so + (zi / g.bdiv) * g.b.si;
-  float *c = g.splits > 1 ? g.part + (long)split * g.M * g.N : g.C + zo * g.c_so + zi * g.c_si;
+  float *c = g.splits > 1 ? g.part + ((long)zb * g.splits + split) * g.M * g.N : g.C + zo * g.c_so + zi * g.c_si;
   const long ldc = g.splits > 1 ? g.N : g.ldc;
   const float alpha = g.splits > 1 ? 1.f : g.alpha, beta = g.splits > 1 ? 0.f : g.beta;
   const int kb = split * g.k_per_split, ke = min(g.K, kb + g.k_per_split);  // multiple of GK apart
@@ -157,14 +157,19 @@ __global__ __launch_bounds__(256) void tgemm_kernel(TGemm g, const TA *__restric
       }
 }
 
-// C[m][n] = alpha * sum over splits (in order) of part[s][m][n] + beta * C[m][n] (one batch entry)
+// C[m][n] = alpha * sum over splits (in order) of part[z][s][m][n] + beta * C[m][n], every batch
+// entry z = (zo, zi)
 __global__ __launch_bounds__(256) void tgemm_reduce_kernel(TGemm g) {
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long)g.M * g.N) return;
-  const int m = (int)(idx / g.N), n = (int)(idx - (long)m * g.N);
+  const long mn = (long)g.M * g.N, idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= mn * g.zo_n * g.zi_n) return;
+  const long zb = idx / mn, r = idx - zb * mn;
+  const int zo = (int)(zb / g.zi_n), zi = (int)(zb - (long)zo * g.zi_n);
+  const int m = (int)(r / g.N), n = (int)(r - (long)m * g.N);
+  const float *part = g.part + zb * g.splits * mn + r;
   float acc = 0.f;
-  for (int sp = 0; sp < g.splits; ++sp) acc += g.part[(long)sp * g.M * g.N + idx];
-  float *p = g.C + (long)m * g.ldc + n;
+#pragma unroll 8
+  for (int sp = 0; sp < g.splits; ++sp) acc += part[(long)sp * mn];
+  float *p = g.C + zo * g.c_so + zi * g.c_si + (long)m * g.ldc + n;
   *p = g.alpha * acc + (g.beta != 0.f ? g.beta * *p : 0.f);
 }
 
@@ -227,20 +232,32 @@ __global__ __launch_bounds__(TB) void rms_bwd_kernel(const float *__restrict__ x
 
 // Column sums in two passes: partial[c][n] = sum over rows m in chunk c (CS rows) of dy[m][n]
 // (* x[m][n] * r[m] when x is set, skipping rows with r = 0), then out[n] = sum over chunks in
-// order; deterministic.
-constexpr int CS = 64;
+// order; deterministic.  A chunk's loads are all issued before its sum, and short chunks give
+// the action rows' sums (50 rows) more than a handful of workgroups.
+constexpr int CS = 16;
 __global__ __launch_bounds__(TB) void colsum_part_kernel(const float *__restrict__ dy, const float *__restrict__ x,
                                                          const float *__restrict__ rstd, int M, int N,
                                                          float *__restrict__ part) {
   const int n = blockIdx.x * TB + threadIdx.x;
   if (n >= N) return;
-  const int m0 = blockIdx.y * CS, m1 = min(M, m0 + CS);
-  float s = 0.f;
-  for (int m = m0; m < m1; ++m) {
+  const int m0 = blockIdx.y * CS;
+  float t[CS];
+#pragma unroll
+  for (int j = 0; j < CS; ++j) {
+    const int m = m0 + j;
     const long k = (long)m * N + n;
-    if (!x) s += dy[k];
-    else if (rstd[m] != 0.f) s += dy[k] * x[k] * rstd[m];
+    t[j] = 0.f;
+    if (m < M) {
+      if (!x) t[j] = dy[k];
+      else {
+        const float r = rstd[m];
+        t[j] = r != 0.f ? dy[k] * x[k] * r : 0.f;
+      }
+    }
   }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < CS; ++j) s += t[j];
   part[(long)blockIdx.y * N + n] = s;
 }
 __global__ __launch_bounds__(TB) void colsum_final_kernel(const float *__restrict__ part, int chunks, int N,
@@ -248,6 +265,7 @@ __global__ __launch_bounds__(TB) void colsum_final_kernel(const float *__restric
   const int n = blockIdx.x * TB + threadIdx.x;
   if (n >= N) return;
   float s = 0.f;
+#pragma unroll 8
   for (int c = 0; c < chunks; ++c) s += part[(long)c * N + n];
   out[n] = s;
 }
@@ -463,11 +481,14 @@ unsigned blocks(long n) { return (unsigned)((n + TB - 1) / TB); }
 // ------------------------------------------------------------------------------- launchers
 
 // Tile shape: the largest of 128 x 128, 128 x 64, 64 x 128 whose grid still gives about one
-// workgroup per CU (>= 200), else 64 x 64.  An unbatched product that still fills fewer than
-// half the CUs splits K (at least 128 per split) until about 256 workgroups, when g.part holds
-// the partial sums (splits x M x N floats, g.part_floats); the reduce runs in split order.
-// Measured on the one-layer DM0-base step (1.15 ms): sizing for two workgroups per CU instead
-// (>= 512 workgroups, splits up to 512) 1.41 ms, k-steps of 32 instead of 16 1.47 ms.
+// workgroup per CU (>= 200), else 64 x 64.  A product with fewer than two workgroups per CU
+// splits K (at least 64 per split) until about four per CU (1024 workgroups), the most the
+// registers of the 128 x 64 tile allow: one workgroup per CU is four waves, one per SIMD, and
+// each k-step's loads then wait out a whole memory round trip.  g.part holds the partial sums
+// (batch entries x splits x M x N floats, at most g.part_floats); the reduce runs in split
+// order.  Measured on the one-layer DM0-base step (same box, interleaved runs): splitting only
+// below 128 workgroups up to 256 1.45 ms, up to 1024 1.22 ms; k-steps of 32 instead of 16 no
+// faster (1.47 ms).
 template <typename TA, typename TB_>
 static void tgemm_t(TGemm g, const void *A, const void *B, hipStream_t s) {
   const long z = (long)g.zo_n * g.zi_n;
@@ -478,9 +499,9 @@ static void tgemm_t(TGemm g, const void *A, const void *B, hipStream_t s) {
   else if (g.N > 64 && z * tiles(64, 128) >= 200) bn = 128;
   const long t = z * tiles(bm, bn);
   int splits = 1;
-  if (z == 1 && g.part && t < 128)
-    while (t * splits * 2 <= 256 && g.K / (splits * 2) >= 128 &&
-           (size_t)(splits * 2) * g.M * g.N <= g.part_floats)
+  if (g.part && t < 512)
+    while (t * splits * 2 <= 1024 && g.K / (splits * 2) >= 64 &&
+           (size_t)(z * splits * 2) * g.M * g.N <= g.part_floats)
       splits *= 2;
   g.splits = splits;
   g.k_per_split = (((g.K + splits - 1) / splits) + GK - 1) / GK * GK;
@@ -491,7 +512,7 @@ static void tgemm_t(TGemm g, const void *A, const void *B, hipStream_t s) {
   else if (bn == 128) go(tgemm_kernel<64, 128, TA, TB_>);
   else go(tgemm_kernel<64, 64, TA, TB_>);
   if (splits > 1)
-    hipLaunchKernelGGL(tgemm_reduce_kernel, dim3(blocks((long)g.M * g.N)), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(tgemm_reduce_kernel, dim3(blocks(z * g.M * g.N)), dim3(256), 0, s, g);
 }
 void launch_tgemm(const TGemm &g, Dt ta, const void *A, Dt tb, const void *B, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.zo_n <= 0 || g.zi_n <= 0) return;
