@@ -12,7 +12,9 @@ new observation in, replay once; section 9.1: model-core against request latency
   other GPU tests hold to the oracle), and model-core replays between them changing nothing
   the next request sees;
 - the FP8-MLP prefill (DM0-base, B = 2) and the time-modulated expert (tiny, B = 3): two
-  requests each, bitwise equal to the separate calls.
+  requests each, bitwise equal to the separate calls;
+- DM0-base bf16 at B = 1 (prefix 816, then 300 under the same 816 cap), where the captured
+  denoise is the single-launch kernel: two requests bitwise equal to the separate calls.
 """
 import dataclasses
 
@@ -169,4 +171,31 @@ def test_engine_equals_separate_calls_for_model_variants(variant):
         print(f"request {name}: max |engine - separate calls| = {float(np.abs(got - ref).max()):.3e}", flush=True)
         np.testing.assert_array_equal(got, ref)
         assert np.isfinite(got).all()
+    eng.close()
+
+
+@pytest.mark.timeout(600)
+def test_engine_dm0_base_batch1_single_launch_equals_separate_calls():
+    wl = dataclasses.replace(workload(5), batch=1)
+    vlm = inputs.make_vlm_weights(wl)
+    aw = inputs.make_action_weights(wl)
+    emb = inputs.make_prefix_embeds(wl)
+    x_a = inputs.make_noise(wl)
+    x_b = np.random.default_rng(11).standard_normal(x_a.shape).astype(np.float32)
+    emb_b = emb.copy()
+    emb_b[0, 300:] = 0.0
+    print("case: engine, DM0-base bf16 B=1 P_cap=816, requests with prefix 816 then 300, 10 steps", flush=True)
+    gpu = Gpu(wl, vlm, aw)
+    eng = _engine(gpu, wl)
+    for name, e, lens, x in (("A", emb, np.array([816], dtype=np.int32), x_a),
+                             ("B", emb_b, np.array([300], dtype=np.int32), x_b)):
+        got = np.zeros_like(x)
+        eng.run(e, lens, x, got)
+        k, v = gpu.prefill(e, lens)
+        ref = gpu.denoise(k, v, lens, x, wl.steps)
+        del k, v
+        torch.cuda.empty_cache()
+        print(f"request {name}: max |engine - separate calls| = {float(np.abs(got - ref).max()):.3e}", flush=True)
+        np.testing.assert_array_equal(got, ref)
+        assert np.isfinite(got).all() and np.abs(got).max() > 0
     eng.close()
