@@ -7,10 +7,11 @@ The step computes in float32 throughout, so the bounds are float32 ones:
   - tiny fp32 model, B = 3 with prefix lengths 0, 17 and 24 (P_cap 24), layer 1, with and
     without knowledge insulation: the loss within 1e-5 relative, every gradient tensor within
     1e-4 of the oracle relative to that tensor's largest magnitude;
-  - DM0-base shapes (one layer, bf16 weights widened exactly), B = 2 with prefixes 816 and 431,
-    with and without knowledge insulation: the loss and every gradient within 1e-4 of the oracle relative to the tensor's largest
-    magnitude, the bound stated for float32 paths (measured: at most 1.6e-6, from float32 sums
-    over up to 6528 rows and softmax rows of up to 866 keys);
+  - DM0-base shapes (one layer, bf16 weights widened exactly), B = 2 with prefixes 816 and 431
+    and the benchmarked B = 1 with prefix 816, with and without knowledge insulation: the loss
+    and every gradient within 1e-4 of the oracle relative to the tensor's largest magnitude,
+    the bound stated for float32 paths (measured: at most 1.6e-6, from float32 sums over up to
+    6528 rows and softmax rows of up to 866 keys);
   - an empty mask gives loss 0 and all-zero gradients; argument checks.
 """
 import dataclasses
@@ -84,15 +85,19 @@ def test_train_step_tiny_fp32(ki):
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("ki", [False, True])
-def test_train_step_dm0_base_one_layer_bf16(ki):
-    wl = dataclasses.replace(workload(2), batch=2)
-    print(f"case: training step, DM0-base one layer (bf16 weights), B=2 prefixes 816 / 431, knowledge insulation {ki}",
-          flush=True)
+@pytest.mark.parametrize("lens", [(816, 431), (816,)], ids=["B2", "B1"])
+def test_train_step_dm0_base_one_layer_bf16(ki, lens):
+    """B = 2 (816 / 431) and the benchmarked B = 1, P = 816, whose products split K differently
+    (the prefix products four ways instead of two)."""
+    wl = dataclasses.replace(workload(2), batch=len(lens))
+    print(f"case: training step, DM0-base one layer (bf16 weights), B={len(lens)} prefixes {list(lens)}, "
+          f"knowledge insulation {ki}", flush=True)
     vlm = inputs.make_vlm_weights(wl)
     aw = inputs.make_action_weights(wl)
     tb = inputs.make_train_batch(wl)
-    tb.lens[:] = [816, 431]
-    tb.h_pre[1, 431:] = 0.0
+    tb.lens[:] = lens
+    for b, n in enumerate(lens):
+        tb.h_pre[b, n:] = 0.0
     _compare(wl, vlm, aw, tb, 0, ki, 1e-4, 1e-4)
 
 
