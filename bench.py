@@ -468,7 +468,8 @@ def merged_layer_times(reps=20):
     """One DM0-base merged layer at batch 1 (816 prefix and 50 action tokens through both experts
     with the joint block-masked attention, prefix K/V written out): mean µs per dm_merged_layer
     call (HIP events around each call on its stream; the inputs are restored between calls,
-    outside the timed spans) and the fraction of dense bf16 MFMA peak over its algorithmic FLOPs."""
+    outside the timed spans) and the fraction of dense bf16 MFMA peak over its algorithmic FLOPs;
+    the same for one replay of the call captured into a graph (graph_us)."""
     import torch
     from dual_expert_merged_amd import binding as bd
     from dual_expert_merged_amd import inputs
@@ -500,14 +501,38 @@ def merged_layer_times(reps=20):
             e1.record(stream)
             stream.synchronize()
             total += e0.elapsed_time(e1)
+    # the same call captured once into a graph (as a deployment captures its fixed-shape work)
+    # and replayed: the GPU-side time without the host's per-launch cost
+    g = torch.cuda.CUDAGraph()
+    hp.copy_(hp0)
+    hs.copy_(hs0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        ctx.merged_layer(dv, da.body, 0, hp, hs, lens, ws, ko, vo)
+    gtotal = 0.0
+    cur = torch.cuda.current_stream()
+    for r in range(reps + 1):
+        hp.copy_(hp0)
+        hs.copy_(hs0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        g.replay()
+        e1.record(cur)
+        cur.synchronize()
+        if r > 0:  # the first replay uploads the graph
+            gtotal += e0.elapsed_time(e1)
+    del g
     ctx.close()
     us = total * 1e3 / reps
+    graph_us = gtotal * 1e3 / reps
     D, Hq = s.head_dim, s.n_q_heads
     params = lambda h, f: s.qkv_rows * h + h * Hq * D + 3 * f * h
     flops = (2 * P * params(s.vlm_hidden, s.vlm_ffn) + 2 * S * params(s.act_hidden, s.act_ffn)
              + 4 * D * Hq * (P * P + S * (P + S)))
     return {"us": round(us, 2), "algorithmic_gflop": round(flops / 1e9, 2),
             "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "graph_us": round(graph_us, 2),
+            "graph_mfma_frac": round(flops / (graph_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "workload": "DM0-base merged layer, bf16, B=1, 816 prefix + 50 action tokens"}
 
 

@@ -54,6 +54,10 @@ struct dm_ctx {
   size_t es;         // bytes per element of the weight dtype
   bool single_ok;    // the device holds all workgroups of the single-launch batch-1 denoise
   hipError_t scratch_status;  // result of looking up the static scratch buffer on `device`
+  // dm_merged_layer runs the action expert's kernels on a second stream beside the VLM
+  // expert's (fork and join through these events); both created on `device` at default priority
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, kv_ready = nullptr, joined = nullptr;
 };
 
 // ---------------------------------------------------------------- static scratch buffer
@@ -108,6 +112,7 @@ struct ExpertPlans {
 struct Layout {
   Region rope, rope_rows;
   Region h, hg, ssq, q, ks, vs, o, act, apart, split;          // action side (h: denoise only)
+  Region split_a;  // merged layer: the action expert's K-split partials (its kernels run beside the VLM's)
   Region hp, hg_p, ssq_p, q_p, kp, vp, o_p, act_p, apart_p;    // prefix side (hp: prefill only)
   Region q8_p, qs_p;                                           // FP8 MLP operand codes and row scales
   Region single;                                               // single-launch batch-1 denoise
@@ -240,6 +245,10 @@ Layout make_layout(const dm_config &c, size_t es, dm_op op, int B, int P_cap) {
   if (op == DM_OP_DENOISE || op == DM_OP_MERGED_LAYER) {
     L.pa = plan_expert(c, dt, (int)Ms, Ha, c.act_ffn);
     split = std::max(split_bytes(L.pa.o, (int)Ms, Ha), split_bytes(L.pa.down, (int)Ms, Ha));
+    if (op == DM_OP_MERGED_LAYER) {  // a region of its own: the two experts' finishes overlap
+      if (split) L.put(L.split_a, split);
+      split = 0;
+    }
     if (op == DM_OP_DENOISE) L.put(L.h, Ms * Ha * sizeof(float));
     L.put(L.hg, Ms * Ha * es);
     L.put(L.ssq, Ms * (Ha / 16) * sizeof(float));
@@ -443,21 +452,33 @@ SplitK splitk(const Layout &L, void *ws, const GemmPlan &p) {
   return s;
 }
 
-// One expert's O-projection + residual and MLP + residual.  `next_attn_norm` is the gain of
-// the norm that follows the layer (NULL after the last layer of a stack).
-void enqueue_finish(const dm_ctx *ctx, const Layout &L, void *ws, const ExpertPlans &pl, const Expert &e,
-                    const Hidden &hid, const void *o, void *act, int M, int F, RowMap rows,
-                    const float *next_attn_norm, hipStream_t s) {
+// One expert's O-projection + residual (enqueue_oproj), then its MLP + residual (enqueue_mlp).
+// `next_attn_norm` is the gain of the norm that follows the layer (NULL after the last layer of
+// a stack).
+void enqueue_oproj(const dm_ctx *ctx, const Layout &L, void *ws, const ExpertPlans &pl, const Expert &e,
+                   const Hidden &hid, const void *o, int M, RowMap rows, hipStream_t s) {
   const dm_config &c = ctx->cfg;
-  GemmPlan po = pl.o, pg = pl.gu, pd = pl.down;
+  GemmPlan po = pl.o;
   po.sk = splitk(L, ws, pl.o);
-  pd.sk = splitk(L, ws, pl.down);
   ResidArgs ro{o, M, c.n_q_heads * c.head_dim, e.w_o, hid, e.mlp_norm, rows};
   launch_resid(ctx->dt, ro, po, s);
+}
+void enqueue_mlp(const dm_ctx *ctx, const Layout &L, void *ws, const ExpertPlans &pl, const Expert &e,
+                 const Hidden &hid, void *act, int M, int F, RowMap rows, const float *next_attn_norm,
+                 hipStream_t s) {
+  const dm_config &c = ctx->cfg;
+  GemmPlan pg = pl.gu, pd = pl.down;
+  pd.sk = splitk(L, ws, pl.down);
   SwigluArgs sg{hid, M, F, c.rms_eps, e.w_gate, e.w_up, act, rows};
   launch_swiglu(ctx->dt, sg, pg, s);
   ResidArgs rd{act, M, F, e.w_down, hid, next_attn_norm, rows};
   launch_resid(ctx->dt, rd, pd, s);
+}
+void enqueue_finish(const dm_ctx *ctx, const Layout &L, void *ws, const ExpertPlans &pl, const Expert &e,
+                    const Hidden &hid, const void *o, void *act, int M, int F, RowMap rows,
+                    const float *next_attn_norm, hipStream_t s) {
+  enqueue_oproj(ctx, L, ws, pl, e, hid, o, M, rows, s);
+  enqueue_mlp(ctx, L, ws, pl, e, hid, act, M, F, rows, next_attn_norm, s);
 }
 
 // The same with the MLP in FP8 E4M3 (page "DM0.5: High-Performance Embodied VLA ...", section
@@ -767,14 +788,34 @@ dm_status dm_ctx_create(const dm_config *cfg, int device, dm_ctx **out) {
   if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(device) == hipSuccess) {
     ctx->single_ok = persist_check_device(device) == hipSuccess;
     ctx->scratch_status = scratch_setup(device);
+    hipError_t e = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->kv_ready, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->joined, hipEventDisableTiming);
     (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+      dm_ctx_destroy(ctx);
+      (void)hipGetLastError();
+      return fail(DM_ERR_HIP, "creating the context's side stream / events: %s", hipGetErrorString(e));
+    }
   }
   (void)hipGetLastError();
   *out = ctx;
   return DM_OK;
 }
 
-void dm_ctx_destroy(dm_ctx *ctx) { delete ctx; }
+void dm_ctx_destroy(dm_ctx *ctx) {
+  if (!ctx) return;
+  int cur = -1;
+  const bool back = hipGetDevice(&cur) == hipSuccess && cur != ctx->device && hipSetDevice(ctx->device) == hipSuccess;
+  if (ctx->fork) (void)hipEventDestroy(ctx->fork);
+  if (ctx->kv_ready) (void)hipEventDestroy(ctx->kv_ready);
+  if (ctx->joined) (void)hipEventDestroy(ctx->joined);
+  if (ctx->side) (void)hipStreamDestroy(ctx->side);
+  if (back) (void)hipSetDevice(cur);
+  (void)hipGetLastError();
+  delete ctx;
+}
 
 size_t dm_workspace_bytes(const dm_ctx *ctx, dm_op op, int B, int P_cap) {
   if (!ctx || B < 1 || P_cap < 1) return 0;
@@ -1001,6 +1042,7 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   REQUIRE(aligned16(h_prefix) && aligned16(h_suffix), DM_ERR_INVALID_ARG, "hidden streams must be 16-byte aligned");
   REQUIRE((k_out == nullptr) == (v_out == nullptr), DM_ERR_INVALID_ARG, "k_out and v_out must both be set or NULL");
   REQUIRE(!k_out || (aligned16(k_out) && aligned16(v_out)), DM_ERR_INVALID_ARG, "k_out / v_out must be aligned");
+  REQUIRE(ctx->side, DM_ERR_HIP, "the context has no side stream (dm_ctx_create could not make the device current)");
   TRY(set_device(ctx));
   hipStream_t s = (hipStream_t)stream;
   const Layout L = make_layout(c, ctx->es, DM_OP_MERGED_LAYER, B, P_cap);
@@ -1014,27 +1056,45 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   const Hidden hp{h_prefix, at<void>(ws, L.hg_p), at<float>(ws, L.ssq_p), c.vlm_hidden};
   const Hidden hs{h_suffix, at<void>(ws, L.hg), at<float>(ws, L.ssq), c.act_hidden};
 
+  // The two experts' kernels share only the prefix K/V and the RoPE table, so they run on two
+  // streams: the VLM expert's on `stream`, the action expert's on the context's side stream
+  // (the action rows' GEMMs are small and leave most CUs to the prefix rows' GEMMs).  The side
+  // stream starts after the RoPE table, its attention waits for the prefix K/V, and `stream`
+  // waits for the side stream's last kernel, so the call's work is ordered on `stream` alone.
+  // Launches are issued one at a time from the host, so the order of enqueueing decides what
+  // can overlap: the VLM chain (the longer one) up to its O-projection first, then the action
+  // expert up to its attention (which then runs beside the VLM O-projection and MLP), the VLM MLP,
+  // and the rest of the action expert.
+  hipStream_t sa = ctx->side;
   launch_rope_table(rope, P_cap + S, D, c.rope_base, s);
-  float2 *rope_rows = at<float2>(ws, L.rope_rows);
-  launch_rope_rows(rope, prefix_lens, P_cap, B, S, D, rope_rows, s);
+  HIP_TRY(hipEventRecord(ctx->fork, s));
   launch_norm_prep(ctx->dt, h_prefix, hp, ev.attn_norm, Mp, s);
-  launch_norm_prep(ctx->dt, h_suffix, hs, ea.attn_norm, Ms, s);
   QkvArgs qv{hp, Mp, c.rms_eps, ev.w_qkv, at<void>(ws, L.q_p), kp, vp, P_cap, prow, rope, Hq, Hkv, D, nullptr,
              ev.q_norm, ev.k_norm};
   launch_qkv(ctx->dt, qv, L.pv.qkv, s);
-  QkvArgs qa{hs, Ms, c.rms_eps, ea.w_qkv, at<void>(ws, L.q), at<void>(ws, L.ks), at<void>(ws, L.vs), S, srow, rope,
-             Hq, Hkv, D, rope_rows, ea.q_norm, ea.k_norm};
-  launch_qkv(ctx->dt, qa, L.pa.qkv, s);
+  HIP_TRY(hipEventRecord(ctx->kv_ready, s));
   AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kp, vp, P_cap, nullptr, nullptr, S, prefix_lens, B, Hq, Hkv, D,
               L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),
               L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr};
   launch_attention(ctx->dt, ap, s);
+  enqueue_oproj(ctx, L, ws, L.pv, ev, hp, at<void>(ws, L.o_p), Mp, prow, s);
+  HIP_TRY(hipStreamWaitEvent(sa, ctx->fork, 0));
+  float2 *rope_rows = at<float2>(ws, L.rope_rows);
+  launch_rope_rows(rope, prefix_lens, P_cap, B, S, D, rope_rows, sa);
+  launch_norm_prep(ctx->dt, h_suffix, hs, ea.attn_norm, Ms, sa);
+  QkvArgs qa{hs, Ms, c.rms_eps, ea.w_qkv, at<void>(ws, L.q), at<void>(ws, L.ks), at<void>(ws, L.vs), S, srow, rope,
+             Hq, Hkv, D, rope_rows, ea.q_norm, ea.k_norm};
+  launch_qkv(ctx->dt, qa, L.pa.qkv, sa);
+  HIP_TRY(hipStreamWaitEvent(sa, ctx->kv_ready, 0));
   AttnArgs as{at<void>(ws, L.q), S, 1, kp, vp, P_cap, at<void>(ws, L.ks), at<void>(ws, L.vs), S, prefix_lens, B, Hq,
               Hkv, D, L.n_chunks, L.chunk_keys, at<void>(ws, L.o), L.n_chunks > 1 ? at<void>(ws, L.apart) : nullptr};
-  launch_attention(ctx->dt, as, s);
-  enqueue_finish(ctx, L, ws, L.pv, ev, hp, at<void>(ws, L.o_p), at<void>(ws, L.act_p), Mp, c.vlm_ffn, prow, nullptr,
-                 s);
-  enqueue_finish(ctx, L, ws, L.pa, ea, hs, at<void>(ws, L.o), at<void>(ws, L.act), Ms, c.act_ffn, srow, nullptr, s);
+  launch_attention(ctx->dt, as, sa);
+  enqueue_mlp(ctx, L, ws, L.pv, ev, hp, at<void>(ws, L.act_p), Mp, c.vlm_ffn, prow, nullptr, s);
+  Layout La = L;  // the action expert's K-split partials in a region of their own
+  La.split = L.split_a;
+  enqueue_finish(ctx, La, ws, L.pa, ea, hs, at<void>(ws, L.o), at<void>(ws, L.act), Ms, c.act_ffn, srow, nullptr, sa);
+  HIP_TRY(hipEventRecord(ctx->joined, sa));
+  HIP_TRY(hipStreamWaitEvent(s, ctx->joined, 0));
   HIP_TRY(hipGetLastError());
   return DM_OK;
 }

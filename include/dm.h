@@ -180,7 +180,12 @@ dm_status dm_prefill_kv(dm_ctx *ctx, const dm_expert_weights *vlm /* (host) */,
  * h_prefix [B][P_cap][Hv] (rows >= P_b untouched) and h_suffix [B][S][Ha].  Prefix rows attend
  * to the sample's P_b prefix tokens; action rows attend to the P_b prefix tokens and all S
  * action tokens.  k_out / v_out: optional [B][Hkv][P_cap][D] receiving this layer's prefix
- * post-RoPE K/V (both NULL or both set). */
+ * post-RoPE K/V (both NULL or both set).
+ * The two experts share only the prefix K/V, so the action expert's kernels run on a second
+ * stream that the context owns (default priority), forked from and joined back into `stream`
+ * with events: the call's work is complete when `stream` reaches that point, and it may be
+ * captured into a graph on `stream`.  The side stream and its events belong to the context:
+ * calls on one context from several host threads at once must be serialised. */
 dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm /* (host) */,
                           const dm_expert_weights *act /* (host) */, int layer,
                           float *h_prefix, float *h_suffix, const int32_t *prefix_lens,

@@ -22,10 +22,11 @@ import pytest
 import torch
 
 import oracle as O
+from dual_expert_merged_amd import binding as bd
 from dual_expert_merged_amd import inputs
 from dual_expert_merged_amd.configs import workload
 from tests.golden import make_config4_chunks as make_golden4
-from tests.gpu_harness import Gpu, err_stats, np32, rel_inf
+from tests.gpu_harness import Gpu, dev_lens, err_stats, np32, rel_inf
 
 pytestmark = pytest.mark.gpu
 CHUNK_MAX, CHUNK_MEAN, INTER_REL = 2e-2, 2e-3, 1e-2
@@ -60,6 +61,52 @@ def test_one_merged_layer_bf16():
         e = rel_inf(g, r)
         print(f"{name}: rel inf err {e:.3e}, max/mean abs {err_stats(g, r)}", flush=True)
         assert e <= INTER_REL, (name, e)
+
+
+def test_merged_layer_side_stream_join_and_graph():
+    """dm_merged_layer runs the action expert's kernels on the context's side stream: a torch op
+    enqueued on the caller's stream right after the call reads the finished values, two calls give
+    the same bits, and a captured graph of the call replays to the eager result (three replays
+    with eager work between them)."""
+    wl = workload(2)
+    print("case: DM0-base merged layer, side-stream join and graph capture, P=816", flush=True)
+    s = wl.shape
+    gpu = Gpu(wl, inputs.make_vlm_weights(wl), inputs.make_action_weights(wl))
+    h_pre, h_suf = inputs.make_prefix_embeds(wl), inputs.make_suffix_hidden(wl)
+    B, P_cap = h_pre.shape[0], h_pre.shape[1]
+    hp0 = torch.from_numpy(np.ascontiguousarray(h_pre, dtype=np.float32)).cuda()
+    hs0 = torch.from_numpy(np.ascontiguousarray(h_suf, dtype=np.float32)).cuda()
+    lens = dev_lens([wl.prefix_len])
+    ws = gpu.ctx.workspace(bd.OP_MERGED_LAYER, B, P_cap)
+    ko = torch.zeros((B, s.n_kv_heads, P_cap, s.head_dim), dtype=gpu.td, device="cuda")
+    vo = torch.zeros_like(ko)
+    hp, hs = hp0.clone(), hs0.clone()
+    torch.cuda.synchronize()
+    eager = []
+    for _ in range(2):
+        hp.copy_(hp0)
+        hs.copy_(hs0)
+        gpu.ctx.merged_layer(gpu.vlm, gpu.aw.body, 0, hp, hs, lens, ws, ko, vo)
+        got = (hs.clone(), hp.clone(), ko.clone())  # same stream, right after the call
+        eager.append([t.cpu() for t in got])
+    for a, b in zip(eager[0], eager[1]):
+        assert torch.equal(a, b)
+    g = torch.cuda.CUDAGraph()
+    hp.copy_(hp0)
+    hs.copy_(hs0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        gpu.ctx.merged_layer(gpu.vlm, gpu.aw.body, 0, hp, hs, lens, ws, ko, vo)
+    for r in range(3):
+        hp.copy_(hp0)
+        hs.copy_(hs0)
+        ko.zero_()
+        g.replay()
+        got = [t.cpu() for t in (hs.clone(), hp.clone(), ko.clone())]
+        for name, a, b in zip(("h_suffix", "h_prefix", "k_out"), got, eager[0]):
+            assert torch.equal(a, b), (r, name)
+        _ = float((hp0 * 2.0).sum().item())  # eager work between replays
+    print("merged layer: two eager calls and three graph replays bitwise equal", flush=True)
 
 
 @pytest.fixture(scope="module")
