@@ -54,10 +54,11 @@ struct dm_ctx {
   size_t es;         // bytes per element of the weight dtype
   bool single_ok;    // the device holds all workgroups of the single-launch batch-1 denoise
   hipError_t scratch_status;  // result of looking up the static scratch buffer on `device`
-  // dm_merged_layer runs the action expert's kernels on a second stream beside the VLM
-  // expert's (fork and join through these events); both created on `device` at default priority
+  // dm_merged_layer and dm_train_merged_layer run independent parts of their work on a second
+  // stream (forked and joined through these events); created on `device` at default priority
+  static constexpr int kEvents = 8;
   hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, kv_ready = nullptr, joined = nullptr;
+  hipEvent_t ev[kEvents] = {};
 };
 
 // ---------------------------------------------------------------- static scratch buffer
@@ -303,7 +304,7 @@ constexpr size_t kTrainSplitFloats = (size_t)24 << 20;
 // prefix rows, T = P_cap + S joined keys.
 struct TrainLayout {
   Region x, u, v, dv, h0, n1, r1, qkv, dqkv, K, V, dK, dV, sc, dp, o, dO, h1, n2, r2, gt, up, act, dgt, dup, dact, h2,
-      nf, rf, dnf, dh2, dn2, dh1, dn1, dh0, np, rp, kvp, dkvp, dnp, split, cpart;
+      nf, rf, dnf, dh2, dn2, dh1, dn1, dh0, np, rp, kvp, dkvp, dnp, split, cpart, split2, cpart2;
   size_t total = 0;
   void put(Region &r, size_t floats) {
     r.off = total;
@@ -331,6 +332,9 @@ TrainLayout train_layout(const dm_config &c, int B, int P_cap) {
   for (Region *r : {&L.kvp, &L.dkvp}) L.put(*r, Mp * 2 * Hkv * D);
   L.put(L.split, kTrainSplitFloats);  // split-K partial sums of the products with few tiles
   L.put(L.cpart, std::max(colsum_part_floats((int)M, (int)std::max(Ha, A)), colsum_part_floats((int)Mp, (int)Hv)));
+  // the same two for the products and column sums on the side stream
+  L.put(L.split2, kTrainSplitFloats);
+  L.put(L.cpart2, colsum_part_floats((int)Mp, (int)Hv));
   return L;
 }
 
@@ -789,9 +793,8 @@ dm_status dm_ctx_create(const dm_config *cfg, int device, dm_ctx **out) {
     ctx->single_ok = persist_check_device(device) == hipSuccess;
     ctx->scratch_status = scratch_setup(device);
     hipError_t e = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->kv_ready, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->joined, hipEventDisableTiming);
+    for (int k = 0; k < dm_ctx::kEvents && e == hipSuccess; ++k)
+      e = hipEventCreateWithFlags(&ctx->ev[k], hipEventDisableTiming);
     (void)hipSetDevice(prev);
     if (e != hipSuccess) {
       dm_ctx_destroy(ctx);
@@ -808,9 +811,8 @@ void dm_ctx_destroy(dm_ctx *ctx) {
   if (!ctx) return;
   int cur = -1;
   const bool back = hipGetDevice(&cur) == hipSuccess && cur != ctx->device && hipSetDevice(ctx->device) == hipSuccess;
-  if (ctx->fork) (void)hipEventDestroy(ctx->fork);
-  if (ctx->kv_ready) (void)hipEventDestroy(ctx->kv_ready);
-  if (ctx->joined) (void)hipEventDestroy(ctx->joined);
+  for (hipEvent_t e : ctx->ev)
+    if (e) (void)hipEventDestroy(e);
   if (ctx->side) (void)hipStreamDestroy(ctx->side);
   if (back) (void)hipSetDevice(cur);
   (void)hipGetLastError();
@@ -1067,25 +1069,25 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   // and the rest of the action expert.
   hipStream_t sa = ctx->side;
   launch_rope_table(rope, P_cap + S, D, c.rope_base, s);
-  HIP_TRY(hipEventRecord(ctx->fork, s));
+  HIP_TRY(hipEventRecord(ctx->ev[0], s));
   launch_norm_prep(ctx->dt, h_prefix, hp, ev.attn_norm, Mp, s);
   QkvArgs qv{hp, Mp, c.rms_eps, ev.w_qkv, at<void>(ws, L.q_p), kp, vp, P_cap, prow, rope, Hq, Hkv, D, nullptr,
              ev.q_norm, ev.k_norm};
   launch_qkv(ctx->dt, qv, L.pv.qkv, s);
-  HIP_TRY(hipEventRecord(ctx->kv_ready, s));
+  HIP_TRY(hipEventRecord(ctx->ev[1], s));
   AttnArgs ap{at<void>(ws, L.q_p), P_cap, 0, kp, vp, P_cap, nullptr, nullptr, S, prefix_lens, B, Hq, Hkv, D,
               L.n_chunks_p, L.chunk_keys_p, at<void>(ws, L.o_p),
               L.n_chunks_p > 1 ? at<void>(ws, L.apart_p) : nullptr};
   launch_attention(ctx->dt, ap, s);
   enqueue_oproj(ctx, L, ws, L.pv, ev, hp, at<void>(ws, L.o_p), Mp, prow, s);
-  HIP_TRY(hipStreamWaitEvent(sa, ctx->fork, 0));
+  HIP_TRY(hipStreamWaitEvent(sa, ctx->ev[0], 0));
   float2 *rope_rows = at<float2>(ws, L.rope_rows);
   launch_rope_rows(rope, prefix_lens, P_cap, B, S, D, rope_rows, sa);
   launch_norm_prep(ctx->dt, h_suffix, hs, ea.attn_norm, Ms, sa);
   QkvArgs qa{hs, Ms, c.rms_eps, ea.w_qkv, at<void>(ws, L.q), at<void>(ws, L.ks), at<void>(ws, L.vs), S, srow, rope,
              Hq, Hkv, D, rope_rows, ea.q_norm, ea.k_norm};
   launch_qkv(ctx->dt, qa, L.pa.qkv, sa);
-  HIP_TRY(hipStreamWaitEvent(sa, ctx->kv_ready, 0));
+  HIP_TRY(hipStreamWaitEvent(sa, ctx->ev[1], 0));
   AttnArgs as{at<void>(ws, L.q), S, 1, kp, vp, P_cap, at<void>(ws, L.ks), at<void>(ws, L.vs), S, prefix_lens, B, Hq,
               Hkv, D, L.n_chunks, L.chunk_keys, at<void>(ws, L.o), L.n_chunks > 1 ? at<void>(ws, L.apart) : nullptr};
   launch_attention(ctx->dt, as, sa);
@@ -1093,8 +1095,8 @@ dm_status dm_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const dm_ex
   Layout La = L;  // the action expert's K-split partials in a region of their own
   La.split = L.split_a;
   enqueue_finish(ctx, La, ws, L.pa, ea, hs, at<void>(ws, L.o), at<void>(ws, L.act), Ms, c.act_ffn, srow, nullptr, sa);
-  HIP_TRY(hipEventRecord(ctx->joined, sa));
-  HIP_TRY(hipStreamWaitEvent(s, ctx->joined, 0));
+  HIP_TRY(hipEventRecord(ctx->ev[2], sa));
+  HIP_TRY(hipStreamWaitEvent(s, ctx->ev[2], 0));
   HIP_TRY(hipGetLastError());
   return DM_OK;
 }
@@ -1137,8 +1139,21 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
   REQUIRE(((uintptr_t)ws & 255u) == 0, DM_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const TrainLayout L = train_layout(c, B, P_cap);
   REQUIRE(ws_bytes >= L.total, DM_ERR_WORKSPACE, "workspace too small: %zu bytes, need %zu", ws_bytes, L.total);
+  REQUIRE(ctx->side, DM_ERR_HIP, "the context has no side stream (dm_ctx_create could not make the device current)");
   TRY(set_device(ctx));
   hipStream_t s = (hipStream_t)stream;
+  // Parts of the step that no later kernel on the critical path reads run on the context's side
+  // stream `s2`, each after an event on `s` that marks its inputs ready: the prefix K/V
+  // projection (forward), the weight gradients of the MLP and the O-projection, and the whole
+  // prefix backward; `s` waits for `s2` at the end, so the step is ordered on `stream` alone.
+  // Each stream has its own split-K and column-sum scratch.
+  hipStream_t s2 = ctx->side;
+  hipEvent_t *ev = ctx->ev;
+  auto fork = [&](int k) {  // s2 waits for what s has enqueued so far
+    HIP_TRY(hipEventRecord(ev[k], s));
+    HIP_TRY(hipStreamWaitEvent(s2, ev[k], 0));
+    return DM_OK;
+  };
 
   const int S = c.chunk, A = c.action_dim, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, grp = Hq / Hkv;
   const int Ha = c.act_hidden, Hv = c.vlm_hidden, F = c.act_ffn, QKV = (Hq + 2 * Hkv) * D, HqD = Hq * D, KV2 = 2 * Hkv * D;
@@ -1156,7 +1171,7 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
         *dup = F32(L.dup), *dact = F32(L.dact), *h2 = F32(L.h2), *nf = F32(L.nf), *rf = F32(L.rf), *dnf = F32(L.dnf),
         *dh2 = F32(L.dh2), *dn2 = F32(L.dn2), *dh1 = F32(L.dh1), *dn1 = F32(L.dn1), *dh0 = F32(L.dh0),
         *np_ = F32(L.np), *rp = F32(L.rp), *kvp = F32(L.kvp), *dkvp = F32(L.dkvp), *dnp = F32(L.dnp),
-        *split = F32(L.split), *cpart = F32(L.cpart);
+        *split = F32(L.split), *cpart = F32(L.cpart), *split2 = F32(L.split2), *cpart2 = F32(L.cpart2);
   const dm_expert_weights &W = aw->body;
   const char *wq = layer_ptr(W.w_qkv, (size_t)QKV * Ha, l, es), *wo = layer_ptr(W.w_o, (size_t)Ha * HqD, l, es);
   const char *wg = layer_ptr(W.w_gate, (size_t)F * Ha, l, es), *wu = layer_ptr(W.w_up, (size_t)F * Ha, l, es);
@@ -1167,27 +1182,33 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
   const TOperand ROW_K = {0, 0, 0, 1};
   auto rows = [&](long ld) { TOperand t = ROW_K; t.sm = ld; return t; };     // X[m][k] row-major, row length ld
   auto cols = [&](long ld) { return TOperand{0, 0, 1, ld}; };                 // X[k][m] read as (m, k)
-  auto mm = [&](int Mm, int Nn, int Kk, TOperand a, Dt ta, const void *pa, TOperand b, Dt tb, const void *pb,
-                float *C, long ldc, float beta = 0.f) {
+  auto mm_on = [&](hipStream_t st, int Mm, int Nn, int Kk, TOperand a, Dt ta, const void *pa, TOperand b, Dt tb,
+                   const void *pb, float *C, long ldc, float beta = 0.f) {
     TGemm g{};
     g.M = Mm, g.N = Nn, g.K = Kk, g.a = a, g.b = b, g.bdiv = 1, g.C = C, g.ldc = ldc, g.zo_n = 1, g.zi_n = 1;
-    g.alpha = 1.f, g.beta = beta, g.part = split, g.part_floats = kTrainSplitFloats;
-    launch_tgemm(g, ta, pa, tb, pb, s);
+    g.alpha = 1.f, g.beta = beta, g.part = st == s ? split : split2, g.part_floats = kTrainSplitFloats;
+    launch_tgemm(g, ta, pa, tb, pb, st);
   };
+  auto mm = [&](int Mm, int Nn, int Kk, TOperand a, Dt ta, const void *pa, TOperand b, Dt tb, const void *pb,
+                float *C, long ldc, float beta = 0.f) { mm_on(s, Mm, Nn, Kk, a, ta, pa, b, tb, pb, C, ldc, beta); };
   auto colsum = [&](const float *dy, const float *xx, const float *rr, int Mm, int Nn, float *out) {
     launch_colsum(dy, xx, rr, Mm, Nn, out, cpart, s);
   };
 
   // ---- forward
+  // prefix (side stream): the VLM expert's pre-norm and K/V rows (rows past each prefix are
+  // zero), RoPE on K
+  TRY(fork(0));
+  launch_rms_fwd(h_prefix, DT_F32, gv, eps, Mp, Hv, lens, P_cap, np_, rp, s2);
+  mm_on(s2, Mp, KV2, Hv, rows(Hv), DT_F32, np_, rows(Hv), dt, wv_kv, kvp, KV2);
+  launch_rope_rows(kvp, Mp, P_cap, KV2, 0, Hkv, D, base, lens, false, 1.0f, s2);
+  HIP_TRY(hipEventRecord(ev[1], s2));
   launch_fm_embed(actions, noise, t, aw->w_in, aw->b_in, B, S, A, Ha, 10000.0f, x, u, h0, s);
-  // prefix: the VLM expert's pre-norm and K/V rows (rows past each prefix are zero), RoPE on K
-  launch_rms_fwd(h_prefix, DT_F32, gv, eps, Mp, Hv, lens, P_cap, np_, rp, s);
-  mm(Mp, KV2, Hv, rows(Hv), DT_F32, np_, rows(Hv), dt, wv_kv, kvp, KV2);
-  launch_rope_rows(kvp, Mp, P_cap, KV2, 0, Hkv, D, base, lens, false, 1.0f, s);
   // action rows: pre-norm, Q/K/V, RoPE on Q and K at positions P_b + s
   launch_rms_fwd(h0, DT_F32, g1, eps, M, Ha, nullptr, 1, n1, r1, s);
   mm(M, QKV, Ha, rows(Ha), DT_F32, n1, rows(Ha), dt, wq, qkv, QKV);
   launch_rope_rows(qkv, M, S, QKV, 0, Hq + Hkv, D, base, lens, true, 1.0f, s);
+  HIP_TRY(hipStreamWaitEvent(s, ev[1], 0));
   launch_gather_kv(kvp, qkv, lens, B, P_cap, S, Hq, Hkv, D, K, V, s);
   // scores[b][h][s][j] = q . k / sqrt(D), softmax over the visible keys, O = P V
   TGemm at_{};
@@ -1228,18 +1249,21 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
   mm(M, Ha, A, rows(A), DT_F32, dv, cols(Ha), DT_F32, aw->w_out, dnf, Ha);
   launch_rms_bwd(h2, DT_F32, aw->final_norm, dnf, rf, nullptr, M, Ha, dh2, s);
   colsum(dnf, h2, rf, M, Ha, G.final_norm);
-  // MLP
-  mm(Ha, F, M, cols(Ha), DT_F32, dh2, cols(F), DT_F32, act, G.w_down, F);
+  // MLP (its weight gradients on the side stream: nothing on `s` reads them)
+  TRY(fork(2));
+  mm_on(s2, Ha, F, M, cols(Ha), DT_F32, dh2, cols(F), DT_F32, act, G.w_down, F);
   mm(M, F, Ha, rows(Ha), DT_F32, dh2, cols(F), dt, wd, dact, F);
   launch_swiglu_bwd(gt, up, dact, (long)M * F, dgt, dup, s);
-  mm(F, Ha, M, cols(F), DT_F32, dgt, cols(Ha), DT_F32, n2, G.w_gate, Ha);
-  mm(F, Ha, M, cols(F), DT_F32, dup, cols(Ha), DT_F32, n2, G.w_up, Ha);
+  TRY(fork(3));
+  mm_on(s2, F, Ha, M, cols(F), DT_F32, dgt, cols(Ha), DT_F32, n2, G.w_gate, Ha);
+  mm_on(s2, F, Ha, M, cols(F), DT_F32, dup, cols(Ha), DT_F32, n2, G.w_up, Ha);
   mm(M, Ha, F, rows(F), DT_F32, dgt, cols(Ha), dt, wg, dn2, Ha);
   mm(M, Ha, F, rows(F), DT_F32, dup, cols(Ha), dt, wu, dn2, Ha, 1.f);
   launch_rms_bwd(h1, DT_F32, g2, dn2, r2, dh2, M, Ha, dh1, s);
   colsum(dn2, h1, r2, M, Ha, G.mlp_norm);
-  // O-projection
-  mm(Ha, HqD, M, cols(Ha), DT_F32, dh1, cols(HqD), DT_F32, o, G.w_o, HqD);
+  // O-projection (weight gradient on the side stream)
+  TRY(fork(4));
+  mm_on(s2, Ha, HqD, M, cols(Ha), DT_F32, dh1, cols(HqD), DT_F32, o, G.w_o, HqD);
   mm(M, HqD, Ha, rows(Ha), DT_F32, dh1, cols(HqD), dt, wo, dO, HqD);
   // attention: dP = dO V^T, dS = P (dP - rowsum(P dP)) / sqrt(D), dQ = dS K, dK = dS^T Q, dV = P^T dO
   {
@@ -1273,6 +1297,21 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
     launch_tgemm(g, DT_F32, sc + (size_t)r * S * T, DT_F32, dO + (size_t)r * D, s);
   }
   launch_scatter_kv(dK, dV, lens, B, P_cap, S, Hq, Hkv, D, dqkv, ki ? nullptr : dkvp, s);
+  // the VLM side (side stream): through the prefix K/V, or nothing with knowledge insulation
+  TRY(fork(5));
+  if (ki) {
+    if (G.vlm_attn_norm) launch_fill(G.vlm_attn_norm, Hv, 0.f, s2);
+    if (G.vlm_w_qkv) launch_fill(G.vlm_w_qkv, (long)QKV * Hv, 0.f, s2);
+    if (G.h_prefix) launch_fill(G.h_prefix, (long)Mp * Hv, 0.f, s2);
+  } else {
+    launch_rope_rows(dkvp, Mp, P_cap, KV2, 0, Hkv, D, base, lens, false, -1.0f, s2);
+    launch_fill(G.vlm_w_qkv, (long)HqD * Hv, 0.f, s2);  // the query rows do not reach the loss
+    mm_on(s2, KV2, Hv, Mp, cols(KV2), DT_F32, dkvp, cols(Hv), DT_F32, np_, G.vlm_w_qkv + (size_t)HqD * Hv, Hv);
+    mm_on(s2, Mp, Hv, KV2, rows(KV2), DT_F32, dkvp, cols(Hv), dt, wv_kv, dnp, Hv);
+    if (G.h_prefix) launch_rms_bwd(h_prefix, DT_F32, gv, dnp, rp, nullptr, Mp, Hv, G.h_prefix, s2);
+    launch_colsum(dnp, h_prefix, rp, Mp, Hv, G.vlm_attn_norm, cpart2, s2);
+  }
+  HIP_TRY(hipEventRecord(ev[6], s2));
   launch_rope_rows(dqkv, M, S, QKV, 0, Hq + Hkv, D, base, lens, true, -1.0f, s);
   // Q/K/V projection and the attention pre-norm
   mm(QKV, Ha, M, cols(QKV), DT_F32, dqkv, cols(Ha), DT_F32, n1, G.w_qkv, Ha);
@@ -1282,19 +1321,7 @@ dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm, const
   // action_in_proj
   mm(Ha, A, M, cols(Ha), DT_F32, dh0, cols(A), DT_F32, x, G.w_in, A);
   colsum(dh0, nullptr, nullptr, M, Ha, G.b_in);
-  // the VLM side: through the prefix K/V, or nothing with knowledge insulation
-  if (ki) {
-    if (G.vlm_attn_norm) launch_fill(G.vlm_attn_norm, Hv, 0.f, s);
-    if (G.vlm_w_qkv) launch_fill(G.vlm_w_qkv, (long)QKV * Hv, 0.f, s);
-    if (G.h_prefix) launch_fill(G.h_prefix, (long)Mp * Hv, 0.f, s);
-  } else {
-    launch_rope_rows(dkvp, Mp, P_cap, KV2, 0, Hkv, D, base, lens, false, -1.0f, s);
-    launch_fill(G.vlm_w_qkv, (long)HqD * Hv, 0.f, s);  // the query rows do not reach the loss
-    mm(KV2, Hv, Mp, cols(KV2), DT_F32, dkvp, cols(Hv), DT_F32, np_, G.vlm_w_qkv + (size_t)HqD * Hv, Hv);
-    mm(Mp, Hv, KV2, rows(KV2), DT_F32, dkvp, cols(Hv), dt, wv_kv, dnp, Hv);
-    if (G.h_prefix) launch_rms_bwd(h_prefix, DT_F32, gv, dnp, rp, nullptr, Mp, Hv, G.h_prefix, s);
-    colsum(dnp, h_prefix, rp, Mp, Hv, G.vlm_attn_norm);
-  }
+  HIP_TRY(hipStreamWaitEvent(s, ev[6], 0));  // join the side stream
   HIP_TRY(hipGetLastError());
   return DM_OK;
 }
