@@ -149,12 +149,14 @@ void attn_split(int B, int Hkv, int nqb, int max_keys, int *n_chunks, int *chunk
 // projections) also split K until ~256 workgroups.
 // Each wave of the skinny kernel holds its whole K slice in registers: at most 8 MFMA k-chunks,
 // otherwise K is split further (residual projections) or the tiled kernel is used.
+constexpr int kSkinnyMaxRows = 128;  // the skinny kernel over several row blocks up to this many rows
+
 GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
   GemmPlan p{};
   p.sk.k_split = 1;
   p.skinny = 0;
   p.nt = 0;  // the tiled kernel
-  if (M > 64) {
+  if (M > kSkinnyMaxRows) {
     // bf16: 128-row tiles, 256 columns when that still gives >= 128 workgroups, else 128; narrow
     // GEMMs take 64 columns, or split K (multiples of 64) until ~200 workgroups.
     if (dt != DT_BF16 || N % 128 != 0 || K % 64 != 0) return p;
@@ -185,21 +187,25 @@ GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
         p.sk.k_split *= 2;
     return p;
   }
+  // Up to 64 rows one row block; more rows (small batches above one sample) take several row
+  // blocks of 16 * rt rows (grid.z), each workgroup re-reading its weight slice, which the
+  // workgroups of one column slice (same XCD) find in L2.
   const int kq = gemm_k_quantum(dt);  // K per k-chunk across the 4 waves
-  if (split_ok && N % 16 == 0 && K % (4 * kq) == 0 && K / (4 * kq) <= 8 && (N / 16) * ((M + 15) / 16) >= 128) {
-    // residual projections: 16 waves per workgroup cover the whole K of 16 columns x 16 rows,
-    // enough workgroups without a K split, so the residual epilogue runs in the same launch
-    // (batch 1, O: 7.7 -> 6.7 us in isolation, one launch fewer)
+  auto blocks = [&](int rows) { return (M + rows - 1) / rows; };
+  if (split_ok && N % 16 == 0 && K % (4 * kq) == 0 && K / (4 * kq) <= 8 && (N / 16) * blocks(16) >= 128) {
+    // residual projections: 16 waves per workgroup cover the whole K of 16 columns x 16 (or 32)
+    // rows, enough workgroups without a K split, so the residual epilogue runs in the same
+    // launch (batch 1, O: 7.7 -> 6.7 us in isolation, one launch fewer)
     p.skinny = 1;
     p.nt = 16;
-    p.rt = 1;
+    p.rt = (N / 16) * blocks(16) <= 256 ? 1 : 2;
     p.nw = 16;
     return p;
   }
   const int nt = N % 32 == 0 ? 32 : 16;
   int ks = 1;
   if (split_ok) {
-    while ((N / nt) * ks < 256 && ks < 16 && K % (2 * ks * kq) == 0) ks *= 2;
+    while ((N / nt) * ks * blocks(64) < 256 && ks < 16 && K % (2 * ks * kq) == 0) ks *= 2;
     while (K / (ks * kq) > 8 && ks < 16 && K % (2 * ks * kq) == 0) ks *= 2;
   }
   if (K % (ks * kq) != 0 || K / (ks * kq) > 8) return p;
@@ -208,7 +214,7 @@ GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
   p.sk.k_split = ks;
   // half-height workgroups when twice as many still fit the 256 CUs in one round: each reads
   // half the activation rows, and twice the CUs pull the weights (QKV at batch 1: 9.2 -> 7.5 us)
-  if (M > 32 && (size_t)(N / nt) * ks * ((M + 31) / 32) <= 256) p.rt = 2;
+  if (M > 32 && (size_t)(N / nt) * ks * blocks(32) <= 256) p.rt = 2;
   return p;
 }
 

@@ -12,8 +12,8 @@
 // by 1/sqrt(mean(h^2) + eps), which is RMSNorm(h) W^T up to the rounding of hg.
 //
 // Three kernels share the epilogues:
-//  * skinny (M <= 64, the batch-1 action chunk): one workgroup owns NT output columns for 64
-//    (or 32) rows and one K slice; its 4 waves each take a quarter of the slice and load MFMA fragments
+//  * skinny (few rows: the action chunk of one or two samples): one workgroup owns NT output
+//    columns for 64 (or 32 / 16) rows and one K slice, more rows taking more row blocks; its 4 waves each take a quarter of the slice and load MFMA fragments
 //    straight from global memory (16 bytes per lane, the whole slice in flight at once), then
 //    reduce through LDS.  Narrow-N GEMMs also split K across workgroups: each writes an fp32 partial
 //    tile and a second launch (resid_reduce_kernel) sums them in split order and runs the
@@ -396,7 +396,7 @@ template <typename T, typename W = T> struct EpiSwiglu {
   }
 };
 
-// ------------------------------------------------------------------------ skinny kernel (M <= 64)
+// ------------------------------------------------------------------------ skinny kernel (few rows)
 // NK: MFMA k-chunks per wave; every fragment of the workgroup's slice is loaded before the first
 // MFMA, so each wave keeps NK*(CT+RT) 16-byte loads per lane in flight.
 // RT: 16-row tiles per workgroup (4, or 2 / 1 to spread a narrow GEMM over more workgroups,

@@ -77,7 +77,7 @@ struct SwigluArgs {
 
 // Tile plan of one GEMM launch, chosen by the host.
 struct GemmPlan {
-  int skinny;   // 1: M <= 64 kernel (K split across waves and workgroups), 0: large-tile or tiled kernel
+  int skinny;   // 1: skinny kernel (M <= 128 in row blocks; K split across waves and workgroups), 0: large-tile or tiled kernel
   int nt;       // skinny: output columns per workgroup (16, 32 or 64); large-tile kernel: 64, 128,
                 // 256 or 384 columns per tile; 0: the tiled kernel
   SplitK sk;
