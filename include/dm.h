@@ -312,7 +312,10 @@ typedef struct {
  * h_prefix [B][P_cap][Hv], actions / noise / mask [B][S][A] (mask 0 or 1), t [B]: float32.
  * Arithmetic is float32 (bf16 weights are widened exactly); the model must have neither
  * DM_FLAG_TIME_MODULATION nor DM_FLAG_QK_NORM (else DM_ERR_UNSUPPORTED).  ws: at least
- * dm_workspace_bytes(ctx, DM_OP_TRAIN, B, P_cap) bytes. */
+ * dm_workspace_bytes(ctx, DM_OP_TRAIN, B, P_cap) bytes.  Like dm_merged_layer, the call runs its
+ * independent parts (the prefix K/V projection, the MLP and O weight gradients, the prefix
+ * backward) on the context's side stream, forked from and joined back into `stream`; calls on
+ * one context from several host threads at once must be serialised. */
 dm_status dm_train_merged_layer(dm_ctx *ctx, const dm_expert_weights *vlm /* (host) */,
                                 const dm_action_weights *aw /* (host) */, int layer,
                                 const float *h_prefix, const int32_t *prefix_lens, int B, int P_cap,
