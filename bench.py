@@ -72,12 +72,27 @@ def algorithmic(wl, lens):
             "weight_bytes_per_step": mat * es + vec, "kv_bytes_per_step": kv}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, aw, kc, vc, x1, lens):
     """The oracle as it stands (float64 numpy), one full chunk of sample 0."""
     import oracle as O
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas_threads = max([i.get("num_threads", 1) for i in libs] or [1])
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}, {blas_threads} threads"
     except Exception:
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
@@ -87,7 +102,23 @@ def cpu_baseline(wl, aw, kc, vc, x1, lens):
     dt = time.perf_counter() - t0
     return {"value": 1.0 / dt, "unit": "chunks/s", "cores": blas_threads or cores, "kind": "oracle",
             "sample": f"one full chunk of sample 0 ({wl.steps} Euler steps x {wl.shape.n_layers} layers, "
-                      f"P={P}) in float64 numpy; {dt:.2f} s on {cores} host cores"}
+                      f"P={P}) in float64 numpy; {dt:.2f} s on {cores} host cores",
+            "cpu": cpu_model(), "numpy": np.__version__, "blas": blas}
+
+
+def environment():
+    """The GPU and software the numbers were taken on."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+            "memory_gib": round(props.total_memory / 2**30, 1), "rocm": rocm, "hip": torch.version.hip,
+            "torch": torch.__version__, "host_cpu": cpu_model()}
 
 
 SOURCES = ["dm_api.cpp", "gemm.hip", "attn.hip", "misc.hip", "persist.hip", "train.hip", "common.h", "kernels.h", "persist_plan.h",
@@ -776,6 +807,7 @@ def main():
                    "euler_steps": wl.steps, "layers": s.n_layers, "parallelism": "single GPU"},
         "latency_ms": latency(res["lat"]),
         "roofline": roof,
+        "env": environment(),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
