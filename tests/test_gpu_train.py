@@ -101,6 +101,49 @@ def test_train_step_dm0_base_one_layer_bf16(ki, lens):
     _compare(wl, vlm, aw, tb, 0, ki, 1e-4, 1e-4)
 
 
+@pytest.mark.timeout(600)
+def test_train_step_results_ordered_on_the_callers_stream():
+    """The step forks part of its work (the prefix K/V projection, the MLP and O weight gradients,
+    the prefix backward) onto the context's side stream and joins it back: copies enqueued on the
+    caller's stream right after the call see every gradient finished (each starts as NaN), two
+    calls give the same bits, and both equal the values after a device-wide synchronisation."""
+    wl = workload(2)
+    print("case: training step, DM0-base one layer, B=1, P=816, read on the caller's (non-default) stream", flush=True)
+    s = wl.shape
+    vlm, aw, tb = inputs.make_vlm_weights(wl), inputs.make_action_weights(wl), inputs.make_train_batch(wl)
+    ctx = bd.Context(s, 0)
+    dvlm, daw = bd.DeviceExpert(vlm, s.dtype), bd.DeviceAction(aw, s.dtype)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    args = (dev(tb.h_pre), dev_lens(tb.lens), dev(tb.a), dev(tb.eps), dev(tb.t), dev(tb.mask))
+    shapes = {"w_qkv": aw.body.w_qkv.shape[1:], "w_o": aw.body.w_o.shape[1:], "w_gate": aw.body.w_gate.shape[1:],
+              "w_up": aw.body.w_up.shape[1:], "w_down": aw.body.w_down.shape[1:], "attn_norm": aw.body.attn_norm.shape[1:],
+              "mlp_norm": aw.body.mlp_norm.shape[1:], "w_in": aw.w_in.shape, "b_in": aw.b_in.shape,
+              "final_norm": aw.final_norm.shape, "w_out": aw.w_out.shape, "b_out": aw.b_out.shape,
+              "vlm_attn_norm": vlm.attn_norm.shape[1:], "vlm_w_qkv": vlm.w_qkv.shape[1:], "h_prefix": tb.h_pre.shape}
+    ws = ctx.workspace(bd.OP_TRAIN, 1, tb.h_pre.shape[1])
+    st = torch.cuda.Stream()
+    snaps = []
+    for _ in range(2):
+        grads = {n: torch.full(tuple(shp), float("nan"), dtype=torch.float32, device="cuda") for n, shp in shapes.items()}
+        loss = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            ctx.train_merged_layer(dvlm, daw, 0, *args, False, loss, grads, ws, stream=st)
+            snap = {n: g.clone() for n, g in grads.items()}  # same stream, right after the call
+            snap["loss"] = loss.clone()
+        st.synchronize()
+        torch.cuda.synchronize()
+        for n, t in snap.items():
+            assert not torch.isnan(t).any(), n
+            final = loss if n == "loss" else grads[n]
+            assert torch.equal(t, final), n
+        snaps.append({n: t.cpu() for n, t in snap.items()})
+    for n in snaps[0]:
+        assert torch.equal(snaps[0][n], snaps[1][n]), n
+    ctx.close()
+    print("training step: results complete on the caller's stream, two calls bitwise equal", flush=True)
+
+
 def test_train_step_empty_mask_and_argument_checks():
     wl = dataclasses.replace(workload(1), batch=2, prefix_len=16, ragged=(1, 16))
     print("case: training step, empty mask and argument checks", flush=True)
