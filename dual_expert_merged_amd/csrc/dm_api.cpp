@@ -185,6 +185,22 @@ GemmPlan plan_gemm(Dt dt, int M, int N, int K, bool split_ok) {
       while ((N / p.nt) * mt * p.sk.k_split < 200 && p.sk.k_split < 8 && K % (2 * p.sk.k_split * 64) == 0 &&
              K / (2 * p.sk.k_split) >= 256)
         p.sk.k_split *= 2;
+    // a few hundred rows (batches of 3 to 8): 128-row tiles leave most CUs idle; 64 x 128 tiles
+    // make twice the workgroups, each streaming three quarters of the bytes
+    const long wg = (long)(N / p.nt) * mt * p.sk.k_split;
+    if (wg < 160) {
+      GemmPlan q = p;
+      q.bm = 64;
+      q.nt = 128;
+      q.sk.k_split = 1;
+      const int mt64 = (M + 63) / 64;
+      if (split_ok)
+        while ((N / 128) * mt64 * q.sk.k_split < 200 && q.sk.k_split < 8 && K % (2 * q.sk.k_split * 64) == 0 &&
+               K / (2 * q.sk.k_split) >= 256)
+          q.sk.k_split *= 2;
+      const long wg64 = (long)(N / 128) * mt64 * q.sk.k_split;
+      if (wg64 > wg && wg64 <= 256) return q;
+    }
     return p;
   }
   // Up to 64 rows one row block; more rows (small batches above one sample) take several row

@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(ResidArgs a, const fl
 }
 
 // ------------------------------------------------------------------------ big kernel (M > 64)
-// Workgroup tile 128 x BN (BN = 128, 256 or 384) or 256 x 256; NW waves as WM x WN (8 as 2 x 4,
+// Workgroup tile 128 x BN (BN = 128, 256 or 384), 256 x 256 or 64 x 128; NW waves as WM x WN (8 as 2 x 4,
 // or 4 x 2 for 256 rows), each (BM/WM) x (BN/WN), i.e. several MFMA 16x16 tiles, so every LDS
 // fragment read feeds several MFMAs, and several waves per SIMD (one LDS-bound workgroup per
 // CU) hide each other's LDS and barrier waits.  Each k-step moves 128 bytes of every row (64
@@ -732,16 +732,17 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
   if constexpr (Epi::kTile && EB == 2) {
     if (epi.tile_ok(BN)) {  // uniform
       // stage the finished tile in LDS (the k-step buffers are free now), then store whole rows;
-      // 128 rows per pass (a 256-row tile takes two, each staged by the waves that own its rows)
-      constexpr int LD = BN + 8;
+      // up to 128 rows per pass (a 256-row tile takes two, each staged by the waves that own its
+      // rows; a 64-row tile one pass of 64)
+      constexpr int LD = BN + 8, PR = BM < 128 ? BM : 128;
       static_assert(64 * LD * 2 <= STAGE, "half a pass fits in one stage buffer");
-      static_assert(BM % 128 == 0 && (BM / WM) <= 128, "a wave's rows lie in one pass");
+      static_assert(BM % PR == 0 && (BM / WM) <= PR, "a wave's rows lie in one pass");
       const TileRows<bf16, LD> ot{reinterpret_cast<bf16 *>(big_buf<STAGE, 0>()), reinterpret_cast<bf16 *>(big_buf<STAGE, 1>())};
-      static_for<0, BM / 128>([&](auto P) {
+      static_for<0, BM / PR>([&](auto P) {
         constexpr int pass = decltype(P)::value;
-        const int pm0 = m0 + pass * 128;
+        const int pm0 = m0 + pass * PR;
         if constexpr (pass > 0) __syncthreads();  // the previous pass's rows are stored
-        if (wm * (BM / WM) / 128 == pass) {  // uniform per wave
+        if (wm * (BM / WM) / PR == pass) {  // uniform per wave
           // the epilogue's loads of row tile i+1 go out before row tile i is processed, so only
           // the first ones are waited for
           typename Epi::St st[2][TN];
@@ -758,11 +759,11 @@ __global__ __launch_bounds__(NW * 64) void big_kernel(const Op *__restrict__ A, 
 #pragma unroll
             for (int j = 0; j < TN; j += 2)
               epi.to_lds2(st[i & 1][j], st[i & 1][j + 1], row0, n0 + wn * (BN / WN) + j * 16 + c16, acc[i][j],
-                          acc[i][j + 1], rinv + pass * 128, pm0, n0, ot);
+                          acc[i][j + 1], rinv + pass * PR, pm0, n0, ot);
           }
         }
         __syncthreads();
-        epi.template lds_out<128, BN>(ot, pm0, n0, M);
+        epi.template lds_out<PR, BN>(ot, pm0, n0, M);
       });
       return;
     }
@@ -811,6 +812,18 @@ static void run_big(const Op *A, int M, int N, int K, const Epi &epi, int nt, in
       dim3 grid(nN, nM, sk.k_split);
       hipLaunchKernelGGL((big_kernel<Op, 64, 4, NW, 4, 128, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM,
                          group_m(128, nM));
+      return;
+    }
+  }
+  if constexpr (sizeof(Op) == 2) {
+    if (bm == 64) {  // 64-row tiles for a few hundred rows: twice the workgroups of 128-row ones
+      const int nM = (M + 63) / 64;
+      dim3 grid(nN, nM, sk.k_split);
+      const int gm = group_m(64, nM);
+      if (nt == 256)  // 40 KB stages, three buffers
+        hipLaunchKernelGGL((big_kernel<Op, 256, 3, NW, WM, 64, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM, gm);
+      else  // 24 KB stages, four buffers
+        hipLaunchKernelGGL((big_kernel<Op, 128, 4, NW, WM, 64, Epi>), grid, dim3(NW * 64), 0, s, A, M, K, epi, sk, nN, nM, gm);
       return;
     }
   }
